@@ -1,0 +1,386 @@
+"""Pins for the fp64 oracle: page-printed examples, closed forms, invariants, a
+library routine (torch's fp64 scaled_dot_product_attention) and brute force.
+
+The last group plants plausible mistakes into copies of the oracle and checks
+that the pins catch each one."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import paged_attention as opa
+
+torch = pytest.importorskip("torch")
+F = torch.nn.functional
+
+NAN = 0x7FC0
+
+
+# ---------------------------------------------------------------------------
+# helpers: pools written by the layout definition, independent of the oracle
+# ---------------------------------------------------------------------------
+def bf16(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.bfloat16) \
+        .view(torch.int16).numpy().view(np.uint16)
+
+
+def empty_pools(nb, Hkv, D, B):
+    k = np.full((nb, Hkv, D // 8, B, 8), NAN, dtype=np.uint16)
+    v = np.full((nb, Hkv, B // 4, D, 4), NAN, dtype=np.uint16)
+    return k, v
+
+
+def write_token(kp, vp, blk, off, kvec, vvec):
+    """Layout definition: K (blk,h,t,d) at [blk,h,d//8,t,d%8]; V at [blk,h,t//4,d,t%4]."""
+    Hkv, D = kvec.shape
+    for h in range(Hkv):
+        for d in range(D):
+            kp[blk, h, d // 8, off, d % 8] = kvec[h, d]
+            vp[blk, h, off // 4, d, off % 4] = vvec[h, d]
+
+
+def paged_case(seed, lens, Hq, Hkv, D, B, *, extra_blocks=3, k_override=None, v_override=None):
+    """Logical per-sequence K/V (bf16 bits) placed at random physical blocks."""
+    rng = np.random.default_rng(seed)
+    nblk = [(L + B - 1) // B for L in lens]
+    nb = sum(nblk) + extra_blocks
+    perm = rng.permutation(nb)
+    kp, vp = empty_pools(nb, Hkv, D, B)
+    W = max(1, max(nblk))
+    bt = np.full((len(lens), W), -1, dtype=np.int32)
+    Ks, Vs = [], []
+    pos = 0
+    for s, L in enumerate(lens):
+        bt[s, :nblk[s]] = perm[pos:pos + nblk[s]]
+        pos += nblk[s]
+        K = bf16(rng.standard_normal((L, Hkv, D)))
+        V = bf16(rng.standard_normal((L, Hkv, D)))
+        if k_override is not None:
+            K = k_override(s, L, K)
+        if v_override is not None:
+            V = v_override(s, L, V)
+        for t in range(L):
+            write_token(kp, vp, bt[s, t // B], t % B, K[t], V[t])
+        Ks.append(K)
+        Vs.append(V)
+    q = bf16(rng.standard_normal((len(lens), Hq, D)))
+    return dict(q=q, kp=kp, vp=vp, bt=bt, lens=np.array(lens, dtype=np.int32), K=Ks, V=Vs, B=B)
+
+
+def sdpa_reference(case, scale):
+    """torch fp64 SDPA on the logical contiguous K/V (a library routine)."""
+    q = oracle.bf16_bits_to_f64(case["q"])
+    S, Hq, D = q.shape
+    out = np.zeros((S, Hq, D))
+    for s in range(S):
+        L = int(case["lens"][s])
+        if L == 0:
+            continue
+        K = torch.from_numpy(oracle.bf16_bits_to_f64(case["K"][s]).transpose(1, 0, 2).copy())[None]
+        V = torch.from_numpy(oracle.bf16_bits_to_f64(case["V"][s]).transpose(1, 0, 2).copy())[None]
+        Q = torch.from_numpy(q[s])[None, :, None, :]
+        o = F.scaled_dot_product_attention(Q, K, V, scale=scale, enable_gqa=True)
+        out[s] = o[0, :, 0, :].numpy()
+    return out
+
+
+def run_decode(case, scale, fn=None):
+    fn = fn or oracle.paged_decode
+    return fn(case["q"], case["kp"], case["vp"], case["bt"], case["lens"], scale, case["B"])
+
+
+SHAPES = [
+    # (lens, Hq, Hkv, D, B)
+    ([1, 17, 100, 40], 8, 2, 64, 16),
+    ([33, 7, 64], 4, 4, 128, 8),
+    ([70, 5], 16, 2, 64, 32),
+    ([129], 3, 1, 64, 16),
+]
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversions
+# ---------------------------------------------------------------------------
+def test_bf16_roundtrip_exhaustive():
+    bits = np.arange(2 ** 16, dtype=np.uint32).astype(np.uint16)
+    x = oracle.bf16_bits_to_f64(bits)
+    keep = ~np.isnan(x)
+    assert np.array_equal(oracle.f64_to_bf16_bits_rne(x[keep]), bits[keep])
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(200000), rng.standard_normal(1000) * 1e-39,
+                        [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.f64_to_bf16_bits_rne(x.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------------------
+# append
+# ---------------------------------------------------------------------------
+def test_append_page_example_roundtrip():
+    """50 tokens, B = 16, block table [7, 23, 4, 19] ("PagedAttention from First
+    Principles", section 5): appending token t at slot table[t//16]*16 + t%16
+    and walking the table gives the tokens back, in order, and touches nothing else."""
+    B, Hkv, D = 16, 2, 64
+    table = [7, 23, 4, 19]
+    kp, vp = empty_pools(24, Hkv, D, B)
+    rng = np.random.default_rng(5)
+    kp[:] = rng.integers(0, 2 ** 15, size=kp.shape, dtype=np.uint16)
+    vp[:] = rng.integers(0, 2 ** 15, size=vp.shape, dtype=np.uint16)
+    k0, v0 = kp.copy(), vp.copy()
+    K = bf16(rng.standard_normal((50, Hkv, D)))
+    V = bf16(rng.standard_normal((50, Hkv, D)))
+    slots = np.array([table[t // B] * B + t % B for t in range(50)], dtype=np.int64)
+    oracle.cache_append(K, V, slots, kp, vp, B)
+    Kc, Vc = oracle.gather_sequence(kp, vp, np.array(table + [-1] * 3), 50, B)
+    assert np.array_equal(Kc, oracle.bf16_bits_to_f64(K).transpose(1, 0, 2))
+    assert np.array_equal(Vc, oracle.bf16_bits_to_f64(V).transpose(1, 0, 2))
+    untouched = [b for b in range(24) if b not in table]
+    assert np.array_equal(kp[untouched], k0[untouched]) and np.array_equal(vp[untouched], v0[untouched])
+    # block 19 holds tokens 48, 49 only: slots 2..15 unchanged
+    assert np.array_equal(kp[19][:, :, 2:, :], k0[19][:, :, 2:, :])
+    for t in range(2, 16):
+        assert np.array_equal(vp[19][:, t // 4, :, t % 4], v0[19][:, t // 4, :, t % 4])
+
+
+def test_append_is_a_bijection_and_skips_negative_slots():
+    B, Hkv, D, nb = 8, 2, 64, 5
+    kp, vp = empty_pools(nb, Hkv, D, B)
+    T = nb * B
+    vals = np.arange(T * Hkv * D, dtype=np.uint32).astype(np.uint16).reshape(T, Hkv, D)
+    order = np.random.default_rng(2).permutation(T)
+    oracle.cache_append(vals, vals, order.astype(np.int64), kp, vp, B)
+    assert len(np.unique(kp)) == kp.size and len(np.unique(vp)) == vp.size
+    k_before = kp.copy()
+    oracle.cache_append(vals[:3] ^ 1, vals[:3] ^ 1, np.array([-1, -1, -1]), kp, vp, B)
+    assert np.array_equal(kp, k_before)
+
+
+# ---------------------------------------------------------------------------
+# decode: library routine and closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", SHAPES)
+def test_decode_matches_torch_sdpa(shape):
+    lens, Hq, Hkv, D, B = shape
+    case = paged_case(11, lens, Hq, Hkv, D, B)
+    scale = 1.0 / math.sqrt(D)
+    ours = run_decode(case, scale)
+    assert np.abs(ours - sdpa_reference(case, scale)).max() <= 1e-12
+
+
+def test_context_len_one_returns_v0_exactly():
+    case = paged_case(12, [1, 1, 1], 8, 2, 64, 16)
+    out = run_decode(case, 0.125)
+    for s in range(3):
+        v0 = oracle.bf16_bits_to_f64(case["V"][s][0])          # [Hkv, D]
+        assert np.array_equal(out[s], np.repeat(v0, 4, axis=0))
+
+
+def test_identical_keys_give_mean_of_values():
+    same_k = lambda s, L, K: np.broadcast_to(K[:1], K.shape).copy()
+    case = paged_case(13, [37, 5], 8, 2, 64, 16, k_override=same_k)
+    out = run_decode(case, 0.125)
+    for s in range(2):
+        mean_v = oracle.bf16_bits_to_f64(case["V"][s]).mean(axis=0)
+        assert np.abs(out[s] - np.repeat(mean_v, 4, axis=0)).max() <= 1e-14
+
+
+def test_two_token_closed_form():
+    """Scores 0 and ln 3 give weights 1/4 and 3/4."""
+    D, B = 64, 8
+    kp, vp = empty_pools(2, 1, D, B)
+    q = np.zeros((1, 1, D), dtype=np.uint16)
+    q[0, 0, 0] = bf16([1.0])[0]
+    k = np.zeros((2, 1, D), dtype=np.float64)
+    k[1, 0, 0] = 1.0
+    v = np.zeros((2, 1, D))
+    v[0, 0, :] = 1.0
+    v[1, 0, :] = -2.0
+    for t in range(2):
+        write_token(kp, vp, 1, t, bf16(k[t]), bf16(v[t]))
+    scale = math.log(3.0)
+    out = oracle.paged_decode(q, kp, vp, np.array([[1]], dtype=np.int32), np.array([2]), scale, B)
+    assert np.abs(out[0, 0] - (0.25 * 1.0 + 0.75 * -2.0)).max() <= 1e-15
+
+
+def test_zero_query_averages_and_gqa_head_mapping():
+    """q = 0 gives uniform weights; V constant per KV head c_g gives out[h] = c_{h // G}."""
+    Hq, Hkv, D, B = 8, 4, 64, 16
+    const_v = lambda s, L, V: np.broadcast_to(
+        bf16(np.arange(1, Hkv + 1, dtype=np.float32))[None, :, None], V.shape).copy()
+    case = paged_case(14, [23, 9], Hq, Hkv, D, B, v_override=const_v)
+    case["q"][:] = 0
+    out = run_decode(case, 0.2)
+    G = Hq // Hkv
+    for h in range(Hq):
+        assert np.all(out[:, h, :] == float(h // G + 1))
+
+
+def test_empty_context_gives_zeros():
+    case = paged_case(15, [0, 12], 4, 2, 64, 16)
+    out = run_decode(case, 0.125)
+    assert np.all(out[0] == 0.0) and np.all(np.isfinite(out))
+
+
+def test_poison_beyond_context_is_never_read():
+    case = paged_case(16, [3, 18], 4, 2, 64, 16)       # tail slots hold NaN
+    out = run_decode(case, 0.125)
+    assert np.all(np.isfinite(out))
+
+
+def test_physical_block_permutation_invariance():
+    case = paged_case(17, [40, 77, 16], 8, 2, 128, 16, extra_blocks=5)
+    ref = run_decode(case, 0.1)
+    nb = case["kp"].shape[0]
+    perm = np.random.default_rng(9).permutation(nb)
+    kp2 = np.empty_like(case["kp"])
+    vp2 = np.empty_like(case["vp"])
+    kp2[perm] = case["kp"]
+    vp2[perm] = case["vp"]
+    bt2 = np.where(case["bt"] >= 0, perm[np.maximum(case["bt"], 0)], -1).astype(np.int32)
+    out = oracle.paged_decode(case["q"], kp2, vp2, bt2, case["lens"], 0.1, 16)
+    assert np.array_equal(out, ref)
+
+
+# ---------------------------------------------------------------------------
+# the pages' other formulations agree with the textbook one
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("shape", SHAPES)
+def test_online_and_eq4_match_textbook(shape):
+    lens, Hq, Hkv, D, B = shape
+    case = paged_case(21, lens, Hq, Hkv, D, B)
+    scale = 1.0 / math.sqrt(D)
+    ref = run_decode(case, scale)
+    assert np.abs(run_decode(case, scale, oracle.paged_decode_online) - ref).max() <= 1e-12
+    assert np.abs(run_decode(case, scale, oracle.paged_decode_eq4) - ref).max() <= 1e-12
+
+
+@pytest.mark.parametrize("part", [16, 64, 512])
+def test_split_lse_combine_matches_textbook(part):
+    case = paged_case(22, [1100, 513, 64], 8, 2, 64, 16)
+    scale = 0.125
+    q = oracle.bf16_bits_to_f64(case["q"])
+    for s in range(3):
+        K, V = oracle.gather_sequence(case["kp"], case["vp"], case["bt"][s], case["lens"][s], 16)
+        ref = oracle.attention_textbook(q[s], K, V, scale)
+        parts = oracle.split_partials(q[s], K, V, scale, part)
+        assert len(parts) == -(-int(case["lens"][s]) // part)
+        assert np.abs(oracle.combine_partials(parts) - ref).max() <= 1e-12
+
+
+def test_brute_force_tiny():
+    """Scalar loops with math.exp against the vectorized oracle."""
+    lens, Hq, Hkv, D, B = [3, 9, 1], 4, 2, 64, 8
+    case = paged_case(23, lens, Hq, Hkv, D, B)
+    scale = 0.37
+    out = run_decode(case, scale)
+    q = oracle.bf16_bits_to_f64(case["q"])
+    G = Hq // Hkv
+    for s, L in enumerate(lens):
+        K = oracle.bf16_bits_to_f64(case["K"][s])
+        V = oracle.bf16_bits_to_f64(case["V"][s])
+        for h in range(Hq):
+            g = h // G
+            sc = [scale * sum(q[s, h, d] * K[t, g, d] for d in range(D)) for t in range(L)]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            z = sum(w)
+            for d in range(D):
+                ref = sum(w[t] * V[t, g, d] for t in range(L)) / z
+                assert abs(out[s, h, d] - ref) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin above
+# ---------------------------------------------------------------------------
+def _pins_pass(decode_fn):
+    """Run the decode pins against ``decode_fn``; False if any fails."""
+    try:
+        for shape in SHAPES[:3]:
+            lens, Hq, Hkv, D, B = shape
+            case = paged_case(11, lens, Hq, Hkv, D, B)
+            scale = 1.0 / math.sqrt(D)
+            out = run_decode(case, scale, decode_fn)
+            if not (np.abs(out - sdpa_reference(case, scale)).max() <= 1e-12):
+                return False
+        return True
+    except (KeyError, IndexError, ValueError, FloatingPointError):
+        return False
+
+
+def test_pins_pass_on_the_real_oracle():
+    assert _pins_pass(oracle.paged_decode)
+
+
+def test_pins_catch_wrong_gqa_mapping(monkeypatch):
+    def bad(q, K, V, scale):
+        Hq, D = q.shape
+        Hkv = K.shape[0]
+        out = np.zeros((Hq, D))
+        for h in range(Hq):
+            g = h % Hkv
+            s = scale * (K[g] @ q[h])
+            p = np.exp(s - s.max())
+            out[h] = (p @ V[g]) / p.sum()
+        return out
+    monkeypatch.setattr(opa, "attention_textbook", bad)
+    assert not _pins_pass(opa.paged_decode)
+
+
+def test_pins_catch_ignored_scale(monkeypatch):
+    real = opa.attention_textbook
+    monkeypatch.setattr(opa, "attention_textbook", lambda q, K, V, scale: real(q, K, V, 1.0))
+    assert not _pins_pass(opa.paged_decode)
+
+
+def test_pins_catch_unmasked_tail(monkeypatch):
+    real = opa._read_block
+    monkeypatch.setattr(opa, "_read_block",
+                        lambda k, v, phys, valid: real(k, v, phys, np.asarray(k[int(phys)]).shape[2]))
+    assert not _pins_pass(opa.paged_decode)
+
+
+def test_pins_catch_transposed_v_layout(monkeypatch):
+    def bad(k_cache, v_cache, phys, valid):
+        kb = np.asarray(k_cache[int(phys)])
+        vb = np.asarray(v_cache[int(phys)])
+        Hkv, d8, B, _ = kb.shape
+        D = d8 * 8
+        k = kb[:, :, :valid, :].transpose(0, 2, 1, 3).reshape(Hkv, valid, D)
+        v = vb.transpose(0, 3, 1, 2).reshape(Hkv, B, D)[:, :valid, :]     # t%4 major: wrong
+        return oracle.bf16_bits_to_f64(k), oracle.bf16_bits_to_f64(v)
+    monkeypatch.setattr(opa, "_read_block", bad)
+    assert not _pins_pass(opa.paged_decode)
+
+
+def test_pins_catch_dropped_rescale():
+    def bad(q_bits, k_cache, v_cache, block_tables, context_lens, scale, block_size):
+        # online loop that forgets to rescale the accumulator when the max grows
+        q = oracle.bf16_bits_to_f64(q_bits)
+        S, Hq, D = q.shape
+        B = int(block_size)
+        out = np.zeros((S, Hq, D))
+        Hkv = np.asarray(k_cache[0]).shape[0]
+        G = Hq // Hkv
+        for s in range(S):
+            L = int(context_lens[s])
+            m = np.full(Hq, -np.inf)
+            l = np.zeros(Hq)
+            acc = np.zeros((Hq, D))
+            for i in range((L + B - 1) // B):
+                valid = min(i * B + B, L) - i * B
+                k, v = opa._read_block(k_cache, v_cache, block_tables[s][i], valid)
+                for h in range(Hq):
+                    sc = scale * (k[h // G] @ q[s, h])
+                    mn = max(m[h], sc.max())
+                    p = np.exp(sc - mn)
+                    l[h] = np.exp(m[h] - mn) * l[h] + p.sum()
+                    acc[h] = acc[h] + p @ v[h // G]
+                    m[h] = mn
+            out[s] = acc / l[:, None]
+        return out
+    assert not _pins_pass(bad)
