@@ -1,0 +1,212 @@
+"""Benchmark of one paged-decode layer step on one MI355X: slot-mapped append of
+this step's K/V, then paged decode attention (with its fused split-K combine).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  ``value`` is effective KV-read GB/s of the whole step
+(sum_s L_s * Hkv * D * 2 (K and V) * 2 bytes, divided by the event-timed
+append + decode time).  Inputs are resident in HBM; before every timed step a
+1 GiB buffer is written so that neither L2 nor the 256 MB Infinity Cache
+still holds the pools (the flush is outside the timed region).  ``roofline``
+is the decode kernel alone against 8 TB/s.  ``cpu_baseline`` is the fp64
+oracle on a bounded sample of the same workload, on this host's CPU.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_CONFIG = "llama3_8b_b64"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    return ap.parse_args()
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    k = (len(xs) - 1) * q / 100.0
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def cpu_baseline(w, budget_s):
+    """Time the fp64 oracle (append + decode) on a growing prefix of sequences."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+
+    order = list(range(w.num_seqs))
+    kst, vst = w.stores()
+    t_total, tokens, done = 0.0, 0, 0
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        for s in order:
+            t0 = time.perf_counter()
+            oracle.cache_append(w.k_new[s:s + 1], w.v_new[s:s + 1], w.slot_mapping[s:s + 1], kst, vst,
+                                w.block_size)
+            oracle.paged_decode(w.q, kst, vst, w.block_tables, w.context_lens, w.scale, w.block_size,
+                                seqs=[s])
+            t_total += time.perf_counter() - t0
+            tokens += int(w.context_lens[s])
+            done += 1
+            if t_total >= budget_s:
+                break
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    kv_bytes = tokens * w.num_kv_heads * w.head_dim * 2 * 2
+    return {
+        "value": round(kv_bytes / t_total / 1e9, 6),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "seqs_per_s": round(done / t_total, 4),
+        "sample": f"first {done} of {w.num_seqs} sequences ({tokens} context tokens), fp64 numpy "
+                  f"oracle append + decode, one BLAS thread, {t_total:.1f} s",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path shards by sequence or KV head with no exchange, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+    from paged_kv_cache_122_amd import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pa.load()
+    torch.cuda.set_device(0)
+
+    w = workloads.make(args.config)
+    dw = dev.upload(w, "cuda:0")
+    out = torch.empty_like(dw.q)
+    eff_bytes = w.effective_kv_bytes()
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
+        pa.decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                  w.block_size)
+
+    for _ in range(args.warmup):
+        flush.zero_()
+        step()
+    torch.cuda.synchronize()
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E(), E()) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        flush.zero_()
+        e0.record()
+        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
+        e1.record()
+        pa.decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                  w.block_size)
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    append_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    decode_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+
+    # back-to-back steps without the flush (caches may hold part of the pools)
+    hot = [(E(), E()) for _ in range(args.steps)]
+    for a, b in hot:
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    hot_ms = [a.elapsed_time(b) for a, b in hot]
+
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    t_step = mean(step_ms) / 1e3
+    t_dec = mean(decode_ms) / 1e3
+    value = eff_bytes / t_step / 1e9
+    achieved = eff_bytes / t_dec / 1e9
+    line = {
+        "metric": "paged decode-attention effective KV GB/s vs HBM peak; seqs/s per layer-step",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean(step_ms), 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "num_seqs": w.num_seqs,
+            "num_q_heads": w.num_q_heads,
+            "num_kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim,
+            "block_size": w.block_size,
+            "num_blocks": w.num_blocks,
+            "context_tokens": int(w.context_lens.sum()),
+            "max_context_len": int(w.context_lens.max()),
+            "effective_kv_bytes": eff_bytes,
+            "seed": w.seed,
+            "step": "pa_cache_append + pa_decode (fused split-K combine), caches flushed before each step",
+        },
+        "seqs_per_s": round(w.num_seqs / t_step, 1),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "decode_ms": {"mean": round(mean(decode_ms), 5), "p10": round(percentile(decode_ms, 10), 5),
+                      "p50": round(percentile(decode_ms, 50), 5),
+                      "p90": round(percentile(decode_ms, 90), 5)},
+        "append_ms": {"mean": round(mean(append_ms), 5), "p50": round(percentile(append_ms, 50), 5)},
+        "unflushed_step_ms": {"mean": round(mean(hot_ms), 5), "p50": round(percentile(hot_ms, 50), 5),
+                              "gbs": round(eff_bytes / (mean(hot_ms) / 1e3) / 1e9, 2)},
+        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode (pa_decode: decode_mfma with fused combine)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

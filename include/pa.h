@@ -1,0 +1,172 @@
+/*
+ * pa.h -- C ABI of libpa: PagedAttention decode for AMD MI355X (gfx950).
+ *
+ * Two operations, as the PagedAttention pages describe them:
+ *
+ *   pa_cache_append  writes each new token's K and V into the slot of the
+ *                    block pool that the host block manager assigned to it
+ *                    ("vLLM - PagedAttention" digest (hungchun0201), "Fused
+ *                    CUDA Kernels", item 1: fused reshape and block write;
+ *                    "PagedAttention from First Principles", section 2: the
+ *                    cache is append-only).
+ *   pa_decode        one query per sequence attends to the sequence's cached
+ *                    tokens, reached through its block table, with an online
+ *                    softmax across blocks ("PagedAttention from First
+ *                    Principles", section 5; Equation 4 of the hungchun0201
+ *                    digest, "Mathematical Formulation").  Long contexts are
+ *                    split into partitions whose partial softmax results are
+ *                    combined by a log-sum-exp reduce ("PagedAttention from
+ *                    First Principles", section 17, the v2 kernel's reduce).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor is device memory owned by the caller (for instance allocated
+ *   by PyTorch) and described by a pa_tensor: element strides, not bytes.
+ *   The library keeps no pointer after a call returns.
+ * - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *   returns without waiting.  A status code covers argument validation and
+ *   launch errors only; pa_last_error() gives the message.  No entry point
+ *   throws, aborts or prints.
+ * - Device-side contracts are preconditions that are checked only in debug
+ *   mode (pa_set_debug): block-table entries read by a sequence lie in
+ *   [0, num_blocks); 0 <= context_lens[s] <= table_width * block_size; the
+ *   slots of one append call are distinct and lie in [-1, num_blocks*B).
+ *
+ * Cache layout (one pool per K and per V, per layer)
+ * --------------------------------------------------
+ *   k_cache: bf16 [num_blocks, num_kv_heads, head_dim/8, block_size, 8]
+ *            token t, dim d of block b, head h at [b, h, d/8, t, d%8]
+ *   v_cache: bf16 [num_blocks, num_kv_heads, block_size/4, head_dim, 4]
+ *            token t, dim d of block b, head h at [b, h, t/4, d, t%4]
+ *   Both fully contiguous.  One (block, head) tile is block_size*head_dim
+ *   contiguous elements.  A slot is block*block_size + offset.
+ *   Supported: head_dim in {64, 128}; block_size in {8, 16, 32}.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,     /* bad argument: null pointer, shape, dtype, stride */
+  PA_ERR_UNSUPPORTED = -2, /* valid but not implemented (head_dim, block_size, path) */
+  PA_ERR_HIP = -3,         /* a HIP runtime call failed */
+  PA_ERR_WORKSPACE = -4,   /* workspace missing or too small */
+  PA_ERR_CONTRACT = -5     /* debug mode: a device-side precondition is violated */
+};
+
+/* element types */
+enum { PA_BF16 = 1, PA_F32 = 2, PA_I32 = 3, PA_I64 = 4 };
+
+#define PA_MAX_DIMS 5
+
+typedef struct {
+  void* data;                   /* device pointer (may be NULL only if numel == 0) */
+  int32_t dtype;                /* PA_BF16, PA_F32, PA_I32, PA_I64 */
+  int32_t ndim;                 /* 1 .. PA_MAX_DIMS */
+  int64_t shape[PA_MAX_DIMS];
+  int64_t stride[PA_MAX_DIMS];  /* in elements */
+} pa_tensor;
+
+/*
+ * pa_cache_append -- slot-mapped write of this step's K/V into the pools.
+ *
+ *   k, v          bf16 [T, num_kv_heads, head_dim]; last dim contiguous, every
+ *                 row 16-byte aligned (row strides multiple of 8 elements).
+ *   slot_mapping  int64 [T]; token i goes to slot slot_mapping[i]
+ *                 (block = slot / B, offset = slot % B); a negative slot skips
+ *                 the token (padding).
+ *   k_cache, v_cache  the pools, layout above; written in place.
+ *
+ * Bit-exact copy.  No other slot of the pools is touched.  T == 0 is a no-op.
+ */
+int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping,
+                    pa_tensor* k_cache, pa_tensor* v_cache, hipStream_t stream);
+
+/*
+ * pa_decode -- paged decode attention, one query token per sequence.
+ *
+ *   out           bf16 (rounded to nearest even) or f32 [S, num_q_heads, head_dim],
+ *                 last dim contiguous.
+ *   q             bf16 [S, num_q_heads, head_dim], last dim contiguous.
+ *   k_cache, v_cache  the pools (read only).
+ *   block_tables  int32 [S, W]; row s lists the physical blocks of sequence s
+ *                 in logical order; only the first ceil(L_s / B) entries are
+ *                 read, the rest may hold any sentinel (-1 by convention).
+ *   context_lens  int32 [S]; L_s tokens, this step's token included.
+ *   scale         multiplies q.k (1/sqrt(head_dim) for standard attention).
+ *   block_size    must equal the pools' block size.
+ *
+ * out[s, h, :] = softmax_t(scale * q[s,h,:] . K[s,t,:]) V[s,t,:] over t < L_s,
+ * with query head h reading KV head h / (num_q_heads / num_kv_heads).  An empty
+ * context (L_s == 0) yields zeros.  Tokens at t >= L_s are never read, so
+ * their values (even NaN) cannot affect the result.  bf16 products, fp32
+ * accumulation; results are bitwise deterministic.
+ *
+ * Long contexts are split into partitions of 512 tokens whose partial results
+ * are combined in ascending partition order.  The partial results live in a
+ * library-owned workspace on the current device, grown with hipMalloc when a
+ * call needs more (never during stream capture: that returns PA_ERR_WORKSPACE;
+ * use pa_decode_ex there).  Calls that need the workspace may not overlap on
+ * one device from different host threads unless they are on the same stream.
+ */
+int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+              const pa_tensor* v_cache, const pa_tensor* block_tables,
+              const pa_tensor* context_lens, float scale, int32_t block_size,
+              hipStream_t stream);
+
+/* options for pa_decode_ex; a zero-initialised struct means "as pa_decode" */
+typedef struct {
+  int32_t partition_tokens; /* 0: 512; -1: never split; else a positive multiple of 32 */
+  int32_t path;             /* 0: auto (MFMA when q heads per KV head >= 3, else VALU);
+                               1: force the VALU path (q heads per KV head <= 2);
+                               2: force the MFMA path */
+  int64_t max_context_len;  /* 0: table width * block_size; else an upper bound on
+                               every context_lens[s], used to size the launch */
+} pa_decode_opts;
+
+/* Bytes of workspace pa_decode_ex needs for these sizes (0 when nothing is split). */
+size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                                 int64_t head_dim, int64_t max_context_len,
+                                 int32_t partition_tokens);
+
+/*
+ * pa_decode_ex -- pa_decode with options and a caller-owned workspace.
+ *
+ * `workspace` is device memory of at least pa_decode_workspace_bytes(...)
+ * bytes, 256-byte aligned, zero-filled before its first use; every call leaves
+ * it ready for the next one.  It must not be shared by calls that may run
+ * concurrently.  Nothing is allocated, so the call may be captured into a
+ * HIP graph.  workspace may be NULL when the required size is 0.
+ */
+int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                 const pa_tensor* v_cache, const pa_tensor* block_tables,
+                 const pa_tensor* context_lens, float scale, int32_t block_size,
+                 const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                 hipStream_t stream);
+
+/* Message of the last failed call on this thread (valid until the next pa_* call). */
+const char* pa_last_error(void);
+
+/*
+ * Debug mode (process-wide, off by default).  When on, pa_cache_append and
+ * pa_decode copy the index tensors to the host, synchronise `stream`, and
+ * check the device-side contracts listed above before launching; a violation
+ * returns PA_ERR_CONTRACT.  Returns the previous setting.
+ */
+int pa_set_debug(int on);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

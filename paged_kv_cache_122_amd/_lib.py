@@ -1,0 +1,162 @@
+"""ctypes binding of libpa.so (include/pa.h).  Argument marshalling only:
+torch tensors become pa_tensor descriptors, torch's current stream becomes the
+hipStream_t, status codes become exceptions.  Every step of the computation runs
+in the library's HIP kernels; there is no fallback.
+
+libpa.so must be loaded after ``import torch`` so that it binds to the HIP
+runtime torch already loaded (both carry the soname libamdhip64.so.7).
+"""
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_CONTRACT = 0, -1, -2, -3, -4, -5
+PA_BF16, PA_F32, PA_I32, PA_I64 = 1, 2, 3, 4
+MAX_DIMS = 5
+
+EXPORTED = ("pa_cache_append", "pa_decode", "pa_decode_ex", "pa_decode_workspace_bytes",
+            "pa_last_error", "pa_set_debug")
+
+_DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.int32: PA_I32, torch.int64: PA_I64}
+
+
+class PaTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * MAX_DIMS), ("stride", ctypes.c_int64 * MAX_DIMS)]
+
+
+class PaDecodeOpts(ctypes.Structure):
+    _fields_ = [("partition_tokens", ctypes.c_int32), ("path", ctypes.c_int32),
+                ("max_context_len", ctypes.c_int64)]
+
+
+class PaError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"libpa error {code}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load(path=None):
+    """Load libpa.so (once).  Raises if it is missing: there is no fallback."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing; build it with `python -m paged_kv_cache_122_amd.build`")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(PaTensor)
+    lib.pa_cache_append.argtypes = [P, P, P, P, P, ctypes.c_void_p]
+    lib.pa_cache_append.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_ex.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32,
+                                 ctypes.POINTER(PaDecodeOpts), ctypes.c_void_p, ctypes.c_size_t,
+                                 ctypes.c_void_p]
+    lib.pa_decode_ex.restype = ctypes.c_int
+    lib.pa_decode_workspace_bytes.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32]
+    lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_last_error.argtypes = []
+    lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_set_debug.argtypes = [ctypes.c_int]
+    lib.pa_set_debug.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def describe(t):
+    """pa_tensor for a torch tensor (no copy; the tensor must outlive the call)."""
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    if t.dim() > MAX_DIMS or t.dim() < 1:
+        raise ValueError("tensor rank must be 1..5")
+    d = PaTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    return d
+
+
+def _device_tensor(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    return t
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(lib, rc):
+    if rc != PA_OK:
+        raise PaError(rc, lib.pa_last_error().decode())
+
+
+def cache_append(k, v, slot_mapping, k_cache, v_cache, stream=None):
+    """pa_cache_append: write k/v [T, Hkv, D] (bf16) at slot_mapping [T] (int64)."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in ((k, "k"), (v, "v"), (slot_mapping, "slot_mapping"),
+                                           (k_cache, "k_cache"), (v_cache, "v_cache"))]
+    ds = [describe(x) for x in ts]
+    _check(lib, lib.pa_cache_append(*[ctypes.byref(d) for d in ds], _stream(stream)))
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None):
+    """pa_decode: out [S, Hq, D] (bf16 or f32) = paged attention of q [S, Hq, D]."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),
+                                           (v_cache, "v_cache"), (block_tables, "block_tables"),
+                                           (context_lens, "context_lens"))]
+    ds = [describe(x) for x in ts]
+    _check(lib, lib.pa_decode(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
+                              ctypes.c_int32(block_size), _stream(stream)))
+
+
+def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                    partition_tokens=0):
+    return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, partition_tokens))
+
+
+def alloc_workspace(nbytes, device):
+    """Zero-filled device workspace for decode_ex (a uint8 tensor; 256-byte aligned)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, *,
+              partition_tokens=0, path=0, max_context_len=0, workspace=None, stream=None):
+    """pa_decode_ex: decode with options and a caller-owned workspace."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),
+                                           (v_cache, "v_cache"), (block_tables, "block_tables"),
+                                           (context_lens, "context_lens"))]
+    ds = [describe(x) for x in ts]
+    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib, lib.pa_decode_ex(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
+                                 ctypes.c_int32(block_size), ctypes.byref(opts),
+                                 ctypes.c_void_p(ws_ptr) if ws_ptr else None,
+                                 ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def set_debug(on):
+    return bool(load().pa_set_debug(1 if on else 0))

@@ -1,0 +1,463 @@
+// Host side of libpa: argument validation, split-K planning, workspace
+// management, debug-mode contract checks and kernel launches.  Implements the
+// C ABI declared in include/pa.h.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
+
+#include "pa.h"
+#include "pa_internal.h"
+
+#define PA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_error;
+std::atomic<int> g_debug{0};
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+const char* dtype_name(int dt) {
+  switch (dt) {
+    case PA_BF16: return "bf16";
+    case PA_F32: return "f32";
+    case PA_I32: return "i32";
+    case PA_I64: return "i64";
+  }
+  return "unknown";
+}
+
+int64_t numel(const pa_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+// Basic descriptor sanity: dtype, rank, non-negative shape, data present.
+int check_desc(const pa_tensor* t, const char* name, int dtype, int ndim) {
+  if (!t) return fail(PA_ERR_INVALID, "%s: descriptor is NULL", name);
+  if (t->dtype != dtype)
+    return fail(PA_ERR_INVALID, "%s: dtype %s, expected %s", name, dtype_name(t->dtype),
+                dtype_name(dtype));
+  if (t->ndim != ndim) return fail(PA_ERR_INVALID, "%s: %d dims, expected %d", name, t->ndim, ndim);
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0 || t->stride[i] < 0)
+      return fail(PA_ERR_INVALID, "%s: negative shape or stride in dim %d", name, i);
+  if (!t->data && numel(t) > 0) return fail(PA_ERR_INVALID, "%s: data pointer is NULL", name);
+  return PA_OK;
+}
+
+bool is_contiguous(const pa_tensor* t) {
+  int64_t expect = 1;
+  for (int i = t->ndim - 1; i >= 0; --i) {
+    if (t->shape[i] != 1 && t->stride[i] != expect) return false;
+    expect *= t->shape[i];
+  }
+  return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct CacheGeom {
+  int64_t num_blocks, kv_heads, head_dim, block_size;
+};
+
+// Validate the two pools against the documented layout.
+int check_caches(const pa_tensor* kc, const pa_tensor* vc, CacheGeom* g) {
+  int rc;
+  if ((rc = check_desc(kc, "k_cache", PA_BF16, 5)) != PA_OK) return rc;
+  if ((rc = check_desc(vc, "v_cache", PA_BF16, 5)) != PA_OK) return rc;
+  const int64_t nb = kc->shape[0], hkv = kc->shape[1], d8 = kc->shape[2], bs = kc->shape[3];
+  if (kc->shape[4] != 8)
+    return fail(PA_ERR_INVALID, "k_cache: last dim %lld, expected 8 (layout [NB,Hkv,D/8,B,8])",
+                (long long)kc->shape[4]);
+  const int64_t d = d8 * 8;
+  if (vc->shape[0] != nb || vc->shape[1] != hkv || vc->shape[2] * 4 != bs || vc->shape[3] != d ||
+      vc->shape[4] != 4)
+    return fail(PA_ERR_INVALID,
+                "v_cache: shape [%lld,%lld,%lld,%lld,%lld] does not match k_cache "
+                "(expected [NB,Hkv,B/4,D,4] = [%lld,%lld,%lld,%lld,4])",
+                (long long)vc->shape[0], (long long)vc->shape[1], (long long)vc->shape[2],
+                (long long)vc->shape[3], (long long)vc->shape[4], (long long)nb, (long long)hkv,
+                (long long)(bs / 4), (long long)d);
+  if (!is_contiguous(kc) || !is_contiguous(vc))
+    return fail(PA_ERR_INVALID, "k_cache/v_cache must be contiguous");
+  if (d != 64 && d != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (supported: 64, 128)", (long long)d);
+  if (bs != 8 && bs != 16 && bs != 32)
+    return fail(PA_ERR_UNSUPPORTED, "block_size %lld (supported: 8, 16, 32)", (long long)bs);
+  if (hkv <= 0) return fail(PA_ERR_INVALID, "num_kv_heads must be positive");
+  if (nb > 0 && (!aligned16(kc->data) || !aligned16(vc->data)))
+    return fail(PA_ERR_INVALID, "k_cache/v_cache must be 16-byte aligned");
+  g->num_blocks = nb;
+  g->kv_heads = hkv;
+  g->head_dim = d;
+  g->block_size = bs;
+  return PA_OK;
+}
+
+// Rows of a [T, H, D] bf16 tensor must be contiguous and 16-byte aligned.
+int check_rows(const pa_tensor* t, const char* name) {
+  if (t->stride[2] != 1 && t->shape[2] > 1)
+    return fail(PA_ERR_INVALID, "%s: last dim must be contiguous", name);
+  if (numel(t) > 0 && (!aligned16(t->data) || (t->stride[0] % 8) || (t->stride[1] % 8)))
+    return fail(PA_ERR_INVALID, "%s: rows must be 16-byte aligned (strides multiple of 8)", name);
+  return PA_OK;
+}
+
+template <typename T>
+int copy_to_host(std::vector<T>* dst, const void* src, size_t n, hipStream_t stream) {
+  dst->resize(n);
+  if (n == 0) return PA_OK;
+  hipError_t e = hipMemcpyAsync(dst->data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "debug copy to host");
+  return PA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// library-owned decode workspace, one per device
+// ---------------------------------------------------------------------------
+struct OwnedWorkspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mutex;
+std::unordered_map<int, OwnedWorkspace> g_ws;
+
+int owned_workspace(size_t need, hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  OwnedWorkspace& w = g_ws[dev];
+  if (w.bytes < need) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(PA_ERR_WORKSPACE,
+                  "pa_decode needs %zu workspace bytes but may not allocate during stream "
+                  "capture; use pa_decode_ex with a caller-owned workspace",
+                  need);
+    if (w.ptr) {
+      e = hipFree(w.ptr);  // synchronises the device: no queued kernel still uses it
+      w.ptr = nullptr;
+      w.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+    }
+    const size_t bytes = need + need / 4;
+    e = hipMalloc(&w.ptr, bytes);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+    e = hipMemsetAsync(w.ptr, 0, bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
+    w.bytes = bytes;
+  }
+  *out = w.ptr;
+  return PA_OK;
+}
+
+struct DecodePlan {
+  int64_t S, Hq, Hkv, D, B, W, NB;
+  int part_tokens, max_parts;
+  pa::Path path;
+  pa::WorkspaceLayout ws;
+};
+
+int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                const pa_tensor* v_cache, const pa_tensor* block_tables,
+                const pa_tensor* context_lens, int32_t block_size, const pa_decode_opts* opts,
+                DecodePlan* pl) {
+  int rc;
+  CacheGeom g;
+  if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
+  if ((rc = check_desc(q, "q", PA_BF16, 3)) != PA_OK) return rc;
+  if (!out) return fail(PA_ERR_INVALID, "out: descriptor is NULL");
+  if (out->dtype != PA_BF16 && out->dtype != PA_F32)
+    return fail(PA_ERR_INVALID, "out: dtype %s, expected bf16 or f32", dtype_name(out->dtype));
+  if ((rc = check_desc(out, "out", out->dtype, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(block_tables, "block_tables", PA_I32, 2)) != PA_OK) return rc;
+  if ((rc = check_desc(context_lens, "context_lens", PA_I32, 1)) != PA_OK) return rc;
+
+  const int64_t S = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  if (D != g.head_dim)
+    return fail(PA_ERR_INVALID, "q: head_dim %lld, caches have %lld", (long long)D, (long long)g.head_dim);
+  if (out->shape[0] != S || out->shape[1] != Hq || out->shape[2] != D)
+    return fail(PA_ERR_INVALID, "out: shape does not match q");
+  if (block_size != g.block_size)
+    return fail(PA_ERR_INVALID, "block_size %d does not match the caches' %lld", block_size,
+                (long long)g.block_size);
+  if (Hq <= 0 || Hq % g.kv_heads)
+    return fail(PA_ERR_INVALID, "num_q_heads %lld is not a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)g.kv_heads);
+  if (block_tables->shape[0] != S || context_lens->shape[0] != S)
+    return fail(PA_ERR_INVALID, "block_tables/context_lens: first dim must be num_seqs %lld", (long long)S);
+  const int64_t W = block_tables->shape[1];
+  if (W < 1) return fail(PA_ERR_INVALID, "block_tables: width must be >= 1");
+  if (block_tables->stride[1] != 1 || block_tables->stride[0] < W)
+    return fail(PA_ERR_INVALID, "block_tables: rows must be contiguous with row stride >= width");
+  if (context_lens->stride[0] != 1 && S > 1)
+    return fail(PA_ERR_INVALID, "context_lens must be contiguous");
+  if ((rc = check_rows(q, "q")) != PA_OK) return rc;
+  if (out->stride[2] != 1 && D > 1) return fail(PA_ERR_INVALID, "out: last dim must be contiguous");
+  if (S > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %lld > 65535", (long long)S);
+
+  const int64_t G = Hq / g.kv_heads;
+  const int want = opts ? opts->path : 0;
+  pa::Path path;
+  if (want == 0)
+    path = G >= 3 ? pa::Path::Mfma : pa::Path::Valu;
+  else if (want == 1)
+    path = pa::Path::Valu;
+  else if (want == 2)
+    path = pa::Path::Mfma;
+  else
+    return fail(PA_ERR_INVALID, "opts.path %d (expected 0, 1 or 2)", want);
+  if (path == pa::Path::Valu && G > 2)
+    return fail(PA_ERR_UNSUPPORTED, "the VALU path takes 1 or 2 query heads per KV head, not %lld",
+                (long long)G);
+
+  int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : W * g.block_size;
+  if (opts && opts->max_context_len < 0) return fail(PA_ERR_INVALID, "opts.max_context_len < 0");
+  const int pt_opt = opts ? opts->partition_tokens : 0;
+  int64_t part;
+  if (pt_opt == 0)
+    part = pa::kDefaultPartition;
+  else if (pt_opt == -1)
+    part = std::max<int64_t>(32, (max_len + 31) / 32 * 32);
+  else if (pt_opt > 0 && pt_opt % 32 == 0)
+    part = pt_opt;
+  else
+    return fail(PA_ERR_INVALID, "opts.partition_tokens %d (0, -1 or a positive multiple of 32)", pt_opt);
+  if (part > (int64_t(1) << 30)) return fail(PA_ERR_UNSUPPORTED, "partition too large");
+  const int64_t max_parts = std::max<int64_t>(1, (max_len + part - 1) / part);
+  if (max_parts > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "%lld partitions per sequence > 65535; raise partition_tokens",
+                (long long)max_parts);
+
+  pl->S = S;
+  pl->Hq = Hq;
+  pl->Hkv = g.kv_heads;
+  pl->D = D;
+  pl->B = g.block_size;
+  pl->W = W;
+  pl->NB = g.num_blocks;
+  pl->part_tokens = int(part);
+  pl->max_parts = int(max_parts);
+  pl->path = path;
+  pl->ws = pa::workspace_layout(S, Hq, g.kv_heads, D, max_parts);
+  if (max_parts == 1) pl->ws.total = 0;
+  return PA_OK;
+}
+
+int debug_check_decode(const DecodePlan& pl, const pa_tensor* block_tables,
+                       const pa_tensor* context_lens, int64_t max_len, hipStream_t stream) {
+  std::vector<int32_t> lens, bt;
+  int rc;
+  if ((rc = copy_to_host(&lens, context_lens->data, size_t(pl.S), stream)) != PA_OK) return rc;
+  const size_t rows = size_t(pl.S), stride = size_t(block_tables->stride[0]);
+  if ((rc = copy_to_host(&bt, block_tables->data, rows ? (rows - 1) * stride + size_t(pl.W) : 0, stream)) != PA_OK)
+    return rc;
+  for (int64_t s = 0; s < pl.S; ++s) {
+    const int64_t L = lens[s];
+    if (L < 0 || L > pl.W * pl.B)
+      return fail(PA_ERR_CONTRACT, "context_lens[%lld] = %lld outside [0, width*block_size = %lld]",
+                  (long long)s, (long long)L, (long long)(pl.W * pl.B));
+    if (L > max_len)
+      return fail(PA_ERR_CONTRACT, "context_lens[%lld] = %lld exceeds opts.max_context_len %lld",
+                  (long long)s, (long long)L, (long long)max_len);
+    const int64_t nblk = (L + pl.B - 1) / pl.B;
+    for (int64_t i = 0; i < nblk; ++i) {
+      const int64_t b = bt[size_t(s) * stride + size_t(i)];
+      if (b < 0 || b >= pl.NB)
+        return fail(PA_ERR_CONTRACT, "block_tables[%lld][%lld] = %lld outside [0, %lld)", (long long)s,
+                    (long long)i, (long long)b, (long long)pl.NB);
+    }
+  }
+  return PA_OK;
+}
+
+int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                  const pa_tensor* v_cache, const pa_tensor* block_tables,
+                  const pa_tensor* context_lens, float scale, int32_t block_size,
+                  const pa_decode_opts* opts, bool owned_ws, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  DecodePlan pl;
+  int rc = plan_decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size, opts, &pl);
+  if (rc != PA_OK) return rc;
+  if (pl.S == 0) return PA_OK;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale must be finite");
+  const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
+  if (g_debug.load() &&
+      (rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK)
+    return rc;
+
+  void* ws = nullptr;
+  if (pl.ws.total > 0) {
+    if (owned_ws) {
+      if ((rc = owned_workspace(pl.ws.total, stream, &ws)) != PA_OK) return rc;
+    } else {
+      if (!workspace || workspace_bytes < pl.ws.total)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
+                    pl.ws.total);
+      if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      ws = workspace;
+    }
+  }
+
+  pa::DecodeParams p{};
+  p.out = out->data;
+  p.out_s = out->stride[0];
+  p.out_h = out->stride[1];
+  p.out_f32 = out->dtype == PA_F32;
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.q_s = q->stride[0];
+  p.q_h = q->stride[1];
+  p.k_cache = static_cast<const uint16_t*>(k_cache->data);
+  p.v_cache = static_cast<const uint16_t*>(v_cache->data);
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.bt_s = block_tables->stride[0];
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.num_seqs = int(pl.S);
+  p.num_q_heads = int(pl.Hq);
+  p.num_kv_heads = int(pl.Hkv);
+  p.group = int(pl.Hq / pl.Hkv);
+  p.head_groups = pl.path == pa::Path::Mfma ? (p.group + 15) / 16 : 1;
+  p.scale_log2 = float(double(scale) * 1.4426950408889634);
+  p.part_tokens = pl.part_tokens;
+  p.max_parts = pl.max_parts;
+  if (ws) {
+    char* base = static_cast<char*>(ws);
+    p.ws_count = reinterpret_cast<int32_t*>(base + pl.ws.count_off);
+    p.ws_ml = reinterpret_cast<float*>(base + pl.ws.ml_off);
+    p.ws_o = reinterpret_cast<float*>(base + pl.ws.o_off);
+  }
+  const hipError_t e = pa::launch_decode(p, int(pl.D), int(pl.B), pl.path, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT const char* pa_last_error(void) { return g_error.c_str(); }
+
+PA_EXPORT int pa_set_debug(int on) { return g_debug.exchange(on ? 1 : 0); }
+
+PA_EXPORT size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads,
+                                           int64_t num_kv_heads, int64_t head_dim,
+                                           int64_t max_context_len, int32_t partition_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0)
+    return 0;
+  int64_t part;
+  if (partition_tokens == 0)
+    part = pa::kDefaultPartition;
+  else if (partition_tokens == -1)
+    return 0;
+  else if (partition_tokens > 0)
+    part = partition_tokens;
+  else
+    return 0;
+  const int64_t max_parts = std::max<int64_t>(1, (max_context_len + part - 1) / part);
+  if (max_parts == 1) return 0;
+  return pa::workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_parts).total;
+}
+
+PA_EXPORT int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                        const pa_tensor* v_cache, const pa_tensor* block_tables,
+                        const pa_tensor* context_lens, float scale, int32_t block_size,
+                        hipStream_t stream) {
+  g_error.clear();
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                       nullptr, true, nullptr, 0, stream);
+}
+
+PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                           const pa_tensor* v_cache, const pa_tensor* block_tables,
+                           const pa_tensor* context_lens, float scale, int32_t block_size,
+                           const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  g_error.clear();
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, opts,
+                       false, workspace, workspace_bytes, stream);
+}
+
+PA_EXPORT int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping,
+                              pa_tensor* k_cache, pa_tensor* v_cache, hipStream_t stream) {
+  g_error.clear();
+  int rc;
+  CacheGeom g;
+  if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
+  if ((rc = check_desc(k, "k", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(v, "v", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(slot_mapping, "slot_mapping", PA_I64, 1)) != PA_OK) return rc;
+  const int64_t T = k->shape[0];
+  if (k->shape[1] != g.kv_heads || k->shape[2] != g.head_dim)
+    return fail(PA_ERR_INVALID, "k: shape [T, %lld, %lld] expected", (long long)g.kv_heads,
+                (long long)g.head_dim);
+  if (v->shape[0] != T || v->shape[1] != g.kv_heads || v->shape[2] != g.head_dim)
+    return fail(PA_ERR_INVALID, "v: shape must equal k's");
+  if (slot_mapping->shape[0] != T)
+    return fail(PA_ERR_INVALID, "slot_mapping: %lld entries for %lld tokens",
+                (long long)slot_mapping->shape[0], (long long)T);
+  if (slot_mapping->stride[0] != 1 && T > 1) return fail(PA_ERR_INVALID, "slot_mapping must be contiguous");
+  if ((rc = check_rows(k, "k")) != PA_OK) return rc;
+  if ((rc = check_rows(v, "v")) != PA_OK) return rc;
+  if (T == 0) return PA_OK;
+  if (T > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+
+  if (g_debug.load()) {
+    std::vector<int64_t> slots;
+    if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(T), stream)) != PA_OK) return rc;
+    std::unordered_set<int64_t> seen;
+    const int64_t nslots = g.num_blocks * g.block_size;
+    for (int64_t i = 0; i < T; ++i) {
+      const int64_t sl = slots[size_t(i)];
+      if (sl < 0) continue;
+      if (sl >= nslots)
+        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld outside [0, %lld)", (long long)i,
+                    (long long)sl, (long long)nslots);
+      if (!seen.insert(sl).second)
+        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld repeats an earlier slot", (long long)i,
+                    (long long)sl);
+    }
+  }
+
+  pa::AppendParams p{};
+  p.k = static_cast<const uint16_t*>(k->data);
+  p.v = static_cast<const uint16_t*>(v->data);
+  p.k_t = k->stride[0];
+  p.k_h = k->stride[1];
+  p.v_t = v->stride[0];
+  p.v_h = v->stride[1];
+  p.slots = static_cast<const int64_t*>(slot_mapping->data);
+  p.k_cache = static_cast<uint16_t*>(k_cache->data);
+  p.v_cache = static_cast<uint16_t*>(v_cache->data);
+  p.num_tokens = int(T);
+  p.num_kv_heads = int(g.kv_heads);
+  const hipError_t e = pa::launch_append(p, int(g.head_dim), int(g.block_size), stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PA_OK;
+}

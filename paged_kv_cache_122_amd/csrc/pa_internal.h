@@ -1,0 +1,67 @@
+// Internal interface between the host API (pa_api.cpp) and the kernels
+// (pa_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace pa {
+
+// Tokens per MFMA row tile: every decode kernel walks the context 16 tokens
+// at a time (one block at B = 16, half a block at B = 32, two at B = 8).
+constexpr int kTileTokens = 16;
+constexpr int kWaves = 4;               // waves per decode workgroup
+constexpr int kDefaultPartition = 512;  // tokens per split-K partition
+
+enum class Path : int { Valu = 1, Mfma = 2 };
+
+struct DecodeParams {
+  // output [S, Hq, D]: bf16 (out_f32 == 0) or f32
+  void* out;
+  int64_t out_s, out_h;
+  int out_f32;
+  // query [S, Hq, D] bf16
+  const uint16_t* q;
+  int64_t q_s, q_h;
+  // pools
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  // block tables [S, W] int32, context lengths [S] int32
+  const int32_t* block_tables;
+  int64_t bt_s;
+  const int32_t* context_lens;
+  int num_seqs, num_q_heads, num_kv_heads;
+  int group;            // q heads per kv head (G)
+  int head_groups;      // ceil(G / 16) column groups per kv head on the MFMA path
+  float scale_log2;     // scale * log2(e)
+  int part_tokens;      // tokens per partition (multiple of 32)
+  int max_parts;        // partitions launched per sequence
+  // split-K workspace (unused when max_parts == 1)
+  float* ws_o;          // [S, Hq, max_parts, D]
+  float* ws_ml;         // [S, Hq, max_parts, 2]  (max in log2 units, sum)
+  int32_t* ws_count;    // [S, Hkv * head_groups], zero between calls
+};
+
+struct AppendParams {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_t, k_h, v_t, v_h;   // element strides of k, v rows
+  const int64_t* slots;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int num_tokens, num_kv_heads;
+};
+
+// Workspace layout shared by the host planner and the kernels.
+struct WorkspaceLayout {
+  size_t count_off, ml_off, o_off, total;
+};
+WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                                 int64_t head_dim, int64_t max_parts);
+
+hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, Path path,
+                         hipStream_t stream);
+hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,58 @@
+"""Device-side plumbing with torch: pool allocation in the library's layout
+and upload of a seeded workload.  No arithmetic on values."""
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import layout
+
+
+def bf16_tensor(bits, device):
+    """uint16 bf16 bit patterns (numpy) -> torch.bfloat16 tensor on ``device``."""
+    a = np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(a).view(torch.bfloat16).to(device)
+
+
+def bf16_bits(t):
+    """torch bf16 tensor -> uint16 numpy bit patterns (host copy)."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def alloc_pools(num_blocks, num_kv_heads, head_dim, block_size, device, fill=float("nan")):
+    """K and V pools in the library layout, every element set to ``fill``."""
+    k = torch.full(layout.k_cache_shape(num_blocks, num_kv_heads, head_dim, block_size), fill,
+                   dtype=torch.bfloat16, device=device)
+    v = torch.full(layout.v_cache_shape(num_blocks, num_kv_heads, head_dim, block_size), fill,
+                   dtype=torch.bfloat16, device=device)
+    return k, v
+
+
+@dataclass
+class DeviceWorkload:
+    q: torch.Tensor
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    slot_mapping: torch.Tensor
+    block_tables: torch.Tensor
+    context_lens: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    owned: torch.Tensor
+
+
+def upload(w, device="cuda"):
+    """Copy a workloads.Workload to the GPU: unowned pool blocks hold NaN."""
+    k_cache, v_cache = alloc_pools(w.num_blocks, w.num_kv_heads, w.head_dim, w.block_size, device)
+    owned = torch.from_numpy(w.owned).to(device)
+    if len(w.owned):
+        k_cache[owned] = bf16_tensor(w.k_blocks, device)
+        v_cache[owned] = bf16_tensor(w.v_blocks, device)
+    return DeviceWorkload(
+        q=bf16_tensor(w.q, device), k_new=bf16_tensor(w.k_new, device),
+        v_new=bf16_tensor(w.v_new, device),
+        slot_mapping=torch.from_numpy(w.slot_mapping).to(device),
+        block_tables=torch.from_numpy(w.block_tables).to(device),
+        context_lens=torch.from_numpy(w.context_lens).to(device),
+        k_cache=k_cache, v_cache=v_cache, owned=owned)
