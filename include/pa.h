@@ -143,8 +143,9 @@ size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t 
  * pa_decode_ex -- pa_decode with options and a caller-owned workspace.
  *
  * `workspace` is device memory of at least pa_decode_workspace_bytes(...)
- * bytes, 256-byte aligned, zero-filled before its first use; every call leaves
- * it ready for the next one.  It must not be shared by calls that may run
+ * bytes, 256-byte aligned, with any contents: when the context is split, the
+ * call first clears the workspace's counters with a small kernel on `stream`
+ * (two launches instead of one).  It must not be shared by calls that may run
  * concurrently.  Nothing is allocated, so the call may be captured into a
  * HIP graph.  workspace may be NULL when the required size is 0.
  */

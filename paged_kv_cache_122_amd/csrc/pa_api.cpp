@@ -140,42 +140,61 @@ int copy_to_host(std::vector<T>* dst, const void* src, size_t n, hipStream_t str
 // ---------------------------------------------------------------------------
 // library-owned decode workspace, one per device
 // ---------------------------------------------------------------------------
-struct OwnedWorkspace {
+// Two buffers per device.  The counter buffer only ever holds split-K counters:
+// it is zeroed when allocated and every decode leaves the counters it used at
+// zero, so it is all-zero at the start of every call whatever that call's
+// sizes.  (One shared buffer would not do: a later call with more counters
+// would find an earlier call's partial results where its counters live.)
+struct DeviceBuffer {
   void* ptr = nullptr;
   size_t bytes = 0;
+};
+struct OwnedWorkspace {
+  DeviceBuffer counters, data;
 };
 std::mutex g_ws_mutex;
 std::unordered_map<int, OwnedWorkspace> g_ws;
 
-int owned_workspace(size_t need, hipStream_t stream, void** out) {
+int grow(DeviceBuffer* b, size_t need, bool zero, hipStream_t stream) {
+  if (b->bytes >= need) return PA_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(stream, &cs);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode needs %zu more workspace bytes but may not allocate during stream "
+                "capture; use pa_decode_ex with a caller-owned workspace",
+                need);
+  if (b->ptr) {
+    e = hipFree(b->ptr);  // synchronises the device: no queued kernel still uses it
+    b->ptr = nullptr;
+    b->bytes = 0;
+    if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
+  }
+  const size_t bytes = (need + need / 4 + 255) & ~size_t(255);
+  e = hipMalloc(&b->ptr, bytes);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
+  if (zero) {
+    e = hipMemsetAsync(b->ptr, 0, bytes, stream);
+    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
+  }
+  b->bytes = bytes;
+  return PA_OK;
+}
+
+// Library-owned counters and partial-result storage for one call.
+int owned_workspace(const pa::WorkspaceLayout& lay, hipStream_t stream, void** counters,
+                    void** data) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_ws_mutex);
   OwnedWorkspace& w = g_ws[dev];
-  if (w.bytes < need) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    e = hipStreamIsCapturing(stream, &cs);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
-    if (cs != hipStreamCaptureStatusNone)
-      return fail(PA_ERR_WORKSPACE,
-                  "pa_decode needs %zu workspace bytes but may not allocate during stream "
-                  "capture; use pa_decode_ex with a caller-owned workspace",
-                  need);
-    if (w.ptr) {
-      e = hipFree(w.ptr);  // synchronises the device: no queued kernel still uses it
-      w.ptr = nullptr;
-      w.bytes = 0;
-      if (e != hipSuccess) return hip_fail(e, "hipFree(workspace)");
-    }
-    const size_t bytes = need + need / 4;
-    e = hipMalloc(&w.ptr, bytes);
-    if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-    e = hipMemsetAsync(w.ptr, 0, bytes, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
-    w.bytes = bytes;
-  }
-  *out = w.ptr;
+  int rc;
+  if ((rc = grow(&w.counters, lay.ml_off - lay.count_off, true, stream)) != PA_OK) return rc;
+  if ((rc = grow(&w.data, lay.total - lay.ml_off, false, stream)) != PA_OK) return rc;
+  *counters = w.counters.ptr;
+  *data = w.data.ptr;
   return PA_OK;
 }
 
@@ -314,17 +333,28 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
       (rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK)
     return rc;
 
-  void* ws = nullptr;
+  char* counters = nullptr;  // split-K counters, all zero when the decode starts
+  char* data = nullptr;      // partial results: (max, sum) at data, outputs at data + o_off - ml_off
   if (pl.ws.total > 0) {
     if (owned_ws) {
-      if ((rc = owned_workspace(pl.ws.total, stream, &ws)) != PA_OK) return rc;
+      void *c, *d;
+      if ((rc = owned_workspace(pl.ws, stream, &c, &d)) != PA_OK) return rc;
+      counters = static_cast<char*>(c);
+      data = static_cast<char*>(d);
     } else {
       if (!workspace || workspace_bytes < pl.ws.total)
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                     pl.ws.total);
       if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-      ws = workspace;
+      // A caller's buffer may have held another call's partial results where this
+      // call's counters go: clear them with a kernel (no memset node, so the call
+      // stays capturable).
+      counters = static_cast<char*>(workspace) + pl.ws.count_off;
+      data = static_cast<char*>(workspace) + pl.ws.ml_off;
+      const size_t n = (pl.ws.ml_off - pl.ws.count_off) / sizeof(int32_t);
+      const hipError_t ez = pa::launch_zero(reinterpret_cast<int32_t*>(counters), n, stream);
+      if (ez != hipSuccess) return hip_fail(ez, "counter clear launch");
     }
   }
 
@@ -349,11 +379,10 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   p.scale_log2 = float(double(scale) * 1.4426950408889634);
   p.part_tokens = pl.part_tokens;
   p.max_parts = pl.max_parts;
-  if (ws) {
-    char* base = static_cast<char*>(ws);
-    p.ws_count = reinterpret_cast<int32_t*>(base + pl.ws.count_off);
-    p.ws_ml = reinterpret_cast<float*>(base + pl.ws.ml_off);
-    p.ws_o = reinterpret_cast<float*>(base + pl.ws.o_off);
+  if (counters) {
+    p.ws_count = reinterpret_cast<int32_t*>(counters);
+    p.ws_ml = reinterpret_cast<float*>(data);
+    p.ws_o = reinterpret_cast<float*>(data + (pl.ws.o_off - pl.ws.ml_off));
   }
   const hipError_t e = pa::launch_decode(p, int(pl.D), int(pl.B), pl.path, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

@@ -63,5 +63,7 @@ WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, Path path,
                          hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
+// n int32 zeros at p, written by a kernel (capturable; no memset node)
+hipError_t launch_zero(int32_t* p, size_t n, hipStream_t stream);
 
 }  // namespace pa

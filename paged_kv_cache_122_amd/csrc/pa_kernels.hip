@@ -33,6 +33,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "pa_internal.h"
 
 namespace pa {
@@ -537,6 +539,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 }
 
+__global__ __launch_bounds__(256) void zero_kernel(int32_t* p, size_t n) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
+    p[i] = 0;
+}
+
 template <int D, int BS>
 hipError_t launch_decode_t(const DecodeParams& p, Path path, hipStream_t stream) {
   const dim3 block(kThreads);
@@ -590,6 +597,13 @@ hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hi
   if (head_dim == 64) return launch_append_d<64>(p, block_size, stream);
   if (head_dim == 128) return launch_append_d<128>(p, block_size, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero(int32_t* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const unsigned blocks = unsigned(std::min<size_t>((n + 255) / 256, 1024));
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
 }
 
 }  // namespace pa
