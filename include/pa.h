@@ -113,7 +113,8 @@ int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slo
  * accumulation; results are bitwise deterministic.
  *
  * Long contexts are split into partitions of 512 tokens whose partial results
- * are combined in ascending partition order.  The partial results live in a
+ * a second kernel combines in ascending partition order (one launch when the
+ * table width allows no split, two otherwise).  The partial results live in a
  * library-owned workspace on the current device, grown with hipMalloc when a
  * call needs more (never during stream capture: that returns PA_ERR_WORKSPACE;
  * use pa_decode_ex there).  Calls that need the workspace may not overlap on
@@ -143,11 +144,11 @@ size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t 
  * pa_decode_ex -- pa_decode with options and a caller-owned workspace.
  *
  * `workspace` is device memory of at least pa_decode_workspace_bytes(...)
- * bytes, 256-byte aligned, with any contents: when the context is split, the
- * call first clears the workspace's counters with a small kernel on `stream`
- * (two launches instead of one).  It must not be shared by calls that may run
- * concurrently.  Nothing is allocated, so the call may be captured into a
- * HIP graph.  workspace may be NULL when the required size is 0.
+ * bytes, 256-byte aligned, with any contents (it only carries partial results
+ * from the decode kernel to the combine kernel of the same call).  It must not
+ * be shared by calls that may run concurrently.  Nothing is allocated, so the
+ * call may be captured into a HIP graph.  workspace may be NULL when the
+ * required size is 0.
  */
 int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
                  const pa_tensor* v_cache, const pa_tensor* block_tables,

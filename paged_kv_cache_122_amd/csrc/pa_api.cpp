@@ -140,22 +140,17 @@ int copy_to_host(std::vector<T>* dst, const void* src, size_t n, hipStream_t str
 // ---------------------------------------------------------------------------
 // library-owned decode workspace, one per device
 // ---------------------------------------------------------------------------
-// Two buffers per device.  The counter buffer only ever holds split-K counters:
-// it is zeroed when allocated and every decode leaves the counters it used at
-// zero, so it is all-zero at the start of every call whatever that call's
-// sizes.  (One shared buffer would not do: a later call with more counters
-// would find an earlier call's partial results where its counters live.)
+// Partial results only: every split call writes each entry before the combine
+// kernel reads it, so the buffer needs no initialisation and no call depends
+// on what an earlier call left in it.
 struct DeviceBuffer {
   void* ptr = nullptr;
   size_t bytes = 0;
 };
-struct OwnedWorkspace {
-  DeviceBuffer counters, data;
-};
 std::mutex g_ws_mutex;
-std::unordered_map<int, OwnedWorkspace> g_ws;
+std::unordered_map<int, DeviceBuffer> g_ws;
 
-int grow(DeviceBuffer* b, size_t need, bool zero, hipStream_t stream) {
+int grow(DeviceBuffer* b, size_t need, hipStream_t stream) {
   if (b->bytes >= need) return PA_OK;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t e = hipStreamIsCapturing(stream, &cs);
@@ -174,27 +169,20 @@ int grow(DeviceBuffer* b, size_t need, bool zero, hipStream_t stream) {
   const size_t bytes = (need + need / 4 + 255) & ~size_t(255);
   e = hipMalloc(&b->ptr, bytes);
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(workspace)");
-  if (zero) {
-    e = hipMemsetAsync(b->ptr, 0, bytes, stream);
-    if (e != hipSuccess) return hip_fail(e, "hipMemsetAsync(workspace)");
-  }
   b->bytes = bytes;
   return PA_OK;
 }
 
-// Library-owned counters and partial-result storage for one call.
-int owned_workspace(const pa::WorkspaceLayout& lay, hipStream_t stream, void** counters,
-                    void** data) {
+// Library-owned partial-result storage on the current device.
+int owned_workspace(size_t need, hipStream_t stream, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::lock_guard<std::mutex> lock(g_ws_mutex);
-  OwnedWorkspace& w = g_ws[dev];
-  int rc;
-  if ((rc = grow(&w.counters, lay.ml_off - lay.count_off, true, stream)) != PA_OK) return rc;
-  if ((rc = grow(&w.data, lay.total - lay.ml_off, false, stream)) != PA_OK) return rc;
-  *counters = w.counters.ptr;
-  *data = w.data.ptr;
+  DeviceBuffer& w = g_ws[dev];
+  const int rc = grow(&w, need, stream);
+  if (rc != PA_OK) return rc;
+  *out = w.ptr;
   return PA_OK;
 }
 
@@ -286,7 +274,7 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
   pl->part_tokens = int(part);
   pl->max_parts = int(max_parts);
   pl->path = path;
-  pl->ws = pa::workspace_layout(S, Hq, g.kv_heads, D, max_parts);
+  pl->ws = pa::workspace_layout(S, Hq, D, max_parts);
   if (max_parts == 1) pl->ws.total = 0;
   return PA_OK;
 }
@@ -333,28 +321,19 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
       (rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK)
     return rc;
 
-  char* counters = nullptr;  // split-K counters, all zero when the decode starts
-  char* data = nullptr;      // partial results: (max, sum) at data, outputs at data + o_off - ml_off
+  char* ws = nullptr;  // partial results of split contexts
   if (pl.ws.total > 0) {
     if (owned_ws) {
-      void *c, *d;
-      if ((rc = owned_workspace(pl.ws, stream, &c, &d)) != PA_OK) return rc;
-      counters = static_cast<char*>(c);
-      data = static_cast<char*>(d);
+      void* w;
+      if ((rc = owned_workspace(pl.ws.total, stream, &w)) != PA_OK) return rc;
+      ws = static_cast<char*>(w);
     } else {
       if (!workspace || workspace_bytes < pl.ws.total)
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes,
                     pl.ws.total);
       if (reinterpret_cast<uintptr_t>(workspace) & 255u)
         return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-      // A caller's buffer may have held another call's partial results where this
-      // call's counters go: clear them with a kernel (no memset node, so the call
-      // stays capturable).
-      counters = static_cast<char*>(workspace) + pl.ws.count_off;
-      data = static_cast<char*>(workspace) + pl.ws.ml_off;
-      const size_t n = (pl.ws.ml_off - pl.ws.count_off) / sizeof(int32_t);
-      const hipError_t ez = pa::launch_zero(reinterpret_cast<int32_t*>(counters), n, stream);
-      if (ez != hipSuccess) return hip_fail(ez, "counter clear launch");
+      ws = static_cast<char*>(workspace);
     }
   }
 
@@ -379,10 +358,9 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   p.scale_log2 = float(double(scale) * 1.4426950408889634);
   p.part_tokens = pl.part_tokens;
   p.max_parts = pl.max_parts;
-  if (counters) {
-    p.ws_count = reinterpret_cast<int32_t*>(counters);
-    p.ws_ml = reinterpret_cast<float*>(data);
-    p.ws_o = reinterpret_cast<float*>(data + (pl.ws.o_off - pl.ws.ml_off));
+  if (ws) {
+    p.ws_ml = reinterpret_cast<float*>(ws + pl.ws.ml_off);
+    p.ws_o = reinterpret_cast<float*>(ws + pl.ws.o_off);
   }
   const hipError_t e = pa::launch_decode(p, int(pl.D), int(pl.B), pl.path, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
@@ -411,7 +389,7 @@ PA_EXPORT size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads
     return 0;
   const int64_t max_parts = std::max<int64_t>(1, (max_context_len + part - 1) / part);
   if (max_parts == 1) return 0;
-  return pa::workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_parts).total;
+  return pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts).total;
 }
 
 PA_EXPORT int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,

@@ -38,9 +38,8 @@ struct DecodeParams {
   int part_tokens;      // tokens per partition (multiple of 32)
   int max_parts;        // partitions launched per sequence
   // split-K workspace (unused when max_parts == 1)
-  float* ws_o;          // [S, Hq, max_parts, D]
-  float* ws_ml;         // [S, Hq, max_parts, 2]  (max in log2 units, sum)
-  int32_t* ws_count;    // [S, Hkv * head_groups], zero between calls
+  float* ws_o;          // [S, Hq, max_parts, D]  normalised partial outputs
+  float* ws_ml;         // [S, Hq, max_parts, 2]  (reference max in log2 units, sum)
 };
 
 struct AppendParams {
@@ -55,15 +54,13 @@ struct AppendParams {
 
 // Workspace layout shared by the host planner and the kernels.
 struct WorkspaceLayout {
-  size_t count_off, ml_off, o_off, total;
+  size_t ml_off, o_off, total;
 };
-WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
-                                 int64_t head_dim, int64_t max_parts);
+WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
+                                 int64_t max_parts);
 
 hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, Path path,
                          hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
-// n int32 zeros at p, written by a kernel (capturable; no memset node)
-hipError_t launch_zero(int32_t* p, size_t n, hipStream_t stream);
 
 }  // namespace pa

@@ -141,8 +141,9 @@ def test_workspace_bytes(lib):
     f = lib.pa_decode_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     # 64 seqs, 32/8 heads, D 128, contexts up to 2048 tokens -> 4 partitions of 512
-    expect = up(4 * 64 * 8) + up(4 * 2 * 64 * 32 * 4) + up(4 * 64 * 32 * 4 * 128)
+    # (max, sum) pairs then outputs, fp32, per (seq, q head, partition)
+    expect = up(4 * 2 * 64 * 32 * 4) + up(4 * 64 * 32 * 4 * 128)
     assert f(64, 32, 8, 128, 2048, 0) == expect
     assert f(64, 32, 8, 128, 512, 0) == 0          # one partition: no workspace
     assert f(64, 32, 8, 128, 2048, -1) == 0        # never split
-    assert f(8, 32, 8, 128, 32768, 512) == up(4 * 8 * 8) + up(4 * 2 * 8 * 32 * 64) + up(4 * 8 * 32 * 64 * 128)
+    assert f(8, 32, 8, 128, 32768, 512) == up(4 * 2 * 8 * 32 * 64) + up(4 * 8 * 32 * 64 * 128)
