@@ -112,9 +112,12 @@ int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slo
  * their values (even NaN) cannot affect the result.  bf16 products, fp32
  * accumulation; results are bitwise deterministic.
  *
- * Long contexts are split into partitions of 512 tokens whose partial results
- * a second kernel combines in ascending partition order (one launch when the
- * table width allows no split, two otherwise).  The partial results live in a
+ * Schedule.  For batches of up to 8192 sequences the tiles of 16 tokens of all
+ * (sequence, KV head) pairs are cut into equal contiguous ranges, one per wave
+ * of a persistent grid ("stream-K"); a context cut between waves is split at
+ * those cuts.  Larger batches use partitions of 512 tokens.  Either way a
+ * second kernel combines the partial results of a split context in ascending
+ * token order with a log-sum-exp reduce.  The partial results live in a
  * library-owned workspace on the current device, grown with hipMalloc when a
  * call needs more (never during stream capture: that returns PA_ERR_WORKSPACE;
  * use pa_decode_ex there).  Calls that need the workspace may not overlap on
@@ -127,12 +130,20 @@ int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
 
 /* options for pa_decode_ex; a zero-initialised struct means "as pa_decode" */
 typedef struct {
-  int32_t partition_tokens; /* 0: 512; -1: never split; else a positive multiple of 32 */
-  int32_t path;             /* 0: auto (MFMA when q heads per KV head >= 3, else VALU);
-                               1: force the VALU path (q heads per KV head <= 2);
-                               2: force the MFMA path */
-  int64_t max_context_len;  /* 0: table width * block_size; else an upper bound on
-                               every context_lens[s], used to size the launch */
+  int32_t partition_tokens;  /* 0: automatic (the stream-K schedule below when it
+                                applies, else partitions of 512 tokens);
+                                -1: one partition per sequence (never split);
+                                else partitions of this many tokens, a positive
+                                multiple of 32 */
+  int32_t path;              /* 0: auto (MFMA when q heads per KV head >= 3, else VALU);
+                                1: force the VALU path (q heads per KV head <= 2);
+                                2: force the MFMA path */
+  int64_t max_context_len;   /* partitioned schedule only.  0: table width *
+                                block_size; else an upper bound on every
+                                context_lens[s], used to size the launch */
+  int32_t workgroups_per_cu; /* stream-K schedule only: persistent workgroups
+                                per compute unit, 0 = default (2), at most 64 */
+  int32_t reserved;          /* must be 0 */
 } pa_decode_opts;
 
 /* Bytes of workspace pa_decode_ex needs for these sizes (0 when nothing is split). */

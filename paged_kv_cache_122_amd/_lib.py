@@ -31,7 +31,8 @@ class PaTensor(ctypes.Structure):
 
 class PaDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("path", ctypes.c_int32),
-                ("max_context_len", ctypes.c_int64)]
+                ("max_context_len", ctypes.c_int64), ("workgroups_per_cu", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class PaError(RuntimeError):
@@ -141,14 +142,15 @@ def alloc_workspace(nbytes, device):
 
 
 def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, *,
-              partition_tokens=0, path=0, max_context_len=0, workspace=None, stream=None):
+              partition_tokens=0, path=0, max_context_len=0, workgroups_per_cu=0, workspace=None,
+              stream=None):
     """pa_decode_ex: decode with options and a caller-owned workspace."""
     lib = load()
     ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),
                                            (v_cache, "v_cache"), (block_tables, "block_tables"),
                                            (context_lens, "context_lens"))]
     ds = [describe(x) for x in ts]
-    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len))
+    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()

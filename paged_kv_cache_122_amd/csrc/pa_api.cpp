@@ -189,9 +189,37 @@ int owned_workspace(size_t need, hipStream_t stream, void** out) {
 struct DecodePlan {
   int64_t S, Hq, Hkv, D, B, W, NB;
   int part_tokens, max_parts;
+  bool stream;          // stream-K schedule (else partitioned)
+  int workgroups_per_cu;
   pa::Path path;
   pa::WorkspaceLayout ws;
 };
+
+// The stream-K schedule keeps its tile prefix in LDS and indexes tiles with
+// 32-bit integers: it takes the batch when both fit.
+bool stream_fits(int64_t S, int64_t pairs, int64_t max_len) {
+  const int64_t tiles = pairs * ((max_len + pa::kTileTokens - 1) / pa::kTileTokens);
+  return S <= pa::kMaxStreamSeqs && tiles < (int64_t(1) << 30);
+}
+
+// CUs of the current device (cached per device).
+int device_cus(int* cus) {
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it == cache.end()) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(multiprocessor count)");
+    it = cache.emplace(dev, n > 0 ? n : 1).first;
+  }
+  *cus = it->second;
+  return PA_OK;
+}
 
 int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
                 const pa_tensor* v_cache, const pa_tensor* block_tables,
@@ -248,7 +276,32 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
 
   int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : W * g.block_size;
   if (opts && opts->max_context_len < 0) return fail(PA_ERR_INVALID, "opts.max_context_len < 0");
+  if (W * g.block_size > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "table width * block_size >= 2^31");
   const int pt_opt = opts ? opts->partition_tokens : 0;
+  const int wpc = opts ? opts->workgroups_per_cu : 0;
+  if (wpc < 0 || wpc > 64) return fail(PA_ERR_INVALID, "opts.workgroups_per_cu %d (0 .. 64)", wpc);
+  if (opts && opts->reserved != 0) return fail(PA_ERR_INVALID, "opts.reserved must be 0");
+  const int64_t head_groups = path == pa::Path::Mfma ? (G + 15) / 16 : 1;
+  const int64_t pairs = S * g.kv_heads * head_groups;
+
+  pl->S = S;
+  pl->Hq = Hq;
+  pl->Hkv = g.kv_heads;
+  pl->D = D;
+  pl->B = g.block_size;
+  pl->W = W;
+  pl->NB = g.num_blocks;
+  pl->path = path;
+  pl->workgroups_per_cu = wpc > 0 ? wpc : pa::kDefaultWorkgroupsPerCu;
+  if (pt_opt == 0 && stream_fits(S, pairs, W * g.block_size)) {
+    pl->stream = true;
+    pl->part_tokens = 0;
+    pl->max_parts = 1;
+    pl->ws = pa::stream_workspace_layout(S, pairs, D);
+    return PA_OK;
+  }
+  pl->stream = false;
+
   int64_t part;
   if (pt_opt == 0)
     part = pa::kDefaultPartition;
@@ -264,16 +317,8 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
     return fail(PA_ERR_UNSUPPORTED, "%lld partitions per sequence > 65535; raise partition_tokens",
                 (long long)max_parts);
 
-  pl->S = S;
-  pl->Hq = Hq;
-  pl->Hkv = g.kv_heads;
-  pl->D = D;
-  pl->B = g.block_size;
-  pl->W = W;
-  pl->NB = g.num_blocks;
   pl->part_tokens = int(part);
   pl->max_parts = int(max_parts);
-  pl->path = path;
   pl->ws = pa::workspace_layout(S, Hq, D, max_parts);
   if (max_parts == 1) pl->ws.total = 0;
   return PA_OK;
@@ -355,14 +400,28 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   p.num_kv_heads = int(pl.Hkv);
   p.group = int(pl.Hq / pl.Hkv);
   p.head_groups = pl.path == pa::Path::Mfma ? (p.group + 15) / 16 : 1;
+  p.max_len = int(pl.W * pl.B);
   p.scale_log2 = float(double(scale) * 1.4426950408889634);
   p.part_tokens = pl.part_tokens;
   p.max_parts = pl.max_parts;
-  if (ws) {
-    p.ws_ml = reinterpret_cast<float*>(ws + pl.ws.ml_off);
-    p.ws_o = reinterpret_cast<float*>(ws + pl.ws.o_off);
+  hipError_t e;
+  if (pl.stream) {
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != PA_OK) return rc;
+    pa::StreamParams sk{};
+    sk.plan = reinterpret_cast<int*>(ws + pl.ws.plan_off);
+    sk.ws_ml = reinterpret_cast<float*>(ws + pl.ws.ml_off);
+    sk.ws_o = reinterpret_cast<float*>(ws + pl.ws.o_off);
+    sk.cus = cus;
+    sk.workgroups_per_cu = pl.workgroups_per_cu;
+    e = pa::launch_decode(p, &sk, int(pl.D), int(pl.B), pl.path, stream);
+  } else {
+    if (ws) {
+      p.ws_ml = reinterpret_cast<float*>(ws + pl.ws.ml_off);
+      p.ws_o = reinterpret_cast<float*>(ws + pl.ws.o_off);
+    }
+    e = pa::launch_decode(p, nullptr, int(pl.D), int(pl.B), pl.path, stream);
   }
-  const hipError_t e = pa::launch_decode(p, int(pl.D), int(pl.B), pl.path, stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PA_OK;
 }
@@ -378,6 +437,10 @@ PA_EXPORT size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads
                                            int64_t max_context_len, int32_t partition_tokens) {
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len < 0)
     return 0;
+  const int64_t group = num_q_heads / num_kv_heads;
+  const int64_t pairs = num_seqs * num_kv_heads * ((group + 15) / 16);
+  if (partition_tokens == 0 && stream_fits(num_seqs, pairs, max_context_len))
+    return pa::stream_workspace_layout(num_seqs, pairs, head_dim).total;
   int64_t part;
   if (partition_tokens == 0)
     part = pa::kDefaultPartition;

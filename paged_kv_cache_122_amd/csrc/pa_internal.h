@@ -12,7 +12,13 @@ namespace pa {
 // at a time (one block at B = 16, half a block at B = 32, two at B = 8).
 constexpr int kTileTokens = 16;
 constexpr int kWaves = 4;               // waves per decode workgroup
-constexpr int kDefaultPartition = 512;  // tokens per split-K partition
+constexpr int kDefaultPartition = 512;  // tokens per partition on the partitioned schedule
+// stream-K schedule limits: the per-workgroup tile prefix lives in LDS, and
+// partial results are sized for at most this many waves
+constexpr int kMaxStreamSeqs = 8192;
+constexpr int kMaxStreamWaves = 4096;
+constexpr int kDefaultWorkgroupsPerCu = 2;
+constexpr int kPlanHeader = 4;  // ints before the tile prefix in the stream-K plan
 
 enum class Path : int { Valu = 1, Mfma = 2 };
 
@@ -33,13 +39,25 @@ struct DecodeParams {
   const int32_t* context_lens;
   int num_seqs, num_q_heads, num_kv_heads;
   int group;            // q heads per kv head (G)
-  int head_groups;      // ceil(G / 16) column groups per kv head on the MFMA path
+  int head_groups;      // ceil(G / 16) column groups per kv head on the MFMA path, 1 on VALU
+  int max_len;          // W * B: longer contexts are clamped (a contract violation)
   float scale_log2;     // scale * log2(e)
+  // partitioned schedule
   int part_tokens;      // tokens per partition (multiple of 32)
   int max_parts;        // partitions launched per sequence
-  // split-K workspace (unused when max_parts == 1)
   float* ws_o;          // [S, Hq, max_parts, D]  normalised partial outputs
   float* ws_ml;         // [S, Hq, max_parts, 2]  (reference max in log2 units, sum)
+};
+
+// stream-K schedule: plan = {tiles per wave, total tiles, -, -, prefix[S + 1]}
+// (written by the decode kernel, read by its combine kernel); partial results
+// are indexed by (pair + wave) * 16 + column.
+struct StreamParams {
+  int* plan;
+  float* ws_ml;  // [pieces * 16, 2]
+  float* ws_o;   // [pieces * 16, D]
+  int cus;              // compute units of the device
+  int workgroups_per_cu;  // requested; the launcher caps it at the kernel's occupancy
 };
 
 struct AppendParams {
@@ -52,15 +70,17 @@ struct AppendParams {
   int num_tokens, num_kv_heads;
 };
 
-// Workspace layout shared by the host planner and the kernels.
+// Workspace layouts shared by the host planner and the kernels.
 struct WorkspaceLayout {
-  size_t ml_off, o_off, total;
+  size_t plan_off, ml_off, o_off, total;
 };
 WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
                                  int64_t max_parts);
+WorkspaceLayout stream_workspace_layout(int64_t num_seqs, int64_t num_pairs, int64_t head_dim);
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, Path path,
-                         hipStream_t stream);
+// sk == nullptr: partitioned schedule
+hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
+                         Path path, hipStream_t stream);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
 
 }  // namespace pa

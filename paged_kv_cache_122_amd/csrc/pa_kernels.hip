@@ -4,24 +4,33 @@
 // Method: one query token per sequence attends to its cached tokens, which
 // live in fixed-size physical blocks reached through a per-sequence block
 // table; the per-block softmax is accumulated online (running max and sum,
-// rescaled when the max grows) and, for long contexts, partitions of the
-// context produce partial results that a reduce step combines
-// ("PagedAttention from First Principles", sections 5 and 17; Equation 4 of
-// the hungchun0201 vLLM digest).  The pages' kernel sketch (one warp per block,
-// reduce across warps) targets other hardware; the design here is gfx950's:
+// rescaled when the max grows) and, for long contexts, partial results of
+// pieces of the context are combined by a reduce step ("PagedAttention from
+// First Principles", sections 5 and 17; Equation 4 of the hungchun0201 vLLM
+// digest).  The pages' kernel sketch (one warp per block, reduce across warps)
+// targets other hardware; the design here is gfx950's:
 //
-// * Work unit = (kv head [x column group], sequence, partition of the
-//   context); a workgroup of 4 wave64s, each wave walking every 4th 16-token
-//   tile of the partition with the next two tiles' loads in flight while it
-//   computes on the current one.
-// * Pool layouts (K [NB, Hkv, D/8, B, 8], V [NB, Hkv, B/4, D, 4]) make every
-//   16-byte lane load land directly in MFMA operand order, 256 contiguous
-//   bytes per 16 lanes, so there is no LDS staging of K/V and no shuffles
-//   before the matrix cores.  Tiles are read with buffer loads whose resource
-//   descriptor is built per tile in scalar registers from the block-table
-//   entry; a descriptor with zero records turns the pipeline's padding loads
-//   past a wave's last tile into free zero loads, so the loop never branches
-//   around a load.
+// * Unit of work: one 16-token tile of one (sequence, KV head [x column
+//   group]) pair.  Lane layouts make every 16-byte lane load land directly in
+//   MFMA operand order (pool layouts K [NB, Hkv, D/8, B, 8], V [NB, Hkv, B/4,
+//   D, 4]; 256 contiguous bytes per 16 lanes), so K/V go from HBM to the
+//   matrix cores without LDS staging or shuffles.
+// * Loads are buffer loads through a resource descriptor built per tile in
+//   scalar registers from the block-table entry, with the non-temporal bit
+//   (the pools are read once per step).  Each wave keeps the next two tiles'
+//   loads in flight while it computes on the current one; past its last tile a
+//   zero-record descriptor turns the padding loads into free zero loads, so
+//   the loop never branches around a load and the compiler waits only for the
+//   tile it is about to use.
+// * Stream-K schedule (default): the tiles of all pairs, in (sequence, head,
+//   tile) order, are cut into one equal contiguous range per wave of a
+//   persistent grid (a few workgroups per CU), so every wave streams the same
+//   number of bytes whatever the length mix, pays its start-up latency once,
+//   and keeps its pipeline full across pair boundaries.  A pair finished inside
+//   one wave is written out directly; a pair cut between waves leaves one
+//   partial result per wave for the combine kernel.
+// * Partitioned schedule (opts.partition_tokens): a grid of (pair, partition)
+//   workgroups of 4 waves, each wave walking every 4th tile of its partition.
 // * GQA path (q heads per KV head >= 3): QK^T is v_mfma_f32_16x16x32_bf16 with
 //   16 tokens as rows and the group's query heads as columns; PV is
 //   v_mfma_f32_16x16x16_bf16 whose B operand is exactly the QK^T accumulator
@@ -32,11 +41,10 @@
 //   cross-lane sums with wave shuffles.
 // * The softmax reference max is raised lazily: only when a tile's max
 //   exceeds it by more than 2^8 in probability, so the accumulator rescale
-//   runs on a handful of tiles instead of every tile.  Results are the same
-//   quantity (numerator and denominator share the reference).
-// * Split contexts: each partition writes (reference max, sum, normalised
-//   output) to a workspace; a second kernel combines the partitions of every
-//   (sequence, head) in ascending order (deterministic).
+//   runs on a handful of tiles instead of every tile.  Numerator and
+//   denominator share the reference, so the result is the same quantity.
+// * Combine: out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - M) over
+//   the pieces of a pair in ascending token order (deterministic).
 
 #include <hip/hip_runtime.h>
 
@@ -50,9 +58,21 @@ WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t 
                                  int64_t max_parts) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   WorkspaceLayout w;
+  w.plan_off = 0;
   w.ml_off = 0;
   w.o_off = up(sizeof(float) * 2 * size_t(num_seqs * num_q_heads * max_parts));
   w.total = w.o_off + up(sizeof(float) * size_t(num_seqs * num_q_heads * max_parts * head_dim));
+  return w;
+}
+
+WorkspaceLayout stream_workspace_layout(int64_t num_seqs, int64_t num_pairs, int64_t head_dim) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t pieces = size_t(num_pairs + kMaxStreamWaves);
+  WorkspaceLayout w;
+  w.plan_off = 0;
+  w.ml_off = up(sizeof(int32_t) * size_t(num_seqs + 1 + kPlanHeader));
+  w.o_off = w.ml_off + up(sizeof(float) * 2 * pieces * 16);
+  w.total = w.o_off + up(sizeof(float) * pieces * 16 * size_t(head_dim));
   return w;
 }
 
@@ -72,6 +92,10 @@ constexpr int kBufferFlags = 0x00020000;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 // lazy rescale threshold (log2 units): probabilities stay <= 2^8
 constexpr float kRescaleSlack = 8.f;
+// K/V tiles are read once per decode step: non-temporal loads (the nt bit)
+// stream them without displacing cached data, and on MI355X sustain ~25 %
+// more HBM read bandwidth than default-policy loads for 4 KiB random tiles.
+constexpr int kStreamingLoad = 2;
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -104,18 +128,31 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, kBufferFlags);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
 }
 
-// K/V tiles are read once per decode step: non-temporal loads (the nt bit)
-// stream them without displacing cached data, and on MI355X sustain ~25 %
-// more HBM read bandwidth than default-policy loads for 4 KiB random tiles.
-constexpr int kStreamingLoad = 2;
-
-__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+__device__ __forceinline__ u32x4 stream_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4,
                             __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kStreamingLoad));
+}
+
+__device__ __forceinline__ u32x4 cached_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0));
+}
+
+__device__ __forceinline__ void store_out(const DecodeParams& p, int s, int h, int d, float r) {
+  const size_t at = size_t(s) * p.out_s + size_t(h) * p.out_h + d;
+  if (p.out_f32)
+    static_cast<float*>(p.out)[at] = r;
+  else
+    static_cast<uint16_t*>(p.out)[at] = uint16_t(bf16_bits(r));
+}
+
+// Context length as the kernels use it: negative lengths count as 0 and
+// lengths past the block table (a contract violation) are clamped to it.
+__device__ __forceinline__ int clamp_len(const DecodeParams& p, int L) {
+  return min(max(L, 0), p.max_len);
 }
 
 // ---------------------------------------------------------------------------
@@ -153,8 +190,8 @@ __device__ __forceinline__ LaneOffsets<D, BS> lane_offsets(int lane) {
   return o;
 }
 
-// Load tile `ts` (wave-uniform first token) whose physical block(s) are
-// phys0 / phys1, or zeros without any memory access when !valid.
+// Load the tile starting at token ts of KV head kvh whose physical block(s)
+// are phys0 / phys1, or zeros without any memory access when !valid.
 template <int D, int BS>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, int kvh, int phys0, int phys1,
                                           int ts, bool valid, const LaneOffsets<D, BS>& lo,
@@ -163,94 +200,41 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int kvh, int ph
   const size_t blk_elems = size_t(p.num_kv_heads) * BS * D;
   const size_t head_off = size_t(kvh) * BS * D;
   const int bytes = valid ? kTileBytes : 0;
-  const __amdgpu_buffer_rsrc_t k0 = tile_rsrc(p.k_cache + size_t(phys0) * blk_elems + head_off, bytes);
-  const __amdgpu_buffer_rsrc_t v0 = tile_rsrc(p.v_cache + size_t(phys0) * blk_elems + head_off, bytes);
+  const auto k0 = make_rsrc(p.k_cache + size_t(phys0) * blk_elems + head_off, bytes);
+  const auto v0 = make_rsrc(p.v_cache + size_t(phys0) * blk_elems + head_off, bytes);
   if constexpr (BS == 8) {
-    const __amdgpu_buffer_rsrc_t k1 = tile_rsrc(p.k_cache + size_t(phys1) * blk_elems + head_off, bytes);
-    const __amdgpu_buffer_rsrc_t v1 = tile_rsrc(p.v_cache + size_t(phys1) * blk_elems + head_off, bytes);
+    const auto k1 = make_rsrc(p.k_cache + size_t(phys1) * blk_elems + head_off, bytes);
+    const auto v1 = make_rsrc(p.v_cache + size_t(phys1) * blk_elems + head_off, bytes);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      k[c] = buffer_load16(k0, lo.k0 + c * 4 * BS * 16) | buffer_load16(k1, lo.k1 + c * 4 * BS * 16);
+      k[c] = stream_load16(k0, lo.k0 + c * 4 * BS * 16) | stream_load16(k1, lo.k1 + c * 4 * BS * 16);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      v[c] = buffer_load16(v0, lo.v0 + c * 256) | buffer_load16(v1, lo.v1 + c * 256);
+      v[c] = stream_load16(v0, lo.v0 + c * 256) | stream_load16(v1, lo.v1 + c * 256);
   } else {
     // B = 32 holds two tiles per block: the second half starts 16 tokens in
     const uint32_t khalf = BS == 32 ? uint32_t(((ts >> 4) & 1) * 16 * 8 * 2) : 0u;
     const uint32_t vhalf = BS == 32 ? uint32_t(((ts >> 4) & 1) * 4 * D * 4 * 2) : 0u;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) k[c] = buffer_load16(k0, lo.k0 + khalf + c * 4 * BS * 16);
+    for (int c = 0; c < D / 32; ++c) k[c] = stream_load16(k0, lo.k0 + khalf + c * 4 * BS * 16);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) v[c] = buffer_load16(v0, lo.v0 + vhalf + c * 256);
+    for (int c = 0; c < D / 32; ++c) v[c] = stream_load16(v0, lo.v0 + vhalf + c * 256);
   }
-  // keep the scheduler from hoisting the previous tile's math above these
-  // loads: issuing them first is what keeps bytes in flight
-  __builtin_amdgcn_sched_barrier(0);
 }
 
-// Block-table entries of up to 64 consecutive tiles of one wave, one per lane,
-// so the tile loop never waits on memory for an address: lane j holds the
-// physical block of the wave's tile k0 + j (b1: second block when B = 8;
-// the first block again when that half lies past the context).
-struct TableCache {
-  int b0, b1;
-};
-
+// Physical block(s) of tile t (tokens 16t .. 16t+15) of a sequence with L
+// tokens; for B = 8 the second block is the first again when it lies past L.
 template <int BS>
-__device__ __forceinline__ TableCache fetch_table(const int32_t* bt, int t0, int t1, int wave,
-                                                  int k0, int n, int lane) {
-  TableCache c{0, 0};
-  const int k = k0 + lane;
-  if (k < n) {
-    const int ts = t0 + 16 * (wave + kWaves * k);
-    if constexpr (BS == 16) {
-      c.b0 = bt[ts >> 4];
-    } else if constexpr (BS == 32) {
-      c.b0 = bt[ts >> 5];
-    } else {
-      c.b0 = bt[ts >> 3];
-      c.b1 = (ts + 8 < t1) ? bt[(ts >> 3) + 1] : c.b0;
-    }
-  }
-  return c;
-}
-
-// Walk this wave's tiles (tiles wave, wave + 4, ... of the partition [t0, t1))
-// with the next two tiles' loads issued before the current tile is computed.
-// Every compute is preceded by the same number of younger loads on every path
-// (past the last tile the loads are zero-record no-ops), so the compiler waits
-// only for the tile it is about to use.
-template <int D, int BS, typename F>
-__device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int32_t* bt, int kvh,
-                                           int t0, int t1, int wave, int lane, F&& compute) {
-  constexpr int NC = D / 32;
-  const int ntiles = (t1 - t0 + 15) >> 4;
-  const int n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
-  const LaneOffsets<D, BS> lo = lane_offsets<D, BS>(lane);
-  for (int k0 = 0; k0 < n; k0 += 64) {
-    const TableCache tc = fetch_table<BS>(bt, t0, t1, wave, k0, n, lane);
-    const int m = min(64, n - k0);
-    auto start = [&](int j) { return t0 + 16 * (wave + kWaves * (k0 + j)); };
-    auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-      const int jj = min(j, m - 1);
-      const int b0 = __builtin_amdgcn_readlane(tc.b0, jj);
-      const int b1 = BS == 8 ? __builtin_amdgcn_readlane(tc.b1, jj) : 0;
-      load_tile<D, BS>(p, kvh, b0, b1, start(jj), j < m, lo, kt, vt);
-    };
-    u32x4 ak[NC], av[NC], bk[NC], bv[NC], ck[NC], cv[NC];
-    load(0, ak, av);
-    load(1, bk, bv);
-    for (int j = 0;; j += 3) {
-      load(j + 2, ck, cv);
-      compute(start(j), ak, av);
-      if (j + 1 >= m) break;
-      load(j + 3, ak, av);
-      compute(start(j + 1), bk, bv);
-      if (j + 2 >= m) break;
-      load(j + 4, bk, bv);
-      compute(start(j + 2), ck, cv);
-      if (j + 3 >= m) break;
-    }
+__device__ __forceinline__ void tile_blocks(const int32_t* bt_row, int t, int L, int& b0, int& b1) {
+  if constexpr (BS == 16) {
+    b0 = bt_row[t];
+    b1 = 0;
+  } else if constexpr (BS == 32) {
+    b0 = bt_row[t >> 1];
+    b1 = 0;
+  } else {
+    b0 = bt_row[2 * t];
+    b1 = (16 * t + 8 < L) ? bt_row[2 * t + 1] : b0;
   }
 }
 
@@ -270,6 +254,627 @@ __device__ __forceinline__ void mask_v(u32x4 (&v)[D / 32], int ts, int t1, int l
   }
 }
 
+// ---------------------------------------------------------------------------
+// per-tile math, GQA path (MFMA)
+//
+// Column r of the accumulators is query head h0 + r.  Lane (g4 = l >> 4, r)
+// holds the scores of tokens 4*g4 .. +3 of the tile and the output rows
+// d = 2*(4*g4 + j) + 32*(mm >> 1) + (mm & 1) of accumulator mm.
+// ---------------------------------------------------------------------------
+template <int D>
+struct MfmaAcc {
+  f32x4 o[D / 16];
+  float m;  // reference max (log2 units) of column r
+  float l;  // this lane's share of the running sum of column r
+};
+
+template <int D>
+__device__ __forceinline__ void mfma_reset(MfmaAcc<D>& a) {
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) a.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  a.m = kNegInf;
+  a.l = 0.f;
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
+                                          int ts, int t1, int lane, u32x4 (&kt)[D / 32],
+                                          u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  const int g4 = lane >> 4;
+  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) sacc = mfma_16x16x32(kt[c], q[c], sacc);
+  float sc[4];
+  float mt = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sc[j] = (ts + 4 * g4 + j < t1) ? sacc[j] * scale_log2 : kNegInf;
+    mt = fmaxf(mt, sc[j]);
+  }
+  // Raise the reference only when some score is far above it; the column max
+  // (over the four 16-lane groups) is needed only then.
+  if (__any(mt > a.m + kRescaleSlack)) {
+    mt = fmaxf(mt, shfl_xor(mt, 16));
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float m_new = fmaxf(a.m, mt);
+    const float alpha = exp2f(a.m - m_new);
+    a.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 2 * NC; ++i) a.o[i] *= alpha;
+    a.m = m_new;
+  }
+  float pr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[j] = exp2f(sc[j] - a.m);
+    a.l += pr[j];
+  }
+  // P as the B operand of PV, split into hi + lo bf16
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hb[j] = bf16_bits(pr[j]);
+    lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
+  }
+  const u32x2 phi = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+  const u32x2 plo = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+  mask_v<D>(vt, ts, t1, lane);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const u32x2 a0 = {vt[c].x, vt[c].y};  // dim 2r + 32c, tokens 4*g4 .. +3
+    const u32x2 a1 = {vt[c].z, vt[c].w};  // dim 2r + 32c + 1
+    a.o[2 * c] = mfma_16x16x16(a0, phi, a.o[2 * c]);
+    a.o[2 * c] = mfma_16x16x16(a0, plo, a.o[2 * c]);
+    a.o[2 * c + 1] = mfma_16x16x16(a1, phi, a.o[2 * c + 1]);
+    a.o[2 * c + 1] = mfma_16x16x16(a1, plo, a.o[2 * c + 1]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// per-tile math, MHA path (VALU)
+//
+// Lane (g4, r) holds token r of the tile and dims 8*(g4 + 4c) .. +7 of K, and
+// output dims 2r + 32c + e (summed over the four 16-lane groups at the end).
+// ---------------------------------------------------------------------------
+template <int D, int VG>
+struct ValuAcc {
+  float o[VG][D / 32][2];
+  float m[VG];  // reference max, the same in every lane
+  float l[VG];  // this lane's share: the probabilities of its token
+};
+
+template <int D, int VG>
+__device__ __forceinline__ void valu_reset(ValuAcc<D, VG>& a) {
+#pragma unroll
+  for (int g = 0; g < VG; ++g) {
+    a.m[g] = kNegInf;
+    a.l[g] = 0.f;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) a.o[g][c][0] = a.o[g][c][1] = 0.f;
+  }
+}
+
+// q in fp32: this lane's dims 8*(g4 + 4c) + e of query heads h0 .. h0+VG-1
+template <int D, int VG>
+__device__ __forceinline__ void valu_load_q(const DecodeParams& p, int s, int h0, int lane,
+                                            float (&qf)[VG][D / 32][8]) {
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < VG; ++g)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const u32x4 u = load16(p.q + size_t(s) * p.q_s + size_t(h0 + g) * p.q_h + 8 * (g4 + 4 * c));
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qf[g][c][2 * e] = bf_lo(w[e]);
+        qf[g][c][2 * e + 1] = bf_hi(w[e]);
+      }
+    }
+}
+
+template <int D, int VG>
+__device__ __forceinline__ void valu_tile(ValuAcc<D, VG>& a, const float (&qf)[VG][D / 32][8],
+                                          float scale_log2, int ts, int t1, int lane,
+                                          u32x4 (&kt)[D / 32], u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  float kf[NC][8];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint32_t w[4] = {kt[c].x, kt[c].y, kt[c].z, kt[c].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kf[c][2 * e] = bf_lo(w[e]);
+      kf[c][2 * e + 1] = bf_hi(w[e]);
+    }
+  }
+  mask_v<D>(vt, ts, t1, lane);
+  const bool valid = ts + r < t1;
+#pragma unroll
+  for (int g = 0; g < VG; ++g) {
+    float dot = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(kf[c][e], qf[g][c][e], dot);
+    dot += shfl_xor(dot, 16);
+    dot += shfl_xor(dot, 32);
+    const float sc = valid ? dot * scale_log2 : kNegInf;  // score of token ts + r
+    float mt = sc;
+    mt = fmaxf(mt, shfl_xor(mt, 1));
+    mt = fmaxf(mt, shfl_xor(mt, 2));
+    mt = fmaxf(mt, shfl_xor(mt, 4));
+    mt = fmaxf(mt, shfl_xor(mt, 8));
+    float alpha = 1.f;
+    if (mt > a.m[g] + kRescaleSlack) {  // the same in every lane
+      const float m_new = fmaxf(a.m[g], mt);
+      alpha = exp2f(a.m[g] - m_new);
+      a.l[g] *= alpha;
+      a.m[g] = m_new;
+    }
+    const float pr = exp2f(sc - a.m[g]);
+    a.l[g] += pr;
+    float pj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pj[j] = __shfl(pr, 4 * g4 + j, 64);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float a0 = a.o[g][c][0] * alpha, a1 = a.o[g][c][1] * alpha;
+      a0 = fmaf(pj[0], bf_lo(vt[c].x), a0);
+      a0 = fmaf(pj[1], bf_hi(vt[c].x), a0);
+      a0 = fmaf(pj[2], bf_lo(vt[c].y), a0);
+      a0 = fmaf(pj[3], bf_hi(vt[c].y), a0);
+      a1 = fmaf(pj[0], bf_lo(vt[c].z), a1);
+      a1 = fmaf(pj[1], bf_hi(vt[c].z), a1);
+      a1 = fmaf(pj[2], bf_lo(vt[c].w), a1);
+      a1 = fmaf(pj[3], bf_hi(vt[c].w), a1);
+      a.o[g][c][0] = a0;
+      a.o[g][c][1] = a1;
+    }
+  }
+}
+
+// ===========================================================================
+// stream-K schedule
+// ===========================================================================
+
+// Exclusive prefix of tiles per sequence into LDS: ps[s] = sum_{s' < s}
+// ceil(L_s' / 16), ps[S] = total.  All threads of the workgroup take part.
+__device__ __forceinline__ void build_prefix(const DecodeParams& p, int* ps, int* scan) {
+  const int S = p.num_seqs;
+  const int per = (S + kThreads - 1) / kThreads;
+  const int b = threadIdx.x * per;
+  const int e = min(S, b + per);
+  int sum = 0;
+  for (int i = b; i < e; ++i) {
+    const int n = (clamp_len(p, p.context_lens[i]) + 15) >> 4;
+    ps[i] = n;
+    sum += n;
+  }
+  scan[threadIdx.x] = sum;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {  // inclusive Hillis-Steele scan
+    const int add = threadIdx.x >= off ? scan[threadIdx.x - off] : 0;
+    __syncthreads();
+    scan[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int run = threadIdx.x ? scan[threadIdx.x - 1] : 0;
+  for (int i = b; i < e; ++i) {
+    const int n = ps[i];
+    ps[i] = run;
+    run += n;
+  }
+  if (threadIdx.x == kThreads - 1) ps[S] = scan[kThreads - 1];
+  __syncthreads();
+}
+
+// Position of global tile T: sequence s (largest with H*ps[s] <= T), head
+// group hg and tile t within the pair.
+__device__ __forceinline__ void locate(const int* ps, int S, int H, int T, int& s, int& hg, int& t) {
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (H * ps[mid] <= T) lo = mid; else hi = mid - 1;
+  }
+  s = lo;
+  const int off = T - H * ps[lo];
+  const int n = ps[lo + 1] - ps[lo];
+  hg = off / n;
+  t = off - hg * n;
+}
+
+// Where a pair's pieces live: pieces are numbered pair + wave (unique because
+// waves take increasing tile ranges), 16 columns each.
+__device__ __forceinline__ size_t piece_row(int pair, int wave, int col) {
+  return (size_t(pair) + size_t(wave)) * 16 + col;
+}
+
+struct StreamRange {
+  int T0, T1;  // this wave's tiles [T0, T1)
+  int w;       // global wave index
+};
+
+// Per-lane cache of the metadata of up to 64 consecutive tiles of the wave:
+// lane j describes tile base + j.
+struct TileMeta {
+  int s, hg, t, L, b0, b1;
+};
+
+template <int BS>
+__device__ __forceinline__ TileMeta fetch_meta(const DecodeParams& p, const int* ps, int H, int T,
+                                               bool live) {
+  TileMeta m{0, 0, 0, 0, 0, 0};
+  if (live) {
+    locate(ps, p.num_seqs, H, T, m.s, m.hg, m.t);
+    m.L = clamp_len(p, p.context_lens[m.s]);
+    tile_blocks<BS>(p.block_tables + size_t(m.s) * p.bt_s, m.t, m.L, m.b0, m.b1);
+  }
+  return m;
+}
+
+struct Uniform {
+  int s, hg, t, L, b0, b1;
+};
+
+__device__ __forceinline__ Uniform read_meta(const TileMeta& m, int j) {
+  return Uniform{__builtin_amdgcn_readlane(m.s, j), __builtin_amdgcn_readlane(m.hg, j),
+                 __builtin_amdgcn_readlane(m.t, j), __builtin_amdgcn_readlane(m.L, j),
+                 __builtin_amdgcn_readlane(m.b0, j), __builtin_amdgcn_readlane(m.b1, j)};
+}
+
+// Query heads of head group hg: h0 .. h0 + ncols - 1
+__device__ __forceinline__ void head_span(const DecodeParams& p, int hg, int& kvh, int& h0, int& ncols) {
+  kvh = hg / p.head_groups;
+  const int cgrp = hg - kvh * p.head_groups;
+  h0 = kvh * p.group + cgrp * 16;
+  ncols = min(16, p.group - cgrp * 16);
+}
+
+// Q of one pair as the B operand of QK^T (column r = head h0 + r, zero past
+// the group), or zeros without memory access when !valid.
+template <int D>
+__device__ __forceinline__ void load_q_operand(const DecodeParams& p, int s, int hg, bool valid,
+                                               int lane, u32x4 (&q)[D / 32]) {
+  int kvh, h0, ncols;
+  head_span(p, hg, kvh, h0, ncols);
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  const int bytes = valid ? int(((ncols - 1) * p.q_h + D) * 2) : 0;
+  const auto rs = make_rsrc(p.q + size_t(s) * p.q_s + size_t(h0) * p.q_h, bytes);
+  const uint32_t off = r < ncols ? uint32_t((r * p.q_h + 8 * g4) * 2) : kOutOfRange;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) q[c] = cached_load16(rs, off + c * 64);
+}
+
+// Write one finished piece of the MFMA path: the output itself when the wave
+// saw the whole pair, else a partial result (reference max, sum, o / sum).
+template <int D>
+__device__ __forceinline__ void mfma_write_piece(const DecodeParams& p, const StreamParams& sk,
+                                                 MfmaAcc<D>& a, int s, int hg, bool whole, int w,
+                                                 int lane) {
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  int kvh, h0, ncols;
+  head_span(p, hg, kvh, h0, ncols);
+  float l = a.l;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  if (r >= ncols) return;
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (whole) {
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        store_out(p, s, h0 + r, 2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1), a.o[mm][j] * inv);
+  } else {
+    const int pair = s * (p.num_kv_heads * p.head_groups) + hg;
+    const size_t row = piece_row(pair, w, r);
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sk.ws_o[row * D + 2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)] = a.o[mm][j] * inv;
+    if (g4 == 0) {
+      sk.ws_ml[row * 2 + 0] = a.m;
+      sk.ws_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+template <int D, int VG>
+__device__ __forceinline__ void valu_write_piece(const DecodeParams& p, const StreamParams& sk,
+                                                 ValuAcc<D, VG>& a, int s, int kvh, bool whole,
+                                                 int w, int lane) {
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int g = 0; g < VG; ++g) {
+    float l = a.l[g];
+    l += shfl_xor(l, 1);
+    l += shfl_xor(l, 2);
+    l += shfl_xor(l, 4);
+    l += shfl_xor(l, 8);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t row = piece_row(s * p.num_kv_heads + kvh, w, g);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        float x = a.o[g][c][e];
+        x += shfl_xor(x, 16);
+        x += shfl_xor(x, 32);
+        const int d = 2 * r + 32 * c + e;
+        if (g4 == 0) {
+          if (whole)
+            store_out(p, s, kvh * VG + g, d, x * inv);
+          else
+            sk.ws_o[row * D + d] = x * inv;
+        }
+      }
+    if (!whole && lane == 0) {
+      sk.ws_ml[row * 2 + 0] = a.m[g];
+      sk.ws_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+// Shared prologue of the stream-K kernels: tile prefix in LDS, this wave's
+// range, and (workgroup 0) the plan the combine kernel reads.
+__device__ __forceinline__ StreamRange stream_prologue(const DecodeParams& p, const StreamParams& sk,
+                                                       int* ps, int* scan, int wave) {
+  build_prefix(p, ps, scan);
+  const int S = p.num_seqs;
+  const int H = p.num_kv_heads * p.head_groups;
+  const int total = H * ps[S];
+  const int nw = gridDim.x * kWaves;
+  const int per = (total + nw - 1) / nw;
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= S; i += kThreads) sk.plan[kPlanHeader + i] = ps[i];
+    if (threadIdx.x == 0) {
+      sk.plan[0] = per;
+      sk.plan[1] = total;
+    }
+  }
+  StreamRange rg;
+  rg.w = blockIdx.x * kWaves + wave;
+  rg.T0 = min(rg.w * per, total);
+  rg.T1 = min(rg.T0 + per, total);
+  return rg;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(kThreads) void decode_mfma_sk(DecodeParams p, StreamParams sk) {
+  constexpr int NC = D / 32;
+  __shared__ int ps[kMaxStreamSeqs + 1];
+  __shared__ int scan[kThreads];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const StreamRange rg = stream_prologue(p, sk, ps, scan, wave);
+  if (rg.T0 >= rg.T1) return;
+  const int H = p.num_kv_heads * p.head_groups;
+  const LaneOffsets<D, BS> lo = lane_offsets<D, BS>(lane);
+
+  MfmaAcc<D> acc;
+  mfma_reset(acc);
+  u32x4 qcur[NC];
+  int cur_s = -1, cur_hg = 0, cur_t0 = 0, cur_tlast = 0, cur_L = 0;
+
+  auto finish = [&]() {
+    const bool whole = cur_t0 == 0 && cur_tlast == ((cur_L + 15) >> 4) - 1;
+    mfma_write_piece<D>(p, sk, acc, cur_s, cur_hg, whole, rg.w, lane);
+  };
+
+  for (int base = rg.T0; base < rg.T1; base += 64) {
+    const int m = min(64, rg.T1 - base);
+    const TileMeta meta = fetch_meta<BS>(p, ps, H, base + lane, lane < m);
+    // load tile j of the chunk into a pipeline slot, with the pair's Q when
+    // the tile opens a pair (zero-record loads otherwise and past the end)
+    auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC], u32x4(&qt)[NC]) {
+      const int jj = min(j, m - 1);
+      const Uniform u = read_meta(meta, jj);
+      int kvh, h0, ncols;
+      head_span(p, u.hg, kvh, h0, ncols);
+      const bool opens = j < m && (u.t == 0 || base + jj == rg.T0);
+      load_tile<D, BS>(p, kvh, u.b0, u.b1, 16 * u.t, j < m, lo, kt, vt);
+      load_q_operand<D>(p, u.s, u.hg, opens, lane, qt);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC], u32x4(&qt)[NC]) {
+      const Uniform u = read_meta(meta, j);
+      if (u.t == 0 || base + j == rg.T0) {  // the tile opens a pair (or this wave's range)
+        if (cur_s >= 0) finish();
+        mfma_reset(acc);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) qcur[c] = qt[c];
+        cur_s = u.s;
+        cur_hg = u.hg;
+        cur_t0 = u.t;
+        cur_L = u.L;
+      }
+      cur_tlast = u.t;
+      mfma_tile<D>(acc, qcur, p.scale_log2, 16 * u.t, u.L, lane, kt, vt);
+    };
+    u32x4 ak[NC], av[NC], aq[NC], bk[NC], bv[NC], bq[NC], ck[NC], cv[NC], cq[NC];
+    load(0, ak, av, aq);
+    load(1, bk, bv, bq);
+    for (int j = 0;; j += 3) {
+      load(j + 2, ck, cv, cq);
+      compute(j, ak, av, aq);
+      if (j + 1 >= m) break;
+      load(j + 3, ak, av, aq);
+      compute(j + 1, bk, bv, bq);
+      if (j + 2 >= m) break;
+      load(j + 4, bk, bv, bq);
+      compute(j + 2, ck, cv, cq);
+      if (j + 3 >= m) break;
+    }
+  }
+  finish();
+}
+
+template <int D, int BS, int VG>
+__global__ __launch_bounds__(kThreads) void decode_valu_sk(DecodeParams p, StreamParams sk) {
+  constexpr int NC = D / 32;
+  __shared__ int ps[kMaxStreamSeqs + 1];
+  __shared__ int scan[kThreads];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const StreamRange rg = stream_prologue(p, sk, ps, scan, wave);
+  if (rg.T0 >= rg.T1) return;
+  const int H = p.num_kv_heads;
+  const LaneOffsets<D, BS> lo = lane_offsets<D, BS>(lane);
+
+  ValuAcc<D, VG> acc;
+  valu_reset(acc);
+  float qf[VG][NC][8];
+  int cur_s = -1, cur_kvh = 0, cur_t0 = 0, cur_tlast = 0, cur_L = 0;
+
+  auto finish = [&]() {
+    const bool whole = cur_t0 == 0 && cur_tlast == ((cur_L + 15) >> 4) - 1;
+    valu_write_piece<D, VG>(p, sk, acc, cur_s, cur_kvh, whole, rg.w, lane);
+  };
+
+  for (int base = rg.T0; base < rg.T1; base += 64) {
+    const int m = min(64, rg.T1 - base);
+    const TileMeta meta = fetch_meta<BS>(p, ps, H, base + lane, lane < m);
+    auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+      const int jj = min(j, m - 1);
+      const Uniform u = read_meta(meta, jj);
+      load_tile<D, BS>(p, u.hg, u.b0, u.b1, 16 * u.t, j < m, lo, kt, vt);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto compute = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+      const Uniform u = read_meta(meta, j);
+      if (u.t == 0 || base + j == rg.T0) {  // a new pair: its q is loaded here (rare)
+        if (cur_s >= 0) finish();
+        valu_reset(acc);
+        valu_load_q<D, VG>(p, u.s, u.hg * VG, lane, qf);
+        cur_s = u.s;
+        cur_kvh = u.hg;
+        cur_t0 = u.t;
+        cur_L = u.L;
+      }
+      cur_tlast = u.t;
+      valu_tile<D, VG>(acc, qf, p.scale_log2, 16 * u.t, u.L, lane, kt, vt);
+    };
+    u32x4 ak[NC], av[NC], bk[NC], bv[NC], ck[NC], cv[NC];
+    load(0, ak, av);
+    load(1, bk, bv);
+    for (int j = 0;; j += 3) {
+      load(j + 2, ck, cv);
+      compute(j, ak, av);
+      if (j + 1 >= m) break;
+      load(j + 3, ak, av);
+      compute(j + 1, bk, bv);
+      if (j + 2 >= m) break;
+      load(j + 4, bk, bv);
+      compute(j + 2, ck, cv);
+      if (j + 3 >= m) break;
+    }
+  }
+  finish();
+}
+
+// Combine the pieces of every pair cut between waves, and write zeros for
+// empty contexts.  One workgroup per (sequence, head group) pair.
+template <int D>
+__global__ __launch_bounds__(256) void combine_sk(DecodeParams p, StreamParams sk) {
+  const int H = p.num_kv_heads * p.head_groups;
+  const int pair = blockIdx.x;
+  const int s = pair / H;
+  const int hg = pair - s * H;
+  int kvh, h0, ncols;
+  head_span(p, hg, kvh, h0, ncols);
+  const int* ps = sk.plan + kPlanHeader;
+  const int n = ps[s + 1] - ps[s];
+  if (n == 0) {
+    for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x)
+      store_out(p, s, h0 + idx / D, idx % D, 0.f);
+    return;
+  }
+  const int per = sk.plan[0];
+  const int first = H * ps[s] + hg * n;
+  const int wa = first / per;
+  const int wb = (first + n - 1) / per;
+  if (wa == wb) return;  // one wave saw the whole pair and wrote it
+  for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x) {
+    const int col = idx / D;
+    const int d = idx - col * D;
+    float M = kNegInf;
+    for (int w = wa; w <= wb; ++w) M = fmaxf(M, sk.ws_ml[piece_row(pair, w, col) * 2]);
+    float num = 0.f, den = 0.f;
+    for (int w = wa; w <= wb; ++w) {
+      const size_t row = piece_row(pair, w, col);
+      const float wt = sk.ws_ml[row * 2 + 1] * exp2f(sk.ws_ml[row * 2] - M);
+      num += wt * sk.ws_o[row * D + d];
+      den += wt;
+    }
+    store_out(p, s, h0 + col, d, num / den);
+  }
+}
+
+// ===========================================================================
+// partitioned schedule
+// ===========================================================================
+
+// Block-table entries of up to 64 consecutive tiles of one wave, one per lane,
+// so the tile loop never waits on memory for an address: lane j holds the
+// physical block of the wave's tile k0 + j.
+struct TableCache {
+  int b0, b1;
+};
+
+template <int BS>
+__device__ __forceinline__ TableCache fetch_table(const int32_t* bt, int t0, int t1, int wave,
+                                                  int k0, int n, int lane) {
+  TableCache c{0, 0};
+  const int k = k0 + lane;
+  if (k < n) tile_blocks<BS>(bt, (t0 >> 4) + wave + kWaves * k, t1, c.b0, c.b1);
+  return c;
+}
+
+// Walk this wave's tiles (tiles wave, wave + 4, ... of the partition [t0, t1))
+// with the next two tiles' loads issued before the current one is computed.
+template <int D, int BS, typename F>
+__device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int32_t* bt, int kvh,
+                                           int t0, int t1, int wave, int lane, F&& compute) {
+  constexpr int NC = D / 32;
+  const int ntiles = (t1 - t0 + 15) >> 4;
+  const int n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const LaneOffsets<D, BS> lo = lane_offsets<D, BS>(lane);
+  for (int k0 = 0; k0 < n; k0 += 64) {
+    const TableCache tc = fetch_table<BS>(bt, t0, t1, wave, k0, n, lane);
+    const int m = min(64, n - k0);
+    auto start = [&](int j) { return t0 + 16 * (wave + kWaves * (k0 + j)); };
+    auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+      const int jj = min(j, m - 1);
+      const int b0 = __builtin_amdgcn_readlane(tc.b0, jj);
+      const int b1 = BS == 8 ? __builtin_amdgcn_readlane(tc.b1, jj) : 0;
+      load_tile<D, BS>(p, kvh, b0, b1, start(jj), j < m, lo, kt, vt);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    u32x4 ak[NC], av[NC], bk[NC], bv[NC], ck[NC], cv[NC];
+    load(0, ak, av);
+    load(1, bk, bv);
+    for (int j = 0;; j += 3) {
+      load(j + 2, ck, cv);
+      compute(start(j), ak, av);
+      if (j + 1 >= m) break;
+      load(j + 3, ak, av);
+      compute(start(j + 1), bk, bv);
+      if (j + 2 >= m) break;
+      load(j + 4, bk, bv);
+      compute(start(j + 2), ck, cv);
+      if (j + 3 >= m) break;
+    }
+  }
+}
+
 // Per-workgroup LDS for the cross-wave combine.
 template <int D>
 struct Smem {
@@ -278,19 +883,11 @@ struct Smem {
   float o[kWaves][D][17];
 };
 
-__device__ __forceinline__ void store_out(const DecodeParams& p, int s, int h, int d, float r) {
-  const size_t at = size_t(s) * p.out_s + size_t(h) * p.out_h + d;
-  if (p.out_f32)
-    static_cast<float*>(p.out)[at] = r;
-  else
-    static_cast<uint16_t*>(p.out)[at] = uint16_t(bf16_bits(r));
-}
-
 // Combine the waves' (m, l, o) and write either the output (one partition)
 // or this partition's partial result for the combine kernel.
 template <int D>
-__device__ __forceinline__ void finish(const DecodeParams& p, Smem<D>& sm, int s, int h0, int ncols,
-                                       int part, int nparts) {
+__device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>& sm, int s, int h0,
+                                                 int ncols, int part, int nparts) {
   __syncthreads();
   for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
     const int g = idx / D;
@@ -321,19 +918,15 @@ __device__ __forceinline__ void finish(const DecodeParams& p, Smem<D>& sm, int s
   }
 }
 
-// Partitions of sequence s that this launch covers (contexts longer than the
-// launch covers violate the caller's contract; clamping keeps the partition
-// count consistent with the grid).
+// Partitions of sequence s that this launch covers (clamping keeps the
+// partition count consistent with the grid for over-long contexts).
 __device__ __forceinline__ int partitions(const DecodeParams& p, int L) {
-  return min((L + p.part_tokens - 1) / p.part_tokens, p.max_parts);
+  return min((clamp_len(p, L) + p.part_tokens - 1) / p.part_tokens, p.max_parts);
 }
 
-// ---------------------------------------------------------------------------
-// GQA decode on the matrix cores
-// ---------------------------------------------------------------------------
 template <int D, int BS>
 __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeParams p) {
-  constexpr int NC = D / 32;  // 16-byte chunks per lane per tile, for K and for V
+  constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
 
   const int lane = threadIdx.x & 63;
@@ -341,103 +934,46 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeParams p) {
   const int r = lane & 15;
   const int g4 = lane >> 4;
   const int hg = blockIdx.x;
-  const int kvh = hg / p.head_groups;
-  const int cgrp = hg - kvh * p.head_groups;
   const int s = blockIdx.y;
   const int part = blockIdx.z;
+  int kvh, h0, ncols;
+  head_span(p, hg, kvh, h0, ncols);
 
-  const int L = p.context_lens[s];
+  const int L = clamp_len(p, p.context_lens[s]);
   const int nparts = partitions(p, L);
   if (part >= (nparts > 0 ? nparts : 1)) return;
   const int t0 = part * p.part_tokens;
   const int t1 = min(L, t0 + p.part_tokens);
-  const int h0 = kvh * p.group + cgrp * 16;
-  const int ncols = min(16, p.group - cgrp * 16);
   const int32_t* bt = p.block_tables + size_t(s) * p.bt_s;
 
-  // Q as the B operand of QK^T: column r = query head h0 + r (zero past the group)
-  u32x4 qv[NC];
+  u32x4 q[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    qv[c] = u32x4{0u, 0u, 0u, 0u};
-    if (r < ncols) qv[c] = load16(p.q + size_t(s) * p.q_s + size_t(h0 + r) * p.q_h + 8 * (g4 + 4 * c));
+    q[c] = u32x4{0u, 0u, 0u, 0u};
+    if (r < ncols) q[c] = load16(p.q + size_t(s) * p.q_s + size_t(h0 + r) * p.q_h + 8 * (g4 + 4 * c));
   }
-
-  f32x4 oacc[2 * NC];
-#pragma unroll
-  for (int i = 0; i < 2 * NC; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf;  // reference max (log2 units) of column r
-  float l_run = 0.f;      // this lane's share of the running sum of column r
-
-  auto compute = [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NC; ++c) sacc = mfma_16x16x32(kt[c], qv[c], sacc);
-    // lane holds scores of tokens ts + 4*g4 + j for query head column r
-    float sc[4];
-    float mt = kNegInf;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = (ts + 4 * g4 + j < t1) ? sacc[j] * p.scale_log2 : kNegInf;
-      mt = fmaxf(mt, sc[j]);
-    }
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    if (__any(mt > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mt);
-      const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 2 * NC; ++i) oacc[i] *= alpha;
-      m_run = m_new;
-    }
-    float pr[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      pr[j] = exp2f(sc[j] - m_run);
-      l_run += pr[j];
-    }
-    // P as the B operand of PV, split into hi + lo bf16
-    uint32_t hb[4], lb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      hb[j] = bf16_bits(pr[j]);
-      lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
-    }
-    const u32x2 phi = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-    const u32x2 plo = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
-    mask_v<D>(vt, ts, t1, lane);
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x2 a0 = {vt[c].x, vt[c].y};  // dim 2r + 32c, tokens 4*g4 .. +3
-      const u32x2 a1 = {vt[c].z, vt[c].w};  // dim 2r + 32c + 1
-      oacc[2 * c] = mfma_16x16x16(a0, phi, oacc[2 * c]);
-      oacc[2 * c] = mfma_16x16x16(a0, plo, oacc[2 * c]);
-      oacc[2 * c + 1] = mfma_16x16x16(a1, phi, oacc[2 * c + 1]);
-      oacc[2 * c + 1] = mfma_16x16x16(a1, plo, oacc[2 * c + 1]);
-    }
-  };
-
-  walk_tiles<D, BS>(p, bt, kvh, t0, t1, wave, lane, compute);
+  MfmaAcc<D> acc;
+  mfma_reset(acc);
+  walk_tiles<D, BS>(p, bt, kvh, t0, t1, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    mfma_tile<D>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
+  });
 
   // column totals over the four 16-lane groups
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
+  float l = acc.l;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
   if (g4 == 0) {
-    sm.m[wave][r] = m_run;
-    sm.l[wave][r] = l_run;
+    sm.m[wave][r] = acc.m;
+    sm.l[wave][r] = l;
   }
 #pragma unroll
-  for (int mm = 0; mm < 2 * NC; ++mm)
+  for (int mm = 0; mm < D / 16; ++mm)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = oacc[mm][j];
+    for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
 
-  finish<D>(p, sm, s, h0, ncols, part, nparts);
+  finish_partition<D>(p, sm, s, h0, ncols, part, nparts);
 }
 
-// ---------------------------------------------------------------------------
-// MHA decode (1 or 2 query heads per KV head) on the vector ALUs
-// ---------------------------------------------------------------------------
 template <int D, int BS, int VG>
 __global__ __launch_bounds__(kThreads) void decode_valu(DecodeParams p) {
   constexpr int NC = D / 32;
@@ -451,7 +987,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeParams p) {
   const int s = blockIdx.y;
   const int part = blockIdx.z;
 
-  const int L = p.context_lens[s];
+  const int L = clamp_len(p, p.context_lens[s]);
   const int nparts = partitions(p, L);
   if (part >= (nparts > 0 ? nparts : 1)) return;
   const int t0 = part * p.part_tokens;
@@ -459,93 +995,17 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeParams p) {
   const int h0 = kvh * VG;
   const int32_t* bt = p.block_tables + size_t(s) * p.bt_s;
 
-  // this lane's q dims: 8*(g4 + 4c) + e
   float qf[VG][NC][8];
-#pragma unroll
-  for (int g = 0; g < VG; ++g)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const u32x4 u = load16(p.q + size_t(s) * p.q_s + size_t(h0 + g) * p.q_h + 8 * (g4 + 4 * c));
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[g][c][2 * e] = bf_lo(w[e]);
-        qf[g][c][2 * e + 1] = bf_hi(w[e]);
-      }
-    }
-
-  float o[VG][NC][2];
-  float m_run[VG], l_run[VG];
-#pragma unroll
-  for (int g = 0; g < VG; ++g) {
-    m_run[g] = kNegInf;
-    l_run[g] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) o[g][c][0] = o[g][c][1] = 0.f;
-  }
-
-  auto compute = [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-    float kf[NC][8];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint32_t w[4] = {kt[c].x, kt[c].y, kt[c].z, kt[c].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[c][2 * e] = bf_lo(w[e]);
-        kf[c][2 * e + 1] = bf_hi(w[e]);
-      }
-    }
-    mask_v<D>(vt, ts, t1, lane);
-    const bool valid = ts + r < t1;
-#pragma unroll
-    for (int g = 0; g < VG; ++g) {
-      float dot = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dot = fmaf(kf[c][e], qf[g][c][e], dot);
-      dot += shfl_xor(dot, 16);
-      dot += shfl_xor(dot, 32);
-      const float sc = valid ? dot * p.scale_log2 : kNegInf;  // score of token ts + r
-      float mt = sc;
-      mt = fmaxf(mt, shfl_xor(mt, 1));
-      mt = fmaxf(mt, shfl_xor(mt, 2));
-      mt = fmaxf(mt, shfl_xor(mt, 4));
-      mt = fmaxf(mt, shfl_xor(mt, 8));
-      float alpha = 1.f;
-      if (mt > m_run[g] + kRescaleSlack) {  // uniform: mt and m_run are the same in every lane
-        const float m_new = fmaxf(m_run[g], mt);
-        alpha = exp2f(m_run[g] - m_new);
-        l_run[g] *= alpha;
-        m_run[g] = m_new;
-      }
-      const float pr = exp2f(sc - m_run[g]);
-      l_run[g] += pr;
-      float pj[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = __shfl(pr, 4 * g4 + j, 64);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        float a0 = o[g][c][0] * alpha, a1 = o[g][c][1] * alpha;
-        a0 = fmaf(pj[0], bf_lo(vt[c].x), a0);
-        a0 = fmaf(pj[1], bf_hi(vt[c].x), a0);
-        a0 = fmaf(pj[2], bf_lo(vt[c].y), a0);
-        a0 = fmaf(pj[3], bf_hi(vt[c].y), a0);
-        a1 = fmaf(pj[0], bf_lo(vt[c].z), a1);
-        a1 = fmaf(pj[1], bf_hi(vt[c].z), a1);
-        a1 = fmaf(pj[2], bf_lo(vt[c].w), a1);
-        a1 = fmaf(pj[3], bf_hi(vt[c].w), a1);
-        o[g][c][0] = a0;
-        o[g][c][1] = a1;
-      }
-    }
-  };
-
-  walk_tiles<D, BS>(p, bt, kvh, t0, t1, wave, lane, compute);
+  valu_load_q<D, VG>(p, s, h0, lane, qf);
+  ValuAcc<D, VG> acc;
+  valu_reset(acc);
+  walk_tiles<D, BS>(p, bt, kvh, t0, t1, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    valu_tile<D, VG>(acc, qf, p.scale_log2, ts, t1, lane, kt, vt);
+  });
 
 #pragma unroll
   for (int g = 0; g < VG; ++g) {
-    float l = l_run[g];  // per-token shares: sum over the 16 token lanes
+    float l = acc.l[g];  // per-token shares: sum over the 16 token lanes
     l += shfl_xor(l, 1);
     l += shfl_xor(l, 2);
     l += shfl_xor(l, 4);
@@ -554,26 +1014,23 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeParams p) {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        float x = o[g][c][e];  // per-quad shares: sum over the four 16-lane groups
+        float x = acc.o[g][c][e];  // per-quad shares: sum over the four 16-lane groups
         x += shfl_xor(x, 16);
         x += shfl_xor(x, 32);
         if (g4 == 0) sm.o[wave][2 * r + 32 * c + e][g] = x;
       }
     if (lane == 0) {
-      sm.m[wave][g] = m_run[g];
+      sm.m[wave][g] = acc.m[g];
       sm.l[wave][g] = l;
     }
   }
 
-  finish<D>(p, sm, s, h0, VG, part, nparts);
+  finish_partition<D>(p, sm, s, h0, VG, part, nparts);
 }
 
-// ---------------------------------------------------------------------------
-// split-K combine: out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - M),
-// M = max_p m_p, partitions in ascending order.  One thread per (head, dim).
-// ---------------------------------------------------------------------------
+// Partition combine: one thread per (head, dim) of a sequence.
 template <int D>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void combine_parts(DecodeParams p) {
   const int s = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.num_q_heads * D) return;
@@ -621,8 +1078,11 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
 template <int D, int BS>
-hipError_t launch_decode_t(const DecodeParams& p, Path path, hipStream_t stream) {
+hipError_t launch_partitioned(const DecodeParams& p, Path path, hipStream_t stream) {
   const dim3 block(kThreads);
   if (path == Path::Mfma) {
     const dim3 grid(p.num_kv_heads * p.head_groups, p.num_seqs, p.max_parts);
@@ -637,16 +1097,45 @@ hipError_t launch_decode_t(const DecodeParams& p, Path path, hipStream_t stream)
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
-  hipLaunchKernelGGL((combine_kernel<D>), cgrid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((combine_parts<D>), cgrid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+// Persistent grid: as many workgroups as can be resident at once (all waves
+// stream concurrently; a second round would repeat the start-up latency).
+template <typename K>
+hipError_t launch_persistent(K kernel, const DecodeParams& p, const StreamParams& sk, hipStream_t stream) {
+  int occ = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0);
+  if (e != hipSuccess) return e;
+  const int per_cu = std::max(1, std::min(sk.workgroups_per_cu, occ));
+  const int wgs = std::min(sk.cus * per_cu, kMaxStreamWaves / kWaves);
+  hipLaunchKernelGGL(kernel, dim3(wgs), dim3(kThreads), 0, stream, p, sk);
+  return hipGetLastError();
+}
+
+template <int D, int BS>
+hipError_t launch_stream(const DecodeParams& p, const StreamParams& sk, Path path, hipStream_t stream) {
+  hipError_t e;
+  if (path == Path::Mfma)
+    e = launch_persistent(decode_mfma_sk<D, BS>, p, sk, stream);
+  else if (p.group == 1)
+    e = launch_persistent(decode_valu_sk<D, BS, 1>, p, sk, stream);
+  else
+    e = launch_persistent(decode_valu_sk<D, BS, 2>, p, sk, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((combine_sk<D>), dim3(p.num_seqs * p.num_kv_heads * p.head_groups), dim3(256), 0,
+                     stream, p, sk);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_decode_d(const DecodeParams& p, int block_size, Path path, hipStream_t stream) {
+hipError_t launch_decode_d(const DecodeParams& p, const StreamParams* sk, int block_size, Path path,
+                           hipStream_t stream) {
   switch (block_size) {
-    case 8: return launch_decode_t<D, 8>(p, path, stream);
-    case 16: return launch_decode_t<D, 16>(p, path, stream);
-    case 32: return launch_decode_t<D, 32>(p, path, stream);
+    case 8: return sk ? launch_stream<D, 8>(p, *sk, path, stream) : launch_partitioned<D, 8>(p, path, stream);
+    case 16: return sk ? launch_stream<D, 16>(p, *sk, path, stream) : launch_partitioned<D, 16>(p, path, stream);
+    case 32: return sk ? launch_stream<D, 32>(p, *sk, path, stream) : launch_partitioned<D, 32>(p, path, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -667,10 +1156,10 @@ hipError_t launch_append_d(const AppendParams& p, int block_size, hipStream_t st
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int head_dim, int block_size, Path path,
-                         hipStream_t stream) {
-  if (head_dim == 64) return launch_decode_d<64>(p, block_size, path, stream);
-  if (head_dim == 128) return launch_decode_d<128>(p, block_size, path, stream);
+hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
+                         Path path, hipStream_t stream) {
+  if (head_dim == 64) return launch_decode_d<64>(p, sk, block_size, path, stream);
+  if (head_dim == 128) return launch_decode_d<128>(p, sk, block_size, path, stream);
   return hipErrorInvalidValue;
 }
 

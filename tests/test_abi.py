@@ -141,9 +141,18 @@ def test_workspace_bytes(lib):
     f = lib.pa_decode_workspace_bytes
     up = lambda x: (x + 255) // 256 * 256
     # 64 seqs, 32/8 heads, D 128, contexts up to 2048 tokens -> 4 partitions of 512
-    # (max, sum) pairs then outputs, fp32, per (seq, q head, partition)
+    # partitioned: (max, sum) pairs then outputs, fp32, per (seq, q head, partition)
     expect = up(4 * 2 * 64 * 32 * 4) + up(4 * 64 * 32 * 4 * 128)
-    assert f(64, 32, 8, 128, 2048, 0) == expect
-    assert f(64, 32, 8, 128, 512, 0) == 0          # one partition: no workspace
+    assert f(64, 32, 8, 128, 2048, 512) == expect
+    assert f(64, 32, 8, 128, 512, 512) == 0        # one partition: no workspace
     assert f(64, 32, 8, 128, 2048, -1) == 0        # never split
     assert f(8, 32, 8, 128, 32768, 512) == up(4 * 2 * 8 * 32 * 64) + up(4 * 8 * 32 * 64 * 128)
+    # stream-K (automatic): plan (4 + S + 1 ints), then 16-column pieces for
+    # (pairs + 4096 waves): (max, sum) and outputs
+    for S, Hq, Hkv, D in ((64, 32, 8, 128), (256, 64, 8, 128), (4, 8, 2, 64), (3, 64, 2, 128)):
+        pairs = S * Hkv * -(-(Hq // Hkv) // 16)
+        pieces = (pairs + 4096) * 16
+        expect = up(4 * (S + 5)) + up(4 * 2 * pieces) + up(4 * pieces * D)
+        assert f(S, Hq, Hkv, D, 2048, 0) == expect
+    # too many sequences for the stream-K prefix: partitions of 512
+    assert f(9000, 8, 8, 128, 1024, 0) == up(4 * 2 * 9000 * 8 * 2) + up(4 * 9000 * 8 * 2 * 128)

@@ -78,6 +78,36 @@ def test_split_variants(part):
                  f"part {part} f32", max_abs=1e-4, rel_rms=1e-4)
 
 
+STREAM_CASES = [
+    # (lens, Hq, Hkv, D, B, workgroups_per_cu)
+    ([3000, 1, 700, 2049, 64], 16, 4, 128, 16, 1),     # tiny per-wave ranges: every pair split
+    ([3000, 1, 700, 2049, 64], 16, 4, 128, 16, 8),
+    ([20000, 30000], 32, 8, 128, 32, 1),               # ranges longer than 64 tiles
+    ([0, 17, 0, 5000, 0], 8, 2, 64, 8, 2),             # empty contexts between live ones
+    ([0, 0, 0], 8, 2, 64, 16, 2),                      # nothing to read at all
+    ([33, 900, 4100, 2], 4, 4, 128, 16, 1),            # MHA (VALU) pieces
+    ([33, 900, 4100, 2], 8, 4, 64, 8, 4),              # two heads per KV head (VALU)
+    ([700, 1, 2500], 64, 2, 128, 16, 2),               # 32 heads per KV head: two column groups
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=[f"stream{i}" for i in range(len(STREAM_CASES))])
+def test_stream_schedule(case):
+    torch = need_gpu()
+    lens, Hq, Hkv, D, B, wpc = case
+    w = workloads.random_workload(71 + len(lens) + wpc, lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                                  head_dim=D, block_size=B)
+    dw = _setup(w)
+    _, _, ref = oracle_step(w)
+    got = _decode(torch, w, dw, torch.float32, workgroups_per_cu=wpc)
+    assert_close(_as_f64(torch, got), ref, f"stream-K wpc={wpc}", max_abs=1e-4, rel_rms=1e-4)
+    got16 = _decode(torch, w, dw, workgroups_per_cu=wpc)
+    assert_close(_as_f64(torch, got16), ref, f"stream-K bf16 wpc={wpc}")
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert torch.all(got[s] == 0)
+
+
 @pytest.mark.parametrize("G", [1, 2])
 def test_valu_and_mfma_paths_agree(G):
     torch = need_gpu()
