@@ -201,7 +201,7 @@ def test_decode_ex_matches_decode_and_checks_workspace():
                                   head_dim=128, block_size=16)
     dw = _setup(w)
     a = dev.bf16_bits(_decode(torch, w, dw))
-    b = dev.bf16_bits(_decode(torch, w, dw, partition_tokens=512))
+    b = dev.bf16_bits(_decode(torch, w, dw, workgroups_per_cu=0))  # same schedule, caller workspace
     assert np.array_equal(a, b)
     out = torch.empty_like(dw.q)
     with pytest.raises(pa.PaError) as e:

@@ -232,6 +232,7 @@ def test_empty_context_reads_no_block():
     w = workloads.random_workload(3, [0, 21, 0], num_q_heads=4, num_kv_heads=2, head_dim=64,
                                   block_size=8)
     kst, vst = w.stores()
+    oracle.cache_append(w.k_new, w.v_new, w.slot_mapping, kst, vst, w.block_size)
     for fn in (oracle.paged_decode, oracle.paged_decode_online, oracle.paged_decode_eq4):
         out = fn(w.q, kst, vst, w.block_tables, w.context_lens, w.scale, w.block_size)
         assert np.all(out[0] == 0) and np.all(out[2] == 0) and np.all(np.isfinite(out[1]))
