@@ -112,12 +112,20 @@ int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slo
  * their values (even NaN) cannot affect the result.  bf16 products, fp32
  * accumulation; results are bitwise deterministic.
  *
- * Schedule.  For batches of up to 8192 sequences the tiles of 16 tokens of all
- * (sequence, KV head) pairs are cut into equal contiguous ranges, one per wave
- * of a persistent grid ("stream-K"); a context cut between waves is split at
- * those cuts.  Larger batches use partitions of 512 tokens.  Either way a
- * second kernel combines the partial results of a split context in ascending
- * token order with a log-sum-exp reduce.  The partial results live in a
+ * Schedule, chosen from the shapes alone (P = num_seqs * num_kv_heads *
+ * ceil(G / 16) pairs, G = q heads per KV head, Lmax = table width *
+ * block_size):
+ *   P >= 512, G >= 3, Lmax <= 8192  one workgroup per pair, no split;
+ *   P >= 512 otherwise              partitions of 1024 tokens;
+ *   P * ceil(Lmax / 16) <= 4096     one workgroup per pair (tiny batch);
+ *   otherwise                       stream-K: the 16-token tiles of all pairs
+ *                                   are cut into equal contiguous ranges, one
+ *                                   per wave of a persistent grid, and a
+ *                                   context is split where a cut falls
+ *                                   (batches of more than 8192 sequences:
+ *                                   partitions of 512 tokens).
+ * A second kernel combines the partial results of a split context in
+ * ascending token order with a log-sum-exp reduce.  The partial results live in a
  * library-owned workspace on the current device, grown with hipMalloc when a
  * call needs more (never during stream capture: that returns PA_ERR_WORKSPACE;
  * use pa_decode_ex there).  Calls that need the workspace may not overlap on
@@ -130,9 +138,9 @@ int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
 
 /* options for pa_decode_ex; a zero-initialised struct means "as pa_decode" */
 typedef struct {
-  int32_t partition_tokens;  /* 0: automatic (the stream-K schedule below when it
-                                applies, else partitions of 512 tokens);
+  int32_t partition_tokens;  /* 0: automatic, from the shapes (see pa_decode);
                                 -1: one partition per sequence (never split);
+                                -2: the stream-K schedule;
                                 else partitions of this many tokens, a positive
                                 multiple of 32 */
   int32_t path;              /* 0: auto (MFMA when q heads per KV head >= 3, else VALU);

@@ -202,6 +202,35 @@ bool stream_fits(int64_t S, int64_t pairs, int64_t max_len) {
   return S <= pa::kMaxStreamSeqs && tiles < (int64_t(1) << 30);
 }
 
+// Schedule of an automatic call, from shapes only (no device read, the same on
+// every device so that pa_decode_workspace_bytes agrees with pa_decode_ex).
+// Measured on MI355X with caches flushed:
+//  * enough (sequence, head group) pairs to give every wave of a full GPU
+//    (256 CUs x 8 waves) its own share -> one workgroup per pair, no split and
+//    no combine launch (Llama-3-8B/70B-shaped batches);
+//  * MHA (1-2 q heads per KV head) with that many pairs -> 1024-token
+//    partitions, which keep the shared prefix blocks of neighbouring sequences
+//    in flight together;
+//  * tiny batches -> one workgroup per pair (the launch cost dominates);
+//  * otherwise (few, long contexts) -> stream-K.
+constexpr int64_t kFullGpuPairs = 512;
+constexpr int64_t kTinyTiles = 4096;
+constexpr int64_t kNoSplitMaxLen = 8192;
+
+struct Schedule {
+  bool stream;
+  int64_t part;  // partitioned: tokens per partition (-1 = one per sequence)
+};
+
+Schedule auto_schedule(int64_t S, int64_t pairs, int64_t group, int64_t max_len) {
+  const int64_t tiles = (max_len + pa::kTileTokens - 1) / pa::kTileTokens;
+  if (pairs >= kFullGpuPairs)
+    return {false, group <= 2 ? 1024 : (max_len <= kNoSplitMaxLen ? -1 : 1024)};
+  if (pairs * tiles <= kTinyTiles) return {false, -1};
+  if (stream_fits(S, pairs, max_len)) return {true, 0};
+  return {false, pa::kDefaultPartition};
+}
+
 // CUs of the current device (cached per device).
 int device_cus(int* cus) {
   static std::mutex mu;
@@ -293,7 +322,20 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
   pl->NB = g.num_blocks;
   pl->path = path;
   pl->workgroups_per_cu = wpc > 0 ? wpc : pa::kDefaultWorkgroupsPerCu;
-  if (pt_opt == 0 && stream_fits(S, pairs, W * g.block_size)) {
+  int64_t want_part;  // -2 stream-K, -1 one partition per sequence, > 0 partition tokens
+  if (pt_opt == 0) {
+    const Schedule sc = auto_schedule(S, S * g.kv_heads * ((G + 15) / 16), G, max_len);
+    want_part = sc.stream ? -2 : sc.part;
+  } else if (pt_opt == -1 || pt_opt == -2 || (pt_opt > 0 && pt_opt % 32 == 0)) {
+    want_part = pt_opt;
+  } else {
+    return fail(PA_ERR_INVALID,
+                "opts.partition_tokens %d (0, -1, -2 or a positive multiple of 32)", pt_opt);
+  }
+  if (want_part == -2) {
+    if (!stream_fits(S, pairs, W * g.block_size))
+      return fail(PA_ERR_UNSUPPORTED, "stream-K schedule: more than %d sequences or too many tiles",
+                  pa::kMaxStreamSeqs);
     pl->stream = true;
     pl->part_tokens = 0;
     pl->max_parts = 1;
@@ -301,16 +343,8 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
     return PA_OK;
   }
   pl->stream = false;
-
-  int64_t part;
-  if (pt_opt == 0)
-    part = pa::kDefaultPartition;
-  else if (pt_opt == -1)
-    part = std::max<int64_t>(32, (max_len + 31) / 32 * 32);
-  else if (pt_opt > 0 && pt_opt % 32 == 0)
-    part = pt_opt;
-  else
-    return fail(PA_ERR_INVALID, "opts.partition_tokens %d (0, -1 or a positive multiple of 32)", pt_opt);
+  const int64_t part =
+      want_part == -1 ? std::max<int64_t>(32, (max_len + 31) / 32 * 32) : want_part;
   if (part > (int64_t(1) << 30)) return fail(PA_ERR_UNSUPPORTED, "partition too large");
   const int64_t max_parts = std::max<int64_t>(1, (max_len + part - 1) / part);
   if (max_parts > 65535)
@@ -439,17 +473,16 @@ PA_EXPORT size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads
     return 0;
   const int64_t group = num_q_heads / num_kv_heads;
   const int64_t pairs = num_seqs * num_kv_heads * ((group + 15) / 16);
-  if (partition_tokens == 0 && stream_fits(num_seqs, pairs, max_context_len))
-    return pa::stream_workspace_layout(num_seqs, pairs, head_dim).total;
-  int64_t part;
-  if (partition_tokens == 0)
-    part = pa::kDefaultPartition;
-  else if (partition_tokens == -1)
-    return 0;
-  else if (partition_tokens > 0)
-    part = partition_tokens;
-  else
-    return 0;
+  int64_t part = partition_tokens;
+  if (part == 0) {
+    const Schedule sc = auto_schedule(num_seqs, pairs, group, max_context_len);
+    part = sc.stream ? -2 : sc.part;
+  }
+  if (part == -2)
+    return stream_fits(num_seqs, pairs, max_context_len)
+               ? pa::stream_workspace_layout(num_seqs, pairs, head_dim).total
+               : 0;
+  if (part <= 0) return 0;  // -1: one partition per sequence, nothing to combine
   const int64_t max_parts = std::max<int64_t>(1, (max_context_len + part - 1) / part);
   if (max_parts == 1) return 0;
   return pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts).total;

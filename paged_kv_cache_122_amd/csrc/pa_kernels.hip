@@ -780,10 +780,44 @@ __global__ __launch_bounds__(kThreads) void decode_valu_sk(DecodeParams p, Strea
   finish();
 }
 
+// Log-sum-exp combine of n pieces (rows row0 + i * stride, i ascending) for
+// dim d: a single pass with a running max, the loads of up to kBatch pieces
+// issued together so the kernel pays one memory latency per batch.
+constexpr int kCombineBatch = 16;
+
+template <int D>
+__device__ __forceinline__ float lse_combine(const float* ml, const float* o, size_t row0,
+                                             size_t stride, int n, int d) {
+  float M = kNegInf, num = 0.f, den = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kCombineBatch) {
+    float m[kCombineBatch], l[kCombineBatch], x[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const bool live = i0 + k < n;
+      const size_t row = row0 + size_t(live ? i0 + k : 0) * stride;
+      m[k] = live ? ml[row * 2] : kNegInf;
+      l[k] = live ? ml[row * 2 + 1] : 0.f;
+      x[k] = live ? o[row * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      if (i0 + k < n) {
+        const float Mn = fmaxf(M, m[k]);
+        const float a = exp2f(M - Mn);
+        const float b = l[k] * exp2f(m[k] - Mn);
+        num = num * a + b * x[k];
+        den = den * a + b;
+        M = Mn;
+      }
+    }
+  }
+  return num / den;
+}
+
 // Combine the pieces of every pair cut between waves, and write zeros for
 // empty contexts.  One workgroup per (sequence, head group) pair.
 template <int D>
-__global__ __launch_bounds__(256) void combine_sk(DecodeParams p, StreamParams sk) {
+__global__ __launch_bounds__(512) void combine_sk(DecodeParams p, StreamParams sk) {
   const int H = p.num_kv_heads * p.head_groups;
   const int pair = blockIdx.x;
   const int s = pair / H;
@@ -805,16 +839,8 @@ __global__ __launch_bounds__(256) void combine_sk(DecodeParams p, StreamParams s
   for (int idx = threadIdx.x; idx < ncols * D; idx += blockDim.x) {
     const int col = idx / D;
     const int d = idx - col * D;
-    float M = kNegInf;
-    for (int w = wa; w <= wb; ++w) M = fmaxf(M, sk.ws_ml[piece_row(pair, w, col) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int w = wa; w <= wb; ++w) {
-      const size_t row = piece_row(pair, w, col);
-      const float wt = sk.ws_ml[row * 2 + 1] * exp2f(sk.ws_ml[row * 2] - M);
-      num += wt * sk.ws_o[row * D + d];
-      den += wt;
-    }
-    store_out(p, s, h0 + col, d, num / den);
+    const float r = lse_combine<D>(sk.ws_ml, sk.ws_o, piece_row(pair, wa, col), 16, wb - wa + 1, d);
+    store_out(p, s, h0 + col, d, r);
   }
 }
 
@@ -1039,15 +1065,7 @@ __global__ __launch_bounds__(256) void combine_parts(DecodeParams p) {
   const int h = idx / D;
   const int d = idx - h * D;
   const size_t row0 = (size_t(s) * p.num_q_heads + h) * p.max_parts;
-  float M = kNegInf;
-  for (int q = 0; q < nparts; ++q) M = fmaxf(M, p.ws_ml[(row0 + q) * 2]);
-  float num = 0.f, den = 0.f;
-  for (int q = 0; q < nparts; ++q) {
-    const float w = p.ws_ml[(row0 + q) * 2 + 1] * exp2f(p.ws_ml[(row0 + q) * 2] - M);
-    num += w * p.ws_o[(row0 + q) * D + d];
-    den += w;
-  }
-  store_out(p, s, h, d, num / den);
+  store_out(p, s, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
 }
 
 // ---------------------------------------------------------------------------
@@ -1124,7 +1142,7 @@ hipError_t launch_stream(const DecodeParams& p, const StreamParams& sk, Path pat
   else
     e = launch_persistent(decode_valu_sk<D, BS, 2>, p, sk, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((combine_sk<D>), dim3(p.num_seqs * p.num_kv_heads * p.head_groups), dim3(256), 0,
+  hipLaunchKernelGGL((combine_sk<D>), dim3(p.num_seqs * p.num_kv_heads * p.head_groups), dim3(512), 0,
                      stream, p, sk);
   return hipGetLastError();
 }

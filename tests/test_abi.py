@@ -107,11 +107,16 @@ def test_validation_errors(lib):
     assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 1, 0)) == pa.PA_ERR_UNSUPPORTED
     assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(48, 0, 0)) == pa.PA_ERR_INVALID
     assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 3, 0)) == pa.PA_ERR_INVALID
-    # W*B = 2048 tokens -> 4 partitions of 512: a workspace is required
-    assert call_decode_ex(lib, decode_args(W=128), pa.PaDecodeOpts(0, 0, 0)) == pa.PA_ERR_WORKSPACE
-    assert call_decode_ex(lib, decode_args(W=128), pa.PaDecodeOpts(0, 0, 0), ctypes.c_void_p(FAKE), 100) \
-        == pa.PA_ERR_WORKSPACE
-    assert b"workspace" in lib.pa_last_error()
+    # W*B = 2048 tokens -> 4 partitions of 512, or the stream-K schedule: a workspace is
+    # required, and a missing or short one is rejected before anything is launched
+    for part in (512, -2):
+        assert call_decode_ex(lib, decode_args(W=128), pa.PaDecodeOpts(part, 0, 0)) == pa.PA_ERR_WORKSPACE
+        assert call_decode_ex(lib, decode_args(W=128), pa.PaDecodeOpts(part, 0, 0),
+                              ctypes.c_void_p(FAKE), 100) == pa.PA_ERR_WORKSPACE
+        assert b"workspace" in lib.pa_last_error()
+    assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(-3, 0, 0)) == pa.PA_ERR_INVALID
+    assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 0, 0, 65)) == pa.PA_ERR_INVALID
+    assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 0, 0, 0, 1)) == pa.PA_ERR_INVALID
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -147,12 +152,20 @@ def test_workspace_bytes(lib):
     assert f(64, 32, 8, 128, 512, 512) == 0        # one partition: no workspace
     assert f(64, 32, 8, 128, 2048, -1) == 0        # never split
     assert f(8, 32, 8, 128, 32768, 512) == up(4 * 2 * 8 * 32 * 64) + up(4 * 8 * 32 * 64 * 128)
-    # stream-K (automatic): plan (4 + S + 1 ints), then 16-column pieces for
-    # (pairs + 4096 waves): (max, sum) and outputs
-    for S, Hq, Hkv, D in ((64, 32, 8, 128), (256, 64, 8, 128), (4, 8, 2, 64), (3, 64, 2, 128)):
+    # stream-K: plan (4 + S + 1 ints), then 16-column pieces for (pairs + 4096
+    # waves): (max, sum) and outputs
+    def stream_bytes(S, Hq, Hkv, D):
         pairs = S * Hkv * -(-(Hq // Hkv) // 16)
         pieces = (pairs + 4096) * 16
-        expect = up(4 * (S + 5)) + up(4 * 2 * pieces) + up(4 * pieces * D)
-        assert f(S, Hq, Hkv, D, 2048, 0) == expect
-    # too many sequences for the stream-K prefix: partitions of 512
-    assert f(9000, 8, 8, 128, 1024, 0) == up(4 * 2 * 9000 * 8 * 2) + up(4 * 9000 * 8 * 2 * 128)
+        return up(4 * (S + 5)) + up(4 * 2 * pieces) + up(4 * pieces * D)
+    for S, Hq, Hkv, D in ((64, 32, 8, 128), (256, 64, 8, 128), (4, 8, 2, 64), (3, 64, 2, 128)):
+        assert f(S, Hq, Hkv, D, 2048, -2) == stream_bytes(S, Hq, Hkv, D)
+    # automatic schedule, from the shapes alone
+    assert f(64, 32, 8, 128, 2048, 0) == 0                                 # 512 pairs: no split
+    assert f(128, 40, 40, 128, 2048, 0) == f(128, 40, 40, 128, 2048, 1024)  # MHA: 1024-token parts
+    assert f(4, 8, 2, 64, 912, 0) == 0                                      # tiny: no split
+    assert f(8, 32, 8, 128, 32768, 0) == stream_bytes(8, 32, 8, 128)        # few long contexts
+    assert f(64, 32, 8, 128, 16384, 0) == f(64, 32, 8, 128, 16384, 1024)   # long, many pairs
+    assert f(9000, 32, 8, 128, 16384, 0) == up(4 * 2 * 9000 * 32 * 16) + up(4 * 9000 * 32 * 16 * 128)
+    # too many sequences for the stream-K prefix: few pairs fall back to 512-token partitions
+    assert f(9000, 8, 8, 128, 1024, -2) == 0

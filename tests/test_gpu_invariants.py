@@ -66,7 +66,7 @@ def test_edge_lengths_every_geometry(D, B, Hq, Hkv):
                  max_abs=1e-4, rel_rms=1e-4)
 
 
-@pytest.mark.parametrize("part", [32, 64, 96, 512, -1])
+@pytest.mark.parametrize("part", [32, 64, 96, 512, -1, -2])
 def test_split_variants(part):
     torch = need_gpu()
     w = workloads.random_workload(31, [3000, 1, 700, 2049, 64], num_q_heads=16, num_kv_heads=4,
@@ -99,9 +99,9 @@ def test_stream_schedule(case):
                                   head_dim=D, block_size=B)
     dw = _setup(w)
     _, _, ref = oracle_step(w)
-    got = _decode(torch, w, dw, torch.float32, workgroups_per_cu=wpc)
+    got = _decode(torch, w, dw, torch.float32, partition_tokens=-2, workgroups_per_cu=wpc)
     assert_close(_as_f64(torch, got), ref, f"stream-K wpc={wpc}", max_abs=1e-4, rel_rms=1e-4)
-    got16 = _decode(torch, w, dw, workgroups_per_cu=wpc)
+    got16 = _decode(torch, w, dw, partition_tokens=-2, workgroups_per_cu=wpc)
     assert_close(_as_f64(torch, got16), ref, f"stream-K bf16 wpc={wpc}")
     for s, L in enumerate(lens):
         if L == 0:
