@@ -162,15 +162,16 @@ def test_block_permutation_gives_identical_bits():
     assert np.array_equal(dev.bf16_bits(_decode(torch, w, dw)), ref)
 
 
-def test_runs_are_bitwise_deterministic():
+@pytest.mark.parametrize("part", [0, 512, -2])
+def test_runs_are_bitwise_deterministic(part):
     torch = need_gpu()
     from paged_kv_cache_122_amd import device as dev
     w = workloads.random_workload(54, [4000, 2500, 100], num_q_heads=32, num_kv_heads=8,
                                   head_dim=128, block_size=16)
     dw = _setup(w)
-    a = dev.bf16_bits(_decode(torch, w, dw))
+    a = dev.bf16_bits(_decode(torch, w, dw, partition_tokens=part))
     for _ in range(3):
-        assert np.array_equal(dev.bf16_bits(_decode(torch, w, dw)), a)
+        assert np.array_equal(dev.bf16_bits(_decode(torch, w, dw, partition_tokens=part)), a)
 
 
 def test_strided_q_and_out():
@@ -204,10 +205,12 @@ def test_decode_ex_matches_decode_and_checks_workspace():
     b = dev.bf16_bits(_decode(torch, w, dw, workgroups_per_cu=0))  # same schedule, caller workspace
     assert np.array_equal(a, b)
     out = torch.empty_like(dw.q)
-    with pytest.raises(pa.PaError) as e:
-        pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                     w.block_size, workspace=torch.zeros(64, dtype=torch.uint8, device=dw.q.device))
-    assert e.value.code == pa.PA_ERR_WORKSPACE
+    for part in (512, -2):
+        with pytest.raises(pa.PaError) as e:
+            pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                         w.block_size, partition_tokens=part,
+                         workspace=torch.zeros(64, dtype=torch.uint8, device=dw.q.device))
+        assert e.value.code == pa.PA_ERR_WORKSPACE
 
 
 def test_workspace_reuse_across_layouts():
