@@ -1,5 +1,5 @@
 """Benchmark of one paged-decode layer step on one MI355X: slot-mapped append of
-this step's K/V, then paged decode attention (with its fused split-K combine).
+this step's K/V, then paged decode attention.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 
@@ -7,12 +7,15 @@ Prints ONE JSON line.  ``value`` is effective KV-read GB/s of the whole step
 (sum_s L_s * Hkv * D * 2 (K and V) * 2 bytes, divided by the event-timed
 append + decode time).  Inputs are resident in HBM; before every timed step a
 1 GiB buffer is written so that neither L2 nor the 256 MB Infinity Cache
-still holds the pools (the flush is outside the timed region).  ``roofline``
-is the decode kernel alone against 8 TB/s.  ``cpu_baseline`` is the fp64
-oracle on a bounded sample of the same workload, on this host's CPU.
+still holds the pools (the flush is outside the timed region).  All work runs
+on one stream of this process and the HIP events are recorded on it.
+``roofline`` is the pa_decode call alone (on the default workload a single
+kernel) against 8 TB/s.  ``cpu_baseline`` is the fp64 oracle on a bounded
+sample of the same workload, on this host's CPU.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +27,15 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "llama3_8b_b64"
 
+# HBM bytes per pa_decode launch on the default workload, from two rocprofv3
+# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by what
+# the counter reads for a plain copy of known size in the same run.  Valid only
+# for the kernel sources they were taken on (sha256 of the files below);
+# reported as null once those change.
+KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
+                  "paged_kv_cache_122_amd/csrc/pa_internal.h")
+MEASURED_TRAFFIC = None  # {"sources_sha256": ..., "config": ..., "fetch_bytes": ..., "write_bytes": ...}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -34,7 +46,39 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--unflushed", action="store_true",
+                    help="also time back-to-back steps without the cache flush")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the benchmark, copy a float32 buffer of this many MiB three "
+                         "times (a known-size kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config):
+    t = MEASURED_TRAFFIC
+    if not t or t["config"] != config or t["sources_sha256"] != sources_sha256():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
+
+def decode_kernels(w, part):
+    """Kernels one automatic pa_decode call launches on this workload."""
+    g = w.num_q_heads // w.num_kv_heads
+    core = f"decode_{'mfma' if g >= 3 else 'valu'}"
+    tmpl = f"<{w.head_dim},{w.block_size}>"
+    if part == -2:
+        return [core + "_sk" + tmpl, f"combine_sk<{w.head_dim}>"], "stream-K"
+    if part == -1 or part >= w.block_tables.shape[1] * w.block_size:
+        return [core + tmpl], "one workgroup per (sequence, head group), no split"
+    return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
 
 
 def percentile(xs, q):
@@ -113,44 +157,64 @@ def main():
     dw = dev.upload(w, "cuda:0")
     out = torch.empty_like(dw.q)
     eff_bytes = w.effective_kv_bytes()
+    max_len = int(w.block_tables.shape[1]) * w.block_size
+    part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
+    kernels, schedule = decode_kernels(w, part)
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
-
-    def step():
-        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
-        pa.decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                  w.block_size)
-
-    for _ in range(args.warmup):
-        flush.zero_()
-        step()
+    stream = torch.cuda.Stream()  # default priority
     torch.cuda.synchronize()
+
+    def append():
+        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, stream=stream)
+
+    def decode():
+        pa.decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                  w.block_size, stream=stream)
 
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [(E(), E(), E()) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for e0, e1, e2 in ev:
-        flush.zero_()
-        e0.record()
-        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
-        e1.record()
-        pa.decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                  w.block_size)
-        e2.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    append_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    decode_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            flush.zero_()
+            append()
+            decode()
+        stream.synchronize()
 
-    # back-to-back steps without the flush (caches may hold part of the pools)
-    hot = [(E(), E()) for _ in range(args.steps)]
-    for a, b in hot:
-        a.record()
-        step()
-        b.record()
-    torch.cuda.synchronize()
-    hot_ms = [a.elapsed_time(b) for a, b in hot]
+        ev = [(E(), E(), E()) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        for e0, e1, e2 in ev:
+            flush.zero_()
+            e0.record(stream)
+            append()
+            e1.record(stream)
+            decode()
+            e2.record(stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        append_ms = [a.elapsed_time(b) for a, b, _ in ev]
+        decode_ms = [b.elapsed_time(c) for _, b, c in ev]
+        step_ms = [a.elapsed_time(c) for a, _, c in ev]
+
+        hot_ms = []
+        if args.unflushed:  # back-to-back steps (caches may hold part of the pools)
+            hot = [(E(), E()) for _ in range(args.steps)]
+            for a, b in hot:
+                a.record(stream)
+                append()
+                decode()
+                b.record(stream)
+            stream.synchronize()
+            hot_ms = [a.elapsed_time(b) for a, b in hot]
+
+        if args.copy_calibration > 0:
+            n = args.copy_calibration << 18  # float32 elements
+            src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            stream.synchronize()
+            del src, dst
 
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     t_step = mean(step_ms) / 1e3
@@ -182,7 +246,8 @@ def main():
             "max_context_len": int(w.context_lens.max()),
             "effective_kv_bytes": eff_bytes,
             "seed": w.seed,
-            "step": "pa_cache_append + pa_decode (fused split-K combine), caches flushed before each step",
+            "step": "pa_cache_append + pa_decode, caches flushed before each step",
+            "schedule": schedule,
         },
         "seqs_per_s": round(w.num_seqs / t_step, 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
@@ -190,19 +255,23 @@ def main():
                       "p50": round(percentile(decode_ms, 50), 5),
                       "p90": round(percentile(decode_ms, 90), 5)},
         "append_ms": {"mean": round(mean(append_ms), 5), "p50": round(percentile(append_ms, 50), 5)},
-        "unflushed_step_ms": {"mean": round(mean(hot_ms), 5), "p50": round(percentile(hot_ms, 50), 5),
-                              "gbs": round(eff_bytes / (mean(hot_ms) / 1e3) / 1e9, 2)},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode (pa_decode: decode_mfma with fused combine)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
+            "kernels": kernels,
+            "algorithmic_bytes": eff_bytes,
+            "timed": "HIP events around each pa_decode call on its stream, caches flushed",
         },
     }
+    if hot_ms:
+        line["unflushed_step_ms"] = {"mean": round(mean(hot_ms), 5),
+                                     "p50": round(percentile(hot_ms, 50), 5),
+                                     "gbs": round(eff_bytes / (mean(hot_ms) / 1e3) / 1e9, 2)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)

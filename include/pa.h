@@ -160,6 +160,17 @@ size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads, int64_t 
                                  int32_t partition_tokens);
 
 /*
+ * The schedule an automatic call (pa_decode, or pa_decode_ex with
+ * partition_tokens 0) takes for these sizes, where max_context_len is the
+ * table width times block_size (or opts.max_context_len): *partition_tokens
+ * receives -1 (no split), -2 (stream-K) or the partition size in tokens.
+ * Returns PA_OK, or PA_ERR_INVALID for a NULL pointer, negative sizes or
+ * num_q_heads not a multiple of num_kv_heads.  Host only; launches nothing.
+ */
+int pa_decode_schedule(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                       int64_t max_context_len, int32_t* partition_tokens);
+
+/*
  * pa_decode_ex -- pa_decode with options and a caller-owned workspace.
  *
  * `workspace` is device memory of at least pa_decode_workspace_bytes(...)

@@ -19,7 +19,7 @@ PA_BF16, PA_F32, PA_I32, PA_I64 = 1, 2, 3, 4
 MAX_DIMS = 5
 
 EXPORTED = ("pa_cache_append", "pa_decode", "pa_decode_ex", "pa_decode_workspace_bytes",
-            "pa_last_error", "pa_set_debug")
+            "pa_decode_schedule", "pa_last_error", "pa_set_debug")
 
 _DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.int32: PA_I32, torch.int64: PA_I64}
 
@@ -64,6 +64,8 @@ def load(path=None):
     lib.pa_decode_ex.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.pa_decode_schedule.argtypes = [ctypes.c_int64] * 4 + [ctypes.POINTER(ctypes.c_int32)]
+    lib.pa_decode_schedule.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
     lib.pa_set_debug.argtypes = [ctypes.c_int]
@@ -134,6 +136,15 @@ def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_l
                     partition_tokens=0):
     return int(load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                 max_context_len, partition_tokens))
+
+
+def schedule(num_seqs, num_q_heads, num_kv_heads, max_context_len):
+    """Partition choice of an automatic call: -1 no split, -2 stream-K, else tokens."""
+    lib = load()
+    part = ctypes.c_int32(0)
+    _check(lib, lib.pa_decode_schedule(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                       ctypes.byref(part)))
+    return int(part.value)
 
 
 def alloc_workspace(nbytes, device):

@@ -488,6 +488,22 @@ PA_EXPORT size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads
   return pa::workspace_layout(num_seqs, num_q_heads, head_dim, max_parts).total;
 }
 
+PA_EXPORT int pa_decode_schedule(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads,
+                                 int64_t max_context_len, int32_t* partition_tokens) {
+  g_error.clear();
+  if (!partition_tokens) return fail(PA_ERR_INVALID, "partition_tokens is NULL");
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_context_len < 0 ||
+      num_q_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "bad sizes (S %lld, Hq %lld, Hkv %lld, max_context_len %lld)",
+                (long long)num_seqs, (long long)num_q_heads, (long long)num_kv_heads,
+                (long long)max_context_len);
+  const int64_t group = num_q_heads / num_kv_heads;
+  const Schedule sc =
+      auto_schedule(num_seqs, num_seqs * num_kv_heads * ((group + 15) / 16), group, max_context_len);
+  *partition_tokens = sc.stream ? -2 : int32_t(sc.part);
+  return PA_OK;
+}
+
 PA_EXPORT int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
                         const pa_tensor* v_cache, const pa_tensor* block_tables,
                         const pa_tensor* context_lens, float scale, int32_t block_size,

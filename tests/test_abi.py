@@ -169,3 +169,23 @@ def test_workspace_bytes(lib):
     assert f(9000, 32, 8, 128, 16384, 0) == up(4 * 2 * 9000 * 32 * 16) + up(4 * 9000 * 32 * 16 * 128)
     # too many sequences for the stream-K prefix: few pairs fall back to 512-token partitions
     assert f(9000, 8, 8, 128, 1024, -2) == 0
+
+
+def test_schedule_query(lib):
+    s = lambda *a: pa.schedule(*a)  # noqa: E731
+    assert s(64, 32, 8, 2048) == -1          # 512 (sequence, head group) pairs: no split
+    assert s(256, 64, 8, 8192) == -1
+    assert s(128, 40, 40, 2048) == 1024      # MHA with many pairs: 1024-token partitions
+    assert s(64, 32, 8, 16384) == 1024       # long contexts, many pairs
+    assert s(4, 8, 2, 912) == -1             # tiny batch
+    assert s(8, 32, 8, 32768) == -2          # few long contexts: stream-K
+    assert s(9000, 64, 8, 1024) == -1        # 72000 pairs
+    assert s(9000, 2, 1, 1 << 20) == 1024
+    with pytest.raises(pa.PaError) as e:
+        s(4, 6, 4, 100)
+    assert e.value.code == pa.PA_ERR_INVALID
+    # every automatic choice is consistent with the workspace size query
+    for args in ((64, 32, 8, 2048), (128, 40, 40, 2048), (8, 32, 8, 32768), (64, 32, 8, 16384)):
+        S, Hq, Hkv, L = args
+        assert lib.pa_decode_workspace_bytes(S, Hq, Hkv, 128, L, 0) == \
+            lib.pa_decode_workspace_bytes(S, Hq, Hkv, 128, L, s(*args))
