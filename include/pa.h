@@ -152,6 +152,10 @@ typedef struct {
   int32_t workgroups_per_cu; /* stream-K schedule only: persistent workgroups
                                 per compute unit, 0 = default (2), at most 64 */
   int32_t reserved;          /* must be 0 */
+  hipEvent_t kernel_start;   /* both NULL, or both events created by the caller:  */
+  hipEvent_t kernel_stop;    /* they then record the start and the end of the
+                                main decode kernel alone (not the combine), as
+                                timed by the GPU (hipExtLaunchKernel) */
 } pa_decode_opts;
 
 /* Bytes of workspace pa_decode_ex needs for these sizes (0 when nothing is split). */

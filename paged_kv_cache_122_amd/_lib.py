@@ -32,7 +32,8 @@ class PaTensor(ctypes.Structure):
 class PaDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("max_context_len", ctypes.c_int64), ("workgroups_per_cu", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("kernel_start", ctypes.c_void_p),
+                ("kernel_stop", ctypes.c_void_p)]
 
 
 class PaError(RuntimeError):
@@ -152,16 +153,34 @@ def alloc_workspace(nbytes, device):
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _event_handle(e):
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use by recording it)."""
+    if e.cuda_event == 0:
+        e.record()  # torch creates the HIP event on its first record
+    h = int(e.cuda_event)
+    if h == 0:
+        raise PaError(PA_ERR_INVALID, "could not create the timing event")
+    return h
+
+
 def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, *,
               partition_tokens=0, path=0, max_context_len=0, workgroups_per_cu=0, workspace=None,
-              stream=None):
-    """pa_decode_ex: decode with options and a caller-owned workspace."""
+              kernel_events=None, stream=None):
+    """pa_decode_ex: decode with options and a caller-owned workspace.
+
+    kernel_events: optional (start, stop) pair of torch.cuda.Event(enable_timing=True)
+    that then time the main decode kernel alone on the GPU.
+    """
     lib = load()
     ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),
                                            (v_cache, "v_cache"), (block_tables, "block_tables"),
                                            (context_lens, "context_lens"))]
     ds = [describe(x) for x in ts]
-    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0)
+    ev = (None, None)
+    if kernel_events is not None:
+        ev = tuple(_event_handle(e) for e in kernel_events)
+    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0,
+                        ev[0], ev[1])
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()

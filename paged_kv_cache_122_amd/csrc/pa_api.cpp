@@ -310,6 +310,8 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
   const int wpc = opts ? opts->workgroups_per_cu : 0;
   if (wpc < 0 || wpc > 64) return fail(PA_ERR_INVALID, "opts.workgroups_per_cu %d (0 .. 64)", wpc);
   if (opts && opts->reserved != 0) return fail(PA_ERR_INVALID, "opts.reserved must be 0");
+  if (opts && (opts->kernel_start == nullptr) != (opts->kernel_stop == nullptr))
+    return fail(PA_ERR_INVALID, "opts.kernel_start and opts.kernel_stop: both or neither");
   const int64_t head_groups = path == pa::Path::Mfma ? (G + 15) / 16 : 1;
   const int64_t pairs = S * g.kv_heads * head_groups;
 
@@ -438,6 +440,8 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   p.scale_log2 = float(double(scale) * 1.4426950408889634);
   p.part_tokens = pl.part_tokens;
   p.max_parts = pl.max_parts;
+  const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr,
+                          opts ? opts->kernel_stop : nullptr};
   hipError_t e;
   if (pl.stream) {
     int cus = 0;
@@ -448,13 +452,13 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
     sk.ws_o = reinterpret_cast<float*>(ws + pl.ws.o_off);
     sk.cus = cus;
     sk.workgroups_per_cu = pl.workgroups_per_cu;
-    e = pa::launch_decode(p, &sk, int(pl.D), int(pl.B), pl.path, stream);
+    e = pa::launch_decode(p, &sk, int(pl.D), int(pl.B), pl.path, ctx);
   } else {
     if (ws) {
       p.ws_ml = reinterpret_cast<float*>(ws + pl.ws.ml_off);
       p.ws_o = reinterpret_cast<float*>(ws + pl.ws.o_off);
     }
-    e = pa::launch_decode(p, nullptr, int(pl.D), int(pl.B), pl.path, stream);
+    e = pa::launch_decode(p, nullptr, int(pl.D), int(pl.B), pl.path, ctx);
   }
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return PA_OK;

@@ -79,8 +79,17 @@ WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t 
 WorkspaceLayout stream_workspace_layout(int64_t num_seqs, int64_t num_pairs, int64_t head_dim);
 
 // sk == nullptr: partitioned schedule
+// Where a decode is enqueued.  When both events are set, the main decode
+// kernel (not the combine) is launched so that they record its own start and
+// end (hipExtLaunchKernel).
+struct LaunchCtx {
+  hipStream_t stream;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
-                         Path path, hipStream_t stream);
+                         Path path, const LaunchCtx& ctx);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
 
 }  // namespace pa

@@ -46,6 +46,7 @@
 // * Combine: out = sum_p w_p o_p / sum_p w_p with w_p = l_p 2^(m_p - M) over
 //   the pieces of a pair in ascending token order (deterministic).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -1099,61 +1100,70 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// The main decode kernel of a call, optionally bracketed by timing events.
+template <typename K, typename... A>
+hipError_t launch_main(K kernel, dim3 grid, dim3 block, const LaunchCtx& c, A... args) {
+  if (c.start && c.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, c.stream, c.start, c.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, c.stream, args...);
+  return hipGetLastError();
+}
+
 template <int D, int BS>
-hipError_t launch_partitioned(const DecodeParams& p, Path path, hipStream_t stream) {
+hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx& c) {
   const dim3 block(kThreads);
+  hipError_t e;
   if (path == Path::Mfma) {
     const dim3 grid(p.num_kv_heads * p.head_groups, p.num_seqs, p.max_parts);
-    hipLaunchKernelGGL((decode_mfma<D, BS>), grid, block, 0, stream, p);
+    e = launch_main(decode_mfma<D, BS>, grid, block, c, p);
   } else {
     const dim3 grid(p.num_kv_heads, p.num_seqs, p.max_parts);
     if (p.group == 1)
-      hipLaunchKernelGGL((decode_valu<D, BS, 1>), grid, block, 0, stream, p);
+      e = launch_main(decode_valu<D, BS, 1>, grid, block, c, p);
     else
-      hipLaunchKernelGGL((decode_valu<D, BS, 2>), grid, block, 0, stream, p);
+      e = launch_main(decode_valu<D, BS, 2>, grid, block, c, p);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
-  hipLaunchKernelGGL((combine_parts<D>), cgrid, dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((combine_parts<D>), cgrid, dim3(256), 0, c.stream, p);
   return hipGetLastError();
 }
 
 // Persistent grid: as many workgroups as can be resident at once (all waves
 // stream concurrently; a second round would repeat the start-up latency).
 template <typename K>
-hipError_t launch_persistent(K kernel, const DecodeParams& p, const StreamParams& sk, hipStream_t stream) {
+hipError_t launch_persistent(K kernel, const DecodeParams& p, const StreamParams& sk, const LaunchCtx& c) {
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0);
   if (e != hipSuccess) return e;
   const int per_cu = std::max(1, std::min(sk.workgroups_per_cu, occ));
   const int wgs = std::min(sk.cus * per_cu, kMaxStreamWaves / kWaves);
-  hipLaunchKernelGGL(kernel, dim3(wgs), dim3(kThreads), 0, stream, p, sk);
-  return hipGetLastError();
+  return launch_main(kernel, dim3(wgs), dim3(kThreads), c, p, sk);
 }
 
 template <int D, int BS>
-hipError_t launch_stream(const DecodeParams& p, const StreamParams& sk, Path path, hipStream_t stream) {
+hipError_t launch_stream(const DecodeParams& p, const StreamParams& sk, Path path, const LaunchCtx& c) {
   hipError_t e;
   if (path == Path::Mfma)
-    e = launch_persistent(decode_mfma_sk<D, BS>, p, sk, stream);
+    e = launch_persistent(decode_mfma_sk<D, BS>, p, sk, c);
   else if (p.group == 1)
-    e = launch_persistent(decode_valu_sk<D, BS, 1>, p, sk, stream);
+    e = launch_persistent(decode_valu_sk<D, BS, 1>, p, sk, c);
   else
-    e = launch_persistent(decode_valu_sk<D, BS, 2>, p, sk, stream);
+    e = launch_persistent(decode_valu_sk<D, BS, 2>, p, sk, c);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((combine_sk<D>), dim3(p.num_seqs * p.num_kv_heads * p.head_groups), dim3(512), 0,
-                     stream, p, sk);
+                     c.stream, p, sk);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_decode_d(const DecodeParams& p, const StreamParams* sk, int block_size, Path path,
-                           hipStream_t stream) {
+                           const LaunchCtx& c) {
   switch (block_size) {
-    case 8: return sk ? launch_stream<D, 8>(p, *sk, path, stream) : launch_partitioned<D, 8>(p, path, stream);
-    case 16: return sk ? launch_stream<D, 16>(p, *sk, path, stream) : launch_partitioned<D, 16>(p, path, stream);
-    case 32: return sk ? launch_stream<D, 32>(p, *sk, path, stream) : launch_partitioned<D, 32>(p, path, stream);
+    case 8: return sk ? launch_stream<D, 8>(p, *sk, path, c) : launch_partitioned<D, 8>(p, path, c);
+    case 16: return sk ? launch_stream<D, 16>(p, *sk, path, c) : launch_partitioned<D, 16>(p, path, c);
+    case 32: return sk ? launch_stream<D, 32>(p, *sk, path, c) : launch_partitioned<D, 32>(p, path, c);
   }
   return hipErrorInvalidValue;
 }
@@ -1175,9 +1185,9 @@ hipError_t launch_append_d(const AppendParams& p, int block_size, hipStream_t st
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
-                         Path path, hipStream_t stream) {
-  if (head_dim == 64) return launch_decode_d<64>(p, sk, block_size, path, stream);
-  if (head_dim == 128) return launch_decode_d<128>(p, sk, block_size, path, stream);
+                         Path path, const LaunchCtx& ctx) {
+  if (head_dim == 64) return launch_decode_d<64>(p, sk, block_size, path, ctx);
+  if (head_dim == 128) return launch_decode_d<128>(p, sk, block_size, path, ctx);
   return hipErrorInvalidValue;
 }
 

@@ -117,6 +117,9 @@ def test_validation_errors(lib):
     assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(-3, 0, 0)) == pa.PA_ERR_INVALID
     assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 0, 0, 65)) == pa.PA_ERR_INVALID
     assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 0, 0, 0, 1)) == pa.PA_ERR_INVALID
+    # timing events: both or neither
+    assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 0, 0, 0, 0, 0x1000, None)) == pa.PA_ERR_INVALID
+    assert call_decode_ex(lib, decode_args(), pa.PaDecodeOpts(0, 0, 0, 0, 0, None, 0x1000)) == pa.PA_ERR_INVALID
 
 
 def test_empty_batch_is_a_no_op(lib):
