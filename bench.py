@@ -166,6 +166,9 @@ def main():
     dw = dev.upload(w, "cuda:0")
     out = torch.empty_like(dw.q)
     eff_bytes = w.effective_kv_bytes()
+    # bytes the kernel must bring from HBM: a physical block shared by several
+    # sequences (a common prefix) counts once
+    algo_bytes = w.unique_kv_bytes()
     max_len = int(w.block_tables.shape[1]) * w.block_size
     part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
     kernels, schedule = decode_kernels(w, part)
@@ -247,7 +250,7 @@ def main():
     t_step = mean(step_ms) / 1e3
     t_kernel = mean(kernel_ms) / 1e3
     value = eff_bytes / t_step / 1e9
-    achieved = eff_bytes / t_kernel / 1e9
+    achieved = algo_bytes / t_kernel / 1e9
     line = {
         "metric": "paged decode-attention effective KV GB/s vs HBM peak; seqs/s per layer-step",
         "value": round(value, 2),
@@ -272,6 +275,7 @@ def main():
             "context_tokens": int(w.context_lens.sum()),
             "max_context_len": int(w.context_lens.max()),
             "effective_kv_bytes": eff_bytes,
+            "unique_kv_bytes": algo_bytes,
             "seed": w.seed,
             "step": "pa_cache_append + pa_decode, caches flushed before each step",
             "schedule": schedule,
@@ -295,7 +299,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.name),
             "kernels": kernels,
-            "algorithmic_bytes": eff_bytes,
+            "algorithmic_bytes": algo_bytes,
             "timed": f"HIP events stamped by the GPU at the start and end of {kernels[0]} "
                      f"(hipExtLaunchKernel), {args.steps} further steps, caches flushed",
         },
