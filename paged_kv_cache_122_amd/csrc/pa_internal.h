@@ -16,6 +16,7 @@ constexpr int kDefaultPartition = 512;  // tokens per partition on the partition
 // stream-K schedule limits: the per-workgroup tile prefix lives in LDS, and
 // partial results are sized for at most this many waves
 constexpr int kMaxStreamSeqs = 8192;
+constexpr int kMaxRankedSeqs = 256;      // partitioned grids order at most this many sequences
 constexpr int kMaxStreamWaves = 4096;
 constexpr int kDefaultWorkgroupsPerCu = 2;
 constexpr int kPlanHeader = 4;  // ints before the tile prefix in the stream-K plan

@@ -851,53 +851,93 @@ __global__ __launch_bounds__(512) void combine_sk(DecodeParams p, StreamParams s
 
 // Block-table entries of up to 64 consecutive tiles of one wave, one per lane,
 // so the tile loop never waits on memory for an address: lane j holds the
-// physical block of the wave's tile k0 + j.
+// entry (entries, for B = 8) of the wave's tile k0 + j.  The load depends
+// only on the tile index, not on the context length, so it can be issued
+// before the length arrives; it is bounded by the table row, and an entry of
+// a tile past the context is never used as an address.
 struct TableCache {
-  int b0, b1;
+  int e0, e1;
 };
 
+// Read-only view of row s of the block table (W entries).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t table_row(const DecodeParams& p, int s, int BS) {
+  return make_rsrc(p.block_tables + size_t(s) * p.bt_s, (p.max_len / BS) * 4);
+}
+
+__device__ __forceinline__ int load_i32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, int(off), 0, 0);
+}
+
 template <int BS>
-__device__ __forceinline__ TableCache fetch_table(const int32_t* bt, int t0, int t1, int wave,
-                                                  int k0, int n, int lane) {
+__device__ __forceinline__ TableCache fetch_table(__amdgpu_buffer_rsrc_t row, int tile0, int wave,
+                                                  int k0, int lane) {
+  const uint32_t t = uint32_t(tile0 + wave + kWaves * (k0 + lane));
   TableCache c{0, 0};
-  const int k = k0 + lane;
-  if (k < n) tile_blocks<BS>(bt, (t0 >> 4) + wave + kWaves * k, t1, c.b0, c.b1);
+  if constexpr (BS == 16) {
+    c.e0 = load_i32(row, t * 4);
+  } else if constexpr (BS == 32) {
+    c.e0 = load_i32(row, (t >> 1) * 4);
+  } else {
+    c.e0 = load_i32(row, t * 8);
+    c.e1 = load_i32(row, t * 8 + 4);
+  }
   return c;
 }
 
+// Tiles whose loads are in flight while one is computed, plus that one: four
+// where the registers fit two waves per SIMD, else three (B = 8 tiles take two
+// loads per operand; the VALU path converts K to fp32 in registers).
+template <int BS, bool Valu>
+constexpr int pipe_slots() { return BS == 8 || Valu ? 3 : 4; }
+
 // Walk this wave's tiles (tiles wave, wave + 4, ... of the partition [t0, t1))
-// with the next two tiles' loads issued before the current one is computed.
-template <int D, int BS, typename F>
-__device__ __forceinline__ void walk_tiles(const DecodeParams& p, const int32_t* bt, int kvh,
-                                           int t0, int t1, int wave, int lane, F&& compute) {
+// with the next S - 1 tiles' loads issued before the current one is
+// computed.  `first` holds the table entries of the wave's first 64 tiles.
+template <int D, int BS, int S, typename F>
+__device__ __forceinline__ void walk_tiles(const DecodeParams& p, __amdgpu_buffer_rsrc_t row,
+                                           TableCache first, int kvh, int t0, int t1, int wave,
+                                           int lane, F&& compute) {
   constexpr int NC = D / 32;
   const int ntiles = (t1 - t0 + 15) >> 4;
   const int n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
   const LaneOffsets<D, BS> lo = lane_offsets<D, BS>(lane);
-  for (int k0 = 0; k0 < n; k0 += 64) {
-    const TableCache tc = fetch_table<BS>(bt, t0, t1, wave, k0, n, lane);
-    const int m = min(64, n - k0);
+  // tiles per table fetch: a whole number of rounds, so that only the last
+  // chunk has padding tiles, and those lie past the context
+  constexpr int kChunk = 64 / S * S;
+  TableCache tc = first;
+  for (int k0 = 0; k0 < n; k0 += kChunk) {
+    if (k0 > 0) tc = fetch_table<BS>(row, t0 >> 4, wave, k0, lane);
+    const int m = min(kChunk, n - k0);
     auto start = [&](int j) { return t0 + 16 * (wave + kWaves * (k0 + j)); };
     auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
       const int jj = min(j, m - 1);
-      const int b0 = __builtin_amdgcn_readlane(tc.b0, jj);
-      const int b1 = BS == 8 ? __builtin_amdgcn_readlane(tc.b1, jj) : 0;
+      const int b0 = __builtin_amdgcn_readlane(tc.e0, jj);
+      int b1 = 0;
+      if constexpr (BS == 8) {
+        // the second block of a tile whose tokens all lie in the first is not
+        // in the table: read the first again (its tokens are masked)
+        b1 = __builtin_amdgcn_readlane(tc.e1, jj);
+        b1 = start(jj) + 8 < t1 ? b1 : b0;
+      }
       load_tile<D, BS>(p, kvh, b0, b1, start(jj), j < m, lo, kt, vt);
       __builtin_amdgcn_sched_barrier(0);
     };
-    u32x4 ak[NC], av[NC], bk[NC], bv[NC], ck[NC], cv[NC];
-    load(0, ak, av);
-    load(1, bk, bv);
-    for (int j = 0;; j += 3) {
-      load(j + 2, ck, cv);
-      compute(start(j), ak, av);
-      if (j + 1 >= m) break;
-      load(j + 3, ak, av);
-      compute(start(j + 1), bk, bv);
-      if (j + 2 >= m) break;
-      load(j + 4, bk, bv);
-      compute(start(j + 2), ck, cv);
-      if (j + 3 >= m) break;
+    // The trip count is rounded up to whole rounds of S tiles: the extra tiles
+    // lie past t1 (only the last chunk is short), load as zeros without
+    // touching memory and add nothing.  A
+    // loop that leaves only at the end of a round reaches its head in the same
+    // state from both edges, so the compiler waits only for the tile it uses
+    // and keeps S - 1 tiles' loads in flight throughout.
+    const int rounds = (m + S - 1) / S;
+    u32x4 kk[S][NC], vv[S][NC];
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) load(i, kk[i], vv[i]);
+    for (int j = 0; j < rounds * S; j += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        load(j + i + S - 1, kk[(i + S - 1) % S], vv[(i + S - 1) % S]);
+        compute(start(j + i), kk[i], vv[i]);
+      }
     }
   }
 }
@@ -945,6 +985,44 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
   }
 }
 
+// Sequence that row y of a partitioned grid works on: the y-th longest context
+// (ties in index order).  Rows are dispatched in order, so the longest
+// contexts start first and the short ones fill the machine at the end, and
+// the first workgroup placed on a compute unit, which the hardware serves
+// ahead of the later ones, gets the most work.  Every workgroup derives the
+// same bijection from the lengths alone.  The rank of a sequence is the
+// number of larger keys (length << 9 | 511 - index, unique).  Grids split into
+// partitions keep the identity order: there the work of a row is bounded by
+// the partition, and neighbouring sequences, which often share prefix blocks
+// (parallel samples of one prompt), stay close in time so that the shared
+// blocks are still cached when the next one reads them.  So do batches of
+// more than kMaxRankedSeqs sequences or with table spans of 2^22 tokens or more.
+__device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
+  const int S = p.num_seqs;
+  if (p.max_parts > 1 || S > kMaxRankedSeqs || p.max_len >= (1 << 22)) return y;
+  __shared__ uint32_t keys[kMaxRankedSeqs];
+  __shared__ int pick;
+  const int S16 = (S + 15) & ~15;  // zero keys pad to whole 16-key steps
+  for (int u = threadIdx.x; u < S16; u += blockDim.x)
+    keys[u] = u < S ? (uint32_t(clamp_len(p, p.context_lens[u])) << 9) | uint32_t(511 - u) : 0u;
+  __syncthreads();
+  for (int c = threadIdx.x; c < S; c += blockDim.x) {
+    const uint32_t kc = keys[c];
+    int rank = 0;
+    for (int u = 0; u < S16; u += 16) {
+      u32x4 k4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) k4[i] = *reinterpret_cast<const u32x4*>(&keys[u + 4 * i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rank += int(k4[i].x > kc) + int(k4[i].y > kc) + int(k4[i].z > kc) + int(k4[i].w > kc);
+    }
+    if (rank == y) pick = c;
+  }
+  __syncthreads();
+  return pick;
+}
+
 // Partitions of sequence s that this launch covers (clamping keeps the
 // partition count consistent with the grid for over-long contexts).
 __device__ __forceinline__ int partitions(const DecodeParams& p, int L) {
@@ -952,7 +1030,7 @@ __device__ __forceinline__ int partitions(const DecodeParams& p, int L) {
 }
 
 template <int D, int BS>
-__global__ __launch_bounds__(kThreads) void decode_mfma(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_mfma(DecodeParams p) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
 
@@ -961,17 +1039,18 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeParams p) {
   const int r = lane & 15;
   const int g4 = lane >> 4;
   const int hg = blockIdx.x;
-  const int s = blockIdx.y;
+  const int s = ranked_seq(p, blockIdx.y);
   const int part = blockIdx.z;
   int kvh, h0, ncols;
   head_span(p, hg, kvh, h0, ncols);
+  const int t0 = part * p.part_tokens;
+  const auto row = table_row(p, s, BS);
+  const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
 
   const int L = clamp_len(p, p.context_lens[s]);
   const int nparts = partitions(p, L);
   if (part >= (nparts > 0 ? nparts : 1)) return;
-  const int t0 = part * p.part_tokens;
   const int t1 = min(L, t0 + p.part_tokens);
-  const int32_t* bt = p.block_tables + size_t(s) * p.bt_s;
 
   u32x4 q[NC];
 #pragma unroll
@@ -981,7 +1060,8 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeParams p) {
   }
   MfmaAcc<D> acc;
   mfma_reset(acc);
-  walk_tiles<D, BS>(p, bt, kvh, t0, t1, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+  walk_tiles<D, BS, pipe_slots<BS, false>()>(p, row, first, kvh, t0, t1, wave, lane,
+                                             [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile<D>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
   });
 
@@ -1002,7 +1082,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma(DecodeParams p) {
 }
 
 template <int D, int BS, int VG>
-__global__ __launch_bounds__(kThreads) void decode_valu(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, BS == 8 || VG == 2 ? 1 : 2) void decode_valu(DecodeParams p) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
 
@@ -1011,22 +1091,24 @@ __global__ __launch_bounds__(kThreads) void decode_valu(DecodeParams p) {
   const int r = lane & 15;
   const int g4 = lane >> 4;
   const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
+  const int s = ranked_seq(p, blockIdx.y);
   const int part = blockIdx.z;
+  const int t0 = part * p.part_tokens;
+  const auto row = table_row(p, s, BS);
+  const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
 
   const int L = clamp_len(p, p.context_lens[s]);
   const int nparts = partitions(p, L);
   if (part >= (nparts > 0 ? nparts : 1)) return;
-  const int t0 = part * p.part_tokens;
   const int t1 = min(L, t0 + p.part_tokens);
   const int h0 = kvh * VG;
-  const int32_t* bt = p.block_tables + size_t(s) * p.bt_s;
 
   float qf[VG][NC][8];
   valu_load_q<D, VG>(p, s, h0, lane, qf);
   ValuAcc<D, VG> acc;
   valu_reset(acc);
-  walk_tiles<D, BS>(p, bt, kvh, t0, t1, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+  walk_tiles<D, BS, pipe_slots<BS, true>()>(p, row, first, kvh, t0, t1, wave, lane,
+                                                [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     valu_tile<D, VG>(acc, qf, p.scale_log2, ts, t1, lane, kt, vt);
   });
 

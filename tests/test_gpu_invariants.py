@@ -314,3 +314,21 @@ def test_kernel_timing_events(part):
         assert np.array_equal(dev.bf16_bits(got), ref)
         t_kernel, t_call = start.elapsed_time(stop), call0.elapsed_time(call1)
         assert 0.0 < t_kernel <= t_call + 1e-3, (t_kernel, t_call)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("S", [5, 256, 257, 300])
+@pytest.mark.parametrize("part", [-1, 64])
+def test_longest_first_order_covers_every_sequence(S, part):
+    """Partitioned grids hand rows to sequences in decreasing length order (the
+    identity order past 256 sequences): with many ties and empty contexts every
+    sequence must still be computed exactly once and land in its own row."""
+    torch = need_gpu()
+    rng = np.random.default_rng(900 + S)
+    lens = rng.choice([0, 1, 16, 17, 100, 100, 100, 250], size=S)
+    w = workloads.random_workload(901 + S, lens, num_q_heads=8, num_kv_heads=2, head_dim=64,
+                                  block_size=16)
+    print(f"S={S} part={part}", flush=True)
+    dw = _setup(w)
+    _, _, ref = oracle_step(w)
+    assert_close(_as_f64(torch, _decode(torch, w, dw, partition_tokens=part)), ref, "bf16 out")
