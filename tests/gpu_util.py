@@ -36,6 +36,30 @@ def assert_close(got, ref, what="", max_abs=TOL_MAX_ABS, rel_rms=TOL_REL_RMS):
     return a, r
 
 
+def bf16_half_ulp(x):
+    """Half the spacing of bf16 numbers at |x| (the most rounding to bf16 can move x)."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.floor(np.log2(ax)).astype(np.int64) - 8)
+
+
+def assert_close_bf16(got, ref, what="", max_abs=TOL_MAX_ABS, rel_rms=TOL_REL_RMS):
+    """The attention bound is on the fp32 arithmetic.  A bf16 output also carries
+    its own rounding, up to half a bf16 ulp of the result: 7.8e-3 for |out| in
+    [2, 4) and 1.6e-2 in [4, 8), where even the correctly rounded exact value can
+    miss 1e-2.  Short
+    contexts give such outputs (an average of two N(0,1) values), so per element
+    the arithmetic bound is applied on top of that rounding."""
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    excess = np.abs(got - ref) - bf16_half_ulp(ref)
+    worst = float(excess.max()) if excess.size else 0.0
+    a, r = errors(got, ref)
+    assert worst <= max_abs and r <= rel_rms, \
+        f"{what}: max|err| beyond bf16 rounding {worst:.3e} (<= {max_abs}), max|err| {a:.3e}, rel RMS {r:.3e} (<= {rel_rms})"
+    return a, r
+
+
 def oracle_step(w, seqs=None):
     """Oracle append of this step's K/V, then oracle decode (fp64)."""
     kst, vst = w.stores()

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import assert_close, need_gpu, oracle_step
+from gpu_util import assert_close, assert_close_bf16, need_gpu, oracle_step
 from paged_kv_cache_122_amd import workloads
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,7 @@ def test_edge_lengths_every_geometry(D, B, Hq, Hkv):
     print(f"geometry D={D} B={B} Hq={Hq} Hkv={Hkv}", flush=True)
     dw = _setup(w)
     _, _, ref = oracle_step(w)
-    assert_close(_as_f64(torch, _decode(torch, w, dw)), ref, "bf16 out")
+    assert_close_bf16(_as_f64(torch, _decode(torch, w, dw)), ref, "bf16 out")
     assert_close(_as_f64(torch, _decode(torch, w, dw, torch.float32)), ref, "f32 out",
                  max_abs=1e-4, rel_rms=1e-4)
 
@@ -73,7 +73,7 @@ def test_split_variants(part):
                                   head_dim=128, block_size=16)
     dw = _setup(w)
     _, _, ref = oracle_step(w)
-    assert_close(_as_f64(torch, _decode(torch, w, dw, partition_tokens=part)), ref, f"part {part}")
+    assert_close_bf16(_as_f64(torch, _decode(torch, w, dw, partition_tokens=part)), ref, f"part {part}")
     assert_close(_as_f64(torch, _decode(torch, w, dw, torch.float32, partition_tokens=part)), ref,
                  f"part {part} f32", max_abs=1e-4, rel_rms=1e-4)
 
@@ -102,7 +102,7 @@ def test_stream_schedule(case):
     got = _decode(torch, w, dw, torch.float32, partition_tokens=-2, workgroups_per_cu=wpc)
     assert_close(_as_f64(torch, got), ref, f"stream-K wpc={wpc}", max_abs=1e-4, rel_rms=1e-4)
     got16 = _decode(torch, w, dw, partition_tokens=-2, workgroups_per_cu=wpc)
-    assert_close(_as_f64(torch, got16), ref, f"stream-K bf16 wpc={wpc}")
+    assert_close_bf16(_as_f64(torch, got16), ref, f"stream-K bf16 wpc={wpc}")
     for s, L in enumerate(lens):
         if L == 0:
             assert torch.all(got[s] == 0)
@@ -141,7 +141,7 @@ def test_empty_context_gives_zeros():
     out = _as_f64(torch, _decode(torch, w, dw))
     assert np.all(out[0] == 0) and np.all(out[2] == 0)
     _, _, ref = oracle_step(w)
-    assert_close(out[1], ref[1], "middle row")
+    assert_close_bf16(out[1], ref[1], "middle row")
 
 
 def test_block_permutation_gives_identical_bits():
@@ -226,7 +226,7 @@ def test_workspace_reuse_across_layouts():
     dbig, dsmall = _setup(big), _setup(small)
     _, _, ref_small = oracle_step(small)
     _decode(torch, big, dbig)                     # library workspace, large layout
-    assert_close(_as_f64(torch, _decode(torch, small, dsmall)), ref_small, "library workspace")
+    assert_close_bf16(_as_f64(torch, _decode(torch, small, dsmall)), ref_small, "library workspace")
     nbytes = max(pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                                     w.table_width * w.block_size) for w in (big, small))
     ws = pa.alloc_workspace(nbytes, dbig.q.device)
@@ -235,7 +235,7 @@ def test_workspace_reuse_across_layouts():
         pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
                      w.block_size, workspace=ws)
     torch.cuda.synchronize()
-    assert_close(_as_f64(torch, out), ref_small, "caller workspace")
+    assert_close_bf16(_as_f64(torch, out), ref_small, "caller workspace")
 
 
 def test_debug_mode_contracts():
@@ -331,4 +331,5 @@ def test_longest_first_order_covers_every_sequence(S, part):
     print(f"S={S} part={part}", flush=True)
     dw = _setup(w)
     _, _, ref = oracle_step(w)
-    assert_close(_as_f64(torch, _decode(torch, w, dw, partition_tokens=part)), ref, "bf16 out")
+    assert_close_bf16(_as_f64(torch, _decode(torch, w, dw, partition_tokens=part)), ref, "bf16 out")
+

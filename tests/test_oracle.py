@@ -396,3 +396,15 @@ def test_pins_catch_dropped_rescale():
             out[s] = acc / l[:, None]
         return out
     assert not _pins_pass(bad)
+
+
+def test_bf16_half_ulp_bounds_the_output_rounding():
+    """The rounding allowance of the bf16-output GPU checks is exactly the most
+    that round-to-nearest-even to bf16 can move a value."""
+    from gpu_util import bf16_half_ulp
+    rng = np.random.default_rng(3)
+    x = np.concatenate([rng.standard_normal(20000) * s for s in (1e-3, 1.0, 3.0, 30.0)])
+    moved = np.abs(oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits_rne(x)) - x)
+    assert np.all(moved <= bf16_half_ulp(x))
+    assert np.max(moved / bf16_half_ulp(x)) > 0.99          # the bound is reached
+    assert bf16_half_ulp(1.0) == 2.0 ** -8 and bf16_half_ulp(-4.4) == 2.0 ** -6
