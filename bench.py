@@ -36,9 +36,9 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "ff130b7ff28e89bb81e025214a638813929ce9c686f77d3e1d3e92f8f39e949f",
+    "sources_sha256": "ed253b3e8628178f8cfd2c7129c5956ae72ba1a2bdaf5e5e9d6dd8e2ccdb315b",
     "config": "llama3_8b_b64",
-    "fetch_bytes": 275295768,  # FETCH_SIZE 134431.2 KiB x 1.9999
+    "fetch_bytes": 275386650,  # FETCH_SIZE 134475.5 KiB x 1.9999
     "write_bytes": 524288,  # WRITE_SIZE 512.0 KiB x 1.0000
 }
 
