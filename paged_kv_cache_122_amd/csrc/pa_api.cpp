@@ -440,12 +440,12 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   p.scale_log2 = float(double(scale) * 1.4426950408889634);
   p.part_tokens = pl.part_tokens;
   p.max_parts = pl.max_parts;
+  int cus = 0;
+  if ((rc = device_cus(&cus)) != PA_OK) return rc;
   const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr,
-                          opts ? opts->kernel_stop : nullptr};
+                          opts ? opts->kernel_stop : nullptr, cus};
   hipError_t e;
   if (pl.stream) {
-    int cus = 0;
-    if ((rc = device_cus(&cus)) != PA_OK) return rc;
     pa::StreamParams sk{};
     sk.plan = reinterpret_cast<int*>(ws + pl.ws.plan_off);
     sk.ws_ml = reinterpret_cast<float*>(ws + pl.ws.ml_off);

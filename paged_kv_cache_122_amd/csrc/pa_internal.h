@@ -46,6 +46,8 @@ struct DecodeParams {
   // partitioned schedule
   int part_tokens;      // tokens per partition (multiple of 32)
   int max_parts;        // partitions launched per sequence
+  int rank_split;       // unsplit grids: rows below it take the longest contexts in
+                        // order, the rows from it on the rest from the shortest up
   float* ws_o;          // [S, Hq, max_parts, D]  normalised partial outputs
   float* ws_ml;         // [S, Hq, max_parts, 2]  (reference max in log2 units, sum)
 };
@@ -87,6 +89,7 @@ struct LaunchCtx {
   hipStream_t stream;
   hipEvent_t start;
   hipEvent_t stop;
+  int cus;  // compute units of the device
 };
 
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,

@@ -985,12 +985,17 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
   }
 }
 
-// Sequence that row y of a partitioned grid works on: the y-th longest context
-// (ties in index order).  Rows are dispatched in order, so the longest
-// contexts start first and the short ones fill the machine at the end, and
-// the first workgroup placed on a compute unit, which the hardware serves
-// ahead of the later ones, gets the most work.  Every workgroup derives the
-// same bijection from the lengths alone.  The rank of a sequence is the
+// Sequence that row y of a partitioned grid works on, by rank of its context
+// length (rank 0 = longest, ties in index order).  Rows are dispatched in
+// order.  When the grid is larger than what the machine holds at once, row y
+// takes rank y: the longest contexts start first and the short ones fill the
+// machine at the end.  When the whole grid is resident, each compute unit
+// receives one workgroup from the rows below p.rank_split and one from the
+// rows after it, and the hardware serves the first ahead of the second; the
+// rows below the split take the longest contexts in order and the rows after
+// it take the rest from the shortest up, so that every compute unit pairs a
+// long context with a short one and all finish at about the same time.
+// Every workgroup derives the same bijection from the lengths alone.  The rank of a sequence is the
 // number of larger keys (length << 9 | 511 - index, unique).  Grids split into
 // partitions keep the identity order: there the work of a row is bounded by
 // the partition, and neighbouring sequences, which often share prefix blocks
@@ -1017,7 +1022,8 @@ __device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
       for (int i = 0; i < 4; ++i)
         rank += int(k4[i].x > kc) + int(k4[i].y > kc) + int(k4[i].z > kc) + int(k4[i].w > kc);
     }
-    if (rank == y) pick = c;
+    const int row = rank < p.rank_split ? rank : S - 1 - (rank - p.rank_split);
+    if (row == y) pick = c;
   }
   __syncthreads();
   return pick;
@@ -1192,20 +1198,35 @@ hipError_t launch_main(K kernel, dim3 grid, dim3 block, const LaunchCtx& c, A...
   return hipGetLastError();
 }
 
+// Split row for ranked_seq: the rows whose workgroups the dispatcher places
+// first, one per compute unit, when the whole grid fits on the machine at
+// once (resident workgroups per compute unit from the kernel's occupancy);
+// else every row, which is plain longest-first.
+template <typename K>
+int rank_split_for(K kernel, const DecodeParams& p, int row_wgs, const LaunchCtx& c) {
+  int occ = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess || occ < 1)
+    occ = 1;
+  const int64_t wgs = int64_t(row_wgs) * p.num_seqs;
+  if (wgs > int64_t(c.cus) * occ) return p.num_seqs;
+  return int(std::min<int64_t>(p.num_seqs, (c.cus + row_wgs - 1) / row_wgs));
+}
+
+template <typename K>
+hipError_t launch_rows(K kernel, DecodeParams p, int row_wgs, const LaunchCtx& c) {
+  p.rank_split = p.max_parts == 1 ? rank_split_for(kernel, p, row_wgs, c) : p.num_seqs;
+  return launch_main(kernel, dim3(row_wgs, p.num_seqs, p.max_parts), dim3(kThreads), c, p);
+}
+
 template <int D, int BS>
 hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx& c) {
-  const dim3 block(kThreads);
   hipError_t e;
-  if (path == Path::Mfma) {
-    const dim3 grid(p.num_kv_heads * p.head_groups, p.num_seqs, p.max_parts);
-    e = launch_main(decode_mfma<D, BS>, grid, block, c, p);
-  } else {
-    const dim3 grid(p.num_kv_heads, p.num_seqs, p.max_parts);
-    if (p.group == 1)
-      e = launch_main(decode_valu<D, BS, 1>, grid, block, c, p);
-    else
-      e = launch_main(decode_valu<D, BS, 2>, grid, block, c, p);
-  }
+  if (path == Path::Mfma)
+    e = launch_rows(decode_mfma<D, BS>, p, p.num_kv_heads * p.head_groups, c);
+  else if (p.group == 1)
+    e = launch_rows(decode_valu<D, BS, 1>, p, p.num_kv_heads, c);
+  else
+    e = launch_rows(decode_valu<D, BS, 2>, p, p.num_kv_heads, c);
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
   hipLaunchKernelGGL((combine_parts<D>), cgrid, dim3(256), 0, c.stream, p);
