@@ -17,26 +17,32 @@
 //   matrix cores without LDS staging or shuffles.
 // * Loads are buffer loads through a resource descriptor built per tile in
 //   scalar registers from the block-table entry, with the non-temporal bit
-//   (the pools are read once per step).  Each wave keeps the next two tiles'
-//   loads in flight while it computes on the current one; past its last tile a
-//   zero-record descriptor turns the padding loads into free zero loads, so
-//   the loop never branches around a load and the compiler waits only for the
-//   tile it is about to use.
-// * Stream-K schedule (default): the tiles of all pairs, in (sequence, head,
-//   tile) order, are cut into one equal contiguous range per wave of a
-//   persistent grid (a few workgroups per CU), so every wave streams the same
-//   number of bytes whatever the length mix, pays its start-up latency once,
-//   and keeps its pipeline full across pair boundaries.  A pair finished inside
-//   one wave is written out directly; a pair cut between waves leaves one
-//   partial result per wave for the combine kernel.
-// * Partitioned schedule (opts.partition_tokens): a grid of (pair, partition)
-//   workgroups of 4 waves, each wave walking every 4th tile of its partition.
+//   (the pools are read once per step).  Each wave keeps the next three tiles'
+//   loads in flight while it computes on the current one (two where registers
+//   would otherwise halve occupancy); past its last tile a zero-record
+//   descriptor turns the padding loads into free zero loads, so the loop never
+//   branches around a load and the compiler waits only for the tile it is
+//   about to use.
+// * Partitioned schedule: a grid of (pair, partition) workgroups of 4 waves,
+//   each wave walking every 4th tile of its partition.  Unsplit grids hand
+//   their rows to the sequences by rank of context length (longest first, or
+//   long paired with short on each compute unit when the whole grid is
+//   resident), so no compute unit is left with the longest work at the end.
+// * Stream-K schedule (few long contexts): the tiles of all pairs, in
+//   (sequence, head, tile) order, are cut into one equal contiguous range per
+//   wave of a persistent grid (a few workgroups per CU), so every wave streams
+//   the same number of bytes whatever the length mix, pays its start-up
+//   latency once, and keeps its pipeline full across pair boundaries.  A pair
+//   finished inside one wave is written out directly; a pair cut between waves
+//   leaves one partial result per wave for the combine kernel.
 // * GQA path (q heads per KV head >= 3): QK^T is v_mfma_f32_16x16x32_bf16 with
-//   16 tokens as rows and the group's query heads as columns; PV is
-//   v_mfma_f32_16x16x16_bf16 whose B operand is exactly the QK^T accumulator
-//   layout, so probabilities go from scores to PV without moving between
-//   lanes.  P is split into a high and a low bf16 part (two MFMAs) so the PV
-//   product keeps ~16 significant bits of P.
+//   16 tokens as rows and the group's query heads as columns.  PV is the same
+//   instruction with V rows as A and P as B: a lane's P values sit exactly where
+//   the QK^T accumulator left them, so probabilities go from scores to PV
+//   without moving between lanes.  P is split into a high and a low bf16 part,
+//   placed in the two halves of each lane's eight k values against the same
+//   four V values twice, so the PV product keeps ~16 significant bits of P at
+//   one MFMA per accumulator.
 // * MHA path (1 or 2 q heads per KV head): fp32 FMAs on the same loads,
 //   cross-lane sums with wave shuffles.
 // * The softmax reference max is raised lazily: only when a tile's max
@@ -81,9 +87,7 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 64 * kWaves;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -122,12 +126,12 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
-                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
-}
-
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
+
+// 2^x with the hardware instruction: results below 2^-126 flush to zero,
+// which a softmax probability can lose (it is then below the fp32 resolution
+// of the running sum), and 2^-inf = 0.
+__device__ __forceinline__ float exp2_ftz(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kBufferFlags);
@@ -286,11 +290,15 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
   f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < NC; ++c) sacc = mfma_16x16x32(kt[c], q[c], sacc);
+  // Only the last tile of a context has tokens at or past t1 (wave-uniform
+  // test): the others skip the score and V masks.
+  const bool partial = ts + kTileTokens > t1;
   float sc[4];
   float mt = kNegInf;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    sc[j] = (ts + 4 * g4 + j < t1) ? sacc[j] * scale_log2 : kNegInf;
+    sc[j] = sacc[j] * scale_log2;
+    if (partial && ts + 4 * g4 + j >= t1) sc[j] = kNegInf;
     mt = fmaxf(mt, sc[j]);
   }
   // Raise the reference only when some score is far above it; the column max
@@ -299,7 +307,7 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
     mt = fmaxf(mt, shfl_xor(mt, 16));
     mt = fmaxf(mt, shfl_xor(mt, 32));
     const float m_new = fmaxf(a.m, mt);
-    const float alpha = exp2f(a.m - m_new);
+    const float alpha = exp2_ftz(a.m - m_new);
     a.l *= alpha;
 #pragma unroll
     for (int i = 0; i < 2 * NC; ++i) a.o[i] *= alpha;
@@ -308,27 +316,27 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
   float pr[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    pr[j] = exp2f(sc[j] - a.m);
+    pr[j] = exp2_ftz(sc[j] - a.m);
     a.l += pr[j];
   }
-  // P as the B operand of PV, split into hi + lo bf16
+  // P as the B operand of PV, split into hi + lo bf16: with K = 32 one MFMA
+  // takes the high halves as its first four k values and the low halves as
+  // the last four, against the same four V values repeated.
   uint32_t hb[4], lb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     hb[j] = bf16_bits(pr[j]);
     lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
   }
-  const u32x2 phi = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
-  const u32x2 plo = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
-  mask_v<D>(vt, ts, t1, lane);
+  const u32x4 pb = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
+                    lb[2] | (lb[3] << 16)};
+  if (partial) mask_v<D>(vt, ts, t1, lane);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const u32x2 a0 = {vt[c].x, vt[c].y};  // dim 2r + 32c, tokens 4*g4 .. +3
-    const u32x2 a1 = {vt[c].z, vt[c].w};  // dim 2r + 32c + 1
-    a.o[2 * c] = mfma_16x16x16(a0, phi, a.o[2 * c]);
-    a.o[2 * c] = mfma_16x16x16(a0, plo, a.o[2 * c]);
-    a.o[2 * c + 1] = mfma_16x16x16(a1, phi, a.o[2 * c + 1]);
-    a.o[2 * c + 1] = mfma_16x16x16(a1, plo, a.o[2 * c + 1]);
+    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};  // dim 2r + 32c, tokens 4*g4 .. +3, twice
+    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};  // dim 2r + 32c + 1
+    a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
+    a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
   }
 }
 
@@ -412,11 +420,11 @@ __device__ __forceinline__ void valu_tile(ValuAcc<D, VG>& a, const float (&qf)[V
     float alpha = 1.f;
     if (mt > a.m[g] + kRescaleSlack) {  // the same in every lane
       const float m_new = fmaxf(a.m[g], mt);
-      alpha = exp2f(a.m[g] - m_new);
+      alpha = exp2_ftz(a.m[g] - m_new);
       a.l[g] *= alpha;
       a.m[g] = m_new;
     }
-    const float pr = exp2f(sc - a.m[g]);
+    const float pr = exp2_ftz(sc - a.m[g]);
     a.l[g] += pr;
     float pj[4];
 #pragma unroll
