@@ -8,7 +8,8 @@ Prints ONE JSON line.  ``value`` is effective KV-read GB/s of the whole step
 append + decode time).  Inputs are resident in HBM; before every timed step a
 1 GiB buffer is written so that neither L2 nor the 256 MB Infinity Cache
 still holds the pools (the flush is outside the timed region).  All work runs
-on one stream of this process and the HIP events are recorded on it.
+on one stream of this process and the HIP events are recorded on it; they are
+created with hipEventDisableSystemFence, so recording them flushes no cache.
 ``roofline`` is the main decode kernel alone (on the default workload the
 only kernel of the call), timed in as many further flushed steps by events
 that the GPU stamps at its start and end, against 8 TB/s.  ``cpu_baseline`` is the fp64 oracle on a bounded
@@ -58,6 +59,50 @@ def parse():
                     help="after the benchmark, copy a float32 buffer of this many MiB three "
                          "times (a known-size kernel for scaling HBM byte counters)")
     return ap.parse_args()
+
+
+class TimingEvents:
+    """HIP events used only for timing, created with hipEventDisableSystemFence:
+    recording one then adds no system-scope cache writeback and invalidation to
+    the timed work (a default event does, and a kernel launched with default
+    events runs measurably longer).  They live in the HIP runtime torch loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def create(self):
+        e = self.ct.c_void_p()
+        self._check(self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+        self.events.append(e.value)
+        return e.value
+
+    def record(self, e, stream):
+        self._check(self.hip.hipEventRecord(e, stream.cuda_stream), "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        ms = self.ct.c_float()
+        self._check(self.hip.hipEventElapsedTime(self.ct.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
 
 
 def sources_sha256():
@@ -188,7 +233,8 @@ def main():
         pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
                      w.block_size, workspace=ws, kernel_events=kernel_events, stream=stream)
 
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    tev = TimingEvents()
+    E = tev.create
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             flush.zero_()
@@ -198,23 +244,21 @@ def main():
 
         ev = [(E(), E(), E()) for _ in range(args.steps)]
         kev = [(E(), E()) for _ in range(args.steps)]
-        for e in [x for t in ev + kev for x in t]:
-            e.record(stream)  # create every event before the timed region
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
         for e0, e1, e2 in ev:
             flush.zero_()
-            e0.record(stream)
+            tev.record(e0, stream)
             append()
-            e1.record(stream)
+            tev.record(e1, stream)
             decode()
-            e2.record(stream)
+            tev.record(e2, stream)
         stream.synchronize()
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-        append_ms = [a.elapsed_time(b) for a, b, _ in ev]
-        decode_ms = [b.elapsed_time(c) for _, b, c in ev]
-        step_ms = [a.elapsed_time(c) for a, _, c in ev]
+        append_ms = [tev.elapsed_ms(a, b) for a, b, _ in ev]
+        decode_ms = [tev.elapsed_ms(b, c) for _, b, c in ev]
+        step_ms = [tev.elapsed_ms(a, c) for a, _, c in ev]
 
         # the same steps again with the main decode kernel bracketed by events
         # that the GPU stamps at its own start and end (such a launch costs the
@@ -224,18 +268,20 @@ def main():
             append()
             decode(kernel_events=k)
         stream.synchronize()
-        kernel_ms = [a.elapsed_time(b) for a, b in kev]
+        kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
 
         hot_ms = []
         if args.unflushed:  # back-to-back steps (caches may hold part of the pools)
             hot = [(E(), E()) for _ in range(args.steps)]
             for a, b in hot:
-                a.record(stream)
+                tev.record(a, stream)
                 append()
                 decode()
-                b.record(stream)
+                tev.record(b, stream)
             stream.synchronize()
-            hot_ms = [a.elapsed_time(b) for a, b in hot]
+            hot_ms = [tev.elapsed_ms(a, b) for a, b in hot]
+
+        tev.close()
 
         if args.copy_calibration > 0:
             n = args.copy_calibration << 18  # float32 elements
@@ -300,8 +346,9 @@ def main():
             "traffic": measured_traffic(w.name),
             "kernels": kernels,
             "algorithmic_bytes": algo_bytes,
-            "timed": f"HIP events stamped by the GPU at the start and end of {kernels[0]} "
-                     f"(hipExtLaunchKernel), {args.steps} further steps, caches flushed",
+            "timed": f"HIP events (created with hipEventDisableSystemFence) stamped by the GPU "
+                     f"at the start and end of {kernels[0]} (hipExtLaunchKernel), {args.steps} "
+                     "further steps, caches flushed",
         },
     }
     if hot_ms:

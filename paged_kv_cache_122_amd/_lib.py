@@ -154,7 +154,10 @@ def alloc_workspace(nbytes, device):
 
 
 def _event_handle(e):
-    """Raw hipEvent_t of a torch.cuda.Event (created on first use by recording it)."""
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use by recording it),
+    or an integer handle passed through."""
+    if isinstance(e, int):
+        return e
     if e.cuda_event == 0:
         e.record()  # torch creates the HIP event on its first record
     h = int(e.cuda_event)
@@ -168,8 +171,9 @@ def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
               kernel_events=None, stream=None):
     """pa_decode_ex: decode with options and a caller-owned workspace.
 
-    kernel_events: optional (start, stop) pair of torch.cuda.Event(enable_timing=True)
-    that then time the main decode kernel alone on the GPU.
+    kernel_events: optional (start, stop) pair of timing events (torch.cuda.Event with
+    enable_timing=True, or raw hipEvent_t handles) that then time the main decode
+    kernel alone on the GPU.
     """
     lib = load()
     ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),

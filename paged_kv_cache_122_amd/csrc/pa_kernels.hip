@@ -287,9 +287,14 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
                                           u32x4 (&vt)[D / 32]) {
   constexpr int NC = D / 32;
   const int g4 = lane >> 4;
-  f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  // two independent accumulation chains, so the QK^T MFMAs overlap
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < NC; ++c) sacc = mfma_16x16x32(kt[c], q[c], sacc);
+  for (int c = 0; c < NC; c += 2) {
+    s0 = mfma_16x16x32(kt[c], q[c], s0);
+    s1 = mfma_16x16x32(kt[c + 1], q[c + 1], s1);
+  }
+  const f32x4 sacc = s0 + s1;
   // Only the last tile of a context has tokens at or past t1 (wave-uniform
   // test): the others skip the score and V masks.
   const bool partial = ts + kTileTokens > t1;
@@ -1087,10 +1092,12 @@ __global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_mfma(DecodeP
     sm.m[wave][r] = acc.m;
     sm.l[wave][r] = l;
   }
+  if (r < ncols) {  // columns past the group hold nothing
 #pragma unroll
-  for (int mm = 0; mm < D / 16; ++mm)
+    for (int mm = 0; mm < D / 16; ++mm)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
+      for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
+  }
 
   finish_partition<D>(p, sm, s, h0, ncols, part, nparts);
 }
