@@ -37,9 +37,9 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "ed253b3e8628178f8cfd2c7129c5956ae72ba1a2bdaf5e5e9d6dd8e2ccdb315b",
+    "sources_sha256": "5b77042548397721337d99fbd1ab1b5d7f8717f8a9631f26e97f2eca78343d63",
     "config": "llama3_8b_b64",
-    "fetch_bytes": 275386650,  # FETCH_SIZE 134475.5 KiB x 1.9999
+    "fetch_bytes": 275398265,  # FETCH_SIZE 134479.6 KiB x 1.9999
     "write_bytes": 524288,  # WRITE_SIZE 512.0 KiB x 1.0000
 }
 
