@@ -160,6 +160,9 @@ def cpu_baseline(w, budget_s):
         passes = 0
         while t_total < budget_s:
             passes += 1
+            t0 = time.perf_counter()
+            oracle.copy_blocks(w.copies, kst, vst)  # the step's copy-on-write copies, if any
+            t_total += time.perf_counter() - t0
             for s in order:
                 t0 = time.perf_counter()
                 oracle.cache_append(w.k_new[s:s + 1], w.v_new[s:s + 1], w.slot_mapping[s:s + 1], kst, vst,
@@ -221,7 +224,12 @@ def main():
     stream = torch.cuda.Stream()  # default priority
     torch.cuda.synchronize()
 
+    has_copies = int(w.copies.shape[0]) > 0
+
     def append():
+        # the step's copy-on-write copies (if any) go first, then the append
+        if has_copies:
+            pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
         pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, stream=stream)
 
     # the call pa_decode makes, with a workspace of our own so that the main
@@ -323,7 +331,9 @@ def main():
             "effective_kv_bytes": eff_bytes,
             "unique_kv_bytes": algo_bytes,
             "seed": w.seed,
-            "step": "pa_cache_append + pa_decode, caches flushed before each step",
+            "step": ("pa_copy_blocks (copy-on-write) + " if has_copies else "")
+                    + "pa_cache_append + pa_decode, caches flushed before each step",
+            "cow_copies": int(w.copies.shape[0]),
             "schedule": schedule,
         },
         "seqs_per_s": round(w.num_seqs / t_step, 1),
@@ -336,6 +346,7 @@ def main():
                       "p50": round(percentile(decode_ms, 50), 5),
                       "p90": round(percentile(decode_ms, 90), 5)},
         "append_ms": {"mean": round(mean(append_ms), 5), "p50": round(percentile(append_ms, 50), 5)},
+        # (the copy-on-write copies, when the step has any, are timed with the append)
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",

@@ -93,6 +93,26 @@ int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slo
                     pa_tensor* k_cache, pa_tensor* v_cache, hipStream_t stream);
 
 /*
+ * pa_copy_blocks -- the copies of copy-on-write, all of a step in one launch.
+ *
+ * Before a sequence writes into a block it shares with others, the block is
+ * duplicated into a free one and only that sequence's table is repointed
+ * ("vLLM - PagedAttention" digest, "Copy-on-Write Logic"; "Fused CUDA
+ * Kernels", item 3: the pending copies are batched into one launch).
+ *
+ *   k_cache, v_cache  the pools (layout above); written in place.
+ *   block_pairs   int64 [N, 2], contiguous; row i = (src, dst): block dst of
+ *                 both pools (every head, every slot) becomes a copy of block src.
+ *
+ * Bit-exact copy.  Preconditions (checked in debug mode only): every id lies
+ * in [0, num_blocks), destinations are distinct and none is also a source
+ * (then the rows are independent and their order does not matter).  A row
+ * naming a block outside the pool is skipped.  N == 0 is a no-op.
+ */
+int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* block_pairs,
+                   hipStream_t stream);
+
+/*
  * pa_decode -- paged decode attention, one query token per sequence.
  *
  *   out           bf16 (rounded to nearest even) or f32 [S, num_q_heads, head_dim],

@@ -8,7 +8,8 @@ is the seeded input generator, which contains none of the attention arithmetic.
 
 Modules
   bf16             exact bf16 bit-pattern <-> float64 conversion
-  paged_attention  slot-mapped append, block-table gather, textbook decode
+  paged_attention  block copy (copy-on-write), slot-mapped append,
+                   block-table gather, textbook decode
                    attention, and the per-block / Equation-4 / split-K
                    formulations used to cross-check it
 
@@ -20,6 +21,7 @@ against page-printed values, closed forms, invariants or a library routine
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits_rne
 from .paged_attention import (
+    copy_blocks,
     cache_append,
     gather_sequence,
     attention_textbook,
@@ -33,6 +35,7 @@ from .paged_attention import (
 __all__ = [
     "bf16_bits_to_f64",
     "f64_to_bf16_bits_rne",
+    "copy_blocks",
     "cache_append",
     "gather_sequence",
     "attention_textbook",

@@ -18,7 +18,7 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_
 PA_BF16, PA_F32, PA_I32, PA_I64 = 1, 2, 3, 4
 MAX_DIMS = 5
 
-EXPORTED = ("pa_cache_append", "pa_decode", "pa_decode_ex", "pa_decode_workspace_bytes",
+EXPORTED = ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_ex", "pa_decode_workspace_bytes",
             "pa_decode_schedule", "pa_last_error", "pa_set_debug")
 
 _DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -57,6 +57,8 @@ def load(path=None):
     P = ctypes.POINTER(PaTensor)
     lib.pa_cache_append.argtypes = [P, P, P, P, P, ctypes.c_void_p]
     lib.pa_cache_append.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [P, P, P, ctypes.c_void_p]
+    lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
     lib.pa_decode.restype = ctypes.c_int
     lib.pa_decode_ex.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32,
@@ -120,6 +122,15 @@ def cache_append(k, v, slot_mapping, k_cache, v_cache, stream=None):
                                            (k_cache, "k_cache"), (v_cache, "v_cache"))]
     ds = [describe(x) for x in ts]
     _check(lib, lib.pa_cache_append(*[ctypes.byref(d) for d in ds], _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, block_pairs, stream=None):
+    """pa_copy_blocks: for each (src, dst) row of block_pairs (int64 [N, 2]), copy block src to dst."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in ((k_cache, "k_cache"), (v_cache, "v_cache"),
+                                           (block_pairs, "block_pairs"))]
+    ds = [describe(x) for x in ts]
+    _check(lib, lib.pa_copy_blocks(*[ctypes.byref(d) for d in ds], _stream(stream)))
 
 
 def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None):

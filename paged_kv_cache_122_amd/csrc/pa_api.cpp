@@ -527,6 +527,53 @@ PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* 
                        false, workspace, workspace_bytes, stream);
 }
 
+PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* block_pairs,
+                             hipStream_t stream) {
+  g_error.clear();
+  int rc;
+  CacheGeom g;
+  if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
+  if ((rc = check_desc(block_pairs, "block_pairs", PA_I64, 2)) != PA_OK) return rc;
+  const int64_t N = block_pairs->shape[0];
+  if (block_pairs->shape[1] != 2)
+    return fail(PA_ERR_INVALID, "block_pairs: shape [N, 2] expected, got [%lld, %lld]",
+                (long long)N, (long long)block_pairs->shape[1]);
+  if (N > 1 && (block_pairs->stride[0] != 2 || block_pairs->stride[1] != 1))
+    return fail(PA_ERR_INVALID, "block_pairs must be contiguous");
+  if (N == 0) return PA_OK;
+  if (N > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many block pairs");
+
+  if (g_debug.load()) {
+    std::vector<int64_t> pairs;
+    if ((rc = copy_to_host(&pairs, block_pairs->data, size_t(2 * N), stream)) != PA_OK) return rc;
+    std::unordered_set<int64_t> srcs, dsts;
+    for (int64_t i = 0; i < N; ++i) srcs.insert(pairs[size_t(2 * i)]);
+    for (int64_t i = 0; i < N; ++i) {
+      const int64_t s = pairs[size_t(2 * i)], d = pairs[size_t(2 * i + 1)];
+      if (s < 0 || s >= g.num_blocks || d < 0 || d >= g.num_blocks)
+        return fail(PA_ERR_CONTRACT, "block_pairs[%lld] = (%lld, %lld) outside [0, %lld)", (long long)i,
+                    (long long)s, (long long)d, (long long)g.num_blocks);
+      if (!dsts.insert(d).second)
+        return fail(PA_ERR_CONTRACT, "block_pairs[%lld]: destination %lld repeats", (long long)i,
+                    (long long)d);
+      if (srcs.count(d))
+        return fail(PA_ERR_CONTRACT, "block_pairs[%lld]: destination %lld is also a source",
+                    (long long)i, (long long)d);
+    }
+  }
+
+  pa::CopyParams p{};
+  p.pairs = static_cast<const int64_t*>(block_pairs->data);
+  p.k_cache = static_cast<uint16_t*>(k_cache->data);
+  p.v_cache = static_cast<uint16_t*>(v_cache->data);
+  p.num_blocks = g.num_blocks;
+  p.block_units = g.kv_heads * g.block_size * g.head_dim * 2 / 16;
+  p.num_pairs = int(N);
+  const hipError_t e = pa::launch_copy(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy launch");
+  return PA_OK;
+}
+
 PA_EXPORT int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping,
                               pa_tensor* k_cache, pa_tensor* v_cache, hipStream_t stream) {
   g_error.clear();

@@ -73,6 +73,15 @@ struct AppendParams {
   int num_tokens, num_kv_heads;
 };
 
+struct CopyParams {
+  const int64_t* pairs;  // [N, 2] (src, dst) physical block ids
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t num_blocks;
+  int64_t block_units;   // 16-byte units in one block of one pool
+  int num_pairs;
+};
+
 // Workspace layouts shared by the host planner and the kernels.
 struct WorkspaceLayout {
   size_t plan_off, ml_off, o_off, total;
@@ -95,5 +104,6 @@ struct LaunchCtx {
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
                          Path path, const LaunchCtx& ctx);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
+hipError_t launch_copy(const CopyParams& p, hipStream_t stream);
 
 }  // namespace pa

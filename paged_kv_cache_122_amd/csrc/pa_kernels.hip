@@ -1201,6 +1201,42 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// batched block copy (copy-on-write): every pending copy of a step in one
+// launch.  Workgroup (x, y) copies kCopyUnits * 256 16-byte units of one
+// pool's block for pair y (the first workgroups of a row take the K pool, the
+// rest the V pool), all loads in flight before the stores; a pair naming a
+// block outside the pool is skipped.
+// ---------------------------------------------------------------------------
+constexpr int kCopyUnits = 4;
+constexpr int kCopyChunk = kCopyUnits * 256;  // units per workgroup
+
+__global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
+  const size_t block_elems = size_t(p.block_units) * 8;
+  const int64_t per_pool = (p.block_units + kCopyChunk - 1) / kCopyChunk;
+  const bool is_v = blockIdx.x >= per_pool;
+  const int64_t chunk = is_v ? blockIdx.x - per_pool : blockIdx.x;
+  uint16_t* const pool = is_v ? p.v_cache : p.k_cache;
+  for (int pair = blockIdx.y; pair < p.num_pairs; pair += gridDim.y) {
+    const int64_t src = p.pairs[2 * size_t(pair)];
+    const int64_t dst = p.pairs[2 * size_t(pair) + 1];
+    if (src < 0 || src >= p.num_blocks || dst < 0 || dst >= p.num_blocks) continue;
+    u32x4 x[kCopyUnits];
+#pragma unroll
+    for (int i = 0; i < kCopyUnits; ++i) {
+      const int64_t u = chunk * kCopyChunk + i * 256 + threadIdx.x;
+      const int64_t uu = u < p.block_units ? u : 0;  // in bounds; not stored
+      x[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(pool + size_t(src) * block_elems + size_t(uu) * 8));
+    }
+#pragma unroll
+    for (int i = 0; i < kCopyUnits; ++i) {
+      const int64_t u = chunk * kCopyChunk + i * 256 + threadIdx.x;
+      if (u < p.block_units) store16(pool + size_t(dst) * block_elems + size_t(u) * 8, x[i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 // The main decode kernel of a call, optionally bracketed by timing events.
@@ -1307,6 +1343,13 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
   if (head_dim == 64) return launch_decode_d<64>(p, sk, block_size, path, ctx);
   if (head_dim == 128) return launch_decode_d<128>(p, sk, block_size, path, ctx);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy(const CopyParams& p, hipStream_t stream) {
+  const int64_t gx = 2 * ((p.block_units + kCopyChunk - 1) / kCopyChunk);
+  const dim3 grid(unsigned(gx), unsigned(std::min(p.num_pairs, 65535)));
+  hipLaunchKernelGGL(copy_kernel, grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream) {

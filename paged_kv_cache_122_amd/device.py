@@ -40,6 +40,7 @@ class DeviceWorkload:
     k_cache: torch.Tensor
     v_cache: torch.Tensor
     owned: torch.Tensor
+    copies: torch.Tensor   # int64 [N, 2] copy-on-write (src, dst) of this step
 
 
 def upload(w, device="cuda"):
@@ -55,4 +56,5 @@ def upload(w, device="cuda"):
         slot_mapping=torch.from_numpy(w.slot_mapping).to(device),
         block_tables=torch.from_numpy(w.block_tables).to(device),
         context_lens=torch.from_numpy(w.context_lens).to(device),
-        k_cache=k_cache, v_cache=v_cache, owned=owned)
+        k_cache=k_cache, v_cache=v_cache, owned=owned,
+        copies=torch.from_numpy(np.ascontiguousarray(w.copies, dtype=np.int64)).to(device))

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import layout
-from .blockpool import BlockPool, Sequence, allocate_tokens, fork, free, slot_of_position
+from .blockpool import BlockPool, Sequence, allocate_tokens, append_token, fork, free, slot_of_position
 from .sizing import blocks_for_tokens, effective_kv_bytes
 
 NAN_BF16 = 0x7FC0
@@ -98,6 +98,9 @@ class Workload:
     v_blocks: np.ndarray          # uint16 [n, Hkv, B/4, D, 4]
     refcount: np.ndarray          # int32 [n]
     meta: dict = field(default_factory=dict)
+    # copy-on-write copies this step performs before its append, int64 [N, 2]
+    # (src, dst); every dst block holds NaN until the copy
+    copies: np.ndarray = field(default_factory=lambda: np.zeros((0, 2), dtype=np.int64))
 
     @property
     def num_seqs(self):
@@ -128,9 +131,11 @@ class Workload:
 
 
 def build_workload(name, seed, rng, *, num_q_heads, num_kv_heads, head_dim, block_size,
-                   num_blocks, tables, context_lens, width, meta=None):
+                   num_blocks, tables, context_lens, width, meta=None, copies=None):
     """Fill values for a placed workload.  ``tables`` are lists of physical ids
-    covering ``ceil(L/B)`` blocks per sequence; ``rng`` continues the stream."""
+    covering ``ceil(L/B)`` blocks per sequence; ``rng`` continues the stream.
+    ``copies`` are the pool's pending copy-on-write copies ``(src, dst, valid)``
+    of this step: ``src`` holds ``valid`` tokens, ``dst`` holds NaN until copied."""
     S = len(context_lens)
     Hq, Hkv, D, B = int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size)
     if Hq % Hkv or D not in layout.SUPPORTED_HEAD_DIMS or B not in layout.SUPPORTED_BLOCK_SIZES:
@@ -152,6 +157,10 @@ def build_workload(name, seed, rng, *, num_q_heads, num_kv_heads, head_dim, bloc
             n_prev = min(B, max(0, (L - 1) - i * B))
             valid_before[b] = max(valid_before.get(b, 0), n_prev)
             users[b] = users.get(b, 0) + 1
+    copies = [tuple(int(x) for x in c) for c in (copies or [])]
+    for src, _dst, valid in copies:
+        valid_before[src] = max(valid_before.get(src, 0), valid)
+        users.setdefault(src, 0)
 
     q = _bf16_normal(rng, (S, Hq, D))
     k_new = _bf16_normal(rng, (S, Hkv, D))
@@ -180,13 +189,18 @@ def build_workload(name, seed, rng, *, num_q_heads, num_kv_heads, head_dim, bloc
     with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
         list(ex.map(lambda j: fill_chunk(*j), jobs))
     pools = [k_blocks, v_blocks]
+    pos = {int(b): i for i, b in enumerate(owned)}
+    for _src, dst, _valid in copies:  # not yet copied: poison
+        k_blocks[pos[dst]] = NAN_BF16
+        v_blocks[pos[dst]] = NAN_BF16
 
     return Workload(
         name=name, seed=int(seed), num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
         num_blocks=int(num_blocks), scale=1.0 / float(np.sqrt(D)), context_lens=lens,
         block_tables=bt, slot_mapping=slots, q=q, k_new=k_new, v_new=v_new, owned=owned,
         k_blocks=pools[0], v_blocks=pools[1],
-        refcount=np.array([users[int(b)] for b in owned], dtype=np.int32), meta=dict(meta or {}))
+        refcount=np.array([users[int(b)] for b in owned], dtype=np.int32), meta=dict(meta or {}),
+        copies=np.array([(c[0], c[1]) for c in copies], dtype=np.int64).reshape(-1, 2))
 
 
 def place_independent(rng, context_lens, block_size, num_blocks):
@@ -286,6 +300,38 @@ def opt13b_prefix_sharing():
                           meta={"groups": groups, "per_group": per, "shared_blocks": prompt // B})
 
 
+def opt13b_cow_fork():
+    """Parallel sampling right after the prompt: 16 prompts of 1,000 tokens (62
+    full blocks and a last block holding 8 of 16 tokens), each forked into 8
+    samples that share every block.  This step each sample appends its first
+    token; the shared last block is copied for every sample but the last
+    writer, which by then holds its only reference (7 copies per prompt).
+    40 q = 40 kv heads, D 128, B 16, pool needed + 10 %."""
+    seed = 1008
+    B, prompt, groups, per = 16, 1000, 16, 8
+    rng = np.random.Generator(np.random.PCG64(seed))
+    need = groups * (blocks_for_tokens(prompt, B) + per - 1)
+    nb = int(np.ceil(1.1 * need))
+    pool = BlockPool(nb, B, free_order=rng.permutation(nb))
+    tables, lens = [], []
+    for _ in range(groups):
+        parent = Sequence()
+        allocate_tokens(pool, parent, prompt)
+        children = [fork(pool, parent) for _ in range(per)]
+        free(pool, parent)
+        for child in children:
+            append_token(pool, child)  # this step's token
+            tables.append(child.table)
+            lens.append(child.length)
+    copies = list(pool.pending_copies)
+    if len(copies) != groups * (per - 1):
+        raise AssertionError("every sample but the last writer copies the shared block")
+    return build_workload("opt13b_cow_fork_b128", seed, rng, num_q_heads=40, num_kv_heads=40,
+                          head_dim=128, block_size=B, num_blocks=nb, tables=tables,
+                          context_lens=lens, width=blocks_for_tokens(prompt + 1, B),
+                          meta={"groups": groups, "per_group": per}, copies=copies)
+
+
 def long_context(block_size):
     """8 seqs x 32,768 tokens, 32 q / 8 kv heads, D 128, B in {8, 16, 32},
     random placement, pool needed + 10 %."""
@@ -309,6 +355,7 @@ CONFIGS = {
     "long32k_b8": lambda: long_context(8),
     "long32k_b16": lambda: long_context(16),
     "long32k_b32": lambda: long_context(32),
+    "opt13b_cow_fork_b128": opt13b_cow_fork,
 }
 
 

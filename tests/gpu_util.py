@@ -61,8 +61,9 @@ def assert_close_bf16(got, ref, what="", max_abs=TOL_MAX_ABS, rel_rms=TOL_REL_RM
 
 
 def oracle_step(w, seqs=None):
-    """Oracle append of this step's K/V, then oracle decode (fp64)."""
+    """Oracle copy-on-write copies and append of this step, then oracle decode (fp64)."""
     kst, vst = w.stores()
+    oracle.copy_blocks(w.copies, kst, vst)
     oracle.cache_append(w.k_new, w.v_new, w.slot_mapping, kst, vst, w.block_size)
     out = oracle.paged_decode(w.q, kst, vst, w.block_tables, w.context_lens, w.scale,
                               w.block_size, seqs=seqs)

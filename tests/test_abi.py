@@ -192,3 +192,20 @@ def test_schedule_query(lib):
         S, Hq, Hkv, L = args
         assert lib.pa_decode_workspace_bytes(S, Hq, Hkv, 128, L, 0) == \
             lib.pa_decode_workspace_bytes(S, Hq, Hkv, 128, L, s(*args))
+
+
+def test_copy_blocks_validation(lib):
+    """pa_copy_blocks checks its arguments before any launch (fake pointers here)."""
+    r = ctypes.byref
+    a = decode_args()
+
+    def call(pairs):
+        return lib.pa_copy_blocks(r(a["k"]), r(a["v"]), r(pairs), None)
+
+    assert call(T([0, 2], pa.PA_I64)) == pa.PA_OK                        # nothing to copy
+    assert call(T([3, 2], pa.PA_I32)) == pa.PA_ERR_INVALID               # int64 pairs
+    assert call(T([3, 3], pa.PA_I64)) == pa.PA_ERR_INVALID               # [N, 2]
+    assert call(T([3, 2], pa.PA_I64, stride=[4, 1])) == pa.PA_ERR_INVALID  # contiguous rows
+    assert call(T([3, 2], pa.PA_I64, data=None)) == pa.PA_ERR_INVALID
+    bad = decode_args(kdt=pa.PA_F32)
+    assert lib.pa_copy_blocks(r(bad["k"]), r(bad["v"]), r(T([3, 2], pa.PA_I64)), None) == pa.PA_ERR_INVALID

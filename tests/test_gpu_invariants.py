@@ -273,6 +273,13 @@ def test_debug_mode_contracts():
         with pytest.raises(pa.PaError) as e:
             pa.cache_append(dw.k_new, dw.v_new, oob, dw.k_cache, dw.v_cache)
         assert e.value.code == pa.PA_ERR_CONTRACT
+        dev_ = dw.q.device
+        for pairs in ([[1, 5], [2, 5]],            # a destination twice
+                      [[1, 5], [5, 6]],            # a destination that is also a source
+                      [[1, w.num_blocks]]):        # outside the pool
+            with pytest.raises(pa.PaError) as e:
+                pa.copy_blocks(dw.k_cache, dw.v_cache, torch.tensor(pairs, dtype=torch.int64, device=dev_))
+            assert e.value.code == pa.PA_ERR_CONTRACT
     finally:
         pa.set_debug(prev)
     torch.cuda.synchronize()
@@ -333,3 +340,36 @@ def test_longest_first_order_covers_every_sequence(S, part):
     _, _, ref = oracle_step(w)
     assert_close_bf16(_as_f64(torch, _decode(torch, w, dw, partition_tokens=part)), ref, "bf16 out")
 
+
+
+@pytest.mark.parametrize("D,B,Hkv", [(128, 16, 8), (64, 8, 2), (128, 32, 40)])
+def test_copy_blocks_bit_exact(D, B, Hkv):
+    """Random batches of block copies match the oracle's copy bit for bit; rows
+    naming a block outside the pool are skipped (pool unchanged)."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+    rng = np.random.default_rng(D + B + Hkv)
+    w = workloads.random_workload(71 + B, rng.integers(1, 200, size=24), num_q_heads=Hkv, num_kv_heads=Hkv,
+                                  head_dim=D, block_size=B)
+    dw = dev.upload(w)
+    owned = w.owned
+    src = rng.choice(owned, size=min(12, len(owned) // 2), replace=False)
+    rest = np.setdiff1d(np.arange(w.num_blocks), src)
+    dst = rng.choice(rest, size=len(src), replace=False)
+    pairs = np.stack([src, dst], 1).astype(np.int64)
+    # the oracle's pools cover every block here: start from the device's contents
+    k_all = dev.bf16_bits(dw.k_cache).copy()
+    v_all = dev.bf16_bits(dw.v_cache).copy()
+    oracle.copy_blocks(pairs, k_all, v_all)
+    pa.copy_blocks(dw.k_cache, dw.v_cache, torch.from_numpy(pairs).to(dw.q.device))
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.bf16_bits(dw.k_cache), k_all)
+    assert np.array_equal(dev.bf16_bits(dw.v_cache), v_all)
+    # out-of-range rows do nothing
+    pa.copy_blocks(dw.k_cache, dw.v_cache,
+                   torch.tensor([[-1, int(dst[0])], [int(src[0]), w.num_blocks], [int(src[0]), -5]],
+                                dtype=torch.int64, device=dw.q.device))
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.bf16_bits(dw.k_cache), k_all)
+    assert np.array_equal(dev.bf16_bits(dw.v_cache), v_all)

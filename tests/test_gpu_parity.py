@@ -1,5 +1,6 @@
-"""GPU parity on the five seeded configurations: the append is bit-exact
-against the oracle's append, and decode matches the fp64 oracle within
+"""GPU parity on the five seeded configurations (and a copy-on-write fork
+case): the copies and the append are bit-exact against the oracle's, and
+decode matches the fp64 oracle within
 max|err| <= 1e-2 and relative RMS <= 2e-3.  Runs pa_decode exactly as bench.py
 launches it (library workspace, default partitions)."""
 
@@ -22,6 +23,7 @@ CASES = [
     ("long32k_b8", 8),
     ("long32k_b16", 8),
     ("long32k_b32", 8),
+    ("opt13b_cow_fork_b128", 32),
 ]
 
 
@@ -38,13 +40,14 @@ def test_config_parity(name, n_check):
     seqs = sample_seqs(w, n_check)
     kst, vst, ref = oracle_step(w, seqs)
 
+    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies)  # copy-on-write, if the step has any
     pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
     out = torch.empty_like(dw.q)
     pa.decode(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
               w.block_size)
     torch.cuda.synchronize()
 
-    # append: owned blocks bit-exact; the pool's NaN count proves nothing else changed
+    # copies and append: owned blocks bit-exact; the pool's NaN count proves nothing else changed
     k_own = dev.bf16_bits(dw.k_cache[dw.owned])
     v_own = dev.bf16_bits(dw.v_cache[dw.owned])
     assert np.array_equal(k_own, kst.blocks), "K pool differs from the oracle's append"

@@ -188,3 +188,38 @@ def test_prefix_sharing_workload_structure():
     for s in range(128):
         assert ref[int(w.slot_mapping[s]) // 16] == 1
     assert w.unique_kv_bytes() < w.effective_kv_bytes()
+
+
+def test_cow_fork_workload_copies_the_shared_partial_block():
+    """Forking 8 samples from a 1,000-token prompt: the last block (8 of 16
+    tokens) is shared, so the first token of every sample but the last writer
+    goes to a fresh copy (the chenyuan1125 essay; the sevydevy CoW script's rule
+    that a shared last block is copied before a write)."""
+    import oracle
+    w = workloads.make("opt13b_cow_fork_b128")
+    B = w.block_size
+    assert w.copies.shape == (16 * 7, 2)
+    assert np.all(w.context_lens == 1001)
+    kst, vst = w.stores()
+    # before the copies every destination is poison
+    for _, dst in w.copies:
+        assert np.all(kst[int(dst)] == workloads.NAN_BF16)
+    oracle.copy_blocks(w.copies, kst, vst)
+    oracle.cache_append(w.k_new, w.v_new, w.slot_mapping, kst, vst, B)
+    for g in range(16):
+        ctx = []
+        for j in range(8):
+            s = 8 * g + j
+            K, V = oracle.gather_sequence(kst, vst, w.block_tables[s], int(w.context_lens[s]), B)
+            assert np.all(np.isfinite(K)) and np.all(np.isfinite(V))
+            ctx.append((K, V))
+            # the new token sits at position 1000 of this sample alone
+            assert np.array_equal(K[:, 1000], oracle.bf16_bits_to_f64(w.k_new[s]))
+        for K, V in ctx[1:]:  # the prompt is the same for every sample of a group
+            assert np.array_equal(K[:, :1000], ctx[0][0][:, :1000])
+            assert np.array_equal(V[:, :1000], ctx[0][1][:, :1000])
+    # skipping the copies leaves the copied samples reading poison
+    kst2, vst2 = w.stores()
+    oracle.cache_append(w.k_new, w.v_new, w.slot_mapping, kst2, vst2, B)
+    K, _ = oracle.gather_sequence(kst2, vst2, w.block_tables[0], 1001, B)
+    assert np.isnan(K[:, 992:1000]).all()
