@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-control", action="store_true",
+                    help="skip the unpaged control (pa_decode_contiguous on a copy of the cache)")
     ap.add_argument("--unflushed", action="store_true",
                     help="also time back-to-back steps without the cache flush")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -289,6 +291,29 @@ def main():
             stream.synchronize()
             hot_ms = [tev.elapsed_ms(a, b) for a, b in hot]
 
+        # paging control: the same decode over an unpaged copy of the cache
+        # (taken after the append, so both see the same tokens), timed the same
+        # way as the paged call above
+        contig_ms, unsplit_ms = [], []
+        if not args.no_control:
+            kc, vc = dev.contiguous_copy(dw, w)
+            out_c = torch.empty_like(out)
+            cev = [(E(), E(), E(), E()) for _ in range(args.steps)]
+            for a, b, c, d in cev:
+                flush.zero_()
+                tev.record(a, stream)
+                pa.decode_contiguous(out_c, dw.q, kc, vc, dw.context_lens, w.scale, stream=stream)
+                tev.record(b, stream)
+                flush.zero_()
+                tev.record(c, stream)  # the paged kernel with the control's schedule
+                pa.decode_ex(out_c, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens,
+                             w.scale, w.block_size, partition_tokens=-1, path=2, stream=stream)
+                tev.record(d, stream)
+            stream.synchronize()
+            contig_ms = [tev.elapsed_ms(a, b) for a, b, _, _ in cev]
+            unsplit_ms = [tev.elapsed_ms(c, d) for _, _, c, d in cev]
+            del kc, vc, out_c
+
         tev.close()
 
         if args.copy_calibration > 0:
@@ -362,6 +387,17 @@ def main():
                      "further steps, caches flushed",
         },
     }
+    if contig_ms:
+        line["paging_control"] = {
+            "contiguous_call_ms": round(mean(contig_ms), 5),
+            "paged_same_schedule_call_ms": round(mean(unsplit_ms), 5),
+            "paged_over_contiguous": round(mean(unsplit_ms) / mean(contig_ms) - 1.0, 4),
+            "paged_auto_call_ms": round(mean(decode_ms), 5),
+            "note": "pa_decode_contiguous on an unpaged copy of the cache (per sequence and KV head a "
+                    "run of 16-token tiles, no block table) vs the paged kernel with the same "
+                    "schedule (one workgroup per sequence and head group, MFMA), alternating, each "
+                    "after a cache flush and timed by events around the call",
+        }
     if hot_ms:
         line["unflushed_step_ms"] = {"mean": round(mean(hot_ms), 5),
                                      "p50": round(percentile(hot_ms, 50), 5),

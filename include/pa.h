@@ -210,6 +210,35 @@ int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
                  const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/*
+ * pa_decode_contiguous -- the control for paging: the same decode over a cache
+ * that is not paged.
+ *
+ * The pages report that table lookups and variable lengths made the paper's
+ * paged kernel 20-26 % slower than an optimized contiguous one (chenyuan1125
+ * essay, "The Block Table Separates Logical from Physical Contiguity";
+ * "PagedAttention Explained" (sevydevy), its list of costs).  This entry
+ * point measures that cost for this library: each (sequence, KV head) owns
+ * one contiguous run of max_len/16 tiles of 16 tokens, each tile in the format
+ * of a 16-token block of one head, and the kernel is pa_decode's MFMA kernel
+ * with the tile address computed instead of looked up.
+ *
+ *   out, q        as for pa_decode.
+ *   k             bf16 [S*Hkv, max_len/16, D/8, 16, 8]: token t, dim d of
+ *                 sequence s, head h at [s*Hkv + h, t/16, d/8, t%16, d%8];
+ *                 contiguous.
+ *   v             bf16 [S*Hkv, max_len/16, 4, D, 4]: at [s*Hkv + h, t/16,
+ *                 (t%16)/4, d, t%4]; contiguous.
+ *   context_lens  int32 [S]; tokens t < L_s are read (L_s > max_len is clamped).
+ *   scale         as for pa_decode.
+ *
+ * max_len * D * 2 < 2^31; head_dim 64 or 128; any query-head grouping (MFMA
+ * path); no split, no workspace.  The result equals pa_decode's unsplit MFMA
+ * schedule on the same values, bit for bit.
+ */
+int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                         const pa_tensor* context_lens, float scale, hipStream_t stream);
+
 /* Message of the last failed call on this thread (valid until the next pa_* call). */
 const char* pa_last_error(void);
 

@@ -26,6 +26,7 @@ from .paged_attention import (
     gather_sequence,
     attention_textbook,
     paged_decode,
+    contiguous_decode,
     paged_decode_online,
     paged_decode_eq4,
     split_partials,
@@ -40,6 +41,7 @@ __all__ = [
     "gather_sequence",
     "attention_textbook",
     "paged_decode",
+    "contiguous_decode",
     "paged_decode_online",
     "paged_decode_eq4",
     "split_partials",

@@ -527,6 +527,75 @@ PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* 
                        false, workspace, workspace_bytes, stream);
 }
 
+PA_EXPORT int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
+                                   const pa_tensor* v, const pa_tensor* context_lens, float scale,
+                                   hipStream_t stream) {
+  g_error.clear();
+  int rc;
+  if ((rc = check_desc(k, "k", PA_BF16, 5)) != PA_OK) return rc;
+  if ((rc = check_desc(v, "v", PA_BF16, 5)) != PA_OK) return rc;
+  if ((rc = check_desc(q, "q", PA_BF16, 3)) != PA_OK) return rc;
+  if (!out) return fail(PA_ERR_INVALID, "out: descriptor is NULL");
+  if (out->dtype != PA_BF16 && out->dtype != PA_F32)
+    return fail(PA_ERR_INVALID, "out: dtype %s, expected bf16 or f32", dtype_name(out->dtype));
+  if ((rc = check_desc(out, "out", out->dtype, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(context_lens, "context_lens", PA_I32, 1)) != PA_OK) return rc;
+  const int64_t S = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  if (k->shape[2] * 8 != D || k->shape[3] != 16 || k->shape[4] != 8)
+    return fail(PA_ERR_INVALID, "k: shape [S*Hkv, max_len/16, D/8, 16, 8] expected");
+  if (S == 0 && k->shape[0] == 0) return PA_OK;
+  if (S <= 0 || k->shape[0] % S)
+    return fail(PA_ERR_INVALID, "k: first dim %lld is not num_seqs * num_kv_heads", (long long)k->shape[0]);
+  const int64_t Hkv = k->shape[0] / S, Lmax = k->shape[1] * 16;
+  const int64_t v_shape[5] = {k->shape[0], k->shape[1], 4, D, 4};
+  for (int i = 0; i < 5; ++i)
+    if (v->shape[i] != v_shape[i])
+      return fail(PA_ERR_INVALID, "v: shape [S*Hkv, max_len/16, 4, D, 4] expected (matching k)");
+  if (!is_contiguous(k) || !is_contiguous(v)) return fail(PA_ERR_INVALID, "k, v must be contiguous");
+  if (D != 64 && D != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %lld (64 or 128)", (long long)D);
+  if (Lmax < 16 || Lmax * D * 2 >= (int64_t(1) << 31))
+    return fail(PA_ERR_UNSUPPORTED, "max_len %lld (max_len * D * 2 must stay below 2^31)",
+                (long long)Lmax);
+  if (out->shape[0] != S || out->shape[1] != Hq || out->shape[2] != D)
+    return fail(PA_ERR_INVALID, "out: shape does not match q");
+  if (Hkv <= 0 || Hq <= 0 || Hq % Hkv)
+    return fail(PA_ERR_INVALID, "num_q_heads %lld is not a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)Hkv);
+  if (context_lens->shape[0] != S) return fail(PA_ERR_INVALID, "context_lens: %lld entries", (long long)S);
+  if (context_lens->stride[0] != 1 && S > 1) return fail(PA_ERR_INVALID, "context_lens must be contiguous");
+  if ((rc = check_rows(q, "q")) != PA_OK) return rc;
+  if (out->stride[2] != 1 && D > 1) return fail(PA_ERR_INVALID, "out: last dim must be contiguous");
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale must be finite");
+  if (S > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %lld > 65535", (long long)S);
+  int cus = 0;
+  if ((rc = device_cus(&cus)) != PA_OK) return rc;
+
+  pa::DecodeParams p{};
+  p.out = out->data;
+  p.out_s = out->stride[0];
+  p.out_h = out->stride[1];
+  p.out_f32 = out->dtype == PA_F32;
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.q_s = q->stride[0];
+  p.q_h = q->stride[1];
+  p.k_cache = static_cast<const uint16_t*>(k->data);
+  p.v_cache = static_cast<const uint16_t*>(v->data);
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.num_seqs = int(S);
+  p.num_q_heads = int(Hq);
+  p.num_kv_heads = int(Hkv);
+  p.group = int(Hq / Hkv);
+  p.head_groups = (p.group + 15) / 16;
+  p.max_len = int(Lmax);
+  p.scale_log2 = float(double(scale) * 1.4426950408889634);
+  p.part_tokens = int(Lmax);
+  p.max_parts = 1;
+  const pa::LaunchCtx ctx{stream, nullptr, nullptr, cus};
+  const hipError_t e = pa::launch_contiguous(p, int(D), ctx);
+  if (e != hipSuccess) return hip_fail(e, "contiguous decode launch");
+  return PA_OK;
+}
+
 PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* block_pairs,
                              hipStream_t stream) {
   g_error.clear();

@@ -105,5 +105,8 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
                          Path path, const LaunchCtx& ctx);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
 hipError_t launch_copy(const CopyParams& p, hipStream_t stream);
+// Contiguous control: k_cache / v_cache hold one region of max_len tokens per
+// (sequence, KV head); MFMA path, no split.
+hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCtx& ctx);
 
 }  // namespace pa

@@ -1042,6 +1042,31 @@ __device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
   return pick;
 }
 
+// The waves' MFMA accumulators of one (sequence, head group) through LDS to the
+// output or to this partition's partial result.
+template <int D>
+__device__ __forceinline__ void mfma_finish(const DecodeParams& p, Smem<D>& sm, const MfmaAcc<D>& acc,
+                                            int s, int h0, int ncols, int part, int nparts, int wave,
+                                            int lane) {
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  // column totals over the four 16-lane groups
+  float l = acc.l;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  if (g4 == 0) {
+    sm.m[wave][r] = acc.m;
+    sm.l[wave][r] = l;
+  }
+  if (r < ncols) {  // columns past the group hold nothing
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
+  }
+  finish_partition<D>(p, sm, s, h0, ncols, part, nparts);
+}
+
 // Partitions of sequence s that this launch covers (clamping keeps the
 // partition count consistent with the grid for over-long contexts).
 __device__ __forceinline__ int partitions(const DecodeParams& p, int L) {
@@ -1084,22 +1109,7 @@ __global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_mfma(DecodeP
     mfma_tile<D>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
   });
 
-  // column totals over the four 16-lane groups
-  float l = acc.l;
-  l += shfl_xor(l, 16);
-  l += shfl_xor(l, 32);
-  if (g4 == 0) {
-    sm.m[wave][r] = acc.m;
-    sm.l[wave][r] = l;
-  }
-  if (r < ncols) {  // columns past the group hold nothing
-#pragma unroll
-    for (int mm = 0; mm < D / 16; ++mm)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
-  }
-
-  finish_partition<D>(p, sm, s, h0, ncols, part, nparts);
+  mfma_finish<D>(p, sm, acc, s, h0, ncols, part, nparts, wave, lane);
 }
 
 template <int D, int BS, int VG>
@@ -1156,6 +1166,81 @@ __global__ __launch_bounds__(kThreads, BS == 8 || VG == 2 ? 1 : 2) void decode_v
   }
 
   finish_partition<D>(p, sm, s, h0, VG, part, nparts);
+}
+
+// ---------------------------------------------------------------------------
+// contiguous control: the same decode over a cache without paging.  Each
+// (sequence, KV head) owns one contiguous run of max_len / 16 tiles, each tile
+// in the format of a 16-token block of one head (K [D/8, 16, 8], V [4, D, 4]),
+// so the loads are the paged kernel's loads with the tile address computed
+// instead of looked up and the tiles of a context adjacent in memory.
+// ---------------------------------------------------------------------------
+template <int D, typename F>
+__device__ __forceinline__ void walk_contiguous(const DecodeParams& p, int s, int kvh, int t1, int wave,
+                                                int lane, F&& compute) {
+  constexpr int NC = D / 32;
+  constexpr int S = 4;
+  constexpr int kTileBytes = kTileTokens * D * 2;
+  const int ntiles = (t1 + kTileTokens - 1) / kTileTokens;
+  const int n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+  const int Lmax = p.max_len;
+  const size_t region = (size_t(s) * p.num_kv_heads + kvh) * size_t(Lmax) * D;
+  const auto rk = make_rsrc(p.k_cache + region, Lmax * D * 2);
+  const auto rv = make_rsrc(p.v_cache + region, Lmax * D * 2);
+  const auto rz = make_rsrc(p.k_cache, 0);  // zero records: a load through it is free and reads zeros
+  const LaneOffsets<D, 16> lo = lane_offsets<D, 16>(lane);
+  auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    const bool valid = j < n;
+    const auto k_r = valid ? rk : rz;
+    const auto v_r = valid ? rv : rz;
+    const int toff = valid ? (wave + kWaves * j) * kTileBytes : 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      kt[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            k_r, int(lo.k0 + c * 4 * kTileTokens * 16), toff, kStreamingLoad));
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      vt[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            v_r, int(lo.v0 + c * 256), toff, kStreamingLoad));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const int rounds = (n + S - 1) / S;
+  u32x4 kk[S][NC], vv[S][NC];
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) load(i, kk[i], vv[i]);
+  for (int j = 0; j < rounds * S; j += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      load(j + i + S - 1, kk[(i + S - 1) % S], vv[(i + S - 1) % S]);
+      compute(kTileTokens * (wave + kWaves * (j + i)), kk[i], vv[i]);
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_contiguous(DecodeParams p) {
+  constexpr int NC = D / 32;
+  __shared__ Smem<D> sm;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  const int s = ranked_seq(p, blockIdx.y);
+  int kvh, h0, ncols;
+  head_span(p, blockIdx.x, kvh, h0, ncols);
+  const int L = clamp_len(p, p.context_lens[s]);
+  u32x4 q[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    q[c] = u32x4{0u, 0u, 0u, 0u};
+    if (r < ncols) q[c] = load16(p.q + size_t(s) * p.q_s + size_t(h0 + r) * p.q_h + 8 * (g4 + 4 * c));
+  }
+  MfmaAcc<D> acc;
+  mfma_reset(acc);
+  walk_contiguous<D>(p, s, kvh, L, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    mfma_tile<D>(acc, q, p.scale_log2, ts, L, lane, kt, vt);
+  });
+  mfma_finish<D>(p, sm, acc, s, h0, ncols, 0, 1, wave, lane);
 }
 
 // Partition combine: one thread per (head, dim) of a sequence.
@@ -1342,6 +1427,15 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
                          Path path, const LaunchCtx& ctx) {
   if (head_dim == 64) return launch_decode_d<64>(p, sk, block_size, path, ctx);
   if (head_dim == 128) return launch_decode_d<128>(p, sk, block_size, path, ctx);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCtx& ctx) {
+  DecodeParams q = p;
+  q.max_parts = 1;
+  const int row_wgs = p.num_kv_heads * p.head_groups;
+  if (head_dim == 64) return launch_rows(decode_mfma_contiguous<64>, q, row_wgs, ctx);
+  if (head_dim == 128) return launch_rows(decode_mfma_contiguous<128>, q, row_wgs, ctx);
   return hipErrorInvalidValue;
 }
 

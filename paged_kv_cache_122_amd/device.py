@@ -58,3 +58,28 @@ def upload(w, device="cuda"):
         context_lens=torch.from_numpy(w.context_lens).to(device),
         k_cache=k_cache, v_cache=v_cache, owned=owned,
         copies=torch.from_numpy(np.ascontiguousarray(w.copies, dtype=np.int64)).to(device))
+
+
+def contiguous_copy(dw, w):
+    """The pools of a device workload without paging, for pa_decode_contiguous:
+    (sequence, KV head) region s*Hkv + h holds that sequence's tokens in logical
+    order as a run of 16-token tiles (K [S*Hkv, T, D/8, 16, 8], V [S*Hkv, T, 4,
+    D, 4], T = table width * B / 16 rounded up).  A gather of whole blocks
+    through the tables; sentinel entries read block 0, whose tokens lie past
+    the context and are never used."""
+    S, W, B = w.num_seqs, w.table_width, w.block_size
+    Hkv, D = w.num_kv_heads, w.head_dim
+    bt = dw.block_tables[:, :W].long().clamp(min=0)
+    if B == 8 and W % 2:                                   # whole 16-token tiles
+        bt = torch.nn.functional.pad(bt, (0, 1))
+        W += 1
+    k = dw.k_cache[bt].permute(0, 2, 1, 3, 4, 5)         # [S, Hkv, W, D/8, B, 8]
+    v = dw.v_cache[bt].permute(0, 2, 1, 3, 4, 5)         # [S, Hkv, W, B/4, D, 4]
+    if B == 32:   # two tiles per block
+        k = k.reshape(S, Hkv, W, D // 8, 2, 16, 8).permute(0, 1, 2, 4, 3, 5, 6)
+    elif B == 8:  # two blocks per tile
+        k = k.reshape(S, Hkv, W // 2, 2, D // 8, 8, 8).permute(0, 1, 2, 4, 3, 5, 6)
+    T = W * B // 16
+    k = k.reshape(S * Hkv, T, D // 8, 16, 8)
+    v = v.reshape(S * Hkv, T, 4, D, 4)
+    return k.contiguous(), v.contiguous()

@@ -209,3 +209,28 @@ def test_copy_blocks_validation(lib):
     assert call(T([3, 2], pa.PA_I64, data=None)) == pa.PA_ERR_INVALID
     bad = decode_args(kdt=pa.PA_F32)
     assert lib.pa_copy_blocks(r(bad["k"]), r(bad["v"]), r(T([3, 2], pa.PA_I64)), None) == pa.PA_ERR_INVALID
+
+
+def test_decode_contiguous_validation(lib):
+    """pa_decode_contiguous checks shapes before any launch (fake pointers here)."""
+    r = ctypes.byref
+
+    def call(S=4, Hq=8, Hkv=2, D=128, T=4, kshape=None, vshape=None, lens=None, scale=0.1):
+        out, q = T_([S, Hq, D], pa.PA_BF16), T_([S, Hq, D], pa.PA_BF16)
+        k = T_(kshape or [S * Hkv, T, D // 8, 16, 8], pa.PA_BF16)
+        v = T_(vshape or [S * Hkv, T, 4, D, 4], pa.PA_BF16)
+        ln = T_([lens if lens is not None else S], pa.PA_I32)
+        return lib.pa_decode_contiguous(r(out), r(q), r(k), r(v), r(ln), scale, None)
+
+    assert call(S=0, kshape=[0, 4, 16, 16, 8], vshape=[0, 4, 4, 128, 4], lens=0) == pa.PA_OK
+    assert call(kshape=[8, 4, 16, 16, 4]) == pa.PA_ERR_INVALID          # last dim 8
+    assert call(kshape=[8, 4, 16, 8, 8]) == pa.PA_ERR_INVALID           # 16-token tiles
+    assert call(kshape=[7, 4, 16, 16, 8]) == pa.PA_ERR_INVALID          # S * Hkv
+    assert call(vshape=[8, 3, 4, 128, 4]) == pa.PA_ERR_INVALID          # matches k
+    assert call(D=96, kshape=[8, 4, 12, 16, 8], vshape=[8, 4, 4, 96, 4]) == pa.PA_ERR_UNSUPPORTED
+    assert call(Hq=7) == pa.PA_ERR_INVALID
+    assert call(lens=3) == pa.PA_ERR_INVALID
+    assert call(scale=float("nan")) == pa.PA_ERR_INVALID
+
+
+T_ = T

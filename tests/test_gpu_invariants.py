@@ -373,3 +373,29 @@ def test_copy_blocks_bit_exact(D, B, Hkv):
     torch.cuda.synchronize()
     assert np.array_equal(dev.bf16_bits(dw.k_cache), k_all)
     assert np.array_equal(dev.bf16_bits(dw.v_cache), v_all)
+
+
+@pytest.mark.parametrize("D,B,Hq,Hkv", [(128, 16, 32, 8), (64, 32, 8, 2), (128, 8, 64, 8), (64, 16, 4, 4)])
+def test_contiguous_control(D, B, Hq, Hkv):
+    """The unpaged control equals the paged decode's unsplit MFMA schedule bit for
+    bit (same tiles in the same order), and the oracle on the unpaged layout."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+    lens = [0, 1, 15, 16, 17, 100, 511, 1000, 1024, 3] * 3
+    w = workloads.random_workload(81 + D + B, lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                  block_size=B)
+    print(f"contiguous D={D} B={B} Hq={Hq} Hkv={Hkv}", flush=True)
+    dw = _setup(w)
+    paged = _decode(torch, w, dw, partition_tokens=-1, path=2)
+    k, v = dev.contiguous_copy(dw, w)
+    out = torch.empty_like(dw.q)
+    pa.decode_contiguous(out, dw.q, k, v, dw.context_lens, w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.bf16_bits(out), dev.bf16_bits(paged))
+    ref = oracle.contiguous_decode(w.q, dev.bf16_bits(k), dev.bf16_bits(v), w.context_lens, w.scale)
+    assert_close_bf16(_as_f64(torch, out), ref, "contiguous")
+    out32 = torch.empty(dw.q.shape, dtype=torch.float32, device=dw.q.device)
+    pa.decode_contiguous(out32, dw.q, k, v, dw.context_lens, w.scale)
+    torch.cuda.synchronize()
+    assert_close(_as_f64(torch, out32), ref, "contiguous f32", max_abs=1e-4, rel_rms=1e-4)

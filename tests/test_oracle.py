@@ -408,3 +408,40 @@ def test_bf16_half_ulp_bounds_the_output_rounding():
     assert np.all(moved <= bf16_half_ulp(x))
     assert np.max(moved / bf16_half_ulp(x)) > 0.99          # the bound is reached
     assert bf16_half_ulp(1.0) == 2.0 ** -8 and bf16_half_ulp(-4.4) == 2.0 ** -6
+
+
+def _contiguous_copy(w, kst, vst):
+    """The cache of a workload unpaged: each (sequence, head) run of 16-token
+    tiles holds its tokens in order (a plain numpy rearrangement), NaN elsewhere."""
+    from paged_kv_cache_122_amd import workloads
+    B, D, Hkv, S = w.block_size, w.head_dim, w.num_kv_heads, w.num_seqs
+    T = -(-w.table_width * B // 16)
+    k = np.full((S * Hkv, T, D // 8, 16, 8), workloads.NAN_BF16, dtype=np.uint16)
+    v = np.full((S * Hkv, T, 4, D, 4), workloads.NAN_BF16, dtype=np.uint16)
+    for s in range(S):
+        L = int(w.context_lens[s])
+        for i in range(-(-L // B)):
+            kb, vb = kst[int(w.block_tables[s, i])], vst[int(w.block_tables[s, i])]
+            for j in range(B):
+                t = i * B + j
+                for h in range(Hkv):
+                    k[s * Hkv + h, t // 16, :, t % 16, :] = kb[h, :, j, :]
+                    v[s * Hkv + h, t // 16, (t % 16) // 4, :, t % 4] = vb[h, j // 4, :, j % 4]
+    return k, v
+
+
+def test_contiguous_control_equals_paged():
+    """Paging changes the layout, not the result (First Principles, section 18):
+    the unpaged control gives exactly the paged decode on the same values."""
+    from paged_kv_cache_122_amd import workloads
+    w = workloads.random_workload(31, [1, 16, 17, 40, 63], num_q_heads=8, num_kv_heads=2,
+                                  head_dim=64, block_size=16)
+    kst, vst = w.stores()
+    oracle.cache_append(w.k_new, w.v_new, w.slot_mapping, kst, vst, w.block_size)
+    paged = oracle.paged_decode(w.q, kst, vst, w.block_tables, w.context_lens, w.scale, w.block_size)
+    k, v = _contiguous_copy(w, kst, vst)
+    contig = oracle.contiguous_decode(w.q, k, v, w.context_lens, w.scale)
+    assert np.array_equal(paged, contig)
+    # a dim index off by one in the V layout would mix dims: planted on a copy
+    v_bad = np.roll(v, 1, axis=3)
+    assert not np.allclose(oracle.contiguous_decode(w.q, k, v_bad, w.context_lens, w.scale), paged)
