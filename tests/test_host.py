@@ -250,3 +250,65 @@ def test_contiguous_copy_matches_a_plain_rearrangement(B):
                 assert np.array_equal(k[r, t // 16, :, t % 16, :], k_ref[r, t // 16, :, t % 16, :])
                 assert np.array_equal(v[r, t // 16, (t % 16) // 4, :, t % 4],
                                       v_ref[r, t // 16, (t % 16) // 4, :, t % 4])
+
+
+# -- prefix cache ---------------------------------------------------------------
+def test_prefix_cache_page_example():
+    """First Principles, section 9: two requests sharing a 32-token prefix share
+    P0 and P1 (refcount 2); the rest is private; P1's hash chains P0's."""
+    from paged_kv_cache_122_amd.prefix_cache import ROOT_HASH, PrefixCache, block_hash
+    pool = BlockPool(16, 16)
+    cache = PrefixCache(pool)
+    prefix = list(range(1000, 1032))
+    r1, hits1 = cache.allocate_prompt(prefix + list(range(20)))       # 52 tokens: 4 blocks
+    r2, hits2 = cache.allocate_prompt(prefix + list(range(50, 60)))   # 42 tokens: 3 blocks
+    assert (hits1, hits2) == (0, 2)
+    assert r1.table[:2] == r2.table[:2] and len(r1.table) == 4 and len(r2.table) == 3
+    assert set(r1.table[2:]).isdisjoint(r2.table[2:])
+    assert [pool.ref[b] for b in r1.table] == [2, 2, 1, 1]
+    h0 = block_hash(ROOT_HASH, prefix[:16])
+    assert cache.hash_of[r1.table[1]] == block_hash(h0, prefix[16:])
+    # the same 16 tokens after a different prefix are a different block
+    assert block_hash(ROOT_HASH, prefix[16:]) != block_hash(h0, prefix[16:])
+    assert pool.blocks_in_use() == 5
+
+
+@pytest.mark.parametrize("B,shared_tokens", [(16, 992), (128, 896)])
+def test_prefix_cache_system_prompt(B, shared_tokens):
+    """sevydevy: 50 chats with the same 1,000-token system prompt; only full
+    blocks are shared (62 of 16 tokens = 992 tokens, or 7 of 128 = 896), each
+    chat keeps a private tail: 112 blocks instead of 3,150 at B = 16."""
+    from paged_kv_cache_122_amd.prefix_cache import PrefixCache
+    pool = BlockPool(4000, B)
+    cache = PrefixCache(pool)
+    prompt = [7 * i % 50021 for i in range(1000)]
+    chats = [cache.allocate_prompt(prompt)[0] for _ in range(50)]
+    n_full = shared_tokens // B
+    assert pool.blocks_in_use() == n_full + 50
+    if B == 16:
+        assert pool.blocks_in_use() == 112 and 50 * len(chats[0].table) == 3150
+    assert all(c.table[:n_full] == chats[0].table[:n_full] for c in chats)
+
+
+def test_prefix_cache_salt_and_eviction():
+    """A cache salt keeps tenants apart; a freed block stays findable until the
+    pool reuses it (least recently freed first), then a lookup misses."""
+    from paged_kv_cache_122_amd.prefix_cache import PrefixCache
+    pool = BlockPool(6, 16)
+    cache = PrefixCache(pool)
+    toks = list(range(48))                                          # 3 full blocks
+    a, _ = cache.allocate_prompt(toks, salt=b"tenant-a")
+    b, hits = cache.allocate_prompt(toks, salt=b"tenant-b")
+    assert hits == 0 and set(a.table).isdisjoint(b.table)
+    a_blocks = list(a.table)
+    free(pool, a)                                                   # refcounts 0, still registered
+    c, hits = cache.allocate_prompt(toks, salt=b"tenant-a")
+    assert hits == 3 and c.table == a_blocks and pool.num_free() == 0
+    free(pool, c)
+    free(pool, b)
+    # reuse the whole pool: every block is handed out again and loses its hash
+    d = Sequence()
+    allocate_tokens(pool, d, 16 * 6)
+    free(pool, d)
+    e, hits = cache.allocate_prompt(toks, salt=b"tenant-a")
+    assert hits == 0 and pool.blocks_in_use() == 3
