@@ -27,6 +27,7 @@ from .paged_attention import (
     attention_textbook,
     paged_decode,
     contiguous_decode,
+    multi_query_decode,
     paged_decode_online,
     paged_decode_eq4,
     split_partials,
@@ -42,6 +43,7 @@ __all__ = [
     "attention_textbook",
     "paged_decode",
     "contiguous_decode",
+    "multi_query_decode",
     "paged_decode_online",
     "paged_decode_eq4",
     "split_partials",

@@ -101,6 +101,10 @@ class Workload:
     # copy-on-write copies this step performs before its append, int64 [N, 2]
     # (src, dst); every dst block holds NaN until the copy
     copies: np.ndarray = field(default_factory=lambda: np.zeros((0, 2), dtype=np.int64))
+    # rows of q / k_new / v_new / slot_mapping per sequence, int32 [S + 1]: one
+    # new token each unless a step brings several (chunked prefill,
+    # speculative verification)
+    query_start: np.ndarray = None
 
     @property
     def num_seqs(self):
@@ -131,30 +135,40 @@ class Workload:
 
 
 def build_workload(name, seed, rng, *, num_q_heads, num_kv_heads, head_dim, block_size,
-                   num_blocks, tables, context_lens, width, meta=None, copies=None):
+                   num_blocks, tables, context_lens, width, meta=None, copies=None, new_tokens=None):
     """Fill values for a placed workload.  ``tables`` are lists of physical ids
     covering ``ceil(L/B)`` blocks per sequence; ``rng`` continues the stream.
     ``copies`` are the pool's pending copy-on-write copies ``(src, dst, valid)``
-    of this step: ``src`` holds ``valid`` tokens, ``dst`` holds NaN until copied."""
+    of this step: ``src`` holds ``valid`` tokens, ``dst`` holds NaN until copied.
+    ``new_tokens[s]`` (default 1) of the ``L`` tokens of sequence ``s`` arrive
+    this step: the pool holds the first ``L - new_tokens[s]``."""
     S = len(context_lens)
     Hq, Hkv, D, B = int(num_q_heads), int(num_kv_heads), int(head_dim), int(block_size)
     if Hq % Hkv or D not in layout.SUPPORTED_HEAD_DIMS or B not in layout.SUPPORTED_BLOCK_SIZES:
         raise ValueError("unsupported head / block geometry")
     lens = np.asarray(context_lens, dtype=np.int32)
+    news = np.ones(S, dtype=np.int64) if new_tokens is None else np.asarray(new_tokens, dtype=np.int64)
+    if np.any(news < 0) or np.any(news > np.maximum(lens, 1)):
+        raise ValueError("new tokens must lie inside the context")
+    qstart = np.zeros(S + 1, dtype=np.int32)
+    qstart[1:] = np.cumsum(news)
+    T = int(qstart[-1])
     bt = np.full((S, int(width)), -1, dtype=np.int32)
-    slots = np.full(S, -1, dtype=np.int64)
+    slots = np.full(T, -1, dtype=np.int64)
     valid_before = {}
     users = {}
     for s in range(S):
         L = int(lens[s])
+        n = int(news[s])
         t = list(tables[s])
         if len(t) != blocks_for_tokens(L, B) or len(t) > width:
             raise ValueError("block table does not match context length")
         bt[s, :len(t)] = t
         if L > 0:
-            slots[s] = slot_of_position(t, L - 1, B)
+            for i in range(n):
+                slots[qstart[s] + i] = slot_of_position(t, L - n + i, B)
         for i, b in enumerate(t):
-            n_prev = min(B, max(0, (L - 1) - i * B))
+            n_prev = min(B, max(0, (L - n) - i * B))
             valid_before[b] = max(valid_before.get(b, 0), n_prev)
             users[b] = users.get(b, 0) + 1
     copies = [tuple(int(x) for x in c) for c in (copies or [])]
@@ -162,9 +176,9 @@ def build_workload(name, seed, rng, *, num_q_heads, num_kv_heads, head_dim, bloc
         valid_before[src] = max(valid_before.get(src, 0), valid)
         users.setdefault(src, 0)
 
-    q = _bf16_normal(rng, (S, Hq, D))
-    k_new = _bf16_normal(rng, (S, Hkv, D))
-    v_new = _bf16_normal(rng, (S, Hkv, D))
+    q = _bf16_normal(rng, (T, Hq, D))
+    k_new = _bf16_normal(rng, (T, Hkv, D))
+    v_new = _bf16_normal(rng, (T, Hkv, D))
 
     owned = np.array(sorted(valid_before), dtype=np.int64)
     n = len(owned)
@@ -200,7 +214,8 @@ def build_workload(name, seed, rng, *, num_q_heads, num_kv_heads, head_dim, bloc
         block_tables=bt, slot_mapping=slots, q=q, k_new=k_new, v_new=v_new, owned=owned,
         k_blocks=pools[0], v_blocks=pools[1],
         refcount=np.array([users[int(b)] for b in owned], dtype=np.int32), meta=dict(meta or {}),
-        copies=np.array([(c[0], c[1]) for c in copies], dtype=np.int64).reshape(-1, 2))
+        copies=np.array([(c[0], c[1]) for c in copies], dtype=np.int64).reshape(-1, 2),
+        query_start=qstart)
 
 
 def place_independent(rng, context_lens, block_size, num_blocks):
@@ -332,6 +347,35 @@ def opt13b_cow_fork():
                           meta={"groups": groups, "per_group": per}, copies=copies)
 
 
+def multi_query_workload(seed, old_lens, new_counts, *, num_q_heads, num_kv_heads, head_dim,
+                         block_size, name="multi_query", width=None):
+    """Sequences with ``old_lens[s]`` cached tokens and ``new_counts[s]`` tokens
+    arriving this step (context ``old + new``); random placement, pool needed
+    + 10 %."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B = int(block_size)
+    lens = [int(o) + int(n) for o, n in zip(old_lens, new_counts)]
+    need = sum(blocks_for_tokens(L, B) for L in lens)
+    nb = max(1, int(np.ceil(1.1 * need)))
+    _, tables = place_independent(rng, lens, B, nb)
+    width = width or max(1, max(blocks_for_tokens(L, B) for L in lens))
+    return build_workload(name, seed, rng, num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                          head_dim=head_dim, block_size=B, num_blocks=nb, tables=tables,
+                          context_lens=lens, width=width, new_tokens=list(new_counts))
+
+
+def llama3_8b_verify5():
+    """Speculative verification on the Llama-3-8B-shaped batch: 64 seqs with
+    U[128, 2048] cached tokens, each verifying 5 drafted tokens this step
+    (32 q / 8 kv heads, D 128, B 16)."""
+    seed = 1009
+    rng = np.random.Generator(np.random.PCG64(seed))
+    old = rng.integers(128, 2048, size=64, endpoint=True).tolist()
+    return multi_query_workload(seed, old, [5] * 64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                block_size=16, name="llama3_8b_verify5_b64",
+                                width=blocks_for_tokens(2048 + 5, 16))
+
+
 def long_context(block_size):
     """8 seqs x 32,768 tokens, 32 q / 8 kv heads, D 128, B in {8, 16, 32},
     random placement, pool needed + 10 %."""
@@ -356,6 +400,7 @@ CONFIGS = {
     "long32k_b16": lambda: long_context(16),
     "long32k_b32": lambda: long_context(32),
     "opt13b_cow_fork_b128": opt13b_cow_fork,
+    "llama3_8b_verify5_b64": llama3_8b_verify5,
 }
 
 
