@@ -1,7 +1,7 @@
 /*
  * pa.h -- C ABI of libpa: PagedAttention decode for AMD MI355X (gfx950).
  *
- * Two operations, as the PagedAttention pages describe them:
+ * The operations, as the PagedAttention pages describe them:
  *
  *   pa_cache_append  writes each new token's K and V into the slot of the
  *                    block pool that the host block manager assigned to it
@@ -17,6 +17,9 @@
  *                    split into partitions whose partial softmax results are
  *                    combined by a log-sum-exp reduce ("PagedAttention from
  *                    First Principles", section 17, the v2 kernel's reduce).
+ *   pa_decode_multi  several new tokens per sequence (chunked prefill,
+ *                    speculative verification): their append and their causal
+ *                    attention in one launch.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -239,14 +242,58 @@ int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
 int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
                          const pa_tensor* context_lens, float scale, hipStream_t stream);
 
+/*
+ * pa_decode_multi -- several new tokens per sequence in one step: the append
+ * and the attention of chunked prefill and of speculative verification.
+ *
+ * A prefill split into chunks brings a chunk of a prompt in one scheduler step
+ * beside other sequences' single decode tokens ("PagedAttention from First
+ * Principles", section 12); a verifier checks the draft's tokens of every
+ * sequence in one pass and appends them to its cache ("PagedAttention from
+ * First Principles", section 14).  Sequence s brings n_s = query_start[s+1] -
+ * query_start[s] tokens, which are its positions L_s - n_s .. L_s - 1.
+ *
+ *   out           bf16 or f32 [T, num_q_heads, head_dim], last dim contiguous;
+ *                 row r belongs to the new token in row r of q.
+ *   q             bf16 [T, num_q_heads, head_dim]; rows query_start[s] ..
+ *                 query_start[s+1]-1 are sequence s's new tokens in order.
+ *   k_new, v_new  bf16 [T, num_kv_heads, head_dim]: their keys and values.
+ *                 q, k_new, v_new: last dim contiguous, rows 16-byte aligned.
+ *   slot_mapping  int64 [T]: the slot of each new token; a negative slot
+ *                 skips the store (the token still takes part in attention).
+ *   query_start   int32 [S + 1], non-decreasing, query_start[S] <= T.
+ *   k_cache, v_cache  the pools (layout above): the new tokens are written,
+ *                 nothing else is touched.
+ *   block_tables, context_lens, scale, block_size  as for pa_decode; L_s
+ *                 counts the new tokens.
+ *   max_query_len an upper bound on n_s (the launch covers that many rows per
+ *                 sequence); max_query_len * (num_q_heads / num_kv_heads) <= 2^24.
+ *
+ * New token i of sequence s (row r = query_start[s] + i) attends to the
+ * positions 0 .. L_s - n_s + i: the cached ones and the new ones up to itself.
+ * out[r, h, :] = softmax_t(scale * q[r,h,:] . K[s,t,:]) V[s,t,:] over those t,
+ * with K and V of the new positions taken from k_new / v_new (equal to what
+ * the store puts in the pools).  Same arithmetic as pa_decode.  Preconditions
+ * (debug mode checks them): 0 <= n_s <= min(L_s, max_query_len); each
+ * non-negative slot is the table's slot for its position and no slot repeats;
+ * no cached position read by the call (t < L_s - n_s of any sequence) lies in
+ * a slot it writes.  Rows outside every sequence's range are not written.
+ * S == 0, T == 0 or max_query_len == 0 is a no-op.
+ */
+int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
+                    const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,
+                    pa_tensor* v_cache, const pa_tensor* block_tables, const pa_tensor* context_lens,
+                    float scale, int32_t block_size, int32_t max_query_len, hipStream_t stream);
+
 /* Message of the last failed call on this thread (valid until the next pa_* call). */
 const char* pa_last_error(void);
 
 /*
- * Debug mode (process-wide, off by default).  When on, pa_cache_append and
- * pa_decode copy the index tensors to the host, synchronise `stream`, and
- * check the device-side contracts listed above before launching; a violation
- * returns PA_ERR_CONTRACT.  Returns the previous setting.
+ * Debug mode (process-wide, off by default).  When on, the entry points that
+ * take index tensors (appends, copies, paged decodes) copy them to the host,
+ * synchronise `stream`, and check the device-side contracts listed above and
+ * at each entry point before launching; a violation returns PA_ERR_CONTRACT.
+ * Returns the previous setting.
  */
 int pa_set_debug(int on);
 

@@ -18,7 +18,8 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_
 PA_BF16, PA_F32, PA_I32, PA_I64 = 1, 2, 3, 4
 MAX_DIMS = 5
 
-EXPORTED = ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous", "pa_decode_ex", "pa_decode_workspace_bytes",
+EXPORTED = ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous", "pa_decode_ex",
+            "pa_decode_multi", "pa_decode_workspace_bytes",
             "pa_decode_schedule", "pa_last_error", "pa_set_debug")
 
 _DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -59,6 +60,7 @@ def load(path=None):
     lib.pa_cache_append.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [P, P, P, ctypes.c_void_p]
     lib.pa_decode_contiguous.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_void_p]
+    lib.pa_decode_multi.argtypes = [P] * 10 + [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
     lib.pa_decode_contiguous.restype = ctypes.c_int
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
@@ -134,6 +136,21 @@ def decode_contiguous(out, q, k, v, context_lens, scale, stream=None):
     ds = [describe(x) for x in ts]
     _check(lib, lib.pa_decode_contiguous(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
                                          _stream(stream)))
+
+
+def decode_multi(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
+                 context_lens, scale, block_size, max_query_len, stream=None):
+    """pa_decode_multi: append the rows of k_new / v_new and attend every row of q
+    [T, Hq, D] causally over its sequence (query_start int32 [S + 1])."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in (
+        (out, "out"), (q, "q"), (k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),
+        (query_start, "query_start"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+        (block_tables, "block_tables"), (context_lens, "context_lens"))]
+    ds = [describe(x) for x in ts]
+    _check(lib, lib.pa_decode_multi(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
+                                    ctypes.c_int32(block_size), ctypes.c_int32(max_query_len),
+                                    _stream(stream)))
 
 
 def copy_blocks(k_cache, v_cache, block_pairs, stream=None):

@@ -596,6 +596,181 @@ PA_EXPORT int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_
   return PA_OK;
 }
 
+namespace {
+
+// Device-side contracts of pa_decode_multi, checked on the host.
+int debug_check_multi(const pa_tensor* slot_mapping, const pa_tensor* query_start,
+                      const pa_tensor* block_tables, const pa_tensor* context_lens, int64_t S,
+                      int64_t T, int64_t W, int64_t B, int64_t NB, int64_t max_query_len,
+                      hipStream_t stream) {
+  std::vector<int32_t> lens, qs, bt;
+  std::vector<int64_t> slots;
+  int rc;
+  if ((rc = copy_to_host(&lens, context_lens->data, size_t(S), stream)) != PA_OK) return rc;
+  if ((rc = copy_to_host(&qs, query_start->data, size_t(S + 1), stream)) != PA_OK) return rc;
+  if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(T), stream)) != PA_OK) return rc;
+  const size_t stride = size_t(block_tables->stride[0]);
+  if ((rc = copy_to_host(&bt, block_tables->data, S ? size_t(S - 1) * stride + size_t(W) : 0, stream)) != PA_OK)
+    return rc;
+  if (qs[0] < 0 || qs[size_t(S)] > T)
+    return fail(PA_ERR_CONTRACT, "query_start spans [%d, %d), outside [0, %lld)", qs[0], qs[size_t(S)],
+                (long long)T);
+  std::unordered_set<int64_t> written;
+  for (int64_t s = 0; s < S; ++s) {
+    const int64_t L = lens[size_t(s)], n = int64_t(qs[size_t(s + 1)]) - qs[size_t(s)];
+    if (L < 0 || L > W * B)
+      return fail(PA_ERR_CONTRACT, "context_lens[%lld] = %lld outside [0, width*block_size = %lld]",
+                  (long long)s, (long long)L, (long long)(W * B));
+    if (n < 0) return fail(PA_ERR_CONTRACT, "query_start decreases at %lld", (long long)s);
+    if (n > L || n > max_query_len)
+      return fail(PA_ERR_CONTRACT, "sequence %lld brings %lld tokens (context %lld, max_query_len %lld)",
+                  (long long)s, (long long)n, (long long)L, (long long)max_query_len);
+    for (int64_t i = 0; i < (L + B - 1) / B; ++i) {
+      const int64_t b = bt[size_t(s) * stride + size_t(i)];
+      if (b < 0 || b >= NB)
+        return fail(PA_ERR_CONTRACT, "block_tables[%lld][%lld] = %lld outside [0, %lld)", (long long)s,
+                    (long long)i, (long long)b, (long long)NB);
+    }
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t pos = L - n + i;
+      const int64_t sl = slots[size_t(qs[size_t(s)] + i)];
+      if (sl < 0) continue;
+      const int64_t want = int64_t(bt[size_t(s) * stride + size_t(pos / B)]) * B + pos % B;
+      if (sl != want)
+        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld, but position %lld of sequence %lld is slot %lld",
+                    (long long)(qs[size_t(s)] + i), (long long)sl, (long long)pos, (long long)s, (long long)want);
+      if (!written.insert(sl).second)
+        return fail(PA_ERR_CONTRACT, "slot %lld is written twice", (long long)sl);
+    }
+  }
+  // no cached token read by this call lies in a slot it writes
+  for (int64_t s = 0; s < S && !written.empty(); ++s) {
+    const int64_t L = lens[size_t(s)], n = int64_t(qs[size_t(s + 1)]) - qs[size_t(s)];
+    for (int64_t pos = 0; pos < L - n; ++pos) {
+      const int64_t sl = int64_t(bt[size_t(s) * stride + size_t(pos / B)]) * B + pos % B;
+      if (written.count(sl))
+        return fail(PA_ERR_CONTRACT, "sequence %lld reads slot %lld, which this call writes", (long long)s,
+                    (long long)sl);
+    }
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new,
+                              const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                              const pa_tensor* query_start, pa_tensor* k_cache, pa_tensor* v_cache,
+                              const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                              int32_t block_size, int32_t max_query_len, hipStream_t stream) {
+  g_error.clear();
+  int rc;
+  CacheGeom g;
+  if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
+  if ((rc = check_desc(q, "q", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(k_new, "k_new", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(v_new, "v_new", PA_BF16, 3)) != PA_OK) return rc;
+  if (!out) return fail(PA_ERR_INVALID, "out: descriptor is NULL");
+  if (out->dtype != PA_BF16 && out->dtype != PA_F32)
+    return fail(PA_ERR_INVALID, "out: dtype %s, expected bf16 or f32", dtype_name(out->dtype));
+  if ((rc = check_desc(out, "out", out->dtype, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(slot_mapping, "slot_mapping", PA_I64, 1)) != PA_OK) return rc;
+  if ((rc = check_desc(query_start, "query_start", PA_I32, 1)) != PA_OK) return rc;
+  if ((rc = check_desc(block_tables, "block_tables", PA_I32, 2)) != PA_OK) return rc;
+  if ((rc = check_desc(context_lens, "context_lens", PA_I32, 1)) != PA_OK) return rc;
+
+  const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2], S = context_lens->shape[0];
+  if (D != g.head_dim)
+    return fail(PA_ERR_INVALID, "q: head_dim %lld, caches have %lld", (long long)D, (long long)g.head_dim);
+  if (out->shape[0] != T || out->shape[1] != Hq || out->shape[2] != D)
+    return fail(PA_ERR_INVALID, "out: shape does not match q");
+  for (const pa_tensor* t : {k_new, v_new})
+    if (t->shape[0] != T || t->shape[1] != g.kv_heads || t->shape[2] != D)
+      return fail(PA_ERR_INVALID, "k_new/v_new: shape [%lld, %lld, %lld] expected", (long long)T,
+                  (long long)g.kv_heads, (long long)D);
+  if (slot_mapping->shape[0] != T || (slot_mapping->stride[0] != 1 && T > 1))
+    return fail(PA_ERR_INVALID, "slot_mapping: %lld contiguous entries expected", (long long)T);
+  if (query_start->shape[0] != S + 1 || (query_start->stride[0] != 1 && S > 0))
+    return fail(PA_ERR_INVALID, "query_start: %lld contiguous entries expected", (long long)(S + 1));
+  if (block_size != g.block_size)
+    return fail(PA_ERR_INVALID, "block_size %d does not match the caches' %lld", block_size,
+                (long long)g.block_size);
+  if (Hq <= 0 || Hq % g.kv_heads)
+    return fail(PA_ERR_INVALID, "num_q_heads %lld is not a positive multiple of num_kv_heads %lld",
+                (long long)Hq, (long long)g.kv_heads);
+  if (block_tables->shape[0] != S)
+    return fail(PA_ERR_INVALID, "block_tables: first dim must be num_seqs %lld", (long long)S);
+  const int64_t W = block_tables->shape[1];
+  if (W < 1) return fail(PA_ERR_INVALID, "block_tables: width must be >= 1");
+  if (block_tables->stride[1] != 1 || block_tables->stride[0] < W)
+    return fail(PA_ERR_INVALID, "block_tables: rows must be contiguous with row stride >= width");
+  if (context_lens->stride[0] != 1 && S > 1) return fail(PA_ERR_INVALID, "context_lens must be contiguous");
+  if ((rc = check_rows(q, "q")) != PA_OK) return rc;
+  if ((rc = check_rows(k_new, "k_new")) != PA_OK) return rc;
+  if ((rc = check_rows(v_new, "v_new")) != PA_OK) return rc;
+  if (out->stride[2] != 1 && D > 1) return fail(PA_ERR_INVALID, "out: last dim must be contiguous");
+  const int64_t G = Hq / g.kv_heads;
+  if (max_query_len < 0 || int64_t(max_query_len) * G > (int64_t(1) << 24))
+    return fail(PA_ERR_INVALID, "max_query_len %d (0 .. 2^24 / query heads per KV head)", max_query_len);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale must be finite");
+  if (S > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %lld > 65535", (long long)S);
+  if (T > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many rows");
+  if (W * g.block_size > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "table width * block_size >= 2^31");
+  if (S == 0 || T == 0 || max_query_len == 0) return PA_OK;
+  if (g_debug.load() &&
+      (rc = debug_check_multi(slot_mapping, query_start, block_tables, context_lens, S, T, W,
+                              g.block_size, g.num_blocks, max_query_len, stream)) != PA_OK)
+    return rc;
+
+  const int64_t cols = int64_t(max_query_len) * G;  // MFMA columns per (sequence, KV head)
+  const int col_sets = cols > 16 ? 2 : 1;
+  const int64_t col_groups = (cols + 16 * col_sets - 1) / (16 * col_sets);
+  if (g.kv_heads * col_groups > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+
+  pa::MultiParams m{};
+  pa::DecodeParams& p = m.d;
+  p.out = out->data;
+  p.out_s = out->stride[0];
+  p.out_h = out->stride[1];
+  p.out_f32 = out->dtype == PA_F32;
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.q_s = q->stride[0];
+  p.q_h = q->stride[1];
+  p.k_cache = static_cast<const uint16_t*>(k_cache->data);
+  p.v_cache = static_cast<const uint16_t*>(v_cache->data);
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.bt_s = block_tables->stride[0];
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.num_seqs = int(S);
+  p.num_q_heads = int(Hq);
+  p.num_kv_heads = int(g.kv_heads);
+  p.group = int(G);
+  p.head_groups = 1;
+  p.max_len = int(W * g.block_size);
+  p.scale_log2 = float(double(scale) * 1.4426950408889634);
+  p.part_tokens = p.max_len;
+  p.max_parts = 1;
+  m.k_new = static_cast<const uint16_t*>(k_new->data);
+  m.v_new = static_cast<const uint16_t*>(v_new->data);
+  m.kn_t = k_new->stride[0];
+  m.kn_h = k_new->stride[1];
+  m.vn_t = v_new->stride[0];
+  m.vn_h = v_new->stride[1];
+  m.slots = static_cast<const int64_t*>(slot_mapping->data);
+  m.query_start = static_cast<const int32_t*>(query_start->data);
+  m.num_rows = int(T);
+  m.max_query_len = max_query_len;
+  m.col_sets = col_sets;
+  m.col_groups = int(col_groups);
+  m.num_slots = g.num_blocks * g.block_size;
+  int cus = 0;
+  if ((rc = device_cus(&cus)) != PA_OK) return rc;
+  const pa::LaunchCtx ctx{stream, nullptr, nullptr, cus};
+  const hipError_t e = pa::launch_multi(m, int(D), int(g.block_size), ctx);
+  if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
+  return PA_OK;
+}
+
 PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* block_pairs,
                              hipStream_t stream) {
   g_error.clear();

@@ -73,6 +73,23 @@ struct AppendParams {
   int num_tokens, num_kv_heads;
 };
 
+// Several new tokens per sequence in one step: DecodeParams describes q / out
+// by row (one row per new token) and the pools, tables and lengths as for
+// decode; the new tokens' K/V come from k_new / v_new and are appended.
+struct MultiParams {
+  DecodeParams d;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  int64_t kn_t, kn_h, vn_t, vn_h;  // element strides of k_new, v_new rows
+  const int64_t* slots;
+  const int32_t* query_start;      // [S + 1]
+  int num_rows;                    // T
+  int max_query_len;               // rows per sequence the grid covers
+  int col_sets;                    // 16-column MFMA sets per workgroup (1 or 2)
+  int col_groups;                  // workgroups per KV head: ceil(max_query_len * G / (16 * col_sets))
+  int64_t num_slots;               // num_blocks * block_size
+};
+
 struct CopyParams {
   const int64_t* pairs;  // [N, 2] (src, dst) physical block ids
   uint16_t* k_cache;
@@ -105,6 +122,7 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
                          Path path, const LaunchCtx& ctx);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
 hipError_t launch_copy(const CopyParams& p, hipStream_t stream);
+hipError_t launch_multi(const MultiParams& p, int head_dim, int block_size, const LaunchCtx& c);
 // Contiguous control: k_cache / v_cache hold one region of max_len tokens per
 // (sequence, KV head); MFMA path, no split.
 hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCtx& ctx);

@@ -281,10 +281,15 @@ __device__ __forceinline__ void mfma_reset(MfmaAcc<D>& a) {
   a.l = 0.f;
 }
 
+// Scores of one tile (QK^T), the online-softmax update of the column
+// references and sums, and P as the B operand of PV, split into hi + lo
+// bf16: with K = 32 one MFMA takes the high halves as its first four k
+// values and the low halves as the last four, against the same four V
+// values repeated.
 template <int D>
-__device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
-                                          int ts, int t1, int lane, u32x4 (&kt)[D / 32],
-                                          u32x4 (&vt)[D / 32]) {
+__device__ __forceinline__ u32x4 mfma_probs(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
+                                            bool partial, int ts, int t1, int lane,
+                                            const u32x4 (&kt)[D / 32]) {
   constexpr int NC = D / 32;
   const int g4 = lane >> 4;
   // two independent accumulation chains, so the QK^T MFMAs overlap
@@ -295,9 +300,6 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
     s1 = mfma_16x16x32(kt[c + 1], q[c + 1], s1);
   }
   const f32x4 sacc = s0 + s1;
-  // Only the last tile of a context has tokens at or past t1 (wave-uniform
-  // test): the others skip the score and V masks.
-  const bool partial = ts + kTileTokens > t1;
   float sc[4];
   float mt = kNegInf;
 #pragma unroll
@@ -324,17 +326,24 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
     pr[j] = exp2_ftz(sc[j] - a.m);
     a.l += pr[j];
   }
-  // P as the B operand of PV, split into hi + lo bf16: with K = 32 one MFMA
-  // takes the high halves as its first four k values and the low halves as
-  // the last four, against the same four V values repeated.
   uint32_t hb[4], lb[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     hb[j] = bf16_bits(pr[j]);
     lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
   }
-  const u32x4 pb = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
-                    lb[2] | (lb[3] << 16)};
+  return u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+}
+
+template <int D>
+__device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
+                                          int ts, int t1, int lane, u32x4 (&kt)[D / 32],
+                                          u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  // Only the last tile of a context has tokens at or past t1 (wave-uniform
+  // test): the others skip the score and V masks.
+  const bool partial = ts + kTileTokens > t1;
+  const u32x4 pb = mfma_probs<D>(a, q, scale_log2, partial, ts, t1, lane, kt);
   if (partial) mask_v<D>(vt, ts, t1, lane);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
@@ -342,6 +351,30 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
     const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};  // dim 2r + 32c + 1
     a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
     a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
+  }
+}
+
+// mfma_tile for NS sets of 16 columns against one tile: each V operand is
+// built once and feeds every set.
+template <int D, int NS>
+__device__ __forceinline__ void mfma_tile_sets(MfmaAcc<D> (&a)[NS], const u32x4 (&q)[NS][D / 32],
+                                               float scale_log2, int ts, int t1, int lane,
+                                               u32x4 (&kt)[D / 32], u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  const bool partial = ts + kTileTokens > t1;
+  u32x4 pb[NS];
+#pragma unroll
+  for (int cs = 0; cs < NS; ++cs) pb[cs] = mfma_probs<D>(a[cs], q[cs], scale_log2, partial, ts, t1, lane, kt);
+  if (partial) mask_v<D>(vt, ts, t1, lane);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};
+    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};
+#pragma unroll
+    for (int cs = 0; cs < NS; ++cs) {
+      a[cs].o[2 * c] = mfma_16x16x32(a0, pb[cs], a[cs].o[2 * c]);
+      a[cs].o[2 * c + 1] = mfma_16x16x32(a1, pb[cs], a[cs].o[2 * c + 1]);
+    }
   }
 }
 
@@ -1243,6 +1276,249 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_contiguous(DecodePara
   mfma_finish<D>(p, sm, acc, s, h0, ncols, 0, 1, wave, lane);
 }
 
+// Dims 8*piece .. +7 of one token's K and V (kv, vv) into slot `slot` of head h.
+template <int D, int BS>
+__device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_cache, int num_kv_heads,
+                                                 int64_t slot, int h, int piece, u32x4 kv, u32x4 vv) {
+  const int64_t blk = slot / BS;
+  const int off = int(slot - blk * BS);
+  const size_t tile = (size_t(blk) * num_kv_heads + h) * (BS * D);
+  store16(k_cache + tile + (piece * BS + off) * 8, kv);
+  uint16_t* vt = v_cache + tile + ((off >> 2) * D + piece * 8) * 4 + (off & 3);
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vt[(2 * e) * 4] = uint16_t(w[e] & 0xffffu);
+    vt[(2 * e + 1) * 4] = uint16_t(w[e] >> 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// several new tokens per sequence (chunked prefill, speculative verification)
+//
+// Workgroup (KV head, column group, sequence).  The MFMA columns are (new
+// token i, query head g of the group) pairs, column 16 * cg + r = i * G + g,
+// so with G * n >= 3 the contraction is real even for MHA.  The cached tokens
+// [0, L - n) stream from the pool as in decode; the n new tokens are read from
+// k_new / v_new, with token j visible to column (i, g) when j <= i.  The
+// column group 0 workgroup of each (sequence, KV head) also appends that
+// head's new K/V to their slots; no workgroup reads those slots in this launch.
+// ---------------------------------------------------------------------------
+
+// One 16-token tile of new tokens (rows 16u .. 16u + 15 of the sequence's n)
+// in the MFMA operand layouts of load_tile; rows past n are zeros.
+template <int D>
+__device__ __forceinline__ void load_new_tile(const MultiParams& p, int r0, int n, int u, int kvh, int lane,
+                                              u32x4 (&kt)[D / 32], u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  const int jk = 16 * u + r;  // K row of this lane
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    kt[c] = u32x4{0u, 0u, 0u, 0u};
+    if (jk < n) kt[c] = load16(p.k_new + size_t(r0 + jk) * p.kn_t + size_t(kvh) * p.kn_h + 8 * (g4 + 4 * c));
+  }
+  // V: dims 2r + 32c and +1 of tokens 16u + 4*g4 .. +3, packed as (token pair) per dim
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = 16 * u + 4 * g4 + t;
+      w[t] = 0u;
+      if (j < n)
+        w[t] = *reinterpret_cast<const uint32_t*>(p.v_new + size_t(r0 + j) * p.vn_t + size_t(kvh) * p.vn_h +
+                                                  2 * r + 32 * c);
+    }
+    vt[c].x = (w[0] & 0xffffu) | (w[1] << 16);
+    vt[c].y = (w[2] & 0xffffu) | (w[3] << 16);
+    vt[c].z = (w[0] >> 16) | (w[1] & 0xffff0000u);
+    vt[c].w = (w[2] >> 16) | (w[3] & 0xffff0000u);
+  }
+}
+
+// mfma_tile for new tokens: token 16u + 4*g4 + j is visible to this lane's
+// column when it is at most climit (the column's query index).  Masked
+// scores contribute exactly zero even before the column has seen a token.
+template <int D>
+__device__ __forceinline__ void mfma_tile_causal(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
+                                                 int tok0, int climit, int lane, const u32x4 (&kt)[D / 32],
+                                                 const u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  const int g4 = lane >> 4;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; c += 2) {
+    s0 = mfma_16x16x32(kt[c], q[c], s0);
+    s1 = mfma_16x16x32(kt[c + 1], q[c + 1], s1);
+  }
+  const f32x4 sacc = s0 + s1;
+  float sc[4];
+  bool vis[4];
+  float mt = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vis[j] = tok0 + 4 * g4 + j <= climit;
+    sc[j] = vis[j] ? sacc[j] * scale_log2 : kNegInf;
+    mt = fmaxf(mt, sc[j]);
+  }
+  if (__any(mt > a.m + kRescaleSlack)) {
+    mt = fmaxf(mt, shfl_xor(mt, 16));
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float m_new = fmaxf(a.m, mt);
+    const float alpha = a.m == kNegInf ? 0.f : exp2_ftz(a.m - m_new);
+    a.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 2 * NC; ++i) a.o[i] *= alpha;
+    a.m = m_new;
+  }
+  float pr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[j] = vis[j] ? exp2_ftz(sc[j] - a.m) : 0.f;
+    a.l += pr[j];
+  }
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hb[j] = bf16_bits(pr[j]);
+    lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
+  }
+  const u32x4 pb = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
+                    lb[2] | (lb[3] << 16)};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};
+    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};
+    a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
+    a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
+  }
+}
+
+// Pipeline depth of the multi-token kernel: a second column set takes the
+// registers of two tile slots (two slots and two workgroups per compute unit
+// measure faster than three or four slots at one workgroup).
+template <int BS, int NS>
+constexpr int multi_slots() { return NS == 1 ? pipe_slots<BS, false>() : 2; }
+
+// A workgroup computes NS sets of 16 columns against each tile it loads, so
+// a (sequence, KV head) with up to 16 * NS columns reads its context once.
+template <int D, int BS, int NS>
+__global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_multi(MultiParams mp) {
+  constexpr int NC = D / 32;
+  __shared__ Smem<D> sm;
+  const DecodeParams& p = mp.d;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  const int kvh = blockIdx.x / mp.col_groups;
+  const int cg = blockIdx.x - kvh * mp.col_groups;
+  const int s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
+  const int G = p.group;
+  // this sequence's rows, kept inside [0, T); at most max_query_len of them
+  const int r0 = min(max(mp.query_start[s], 0), mp.num_rows);
+  const int r1 = min(max(mp.query_start[s + 1], r0), mp.num_rows);
+  const int L = clamp_len(p, p.context_lens[s]);
+  const int n = min(min(r1 - r0, L), mp.max_query_len);
+  const int L_old = L - n;
+
+  if (cg == 0) {  // append this head's new tokens
+    for (int u = threadIdx.x; u < n * (D / 8); u += kThreads) {
+      const int i = u / (D / 8);
+      const int piece = u - i * (D / 8);
+      const int64_t slot = mp.slots[r0 + i];
+      if (slot < 0 || slot >= mp.num_slots) continue;
+      const u32x4 kv = load16(mp.k_new + size_t(r0 + i) * mp.kn_t + size_t(kvh) * mp.kn_h + piece * 8);
+      const u32x4 vv = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
+      write_slot_piece<D, BS>(const_cast<uint16_t*>(p.k_cache), const_cast<uint16_t*>(p.v_cache),
+                              p.num_kv_heads, slot, kvh, piece, kv, vv);
+    }
+  }
+  const int cols = n * G;             // (query, head) columns of this KV head
+  const int col0 = 16 * NS * cg;      // first column of this workgroup
+  if (col0 >= cols) return;           // workgroup-uniform
+
+  const auto row = table_row(p, s, BS);
+  const TableCache first = fetch_table<BS>(row, 0, wave, 0, lane);
+  // column set cs: columns col0 + 16 cs + r; columns past the last query
+  // compute with a zero query (never stored) and see every new token
+  u32x4 q[NS][NC];
+  int qi[NS];
+#pragma unroll
+  for (int cs = 0; cs < NS; ++cs) {
+    const int c = col0 + 16 * cs + r;
+    const bool ok = c < cols;
+    qi[cs] = ok ? c / G : n - 1;
+    const int qh = kvh * G + (ok ? c - qi[cs] * G : 0);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      q[cs][k] = u32x4{0u, 0u, 0u, 0u};
+      if (ok) q[cs][k] = load16(p.q + size_t(r0 + qi[cs]) * p.q_s + size_t(qh) * p.q_h + 8 * (g4 + 4 * k));
+    }
+  }
+  MfmaAcc<D> acc[NS];
+#pragma unroll
+  for (int cs = 0; cs < NS; ++cs) mfma_reset(acc[cs]);
+  walk_tiles<D, BS, multi_slots<BS, NS>()>(p, row, first, kvh, 0, L_old, wave, lane,
+                                           [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, L_old, lane, kt, vt);
+  });
+  // the new tiles continue the cached tiles' round robin over the waves
+  const int old_tiles = (L_old + 15) >> 4;
+  for (int u = (wave + kWaves - old_tiles % kWaves) % kWaves; 16 * u < n; u += kWaves) {
+    u32x4 kt[NC], vt[NC];
+    load_new_tile<D>(mp, r0, n, u, kvh, lane, kt, vt);
+#pragma unroll
+    for (int cs = 0; cs < NS; ++cs)
+      mfma_tile_causal<D>(acc[cs], q[cs], p.scale_log2, 16 * u, qi[cs], lane, kt, vt);
+  }
+
+  // combine the waves set by set; column (i, g) goes to row r0 + i, head kvh * G + g
+#pragma unroll
+  for (int cs = 0; cs < NS; ++cs) {
+    const int cbase = col0 + 16 * cs;
+    const int ncols = min(16, cols - cbase);
+    if (ncols <= 0) break;        // workgroup-uniform
+    if (cs > 0) __syncthreads();  // the previous set's readers are done with sm
+    float l = acc[cs].l;
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    if (g4 == 0) {
+      sm.m[wave][r] = acc[cs].m;
+      sm.l[wave][r] = l;
+    }
+    if (r < ncols) {
+#pragma unroll
+      for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc[cs].o[mm][j];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
+      const int col = idx / D;
+      const int d = idx - col * D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][col]);
+      float o = 0.f, lsum = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float e = exp2f(sm.m[w][col] - M);
+          o += sm.o[w][d][col] * e;
+          lsum += sm.l[w][col] * e;
+        }
+      }
+      const int cc = cbase + col;
+      const int i = cc / G;
+      store_out(p, r0 + i, kvh * G + (cc - i * G), d, lsum > 0.f ? o / lsum : 0.f);
+    }
+  }
+}
+
 // Partition combine: one thread per (head, dim) of a sequence.
 template <int D>
 __global__ __launch_bounds__(256) void combine_parts(DecodeParams p) {
@@ -1265,23 +1541,13 @@ __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int i = blockIdx.x;
   const int64_t slot = p.slots[i];
   if (slot < 0) return;
-  const int64_t blk = slot / BS;
-  const int off = int(slot - blk * BS);
   const int units = p.num_kv_heads * (D / 8);
   for (int u = blockIdx.y * blockDim.x + threadIdx.x; u < units; u += gridDim.y * blockDim.x) {
     const int h = u / (D / 8);
     const int piece = u - h * (D / 8);
     const u32x4 kv = load16(p.k + size_t(i) * p.k_t + size_t(h) * p.k_h + piece * 8);
     const u32x4 vv = load16(p.v + size_t(i) * p.v_t + size_t(h) * p.v_h + piece * 8);
-    const size_t tile = (size_t(blk) * p.num_kv_heads + h) * (BS * D);
-    store16(p.k_cache + tile + (piece * BS + off) * 8, kv);
-    uint16_t* vt = p.v_cache + tile + ((off >> 2) * D + piece * 8) * 4 + (off & 3);
-    const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      vt[(2 * e) * 4] = uint16_t(w[e] & 0xffffu);
-      vt[(2 * e + 1) * 4] = uint16_t(w[e] >> 16);
-    }
+    write_slot_piece<D, BS>(p.k_cache, p.v_cache, p.num_kv_heads, slot, h, piece, kv, vv);
   }
 }
 
@@ -1436,6 +1702,34 @@ hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCt
   const int row_wgs = p.num_kv_heads * p.head_groups;
   if (head_dim == 64) return launch_rows(decode_mfma_contiguous<64>, q, row_wgs, ctx);
   if (head_dim == 128) return launch_rows(decode_mfma_contiguous<128>, q, row_wgs, ctx);
+  return hipErrorInvalidValue;
+}
+
+template <typename K>
+hipError_t launch_multi_k(K kernel, MultiParams p, const LaunchCtx& c) {
+  const int row_wgs = p.d.num_kv_heads * p.col_groups;
+  p.d.rank_split = rank_split_for(kernel, p.d, row_wgs, c);
+  return launch_main(kernel, dim3(row_wgs, p.d.num_seqs), dim3(kThreads), c, p);
+}
+
+template <int D, int NS>
+hipError_t launch_multi_ns(const MultiParams& p, int block_size, const LaunchCtx& c) {
+  switch (block_size) {
+    case 8: return launch_multi_k(decode_multi<D, 8, NS>, p, c);
+    case 16: return launch_multi_k(decode_multi<D, 16, NS>, p, c);
+    case 32: return launch_multi_k(decode_multi<D, 32, NS>, p, c);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D>
+hipError_t launch_multi_d(const MultiParams& p, int block_size, const LaunchCtx& c) {
+  return p.col_sets == 1 ? launch_multi_ns<D, 1>(p, block_size, c) : launch_multi_ns<D, 2>(p, block_size, c);
+}
+
+hipError_t launch_multi(const MultiParams& p, int head_dim, int block_size, const LaunchCtx& c) {
+  if (head_dim == 64) return launch_multi_d<64>(p, block_size, c);
+  if (head_dim == 128) return launch_multi_d<128>(p, block_size, c);
   return hipErrorInvalidValue;
 }
 

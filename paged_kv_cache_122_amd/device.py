@@ -41,6 +41,7 @@ class DeviceWorkload:
     v_cache: torch.Tensor
     owned: torch.Tensor
     copies: torch.Tensor   # int64 [N, 2] copy-on-write (src, dst) of this step
+    query_start: torch.Tensor = None  # int32 [S + 1] rows of q / k_new / v_new per sequence
 
 
 def upload(w, device="cuda"):
@@ -57,7 +58,8 @@ def upload(w, device="cuda"):
         block_tables=torch.from_numpy(w.block_tables).to(device),
         context_lens=torch.from_numpy(w.context_lens).to(device),
         k_cache=k_cache, v_cache=v_cache, owned=owned,
-        copies=torch.from_numpy(np.ascontiguousarray(w.copies, dtype=np.int64)).to(device))
+        copies=torch.from_numpy(np.ascontiguousarray(w.copies, dtype=np.int64)).to(device),
+        query_start=torch.from_numpy(np.ascontiguousarray(w.query_start, dtype=np.int32)).to(device))
 
 
 def contiguous_copy(dw, w):

@@ -234,3 +234,37 @@ def test_decode_contiguous_validation(lib):
 
 
 T_ = T
+
+
+def test_decode_multi_validation(lib):
+    """pa_decode_multi checks shapes before any launch (fake pointers here: every
+    call either fails validation or is a no-op)."""
+    r = ctypes.byref
+
+    def call(S=4, T=10, Hq=8, Hkv=2, D=128, B=16, NB=64, W=8, mql=5, scale=0.1, block_size=16,
+             kn=None, qs=None, slots=None, out_dt=pa.PA_BF16, qs_dt=pa.PA_I32):
+        out, q = T_([T, Hq, D], out_dt), T_([T, Hq, D], pa.PA_BF16)
+        k_new = T_(kn or [T, Hkv, D], pa.PA_BF16)
+        v_new = T_([T, Hkv, D], pa.PA_BF16)
+        sl = T_([slots if slots is not None else T], pa.PA_I64)
+        qst = T_([qs if qs is not None else S + 1], qs_dt)
+        kc, vc = T_([NB, Hkv, D // 8, B, 8], pa.PA_BF16), T_([NB, Hkv, B // 4, D, 4], pa.PA_BF16)
+        bt, ln = T_([S, W], pa.PA_I32), T_([S], pa.PA_I32)
+        return lib.pa_decode_multi(r(out), r(q), r(k_new), r(v_new), r(sl), r(qst), r(kc), r(vc),
+                                   r(bt), r(ln), scale, block_size, mql, None)
+
+    assert call(S=0) == pa.PA_OK                                   # nothing to do
+    assert call(T=0) == pa.PA_OK
+    assert call(mql=0) == pa.PA_OK
+    assert call(kn=[10, 3, 128]) == pa.PA_ERR_INVALID              # KV heads of the pools
+    assert call(kn=[9, 2, 128]) == pa.PA_ERR_INVALID               # one row per q row
+    assert call(slots=9) == pa.PA_ERR_INVALID
+    assert call(qs=4) == pa.PA_ERR_INVALID                         # S + 1 entries
+    assert call(qs_dt=pa.PA_I64) == pa.PA_ERR_INVALID
+    assert call(out_dt=pa.PA_I32) == pa.PA_ERR_INVALID
+    assert call(Hq=7) == pa.PA_ERR_INVALID
+    assert call(block_size=32) == pa.PA_ERR_INVALID
+    assert call(mql=-1) == pa.PA_ERR_INVALID
+    assert call(mql=1 << 22, Hq=32) == pa.PA_ERR_INVALID           # columns past 2^24
+    assert call(scale=float("inf")) == pa.PA_ERR_INVALID
+    assert call(D=96) == pa.PA_ERR_UNSUPPORTED                      # pools reject the head size

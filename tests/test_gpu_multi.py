@@ -1,0 +1,163 @@
+"""GPU parity of pa_decode_multi, several new tokens per sequence (chunked
+prefill, speculative verification): the appended pools are bit-exact against
+the oracle's append, and every row's attention matches the fp64 oracle's
+causal multi-token attention within max|err| <= 1e-2 and relative RMS <= 2e-3
+(bf16 outputs: beyond their own rounding)."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, assert_close_bf16, need_gpu
+from paged_kv_cache_122_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def run_multi(w, *, max_query_len=None, out_f32=False, slot_override=None):
+    """Upload w, run pa_decode_multi once; returns (out as fp64, device workload)."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    dw = dev.upload(w)
+    if slot_override is not None:
+        dw.slot_mapping = torch.from_numpy(slot_override).to(dw.slot_mapping.device)
+    n = np.diff(w.query_start)
+    mql = int(n.max()) if max_query_len is None else int(max_query_len)
+    out = torch.empty(dw.q.shape, dtype=torch.float32 if out_f32 else torch.bfloat16, device=dw.q.device)
+    pa.decode_multi(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache,
+                    dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size, mql)
+    torch.cuda.synchronize()
+    got = out.double().cpu().numpy() if out_f32 else oracle.bf16_bits_to_f64(dev.bf16_bits(out))
+    return got, dw
+
+
+def oracle_multi(w):
+    kst, vst = w.stores()
+    ref = oracle.multi_query_decode(w.q, w.k_new, w.v_new, w.slot_mapping, w.query_start, kst, vst,
+                                    w.block_tables, w.context_lens, w.scale, w.block_size)
+    return kst, vst, ref
+
+
+def check_pools(w, dw, kst, vst):
+    from paged_kv_cache_122_amd import device as dev
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+    # nothing outside the owned blocks was written (they hold NaN from the upload)
+    torch = need_gpu()
+    per_block = w.num_kv_heads * w.head_dim * w.block_size
+    unowned = (w.num_blocks - len(w.owned)) * per_block
+    assert int(torch.isnan(dw.k_cache).sum()) == unowned + int((kst.blocks == workloads.NAN_BF16).sum())
+    assert int(torch.isnan(dw.v_cache).sum()) == unowned + int((vst.blocks == workloads.NAN_BF16).sum())
+
+
+def test_verify5_parity():
+    """Llama-3-8B-shaped verification batch: 64 seqs x 5 drafted tokens, GQA 4."""
+    w = workloads.make("llama3_8b_verify5_b64")
+    print(f"[verify5] T={w.q.shape[0]} S={w.num_seqs}", flush=True)
+    kst, vst, ref = oracle_multi(w)
+    got, dw = run_multi(w)
+    check_pools(w, dw, kst, vst)
+    a, r = assert_close_bf16(got, ref, "verify5")
+    print(f"[verify5] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+
+
+# (name, old lens, new counts, Hq, Hkv, D, B): mixed steps, pure prefill chunks
+# (nothing cached), sequences with no new token, new-token counts past one
+# 16-token tile and past one 16-column MFMA set, every block size and grouping
+EDGE = [
+    ("mixed_gqa4", [0, 37, 100, 5, 16, 300], [20, 1, 5, 0, 16, 37], 16, 4, 128, 16),
+    ("mha_d64_b8", [11, 0, 64], [3, 9, 1], 4, 4, 64, 8),
+    ("gqa8_b32_cols16", [33, 70, 1], [2, 1, 2], 16, 2, 128, 32),
+    ("gqa8_b32_cols24", [33, 70, 1], [3, 1, 2], 16, 2, 128, 32),
+    ("decode_only", [90, 1, 513, 17], [1, 1, 1, 1], 8, 2, 128, 16),
+    ("prefill_chunk_and_decodes", [0, 400, 700, 250], [64, 1, 1, 1], 32, 8, 128, 16),
+    ("long_chunk_gqa2", [1000], [100], 4, 2, 64, 16),
+]
+
+
+@pytest.mark.parametrize("name,old,new,hq,hkv,d,b", EDGE, ids=[e[0] for e in EDGE])
+def test_multi_edge_cases(name, old, new, hq, hkv, d, b):
+    w = workloads.multi_query_workload(2000 + len(name), old, new, num_q_heads=hq, num_kv_heads=hkv,
+                                       head_dim=d, block_size=b, name=name)
+    print(f"[{name}] old={old} new={new}", flush=True)
+    kst, vst, ref = oracle_multi(w)
+    got, dw = run_multi(w, out_f32=True)
+    check_pools(w, dw, kst, vst)
+    a, r = assert_close(got, ref, name)
+    print(f"[{name}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+
+
+def test_multi_slack_and_bf16_out():
+    """A max_query_len above every sequence's count launches idle column groups
+    that write nothing; bf16 output equals the rounded f32 result's tolerance."""
+    w = workloads.multi_query_workload(2100, [40, 7, 129], [5, 2, 3], num_q_heads=32, num_kv_heads=8,
+                                       head_dim=128, block_size=16, name="slack")
+    kst, vst, ref = oracle_multi(w)
+    got, dw = run_multi(w, max_query_len=40)
+    check_pools(w, dw, kst, vst)
+    assert_close_bf16(got, ref, "slack")
+
+
+def test_negative_slot_skips_the_store_only():
+    """A negative slot leaves the pool untouched; the token's K/V still take part
+    in the attention (read from k_new / v_new)."""
+    w = workloads.multi_query_workload(2200, [20, 50], [4, 3], num_q_heads=8, num_kv_heads=2,
+                                       head_dim=128, block_size=16, name="skip")
+    kst, vst, ref = oracle_multi(w)           # the oracle stores every token
+    slots = w.slot_mapping.copy()
+    skipped = [1, 5]
+    slots[skipped] = -1
+    got, dw = run_multi(w, out_f32=True, slot_override=slots)
+    assert_close(got, ref, "skip")
+    # the pool equals the oracle's except at the skipped slots, which keep the pre-step NaN
+    from paged_kv_cache_122_amd import device as dev
+    k_before, _ = w.stores()
+    k_got = dev.bf16_bits(dw.k_cache[dw.owned])
+    pos = {int(b): i for i, b in enumerate(w.owned)}
+    B, D = w.block_size, w.head_dim
+    mask = np.zeros(k_got.shape, dtype=bool)
+    for r in skipped:
+        s = int(w.slot_mapping[r])
+        mask[pos[s // B], :, :, s % B, :] = True
+    assert np.array_equal(k_got[~mask], kst.blocks[~mask])
+    assert np.array_equal(k_got[mask], k_before.blocks[mask])
+
+
+def test_multi_debug_contracts():
+    """Debug mode rejects what the kernel cannot check: more tokens than the
+    context or than max_query_len, decreasing query_start, slots that disagree
+    with the tables."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.multi_query_workload(2300, [10, 30], [3, 2], num_q_heads=8, num_kv_heads=2,
+                                       head_dim=64, block_size=16, name="contracts")
+    dw = dev.upload(w)
+    out = torch.empty_like(dw.q)
+
+    def call(qs=None, slots=None, lens=None, mql=3):
+        pa.decode_multi(out, dw.q, dw.k_new, dw.v_new,
+                        dw.slot_mapping if slots is None else slots,
+                        dw.query_start if qs is None else qs, dw.k_cache, dw.v_cache,
+                        dw.block_tables, dw.context_lens if lens is None else lens, w.scale,
+                        w.block_size, mql)
+
+    old = pa.set_debug(True)
+    try:
+        call()  # the valid step passes
+        torch.cuda.synchronize()
+        cases = [
+            dict(mql=2),                                                      # 3 > max_query_len
+            dict(lens=torch.tensor([2, 32], dtype=torch.int32, device="cuda")),  # 3 > L
+            dict(qs=torch.tensor([0, 4, 3], dtype=torch.int32, device="cuda")),  # decreasing
+            dict(slots=dw.slot_mapping.flip(0).contiguous()),                 # not the tables' slots
+        ]
+        for kw in cases:
+            with pytest.raises(pa.PaError) as e:
+                call(**kw)
+            assert e.value.code == pa.PA_ERR_CONTRACT, kw
+    finally:
+        pa.set_debug(old)

@@ -468,7 +468,7 @@ def test_multi_query_with_one_token_each_is_decode():
 
 def test_multi_query_equals_successive_single_token_steps():
     """n tokens verified at once give what n decode steps give one token at a
-    time (First Principles, section 13: the verifier step is n decode steps)."""
+    time (First Principles, section 14: the verifier step is n decode steps)."""
     w = _mq_workload()
     k1, v1 = w.stores()
     got = oracle.multi_query_decode(w.q, w.k_new, w.v_new, w.slot_mapping, w.query_start, k1, v1,
