@@ -12,7 +12,10 @@ on one stream of this process and the HIP events are recorded on it; they are
 created with hipEventDisableSystemFence, so recording them flushes no cache.
 ``roofline`` is the main decode kernel alone (on the default workload the
 only kernel of the call), timed in as many further flushed steps by events
-that the GPU stamps at its start and end, against 8 TB/s.  ``cpu_baseline`` is the fp64 oracle on a bounded
+that the GPU stamps at its start and end, against 8 TB/s.  ``paging_control``
+times the same decode over an unpaged copy of the cache; ``multi_query`` times
+pa_decode_multi (several new tokens per sequence: speculative verification)
+on the Llama-3-8B-shaped batch with 5 drafted tokens per sequence.  ``cpu_baseline`` is the fp64 oracle on a bounded
 sample of the same workload, on this host's CPU.
 """
 
@@ -37,10 +40,11 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "5b77042548397721337d99fbd1ab1b5d7f8717f8a9631f26e97f2eca78343d63",
-    "config": "llama3_8b_b64",
-    "fetch_bytes": 275398265,  # FETCH_SIZE 134479.6 KiB x 1.9999
-    "write_bytes": 524288,  # WRITE_SIZE 512.0 KiB x 1.0000
+    "sources_sha256": "43560bdd0982b981af5b2eb2c9197aa8e5404a059763f8c47a1bf0d50504f869",
+    # pa_decode's kernel decode_mfma<128,16>: FETCH_SIZE 134478.7 KiB x 1.9999, WRITE_SIZE 512.0 KiB x 1.0
+    "llama3_8b_b64": {"fetch_bytes": 275395566, "write_bytes": 524288},
+    # pa_decode_multi's kernel decode_multi<128,16,2>: FETCH_SIZE 141212.6 KiB x 1.9999, WRITE_SIZE 4355.9 KiB x 1.0
+    "llama3_8b_verify5_b64": {"fetch_bytes": 289185815, "write_bytes": 4460425},
 }
 
 
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-multi", action="store_true",
+                    help="skip the multi-token (speculative verification) leg")
     ap.add_argument("--no-control", action="store_true",
                     help="skip the unpaged control (pa_decode_contiguous on a copy of the cache)")
     ap.add_argument("--unflushed", action="store_true",
@@ -117,9 +123,9 @@ def sources_sha256():
 
 def measured_traffic(config):
     t = MEASURED_TRAFFIC
-    if not t or t["config"] != config or t["sources_sha256"] != sources_sha256():
+    if config not in t or t["sources_sha256"] != sources_sha256():
         return None
-    return t["fetch_bytes"] + t["write_bytes"]
+    return t[config]["fetch_bytes"] + t[config]["write_bytes"]
 
 
 def decode_kernels(w, part):
@@ -132,6 +138,84 @@ def decode_kernels(w, part):
     if part == -1 or part >= w.block_tables.shape[1] * w.block_size:
         return [core + tmpl], "one workgroup per (sequence, head group), no split"
     return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
+
+
+MULTI_CONFIG = "llama3_8b_verify5_b64"
+
+
+def multi_query_leg(steps, warmup, tev, stream, flush):
+    """pa_decode_multi on the verification batch (64 sequences, 5 drafted tokens
+    each): the append of the drafted tokens and their causal attention, one
+    launch.  Beside it, pa_decode of one token per sequence over the same pools
+    (same KV bytes).  Each call after a cache flush, timed by events around it."""
+    import numpy as np
+    import torch
+
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+    from paged_kv_cache_122_amd import workloads
+
+    w = workloads.make(MULTI_CONFIG)
+    dw = dev.upload(w, "cuda:0")
+    counts = np.diff(w.query_start)
+    mql = int(counts.max())
+    out = torch.empty_like(dw.q)
+    first = dw.query_start[:-1].long()
+    q1 = dw.q[first].contiguous()
+    out1 = torch.empty_like(q1)
+
+    def multi():
+        pa.decode_multi(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache,
+                        dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size, mql,
+                        stream=stream)
+
+    def single():
+        pa.decode(out1, q1, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                  w.block_size, stream=stream)
+
+    E = tev.create
+    for _ in range(warmup):
+        flush.zero_()
+        multi()
+        single()
+    ev = [(E(), E(), E(), E()) for _ in range(steps)]
+    for a, b, c, d in ev:
+        flush.zero_()
+        tev.record(a, stream)
+        multi()
+        tev.record(b, stream)
+        flush.zero_()
+        tev.record(c, stream)
+        single()
+        tev.record(d, stream)
+    stream.synchronize()
+    multi_ms = [tev.elapsed_ms(a, b) for a, b, _, _ in ev]
+    single_ms = [tev.elapsed_ms(c, d) for _, _, c, d in ev]
+    T = int(w.q.shape[0])
+    new_kv = T * w.num_kv_heads * w.head_dim * 2 * 2
+    # K/V of every context token read once (cached ones from the pool, new ones
+    # from k_new / v_new), the new K/V written, q read and out written
+    algo = w.unique_kv_bytes() + new_kv + 2 * T * w.num_q_heads * w.head_dim * 2
+    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    t = mean(multi_ms) / 1e3
+    del dw
+    return {
+        "workload": w.name,
+        "num_seqs": w.num_seqs,
+        "new_tokens": T,
+        "max_query_len": mql,
+        "context_tokens": int(w.context_lens.sum()),
+        "call_ms": {"mean": round(mean(multi_ms), 5), "p50": round(percentile(multi_ms, 50), 5)},
+        "algorithmic_bytes": algo,
+        "achieved_gbs": round(algo / t / 1e9, 2),
+        "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
+        "traffic": measured_traffic(w.name),
+        "tokens_per_s": round(T / t, 1),
+        "single_token_decode_same_pools_call_ms": round(mean(single_ms), 5),
+        "note": "pa_decode_multi (append fused, causal over cached + drafted tokens) vs pa_decode of "
+                "one token per sequence on the same pools, alternating, each after a cache flush, "
+                "events around the call (launch included)",
+    }
 
 
 def percentile(xs, q):
@@ -314,6 +398,10 @@ def main():
             unsplit_ms = [tev.elapsed_ms(c, d) for _, _, c, d in cev]
             del kc, vc, out_c
 
+        multi = None
+        if not args.no_multi:
+            multi = multi_query_leg(args.steps, args.warmup, tev, stream, flush)
+
         tev.close()
 
         if args.copy_calibration > 0:
@@ -398,6 +486,8 @@ def main():
                     "schedule (one workgroup per sequence and head group, MFMA), alternating, each "
                     "after a cache flush and timed by events around the call",
         }
+    if multi:
+        line["multi_query"] = multi
     if hot_ms:
         line["unflushed_step_ms"] = {"mean": round(mean(hot_ms), 5),
                                      "p50": round(percentile(hot_ms, 50), 5),
