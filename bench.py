@@ -13,7 +13,8 @@ created with hipEventDisableSystemFence, so recording them flushes no cache.
 ``roofline`` is the main decode kernel alone (on the default workload the
 only kernel of the call), timed in as many further flushed steps by events
 that the GPU stamps at its start and end, against 8 TB/s.  ``paging_control``
-times the same decode over an unpaged copy of the cache; ``multi_query`` times
+times the same decode over an unpaged copy of the cache; ``fused_step`` times
+the step as one launch (pa_decode_multi appends and attends); ``multi_query`` times
 pa_decode_multi (several new tokens per sequence: speculative verification)
 on the Llama-3-8B-shaped batch with 5 drafted tokens per sequence.  ``cpu_baseline`` is the fp64 oracle on a bounded
 sample of the same workload, on this host's CPU.
@@ -57,6 +58,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused step (append and decode in one pa_decode_multi launch)")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the multi-token (speculative verification) leg")
     ap.add_argument("--no-control", action="store_true",
@@ -364,6 +367,27 @@ def main():
         stream.synchronize()
         kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
 
+        # the same step with the append fused into the attention launch:
+        # pa_decode_multi with one new token per sequence (after the copies)
+        fused_ms = []
+        if not args.no_fused:
+            import numpy as np
+            mql = int(np.diff(w.query_start).max())
+            out_f = torch.empty_like(out)
+            fev = [(E(), E()) for _ in range(args.steps)]
+            for a, b in fev:
+                flush.zero_()
+                tev.record(a, stream)
+                if has_copies:
+                    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
+                pa.decode_multi(out_f, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start,
+                                dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                                w.block_size, mql, stream=stream)
+                tev.record(b, stream)
+            stream.synchronize()
+            fused_ms = [tev.elapsed_ms(a, b) for a, b in fev]
+            del out_f
+
         hot_ms = []
         if args.unflushed:  # back-to-back steps (caches may hold part of the pools)
             hot = [(E(), E()) for _ in range(args.steps)]
@@ -485,6 +509,16 @@ def main():
                     "run of 16-token tiles, no block table) vs the paged kernel with the same "
                     "schedule (one workgroup per sequence and head group, MFMA), alternating, each "
                     "after a cache flush and timed by events around the call",
+        }
+    if fused_ms:
+        line["fused_step"] = {
+            "step_ms": {"mean": round(mean(fused_ms), 5), "p50": round(percentile(fused_ms, 50), 5)},
+            "value": round(eff_bytes / (mean(fused_ms) / 1e3) / 1e9, 2),
+            "unit": "GB/s",
+            "note": "the same step as one launch: pa_decode_multi with one new token per sequence "
+                    "stores the token's K/V and attends (one workgroup per sequence and KV head, no "
+                    "split)" + (", after pa_copy_blocks" if has_copies else "") +
+                    "; flushed, events around the step; value = effective KV bytes / mean step time",
         }
     if multi:
         line["multi_query"] = multi

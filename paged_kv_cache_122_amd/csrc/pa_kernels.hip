@@ -1424,21 +1424,43 @@ __global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_multi(MultiP
   const int n = min(min(r1 - r0, L), mp.max_query_len);
   const int L_old = L - n;
 
-  if (cg == 0) {  // append this head's new tokens
-    for (int u = threadIdx.x; u < n * (D / 8); u += kThreads) {
+  // The column-group-0 workgroup appends this head's new tokens: its loads
+  // are issued first and its pool stores come after the walk, since pool
+  // stores ahead of it would hold the walk's pool loads back (loads are not
+  // moved across stores that may alias them).  One 16-byte piece per thread
+  // here; pieces past the first kThreads are copied at the end.
+  const int units = cg == 0 ? n * (D / 8) : 0;
+  const int staged = min(units, kThreads);
+  u32x4 app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
+  int64_t app_slot = -1;
+  if (int(threadIdx.x) < staged) {
+    const int i = threadIdx.x / (D / 8);
+    const int piece = threadIdx.x - i * (D / 8);
+    app_slot = mp.slots[r0 + i];
+    app_k = load16(mp.k_new + size_t(r0 + i) * mp.kn_t + size_t(kvh) * mp.kn_h + piece * 8);
+    app_v = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
+  }
+  auto append = [&]() {
+    uint16_t* kc = const_cast<uint16_t*>(p.k_cache);
+    uint16_t* vc = const_cast<uint16_t*>(p.v_cache);
+    if (int(threadIdx.x) < staged && app_slot >= 0 && app_slot < mp.num_slots)
+      write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, app_slot, kvh, threadIdx.x % (D / 8), app_k, app_v);
+    for (int u = threadIdx.x + staged; u < units; u += kThreads) {
       const int i = u / (D / 8);
       const int piece = u - i * (D / 8);
       const int64_t slot = mp.slots[r0 + i];
       if (slot < 0 || slot >= mp.num_slots) continue;
       const u32x4 kv = load16(mp.k_new + size_t(r0 + i) * mp.kn_t + size_t(kvh) * mp.kn_h + piece * 8);
       const u32x4 vv = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
-      write_slot_piece<D, BS>(const_cast<uint16_t*>(p.k_cache), const_cast<uint16_t*>(p.v_cache),
-                              p.num_kv_heads, slot, kvh, piece, kv, vv);
+      write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, slot, kvh, piece, kv, vv);
     }
-  }
+  };
   const int cols = n * G;             // (query, head) columns of this KV head
   const int col0 = 16 * NS * cg;      // first column of this workgroup
-  if (col0 >= cols) return;           // workgroup-uniform
+  if (col0 >= cols) {                 // workgroup-uniform; column group 0 only when n == 0
+    append();
+    return;
+  }
 
   const auto row = table_row(p, s, BS);
   const TableCache first = fetch_table<BS>(row, 0, wave, 0, lane);
@@ -1474,6 +1496,7 @@ __global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_multi(MultiP
     for (int cs = 0; cs < NS; ++cs)
       mfma_tile_causal<D>(acc[cs], q[cs], p.scale_log2, 16 * u, qi[cs], lane, kt, vt);
   }
+  append();  // every pool read of this workgroup is done
 
   // combine the waves set by set; column (i, g) goes to row r0 + i, head kvh * G + g
 #pragma unroll
