@@ -41,11 +41,11 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "43560bdd0982b981af5b2eb2c9197aa8e5404a059763f8c47a1bf0d50504f869",
-    # pa_decode's kernel decode_mfma<128,16>: FETCH_SIZE 134478.7 KiB x 1.9999, WRITE_SIZE 512.0 KiB x 1.0
-    "llama3_8b_b64": {"fetch_bytes": 275395566, "write_bytes": 524288},
-    # pa_decode_multi's kernel decode_multi<128,16,2>: FETCH_SIZE 141212.6 KiB x 1.9999, WRITE_SIZE 4355.9 KiB x 1.0
-    "llama3_8b_verify5_b64": {"fetch_bytes": 289185815, "write_bytes": 4460425},
+    "sources_sha256": "357118679243bc72895c7c7cdc5983bf09454c8c4dd6f2a2908b3084abda9fad",
+    # pa_decode's kernel decode_mfma<128,16,2>: FETCH_SIZE 134457.7 KiB x 1.9999, WRITE_SIZE 512.0 KiB x 1.0
+    "llama3_8b_b64": {"fetch_bytes": 275353017, "write_bytes": 524288},
+    # pa_decode_multi's kernel decode_multi<128,16,2>: FETCH_SIZE 141212.3 KiB x 1.9999, WRITE_SIZE 4353.1 KiB x 1.0
+    "llama3_8b_verify5_b64": {"fetch_bytes": 289185597, "write_bytes": 4457550},
 }
 
 

@@ -930,11 +930,14 @@ __device__ __forceinline__ TableCache fetch_table(__amdgpu_buffer_rsrc_t row, in
   return c;
 }
 
-// Tiles whose loads are in flight while one is computed, plus that one: four
-// where the registers fit two waves per SIMD, else three (B = 8 tiles take two
-// loads per operand; the VALU path converts K to fp32 in registers).
-template <int BS, bool Valu>
-constexpr int pipe_slots() { return BS == 8 || Valu ? 3 : 4; }
+// Register slots of the tile pipeline: the tile being computed and one whose
+// loads are in flight.  That is enough once every compute unit runs a
+// workgroup or more: the memory system is saturated and further loads only
+// queue (three or four slots measured no faster), while the registers they
+// take keep a third workgroup off each compute unit.  Smaller grids, with a
+// wave or two per compute unit, are latency-bound and take kDeepSlots.
+constexpr int kPipeSlots = 2;
+constexpr int kDeepSlots = 4;
 
 // Walk this wave's tiles (tiles wave, wave + 4, ... of the partition [t0, t1))
 // with the next S - 1 tiles' loads issued before the current one is
@@ -1106,8 +1109,10 @@ __device__ __forceinline__ int partitions(const DecodeParams& p, int L) {
   return min((clamp_len(p, L) + p.part_tokens - 1) / p.part_tokens, p.max_parts);
 }
 
-template <int D, int BS>
-__global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_mfma(DecodeParams p) {
+// SL pipeline slots; the deep pipeline runs where grids hold at most one
+// workgroup per compute unit, so it may take the registers of two.
+template <int D, int BS, int SL>
+__global__ __launch_bounds__(kThreads, (SL == kPipeSlots ? 2 : 1)) void decode_mfma(DecodeParams p) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
 
@@ -1137,7 +1142,7 @@ __global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_mfma(DecodeP
   }
   MfmaAcc<D> acc;
   mfma_reset(acc);
-  walk_tiles<D, BS, pipe_slots<BS, false>()>(p, row, first, kvh, t0, t1, wave, lane,
+  walk_tiles<D, BS, SL>(p, row, first, kvh, t0, t1, wave, lane,
                                              [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile<D>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
   });
@@ -1171,7 +1176,7 @@ __global__ __launch_bounds__(kThreads, BS == 8 || VG == 2 ? 1 : 2) void decode_v
   valu_load_q<D, VG>(p, s, h0, lane, qf);
   ValuAcc<D, VG> acc;
   valu_reset(acc);
-  walk_tiles<D, BS, pipe_slots<BS, true>()>(p, row, first, kvh, t0, t1, wave, lane,
+  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
                                                 [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     valu_tile<D, VG>(acc, qf, p.scale_log2, ts, t1, lane, kt, vt);
   });
@@ -1208,11 +1213,10 @@ __global__ __launch_bounds__(kThreads, BS == 8 || VG == 2 ? 1 : 2) void decode_v
 // so the loads are the paged kernel's loads with the tile address computed
 // instead of looked up and the tiles of a context adjacent in memory.
 // ---------------------------------------------------------------------------
-template <int D, typename F>
+template <int D, int S, typename F>
 __device__ __forceinline__ void walk_contiguous(const DecodeParams& p, int s, int kvh, int t1, int wave,
                                                 int lane, F&& compute) {
   constexpr int NC = D / 32;
-  constexpr int S = 4;
   constexpr int kTileBytes = kTileTokens * D * 2;
   const int ntiles = (t1 + kTileTokens - 1) / kTileTokens;
   const int n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
@@ -1250,8 +1254,8 @@ __device__ __forceinline__ void walk_contiguous(const DecodeParams& p, int s, in
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_contiguous(DecodeParams p) {
+template <int D, int SL>
+__global__ __launch_bounds__(kThreads, (SL == kPipeSlots ? 2 : 1)) void decode_mfma_contiguous(DecodeParams p) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
   const int lane = threadIdx.x & 63;
@@ -1270,7 +1274,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_contiguous(DecodePara
   }
   MfmaAcc<D> acc;
   mfma_reset(acc);
-  walk_contiguous<D>(p, s, kvh, L, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+  walk_contiguous<D, SL>(p, s, kvh, L, wave, lane, [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile<D>(acc, q, p.scale_log2, ts, L, lane, kt, vt);
   });
   mfma_finish<D>(p, sm, acc, s, h0, ncols, 0, 1, wave, lane);
@@ -1396,16 +1400,11 @@ __device__ __forceinline__ void mfma_tile_causal(MfmaAcc<D>& a, const u32x4 (&q)
   }
 }
 
-// Pipeline depth of the multi-token kernel: a second column set takes the
-// registers of two tile slots (two slots and two workgroups per compute unit
-// measure faster than three or four slots at one workgroup).
-template <int BS, int NS>
-constexpr int multi_slots() { return NS == 1 ? pipe_slots<BS, false>() : 2; }
 
 // A workgroup computes NS sets of 16 columns against each tile it loads, so
 // a (sequence, KV head) with up to 16 * NS columns reads its context once.
 template <int D, int BS, int NS>
-__global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_multi(MultiParams mp) {
+__global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode_multi(MultiParams mp) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
   const DecodeParams& p = mp.d;
@@ -1483,7 +1482,7 @@ __global__ __launch_bounds__(kThreads, BS == 8 ? 1 : 2) void decode_multi(MultiP
   MfmaAcc<D> acc[NS];
 #pragma unroll
   for (int cs = 0; cs < NS; ++cs) mfma_reset(acc[cs]);
-  walk_tiles<D, BS, multi_slots<BS, NS>()>(p, row, first, kvh, 0, L_old, wave, lane,
+  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, 0, L_old, wave, lane,
                                            [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, L_old, lane, kt, vt);
   });
@@ -1643,11 +1642,18 @@ hipError_t launch_rows(K kernel, DecodeParams p, int row_wgs, const LaunchCtx& c
   return launch_main(kernel, dim3(row_wgs, p.num_seqs, p.max_parts), dim3(kThreads), c, p);
 }
 
+// Fewer MFMA workgroups than compute units: take the deep pipeline.
+inline bool deep_pipeline(const DecodeParams& p, const LaunchCtx& c) {
+  return int64_t(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_parts < c.cus;
+}
+
 template <int D, int BS>
 hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx& c) {
+  static_assert(kDeepSlots > kPipeSlots, "");
   hipError_t e;
   if (path == Path::Mfma)
-    e = launch_rows(decode_mfma<D, BS>, p, p.num_kv_heads * p.head_groups, c);
+    e = deep_pipeline(p, c) ? launch_rows(decode_mfma<D, BS, kDeepSlots>, p, p.num_kv_heads * p.head_groups, c)
+                            : launch_rows(decode_mfma<D, BS, kPipeSlots>, p, p.num_kv_heads * p.head_groups, c);
   else if (p.group == 1)
     e = launch_rows(decode_valu<D, BS, 1>, p, p.num_kv_heads, c);
   else
@@ -1723,8 +1729,14 @@ hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCt
   DecodeParams q = p;
   q.max_parts = 1;
   const int row_wgs = p.num_kv_heads * p.head_groups;
-  if (head_dim == 64) return launch_rows(decode_mfma_contiguous<64>, q, row_wgs, ctx);
-  if (head_dim == 128) return launch_rows(decode_mfma_contiguous<128>, q, row_wgs, ctx);
+  // the pipeline depth the paged kernel takes for the same grid
+  const bool deep = deep_pipeline(q, ctx);
+  if (head_dim == 64)
+    return deep ? launch_rows(decode_mfma_contiguous<64, kDeepSlots>, q, row_wgs, ctx)
+                : launch_rows(decode_mfma_contiguous<64, kPipeSlots>, q, row_wgs, ctx);
+  if (head_dim == 128)
+    return deep ? launch_rows(decode_mfma_contiguous<128, kDeepSlots>, q, row_wgs, ctx)
+                : launch_rows(decode_mfma_contiguous<128, kPipeSlots>, q, row_wgs, ctx);
   return hipErrorInvalidValue;
 }
 
