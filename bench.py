@@ -1,20 +1,21 @@
 """Benchmark of one paged-decode layer step on one MI355X: slot-mapped append of
-this step's K/V, then paged decode attention.
+this step's K/V and paged decode attention, as one pa_append_decode call (one
+launch where the decode schedule is unsplit MFMA, else the append kernel and
+then the decode schedule).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
 
 Prints ONE JSON line.  ``value`` is effective KV-read GB/s of the whole step
-(sum_s L_s * Hkv * D * 2 (K and V) * 2 bytes, divided by the event-timed
-append + decode time).  Inputs are resident in HBM; before every timed step a
+(sum_s L_s * Hkv * D * 2 (K and V) * 2 bytes, divided by the event-timed step).  Inputs are resident in HBM; before every timed step a
 1 GiB buffer is written so that neither L2 nor the 256 MB Infinity Cache
 still holds the pools (the flush is outside the timed region).  All work runs
 on one stream of this process and the HIP events are recorded on it; they are
 created with hipEventDisableSystemFence, so recording them flushes no cache.
-``roofline`` is the main decode kernel alone (on the default workload the
-only kernel of the call), timed in as many further flushed steps by events
-that the GPU stamps at its start and end, against 8 TB/s.  ``paging_control``
-times the same decode over an unpaged copy of the cache; ``fused_step`` times
-the step as one launch (pa_decode_multi appends and attends); ``multi_query`` times
+``roofline`` is the step's main kernel alone (on the default workload the
+only kernel of the step), timed in as many further flushed steps by events
+that the GPU stamps at its start and end, against 8 TB/s.  ``two_call_step``
+times the same step as pa_cache_append + pa_decode.  ``paging_control``
+times the same decode over an unpaged copy of the cache; ``multi_query`` times
 pa_decode_multi (several new tokens per sequence: speculative verification)
 on the Llama-3-8B-shaped batch with 5 drafted tokens per sequence.  ``cpu_baseline`` is the fp64 oracle on a bounded
 sample of the same workload, on this host's CPU.
@@ -33,7 +34,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "llama3_8b_b64"
 
-# HBM bytes per pa_decode launch on the default workload, from two rocprofv3
+# HBM bytes per launch of a step's main kernel, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by what
 # the counter reads for a plain copy of known size in the same run.  Valid only
 # for the kernel sources they were taken on (sha256 of the files below);
@@ -41,11 +42,11 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "357118679243bc72895c7c7cdc5983bf09454c8c4dd6f2a2908b3084abda9fad",
-    # pa_decode's kernel decode_mfma<128,16,2>: FETCH_SIZE 134457.7 KiB x 1.9999, WRITE_SIZE 512.0 KiB x 1.0
-    "llama3_8b_b64": {"fetch_bytes": 275353017, "write_bytes": 524288},
-    # pa_decode_multi's kernel decode_multi<128,16,2>: FETCH_SIZE 141212.3 KiB x 1.9999, WRITE_SIZE 4353.1 KiB x 1.0
-    "llama3_8b_verify5_b64": {"fetch_bytes": 289185597, "write_bytes": 4457550},
+    "sources_sha256": "6ec9d10421af3516b3a8d6d57c383abafc236105bc9a8314ef807648279ba0d8",
+    # the step's one launch: FETCH_SIZE 134430.5 KiB x 1.9999, WRITE_SIZE 1280.2 KiB x 1.0
+    "llama3_8b_b64 decode_multi<128,16,1>": {"fetch_bytes": 275297179, "write_bytes": 1310965},
+    # the verification batch: FETCH_SIZE 141223.4 KiB x 1.9999, WRITE_SIZE 4353.6 KiB x 1.0
+    "llama3_8b_verify5_b64 decode_multi<128,16,2>": {"fetch_bytes": 289208279, "write_bytes": 4458062},
 }
 
 
@@ -58,8 +59,6 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
-    ap.add_argument("--no-fused", action="store_true",
-                    help="skip the fused step (append and decode in one pa_decode_multi launch)")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the multi-token (speculative verification) leg")
     ap.add_argument("--no-control", action="store_true",
@@ -124,21 +123,27 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(config):
+def measured_traffic(config, kernel):
     t = MEASURED_TRAFFIC
-    if config not in t or t["sources_sha256"] != sources_sha256():
+    key = f"{config} {kernel}"
+    if key not in t or t["sources_sha256"] != sources_sha256():
         return None
-    return t[config]["fetch_bytes"] + t[config]["write_bytes"]
+    return t[key]["fetch_bytes"] + t[key]["write_bytes"]
 
 
-def decode_kernels(w, part):
+def decode_kernels(w, part, cus):
     """Kernels one automatic pa_decode call launches on this workload."""
     g = w.num_q_heads // w.num_kv_heads
     core = f"decode_{'mfma' if g >= 3 else 'valu'}"
     tmpl = f"<{w.head_dim},{w.block_size}>"
     if part == -2:
         return [core + "_sk" + tmpl, f"combine_sk<{w.head_dim}>"], "stream-K"
-    if part == -1 or part >= w.block_tables.shape[1] * w.block_size:
+    max_len = w.block_tables.shape[1] * w.block_size
+    parts = 1 if part == -1 else -(-max_len // part)
+    if g >= 3:  # pipeline slots: two once the grid has a workgroup per compute unit
+        wgs = w.num_seqs * w.num_kv_heads * -(-g // 16) * parts
+        tmpl = f"<{w.head_dim},{w.block_size},{2 if wgs >= cus else 4}>"
+    if parts == 1:
         return [core + tmpl], "one workgroup per (sequence, head group), no split"
     return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
 
@@ -212,13 +217,21 @@ def multi_query_leg(steps, warmup, tev, stream, flush):
         "algorithmic_bytes": algo,
         "achieved_gbs": round(algo / t / 1e9, 2),
         "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(w.name),
+        "traffic": measured_traffic(w.name, "decode_multi<128,16,2>"),
         "tokens_per_s": round(T / t, 1),
         "single_token_decode_same_pools_call_ms": round(mean(single_ms), 5),
         "note": "pa_decode_multi (append fused, causal over cached + drafted tokens) vs pa_decode of "
                 "one token per sequence on the same pools, alternating, each after a cache flush, "
                 "events around the call (launch included)",
     }
+
+
+def fused_step(w, part):
+    """Whether pa_append_decode runs this workload as one launch (the unsplit
+    MFMA schedule), and that kernel's name."""
+    g = w.num_q_heads // w.num_kv_heads
+    unsplit = part == -1 or part >= w.block_tables.shape[1] * w.block_size
+    return g >= 3 and unsplit, f"decode_multi<{w.head_dim},{w.block_size},{2 if g > 16 else 1}>"
 
 
 def percentile(xs, q):
@@ -308,7 +321,13 @@ def main():
     algo_bytes = w.unique_kv_bytes()
     max_len = int(w.block_tables.shape[1]) * w.block_size
     part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
-    kernels, schedule = decode_kernels(w, part)
+    kernels, schedule = decode_kernels(w, part, torch.cuda.get_device_properties(0).multi_processor_count)
+    fused, fused_kernel = fused_step(w, part)
+    new_kv_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
+    if fused:
+        # one launch reads the context (the new token from k / v) and writes the new token
+        kernels, schedule = [fused_kernel], schedule + "; append fused into the decode launch"
+        algo_bytes += new_kv_bytes
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.Stream()  # default priority
     torch.cuda.synchronize()
@@ -330,20 +349,48 @@ def main():
         pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
                      w.block_size, workspace=ws, kernel_events=kernel_events, stream=stream)
 
+    def step(kernel_events=None):
+        # the step's copy-on-write copies (if any), then append + decode in one call
+        if has_copies:
+            pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
+        pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                         dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=ws,
+                         kernel_events=kernel_events, stream=stream)
+
     tev = TimingEvents()
     E = tev.create
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             flush.zero_()
-            append()
-            decode()
+            step()
         stream.synchronize()
 
-        ev = [(E(), E(), E()) for _ in range(args.steps)]
+        ev = [(E(), E()) for _ in range(args.steps)]
         kev = [(E(), E()) for _ in range(args.steps)]
         torch.cuda.synchronize()
         wall0 = time.perf_counter()
-        for e0, e1, e2 in ev:
+        for e0, e1 in ev:
+            flush.zero_()
+            tev.record(e0, stream)
+            step()
+            tev.record(e1, stream)
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        step_ms = [tev.elapsed_ms(a, b) for a, b in ev]
+
+        # the same steps again with the main kernel bracketed by events that the
+        # GPU stamps at its own start and end (such a launch costs the stream a
+        # few microseconds more, so it is kept out of the steps above)
+        for k in kev:
+            flush.zero_()
+            step(kernel_events=k)
+        stream.synchronize()
+        kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
+
+        # the step as two calls: pa_cache_append, then pa_decode's schedule
+        tw = [(E(), E(), E()) for _ in range(args.steps)]
+        for e0, e1, e2 in tw:
             flush.zero_()
             tev.record(e0, stream)
             append()
@@ -351,50 +398,16 @@ def main():
             decode()
             tev.record(e2, stream)
         stream.synchronize()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        append_ms = [tev.elapsed_ms(a, b) for a, b, _ in ev]
-        decode_ms = [tev.elapsed_ms(b, c) for _, b, c in ev]
-        step_ms = [tev.elapsed_ms(a, c) for a, _, c in ev]
-
-        # the same steps again with the main decode kernel bracketed by events
-        # that the GPU stamps at its own start and end (such a launch costs the
-        # stream a few microseconds more, so it is kept out of the steps above)
-        for k in kev:
-            flush.zero_()
-            append()
-            decode(kernel_events=k)
-        stream.synchronize()
-        kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
-
-        # the same step with the append fused into the attention launch:
-        # pa_decode_multi with one new token per sequence (after the copies)
-        fused_ms = []
-        if not args.no_fused:
-            import numpy as np
-            mql = int(np.diff(w.query_start).max())
-            out_f = torch.empty_like(out)
-            fev = [(E(), E()) for _ in range(args.steps)]
-            for a, b in fev:
-                flush.zero_()
-                tev.record(a, stream)
-                if has_copies:
-                    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
-                pa.decode_multi(out_f, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start,
-                                dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                                w.block_size, mql, stream=stream)
-                tev.record(b, stream)
-            stream.synchronize()
-            fused_ms = [tev.elapsed_ms(a, b) for a, b in fev]
-            del out_f
+        append_ms = [tev.elapsed_ms(a, b) for a, b, _ in tw]
+        decode_ms = [tev.elapsed_ms(b, c) for _, b, c in tw]
+        two_ms = [tev.elapsed_ms(a, c) for a, _, c in tw]
 
         hot_ms = []
         if args.unflushed:  # back-to-back steps (caches may hold part of the pools)
             hot = [(E(), E()) for _ in range(args.steps)]
             for a, b in hot:
                 tev.record(a, stream)
-                append()
-                decode()
+                step()
                 tev.record(b, stream)
             stream.synchronize()
             hot_ms = [tev.elapsed_ms(a, b) for a, b in hot]
@@ -466,24 +479,21 @@ def main():
             "context_tokens": int(w.context_lens.sum()),
             "max_context_len": int(w.context_lens.max()),
             "effective_kv_bytes": eff_bytes,
-            "unique_kv_bytes": algo_bytes,
+            "unique_kv_bytes": w.unique_kv_bytes(),
             "seed": w.seed,
             "step": ("pa_copy_blocks (copy-on-write) + " if has_copies else "")
-                    + "pa_cache_append + pa_decode, caches flushed before each step",
+                    + "pa_append_decode (" + ("one launch: the new token stored and attended"
+                                              if fused else "append kernel, then the decode schedule")
+                    + "), caches flushed before each step",
             "cow_copies": int(w.copies.shape[0]),
             "schedule": schedule,
         },
         "seqs_per_s": round(w.num_seqs / t_step, 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
-        "decode_kernel_ms": {"mean": round(mean(kernel_ms), 5),
-                             "p10": round(percentile(kernel_ms, 10), 5),
-                             "p50": round(percentile(kernel_ms, 50), 5),
-                             "p90": round(percentile(kernel_ms, 90), 5)},
-        "decode_call_ms": {"mean": round(mean(decode_ms), 5), "p10": round(percentile(decode_ms, 10), 5),
-                      "p50": round(percentile(decode_ms, 50), 5),
-                      "p90": round(percentile(decode_ms, 90), 5)},
-        "append_ms": {"mean": round(mean(append_ms), 5), "p50": round(percentile(append_ms, 50), 5)},
-        # (the copy-on-write copies, when the step has any, are timed with the append)
+        "main_kernel_ms": {"mean": round(mean(kernel_ms), 5),
+                           "p10": round(percentile(kernel_ms, 10), 5),
+                           "p50": round(percentile(kernel_ms, 50), 5),
+                           "p90": round(percentile(kernel_ms, 90), 5)},
         "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",
@@ -491,7 +501,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(w.name, kernels[0]),
             "kernels": kernels,
             "algorithmic_bytes": algo_bytes,
             "timed": f"HIP events (created with hipEventDisableSystemFence) stamped by the GPU "
@@ -510,16 +520,17 @@ def main():
                     "schedule (one workgroup per sequence and head group, MFMA), alternating, each "
                     "after a cache flush and timed by events around the call",
         }
-    if fused_ms:
-        line["fused_step"] = {
-            "step_ms": {"mean": round(mean(fused_ms), 5), "p50": round(percentile(fused_ms, 50), 5)},
-            "value": round(eff_bytes / (mean(fused_ms) / 1e3) / 1e9, 2),
-            "unit": "GB/s",
-            "note": "the same step as one launch: pa_decode_multi with one new token per sequence "
-                    "stores the token's K/V and attends (one workgroup per sequence and KV head, no "
-                    "split)" + (", after pa_copy_blocks" if has_copies else "") +
-                    "; flushed, events around the step; value = effective KV bytes / mean step time",
-        }
+    line["two_call_step"] = {
+        "step_ms": {"mean": round(mean(two_ms), 5), "p50": round(percentile(two_ms, 50), 5)},
+        "value": round(eff_bytes / (mean(two_ms) / 1e3) / 1e9, 2),
+        "unit": "GB/s",
+        "append_call_ms": {"mean": round(mean(append_ms), 5), "p50": round(percentile(append_ms, 50), 5)},
+        "decode_call_ms": {"mean": round(mean(decode_ms), 5), "p10": round(percentile(decode_ms, 10), 5),
+                           "p50": round(percentile(decode_ms, 50), 5),
+                           "p90": round(percentile(decode_ms, 90), 5)},
+        "note": "the same step as " + ("pa_copy_blocks + " if has_copies else "") + "pa_cache_append + "
+                "pa_decode (the append kernel, then the decode schedule), flushed, events around the calls",
+    }
     if multi:
         line["multi_query"] = multi
     if hot_ms:

@@ -17,6 +17,8 @@
  *                    split into partitions whose partial softmax results are
  *                    combined by a log-sum-exp reduce ("PagedAttention from
  *                    First Principles", section 17, the v2 kernel's reduce).
+ *   pa_append_decode the append and the decode of a step in one call, one
+ *                    launch where the schedule allows.
  *   pa_decode_multi  several new tokens per sequence (chunked prefill,
  *                    speculative verification): their append and their causal
  *                    attention in one launch.
@@ -241,6 +243,36 @@ int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
  */
 int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
                          const pa_tensor* context_lens, float scale, hipStream_t stream);
+
+/*
+ * pa_append_decode -- one decode step in one call: this step's K/V appended
+ * at their slots, then pa_decode_ex over the updated pools.
+ *
+ * The append and the attention are the two halves of a decode step ("vLLM -
+ * PagedAttention" digest, "Fused CUDA Kernels": the write into the cache is
+ * fused to cut launches; "PagedAttention from First Principles", section 5).
+ * Where the decode schedule is unsplit on the MFMA path, one kernel does both:
+ * it stores the new token and takes its K/V from k / v for the attention.
+ * Otherwise the append kernel runs, then the decode the schedule chooses.
+ *
+ *   out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+ *   opts, workspace, workspace_bytes: as for pa_decode_ex (kernel events in
+ *                 opts time the fused kernel, or the main decode kernel).
+ *   k, v          bf16 [S, num_kv_heads, head_dim]: sequence s's new token,
+ *                 its position L_s - 1; last dim contiguous, rows 16-byte aligned.
+ *   slot_mapping  int64 [S]: the slot of that position.
+ *
+ * The result equals pa_cache_append followed by pa_decode_ex with the same
+ * options.  Preconditions (debug mode checks them, with pa_decode's): for
+ * every sequence with L_s > 0, slot_mapping[s] is the slot its block table
+ * gives position L_s - 1.  Every argument, the workspace included, is checked
+ * before anything is launched.  S == 0 is a no-op.
+ */
+int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                     const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
+                     const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                     int32_t block_size, const pa_decode_opts* opts, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
 
 /*
  * pa_decode_multi -- several new tokens per sequence in one step: the append

@@ -18,7 +18,8 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_HIP, PA_ERR_WORKSPACE, PA_ERR_
 PA_BF16, PA_F32, PA_I32, PA_I64 = 1, 2, 3, 4
 MAX_DIMS = 5
 
-EXPORTED = ("pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous", "pa_decode_ex",
+EXPORTED = ("pa_append_decode", "pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous",
+            "pa_decode_ex",
             "pa_decode_multi", "pa_decode_workspace_bytes",
             "pa_decode_schedule", "pa_last_error", "pa_set_debug")
 
@@ -69,6 +70,9 @@ def load(path=None):
                                  ctypes.POINTER(PaDecodeOpts), ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p]
     lib.pa_decode_ex.restype = ctypes.c_int
+    lib.pa_append_decode.argtypes = [P] * 9 + [ctypes.c_float, ctypes.c_int32, ctypes.POINTER(PaDecodeOpts),
+                                               ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.pa_append_decode.restype = ctypes.c_int
     lib.pa_decode_workspace_bytes.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32]
     lib.pa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode_schedule.argtypes = [ctypes.c_int64] * 4 + [ctypes.POINTER(ctypes.c_int32)]
@@ -232,6 +236,30 @@ def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
                                  ctypes.c_int32(block_size), ctypes.byref(opts),
                                  ctypes.c_void_p(ws_ptr) if ws_ptr else None,
                                  ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def append_decode(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale, block_size,
+                  *, partition_tokens=0, path=0, max_context_len=0, workgroups_per_cu=0, workspace=None,
+                  kernel_events=None, stream=None):
+    """pa_append_decode: this step's k/v [S, Hkv, D] appended at slot_mapping [S], then the
+    decode of q [S, Hq, D], as one call (one launch where the schedule is unsplit MFMA)."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in (
+        (out, "out"), (q, "q"), (k, "k"), (v, "v"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"),
+        (v_cache, "v_cache"), (block_tables, "block_tables"), (context_lens, "context_lens"))]
+    ds = [describe(x) for x in ts]
+    ev = (None, None)
+    if kernel_events is not None:
+        ev = tuple(_event_handle(e) for e in kernel_events)
+    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0,
+                        ev[0], ev[1])
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib, lib.pa_append_decode(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
+                                     ctypes.c_int32(block_size), ctypes.byref(opts),
+                                     ctypes.c_void_p(ws_ptr) if ws_ptr else None,
+                                     ctypes.c_size_t(ws_bytes), _stream(stream)))
 
 
 def set_debug(on):

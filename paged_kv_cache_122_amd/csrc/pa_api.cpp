@@ -391,15 +391,14 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
                   const pa_tensor* v_cache, const pa_tensor* block_tables,
                   const pa_tensor* context_lens, float scale, int32_t block_size,
                   const pa_decode_opts* opts, bool owned_ws, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+                  size_t workspace_bytes, bool debug, hipStream_t stream) {
   DecodePlan pl;
   int rc = plan_decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size, opts, &pl);
   if (rc != PA_OK) return rc;
   if (pl.S == 0) return PA_OK;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale must be finite");
   const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
-  if (g_debug.load() &&
-      (rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK)
+  if (debug && (rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK)
     return rc;
 
   char* ws = nullptr;  // partial results of split contexts
@@ -514,7 +513,7 @@ PA_EXPORT int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_c
                         hipStream_t stream) {
   g_error.clear();
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
-                       nullptr, true, nullptr, 0, stream);
+                       nullptr, true, nullptr, 0, g_debug.load() != 0, stream);
 }
 
 PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
@@ -524,7 +523,7 @@ PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* 
                            hipStream_t stream) {
   g_error.clear();
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, opts,
-                       false, workspace, workspace_bytes, stream);
+                       false, workspace, workspace_bytes, g_debug.load() != 0, stream);
 }
 
 PA_EXPORT int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
@@ -597,6 +596,58 @@ PA_EXPORT int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_
 }
 
 namespace {
+
+// Kernel arguments of the multi-token kernel (shapes already validated);
+// query_start may be NULL: one new token per sequence, row s.
+int multi_params(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
+                 const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,
+                 pa_tensor* v_cache, const pa_tensor* block_tables, const pa_tensor* context_lens,
+                 const CacheGeom& g, float scale, int32_t max_query_len, pa::MultiParams* mp) {
+  const int64_t T = q->shape[0], Hq = q->shape[1], S = context_lens->shape[0];
+  const int64_t G = Hq / g.kv_heads, W = block_tables->shape[1];
+  const int64_t cols = int64_t(max_query_len) * G;  // MFMA columns per (sequence, KV head)
+  const int col_sets = cols > 16 ? 2 : 1;
+  const int64_t col_groups = (cols + 16 * col_sets - 1) / (16 * col_sets);
+  if (g.kv_heads * col_groups > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "grid too large");
+  pa::MultiParams m{};
+  pa::DecodeParams& p = m.d;
+  p.out = out->data;
+  p.out_s = out->stride[0];
+  p.out_h = out->stride[1];
+  p.out_f32 = out->dtype == PA_F32;
+  p.q = static_cast<const uint16_t*>(q->data);
+  p.q_s = q->stride[0];
+  p.q_h = q->stride[1];
+  p.k_cache = static_cast<const uint16_t*>(k_cache->data);
+  p.v_cache = static_cast<const uint16_t*>(v_cache->data);
+  p.block_tables = static_cast<const int32_t*>(block_tables->data);
+  p.bt_s = block_tables->stride[0];
+  p.context_lens = static_cast<const int32_t*>(context_lens->data);
+  p.num_seqs = int(S);
+  p.num_q_heads = int(Hq);
+  p.num_kv_heads = int(g.kv_heads);
+  p.group = int(G);
+  p.head_groups = 1;
+  p.max_len = int(W * g.block_size);
+  p.scale_log2 = float(double(scale) * 1.4426950408889634);
+  p.part_tokens = p.max_len;
+  p.max_parts = 1;
+  m.k_new = static_cast<const uint16_t*>(k_new->data);
+  m.v_new = static_cast<const uint16_t*>(v_new->data);
+  m.kn_t = k_new->stride[0];
+  m.kn_h = k_new->stride[1];
+  m.vn_t = v_new->stride[0];
+  m.vn_h = v_new->stride[1];
+  m.slots = static_cast<const int64_t*>(slot_mapping->data);
+  m.query_start = query_start ? static_cast<const int32_t*>(query_start->data) : nullptr;
+  m.num_rows = int(T);
+  m.max_query_len = max_query_len;
+  m.col_sets = col_sets;
+  m.col_groups = int(col_groups);
+  m.num_slots = g.num_blocks * g.block_size;
+  *mp = m;
+  return PA_OK;
+}
 
 // Device-side contracts of pa_decode_multi, checked on the host.
 int debug_check_multi(const pa_tensor* slot_mapping, const pa_tensor* query_start,
@@ -722,53 +773,150 @@ PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tenso
                               g.block_size, g.num_blocks, max_query_len, stream)) != PA_OK)
     return rc;
 
-  const int64_t cols = int64_t(max_query_len) * G;  // MFMA columns per (sequence, KV head)
-  const int col_sets = cols > 16 ? 2 : 1;
-  const int64_t col_groups = (cols + 16 * col_sets - 1) / (16 * col_sets);
-  if (g.kv_heads * col_groups > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "grid too large");
-
-  pa::MultiParams m{};
-  pa::DecodeParams& p = m.d;
-  p.out = out->data;
-  p.out_s = out->stride[0];
-  p.out_h = out->stride[1];
-  p.out_f32 = out->dtype == PA_F32;
-  p.q = static_cast<const uint16_t*>(q->data);
-  p.q_s = q->stride[0];
-  p.q_h = q->stride[1];
-  p.k_cache = static_cast<const uint16_t*>(k_cache->data);
-  p.v_cache = static_cast<const uint16_t*>(v_cache->data);
-  p.block_tables = static_cast<const int32_t*>(block_tables->data);
-  p.bt_s = block_tables->stride[0];
-  p.context_lens = static_cast<const int32_t*>(context_lens->data);
-  p.num_seqs = int(S);
-  p.num_q_heads = int(Hq);
-  p.num_kv_heads = int(g.kv_heads);
-  p.group = int(G);
-  p.head_groups = 1;
-  p.max_len = int(W * g.block_size);
-  p.scale_log2 = float(double(scale) * 1.4426950408889634);
-  p.part_tokens = p.max_len;
-  p.max_parts = 1;
-  m.k_new = static_cast<const uint16_t*>(k_new->data);
-  m.v_new = static_cast<const uint16_t*>(v_new->data);
-  m.kn_t = k_new->stride[0];
-  m.kn_h = k_new->stride[1];
-  m.vn_t = v_new->stride[0];
-  m.vn_h = v_new->stride[1];
-  m.slots = static_cast<const int64_t*>(slot_mapping->data);
-  m.query_start = static_cast<const int32_t*>(query_start->data);
-  m.num_rows = int(T);
-  m.max_query_len = max_query_len;
-  m.col_sets = col_sets;
-  m.col_groups = int(col_groups);
-  m.num_slots = g.num_blocks * g.block_size;
+  pa::MultiParams m;
+  if ((rc = multi_params(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
+                         context_lens, g, scale, max_query_len, &m)) != PA_OK)
+    return rc;
   int cus = 0;
   if ((rc = device_cus(&cus)) != PA_OK) return rc;
   const pa::LaunchCtx ctx{stream, nullptr, nullptr, cus};
   const hipError_t e = pa::launch_multi(m, int(D), int(g.block_size), ctx);
   if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
   return PA_OK;
+}
+
+namespace {
+
+// pa_cache_append's work; `debug` checks the slot contract first.
+int cache_append_impl(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping, pa_tensor* k_cache,
+                      pa_tensor* v_cache, bool debug, hipStream_t stream) {
+  int rc;
+  CacheGeom g;
+  if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
+  if ((rc = check_desc(k, "k", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(v, "v", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(slot_mapping, "slot_mapping", PA_I64, 1)) != PA_OK) return rc;
+  const int64_t T = k->shape[0];
+  if (k->shape[1] != g.kv_heads || k->shape[2] != g.head_dim)
+    return fail(PA_ERR_INVALID, "k: shape [T, %lld, %lld] expected", (long long)g.kv_heads,
+                (long long)g.head_dim);
+  if (v->shape[0] != T || v->shape[1] != g.kv_heads || v->shape[2] != g.head_dim)
+    return fail(PA_ERR_INVALID, "v: shape must equal k's");
+  if (slot_mapping->shape[0] != T)
+    return fail(PA_ERR_INVALID, "slot_mapping: %lld entries for %lld tokens",
+                (long long)slot_mapping->shape[0], (long long)T);
+  if (slot_mapping->stride[0] != 1 && T > 1) return fail(PA_ERR_INVALID, "slot_mapping must be contiguous");
+  if ((rc = check_rows(k, "k")) != PA_OK) return rc;
+  if ((rc = check_rows(v, "v")) != PA_OK) return rc;
+  if (T == 0) return PA_OK;
+  if (T > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
+
+  if (debug) {
+    std::vector<int64_t> slots;
+    if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(T), stream)) != PA_OK) return rc;
+    std::unordered_set<int64_t> seen;
+    const int64_t nslots = g.num_blocks * g.block_size;
+    for (int64_t i = 0; i < T; ++i) {
+      const int64_t sl = slots[size_t(i)];
+      if (sl < 0) continue;
+      if (sl >= nslots)
+        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld outside [0, %lld)", (long long)i,
+                    (long long)sl, (long long)nslots);
+      if (!seen.insert(sl).second)
+        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld repeats an earlier slot", (long long)i,
+                    (long long)sl);
+    }
+  }
+
+  pa::AppendParams p{};
+  p.k = static_cast<const uint16_t*>(k->data);
+  p.v = static_cast<const uint16_t*>(v->data);
+  p.k_t = k->stride[0];
+  p.k_h = k->stride[1];
+  p.v_t = v->stride[0];
+  p.v_h = v->stride[1];
+  p.slots = static_cast<const int64_t*>(slot_mapping->data);
+  p.k_cache = static_cast<uint16_t*>(k_cache->data);
+  p.v_cache = static_cast<uint16_t*>(v_cache->data);
+  p.num_tokens = int(T);
+  p.num_kv_heads = int(g.kv_heads);
+  const hipError_t e = pa::launch_append(p, int(g.head_dim), int(g.block_size), stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
+                               const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
+                               const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                               int32_t block_size, const pa_decode_opts* opts, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  g_error.clear();
+  int rc;
+  DecodePlan pl;
+  if ((rc = plan_decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size, opts, &pl)) != PA_OK)
+    return rc;
+  if ((rc = check_desc(k, "k", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(v, "v", PA_BF16, 3)) != PA_OK) return rc;
+  if ((rc = check_desc(slot_mapping, "slot_mapping", PA_I64, 1)) != PA_OK) return rc;
+  for (const pa_tensor* t : {k, v})
+    if (t->shape[0] != pl.S || t->shape[1] != pl.Hkv || t->shape[2] != pl.D)
+      return fail(PA_ERR_INVALID, "k/v: shape [%lld, %lld, %lld] expected (one new token per sequence)",
+                  (long long)pl.S, (long long)pl.Hkv, (long long)pl.D);
+  if (slot_mapping->shape[0] != pl.S || (slot_mapping->stride[0] != 1 && pl.S > 1))
+    return fail(PA_ERR_INVALID, "slot_mapping: %lld contiguous entries expected", (long long)pl.S);
+  if ((rc = check_rows(k, "k")) != PA_OK) return rc;
+  if ((rc = check_rows(v, "v")) != PA_OK) return rc;
+  if (pl.S == 0) return PA_OK;
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale must be finite");
+  // everything the decode will check, checked before the append launches
+  if (pl.ws.total > 0) {
+    if (!workspace || workspace_bytes < pl.ws.total)
+      return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, pl.ws.total);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
+  if (g_debug.load()) {
+    if ((rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK) return rc;
+    std::vector<int32_t> lens, bt;
+    std::vector<int64_t> slots;
+    const size_t stride = size_t(block_tables->stride[0]);
+    if ((rc = copy_to_host(&lens, context_lens->data, size_t(pl.S), stream)) != PA_OK) return rc;
+    if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(pl.S), stream)) != PA_OK) return rc;
+    if ((rc = copy_to_host(&bt, block_tables->data, size_t(pl.S - 1) * stride + size_t(pl.W), stream)) != PA_OK)
+      return rc;
+    for (int64_t s = 0; s < pl.S; ++s) {
+      const int64_t L = lens[size_t(s)];
+      if (L == 0) continue;
+      const int64_t want = int64_t(bt[size_t(s) * stride + size_t((L - 1) / pl.B)]) * pl.B + (L - 1) % pl.B;
+      if (slots[size_t(s)] != want)
+        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld, but position %lld of sequence %lld is slot %lld",
+                    (long long)s, (long long)slots[size_t(s)], (long long)(L - 1), (long long)s, (long long)want);
+    }
+  }
+
+  if (!pl.stream && pl.max_parts == 1 && pl.path == pa::Path::Mfma) {
+    // unsplit MFMA schedule: the multi-token kernel with one new token per
+    // sequence stores it and attends in one launch
+    const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
+    pa::MultiParams m;
+    if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
+                           g, scale, 1, &m)) != PA_OK)
+      return rc;
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != PA_OK) return rc;
+    const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus};
+    const hipError_t e = pa::launch_multi(m, int(pl.D), int(pl.B), ctx);
+    if (e != hipSuccess) return hip_fail(e, "fused append + decode launch");
+    return PA_OK;
+  }
+  // otherwise the append kernel, then the decode the plan chose (contracts
+  // were checked above)
+  if ((rc = cache_append_impl(k, v, slot_mapping, k_cache, v_cache, false, stream)) != PA_OK) return rc;
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, opts, false,
+                       workspace, workspace_bytes, false, stream);
 }
 
 PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* block_pairs,
@@ -821,57 +969,5 @@ PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_te
 PA_EXPORT int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping,
                               pa_tensor* k_cache, pa_tensor* v_cache, hipStream_t stream) {
   g_error.clear();
-  int rc;
-  CacheGeom g;
-  if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
-  if ((rc = check_desc(k, "k", PA_BF16, 3)) != PA_OK) return rc;
-  if ((rc = check_desc(v, "v", PA_BF16, 3)) != PA_OK) return rc;
-  if ((rc = check_desc(slot_mapping, "slot_mapping", PA_I64, 1)) != PA_OK) return rc;
-  const int64_t T = k->shape[0];
-  if (k->shape[1] != g.kv_heads || k->shape[2] != g.head_dim)
-    return fail(PA_ERR_INVALID, "k: shape [T, %lld, %lld] expected", (long long)g.kv_heads,
-                (long long)g.head_dim);
-  if (v->shape[0] != T || v->shape[1] != g.kv_heads || v->shape[2] != g.head_dim)
-    return fail(PA_ERR_INVALID, "v: shape must equal k's");
-  if (slot_mapping->shape[0] != T)
-    return fail(PA_ERR_INVALID, "slot_mapping: %lld entries for %lld tokens",
-                (long long)slot_mapping->shape[0], (long long)T);
-  if (slot_mapping->stride[0] != 1 && T > 1) return fail(PA_ERR_INVALID, "slot_mapping must be contiguous");
-  if ((rc = check_rows(k, "k")) != PA_OK) return rc;
-  if ((rc = check_rows(v, "v")) != PA_OK) return rc;
-  if (T == 0) return PA_OK;
-  if (T > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many tokens");
-
-  if (g_debug.load()) {
-    std::vector<int64_t> slots;
-    if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(T), stream)) != PA_OK) return rc;
-    std::unordered_set<int64_t> seen;
-    const int64_t nslots = g.num_blocks * g.block_size;
-    for (int64_t i = 0; i < T; ++i) {
-      const int64_t sl = slots[size_t(i)];
-      if (sl < 0) continue;
-      if (sl >= nslots)
-        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld outside [0, %lld)", (long long)i,
-                    (long long)sl, (long long)nslots);
-      if (!seen.insert(sl).second)
-        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld repeats an earlier slot", (long long)i,
-                    (long long)sl);
-    }
-  }
-
-  pa::AppendParams p{};
-  p.k = static_cast<const uint16_t*>(k->data);
-  p.v = static_cast<const uint16_t*>(v->data);
-  p.k_t = k->stride[0];
-  p.k_h = k->stride[1];
-  p.v_t = v->stride[0];
-  p.v_h = v->stride[1];
-  p.slots = static_cast<const int64_t*>(slot_mapping->data);
-  p.k_cache = static_cast<uint16_t*>(k_cache->data);
-  p.v_cache = static_cast<uint16_t*>(v_cache->data);
-  p.num_tokens = int(T);
-  p.num_kv_heads = int(g.kv_heads);
-  const hipError_t e = pa::launch_append(p, int(g.head_dim), int(g.block_size), stream);
-  if (e != hipSuccess) return hip_fail(e, "append launch");
-  return PA_OK;
+  return cache_append_impl(k, v, slot_mapping, k_cache, v_cache, g_debug.load() != 0, stream);
 }

@@ -82,7 +82,7 @@ struct MultiParams {
   const uint16_t* v_new;
   int64_t kn_t, kn_h, vn_t, vn_h;  // element strides of k_new, v_new rows
   const int64_t* slots;
-  const int32_t* query_start;      // [S + 1]
+  const int32_t* query_start;      // [S + 1], or null: row s is sequence s's one new token
   int num_rows;                    // T
   int max_query_len;               // rows per sequence the grid covers
   int col_sets;                    // 16-column MFMA sets per workgroup (1 or 2)

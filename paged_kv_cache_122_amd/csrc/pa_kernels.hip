@@ -1417,8 +1417,9 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
   const int s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
   const int G = p.group;
   // this sequence's rows, kept inside [0, T); at most max_query_len of them
-  const int r0 = min(max(mp.query_start[s], 0), mp.num_rows);
-  const int r1 = min(max(mp.query_start[s + 1], r0), mp.num_rows);
+  // (no query_start: row s, one new token per sequence)
+  const int r0 = mp.query_start ? min(max(mp.query_start[s], 0), mp.num_rows) : min(s, mp.num_rows);
+  const int r1 = mp.query_start ? min(max(mp.query_start[s + 1], r0), mp.num_rows) : min(s + 1, mp.num_rows);
   const int L = clamp_len(p, p.context_lens[s]);
   const int n = min(min(r1 - r0, L), mp.max_query_len);
   const int L_old = L - n;

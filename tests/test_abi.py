@@ -268,3 +268,32 @@ def test_decode_multi_validation(lib):
     assert call(mql=1 << 22, Hq=32) == pa.PA_ERR_INVALID           # columns past 2^24
     assert call(scale=float("inf")) == pa.PA_ERR_INVALID
     assert call(D=96) == pa.PA_ERR_UNSUPPORTED                      # pools reject the head size
+
+
+def test_append_decode_validation(lib):
+    """pa_append_decode checks the append's and the decode's arguments, and the
+    workspace, before anything is launched (fake pointers here)."""
+    r = ctypes.byref
+
+    def call(a=None, kshape=None, slots=None, opts=None, ws=None, ws_bytes=0, kdt=pa.PA_BF16):
+        a = a or decode_args()
+        S, Hkv, D = a["q"].shape[0], a["k"].shape[1], a["q"].shape[2]
+        k = T(kshape or [S, Hkv, D], kdt)
+        v = T([S, Hkv, D], pa.PA_BF16)
+        sl = T([S if slots is None else slots], pa.PA_I64)
+        return lib.pa_append_decode(r(a["out"]), r(a["q"]), r(k), r(v), r(sl), r(a["k"]), r(a["v"]),
+                                    r(a["bt"]), r(a["lens"]), 0.1, 16, r(opts) if opts else None, ws,
+                                    ws_bytes, None)
+
+    assert call(decode_args(S=0)) == pa.PA_OK                              # nothing to do
+    assert call(kshape=[4, 3, 128]) == pa.PA_ERR_INVALID                    # KV heads of the pools
+    assert call(kshape=[3, 2, 128]) == pa.PA_ERR_INVALID                    # one new token per sequence
+    assert call(kdt=pa.PA_F32) == pa.PA_ERR_INVALID
+    assert call(slots=5) == pa.PA_ERR_INVALID
+    bad = decode_args()
+    bad["lens"] = T([3], pa.PA_I32)
+    assert call(bad) == pa.PA_ERR_INVALID                                   # decode arguments too
+    # a split schedule needs the caller's workspace: rejected before the append runs
+    assert call(decode_args(W=128), opts=pa.PaDecodeOpts(512, 0, 0)) == pa.PA_ERR_WORKSPACE
+    assert call(decode_args(W=128), opts=pa.PaDecodeOpts(512, 0, 0), ws=ctypes.c_void_p(FAKE),
+                ws_bytes=100) == pa.PA_ERR_WORKSPACE

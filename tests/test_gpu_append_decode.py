@@ -1,0 +1,111 @@
+"""GPU checks of pa_append_decode, the decode step in one call: the appended
+pools are bit-exact against the oracle's append, the attention matches the fp64
+oracle (max|err| <= 1e-2, relative RMS <= 2e-3), on the fused one-launch path
+(unsplit MFMA schedules) and on the append-then-decode path (VALU, split and
+stream-K schedules), where it equals pa_cache_append + pa_decode_ex bit for bit."""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_close, need_gpu, oracle_step, sample_seqs
+from paged_kv_cache_122_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+# (config, options, sequences the oracle checks): fused path first, then the
+# append-then-decode schedules
+CASES = [
+    ("tiny_gqa4_d64", {}, 64),
+    ("llama3_8b_b64", {}, 24),
+    ("llama3_70b_b256", {}, 16),
+    ("llama3_8b_b64", {"partition_tokens": 512}, 16),
+    ("long32k_b16", {}, 4),
+    ("opt13b_mha_prefix_b128", {}, 12),
+]
+
+
+def _run(pa, dw, w, out, opts, kernel_events=None):
+    torch = need_gpu()
+    maxlen = w.table_width * w.block_size
+    nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen,
+                            opts.get("partition_tokens", 0))
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, dw.block_tables,
+                     dw.context_lens, w.scale, w.block_size, workspace=ws, kernel_events=kernel_events, **opts)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("name,opts,n_check", CASES, ids=[f"{c[0]}-{c[1]}" for c in CASES])
+def test_append_decode_parity(name, opts, n_check):
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.make(name)
+    print(f"[{name} {opts}] S={w.num_seqs}", flush=True)
+    dw = dev.upload(w)
+    seqs = sample_seqs(w, n_check)
+    kst, vst, ref = oracle_step(w, seqs)
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    _run(pa, dw, w, out, opts)
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+    a, r = assert_close(out.double().cpu().numpy()[seqs], ref[seqs], name)
+    print(f"[{name} {opts}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_append_decode_equals_two_calls_where_unfused():
+    """Split and VALU schedules run the append kernel, then pa_decode_ex's own
+    kernels: the output equals the two separate calls bit for bit."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    for name, opts in (("llama3_8b_b64", {"partition_tokens": 512}), ("opt13b_mha_prefix_b128", {}),
+                       ("long32k_b16", {})):
+        w = workloads.make(name)
+        dw1, dw2 = dev.upload(w), dev.upload(w)
+        o1, o2 = torch.empty_like(dw1.q), torch.empty_like(dw2.q)
+        _run(pa, dw1, w, o1, opts)
+        maxlen = w.table_width * w.block_size
+        nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen,
+                                opts.get("partition_tokens", 0))
+        ws = pa.alloc_workspace(nb, "cuda") if nb else None
+        pa.cache_append(dw2.k_new, dw2.v_new, dw2.slot_mapping, dw2.k_cache, dw2.v_cache)
+        pa.decode_ex(o2, dw2.q, dw2.k_cache, dw2.v_cache, dw2.block_tables, dw2.context_lens, w.scale,
+                     w.block_size, workspace=ws, **opts)
+        torch.cuda.synchronize()
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), name
+        assert torch.equal(dw1.k_cache.view(torch.int16), dw2.k_cache.view(torch.int16)), name
+        del dw1, dw2
+        torch.cuda.empty_cache()
+
+
+def test_append_decode_events_and_contracts():
+    """Kernel events time the fused kernel (or the decode kernel); debug mode
+    rejects a slot that is not the table's slot of the new position."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.make("tiny_gqa4_d64")
+    dw = dev.upload(w)
+    out = torch.empty_like(dw.q)
+    for opts in ({}, {"partition_tokens": 32}):
+        ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        _run(pa, dw, w, out, opts, kernel_events=ev)
+        assert ev[0].elapsed_time(ev[1]) > 0.0
+    old = pa.set_debug(True)
+    try:
+        _run(pa, dw, w, out, {})  # valid
+        bad = dw.slot_mapping.clone()
+        bad[0] += 1
+        with pytest.raises(pa.PaError) as e:
+            pa.append_decode(out, dw.q, dw.k_new, dw.v_new, bad, dw.k_cache, dw.v_cache, dw.block_tables,
+                             dw.context_lens, w.scale, w.block_size)
+        assert e.value.code == pa.PA_ERR_CONTRACT
+    finally:
+        pa.set_debug(old)
