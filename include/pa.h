@@ -265,7 +265,8 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * The result equals pa_cache_append followed by pa_decode_ex with the same
  * options.  Preconditions (debug mode checks them, with pa_decode's): for
  * every sequence with L_s > 0, slot_mapping[s] is the slot its block table
- * gives position L_s - 1.  Every argument, the workspace included, is checked
+ * gives position L_s - 1; a sequence with L_s == 0 has no new token and a
+ * negative slot.  Every argument, the workspace included, is checked
  * before anything is launched.  S == 0 is a no-op.
  */
 int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
@@ -309,7 +310,8 @@ int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, con
  * (debug mode checks them): 0 <= n_s <= min(L_s, max_query_len); each
  * non-negative slot is the table's slot for its position and no slot repeats;
  * no cached position read by the call (t < L_s - n_s of any sequence) lies in
- * a slot it writes.  Rows outside every sequence's range are not written.
+ * a slot it writes.  Rows outside every sequence's range are not written; a
+ * sequence's rows past its context length (n_s > L_s) are written as zeros.
  * S == 0, T == 0 or max_query_len == 0 is a no-op.
  */
 int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,

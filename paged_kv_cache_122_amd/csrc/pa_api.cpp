@@ -889,7 +889,12 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
       return rc;
     for (int64_t s = 0; s < pl.S; ++s) {
       const int64_t L = lens[size_t(s)];
-      if (L == 0) continue;
+      if (L == 0) {
+        if (slots[size_t(s)] >= 0)
+          return fail(PA_ERR_CONTRACT, "sequence %lld has no token (context length 0) but slot %lld",
+                      (long long)s, (long long)slots[size_t(s)]);
+        continue;
+      }
       const int64_t want = int64_t(bt[size_t(s) * stride + size_t((L - 1) / pl.B)]) * pl.B + (L - 1) % pl.B;
       if (slots[size_t(s)] != want)
         return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld, but position %lld of sequence %lld is slot %lld",

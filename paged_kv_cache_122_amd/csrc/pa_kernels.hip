@@ -1455,6 +1455,14 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
       write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, slot, kvh, piece, kv, vv);
     }
   };
+  if (cg == 0) {  // rows past the context (a sequence with no tokens) read as empty: zeros
+    const int rows = min(r1 - r0, mp.max_query_len);
+    for (int idx = threadIdx.x; idx < (rows - n) * G * D; idx += kThreads) {
+      const int i = idx / (G * D);
+      const int hd = idx - i * (G * D);
+      store_out(p, r0 + n + i, kvh * G + hd / D, hd % D, 0.f);
+    }
+  }
   const int cols = n * G;             // (query, head) columns of this KV head
   const int col0 = 16 * NS * cg;      // first column of this workgroup
   if (col0 >= cols) {                 // workgroup-uniform; column group 0 only when n == 0

@@ -107,5 +107,37 @@ def test_append_decode_events_and_contracts():
             pa.append_decode(out, dw.q, dw.k_new, dw.v_new, bad, dw.k_cache, dw.v_cache, dw.block_tables,
                              dw.context_lens, w.scale, w.block_size)
         assert e.value.code == pa.PA_ERR_CONTRACT
+        # no token (context length 0) but a slot to store it in
+        lens = dw.context_lens.clone()
+        lens[0] = 0
+        with pytest.raises(pa.PaError) as e:
+            pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                             dw.block_tables, lens, w.scale, w.block_size)
+        assert e.value.code == pa.PA_ERR_CONTRACT
     finally:
         pa.set_debug(old)
+
+
+def test_append_decode_empty_contexts():
+    """Sequences with no tokens (length 0, slot -1) beside others: their rows are
+    zeros and nothing is stored for them, on the one-launch path."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    rng = np.random.Generator(np.random.PCG64(77))
+    lens = [0, 33, 0, 200, 1]
+    nb = 40
+    _, tables = workloads.place_independent(rng, lens, 16, nb)
+    w = workloads.build_workload("empty_contexts", 77, rng, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                                 block_size=16, num_blocks=nb, tables=tables, context_lens=lens, width=16)
+    assert list(w.slot_mapping[[0, 2]]) == [-1, -1]
+    dw = dev.upload(w)
+    kst, vst, ref = oracle_step(w)
+    out = torch.full(dw.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    _run(pa, dw, w, out, {})
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks)
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks)
+    got = out.double().cpu().numpy()
+    assert np.all(got[[0, 2]] == 0.0)
+    assert_close(got, ref, "empty_contexts")
