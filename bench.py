@@ -145,6 +145,10 @@ def decode_kernels(w, part, cus):
         tmpl = f"<{w.head_dim},{w.block_size},{2 if wgs >= cus else 4}>"
     if parts == 1:
         return [core + tmpl], "one workgroup per (sequence, head group), no split"
+    wgs = w.num_seqs * w.num_kv_heads * -(-g // 16) * parts
+    if g <= 16 and wgs >= cus:  # split schedules read shared partitions once
+        return ([f"decode_shared<{w.head_dim},{w.block_size}>", f"combine_parts<{w.head_dim}>"],
+                f"partitions of {part} tokens, shared partitions read once")
     return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
 
 

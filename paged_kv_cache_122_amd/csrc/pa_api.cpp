@@ -355,6 +355,10 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
 
   pl->part_tokens = int(part);
   pl->max_parts = int(max_parts);
+  // A split schedule with the automatic path takes the MFMA kernel for any
+  // grouping up to 16: it reads a partition that consecutive sequences share
+  // (a common prefix) once for all of them, which the VALU kernel cannot.
+  if (want == 0 && max_parts > 1 && G <= 16) pl->path = pa::Path::Mfma;
   pl->ws = pa::workspace_layout(S, Hq, D, max_parts);
   if (max_parts == 1) pl->ws.total = 0;
   return PA_OK;

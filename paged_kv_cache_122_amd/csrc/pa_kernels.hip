@@ -1150,6 +1150,127 @@ __global__ __launch_bounds__(kThreads, (SL == kPipeSlots ? 2 : 1)) void decode_m
   mfma_finish<D>(p, sm, acc, s, h0, ncols, part, nparts, wave, lane);
 }
 
+// ---------------------------------------------------------------------------
+// shared partitions (partitioned schedule, G <= 16)
+//
+// Sequences that share a prefix hold the same physical blocks for it.  When
+// consecutive sequences s, s+1, ... all fill partition j and their tables name
+// the same blocks there, the workgroup of the first computes partition j for
+// all of them: its MFMA columns are (member, query head) pairs, member i's
+// column i*G + g holding sequence s+i's query head kvh*G + g, so each shared
+// tile is read once.  The others skip partition j.  Runs are cut at aligned
+// windows of 16/G sequences (the columns of one workgroup), so the test only
+// looks inside the window: s-1 (is s a follower?) and s+1 ... (members).
+// Each member's partial result goes where its own workgroup would have put
+// it, and the combine kernel is unchanged.
+// ---------------------------------------------------------------------------
+constexpr int kMaxShare = 16;  // members per workgroup at G = 1
+
+template <int D, int BS>
+__global__ __launch_bounds__(kThreads, 2) void decode_shared(DecodeParams p) {
+  constexpr int NC = D / 32;
+  __shared__ Smem<D> sm;
+  __shared__ int differs[kMaxShare + 1];  // window members from s-1: 1 = not sharing s's partition
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int part = blockIdx.z;
+  const int G = p.group;
+  const int M = 16 / G;  // members one workgroup carries
+  const int t0 = part * p.part_tokens;
+  const auto row = table_row(p, s, BS);
+  const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
+
+  const int L = clamp_len(p, p.context_lens[s]);
+  const int nparts = partitions(p, L);
+  if (part >= (nparts > 0 ? nparts : 1)) return;
+  const int t1 = min(L, t0 + p.part_tokens);
+
+  int m = 1;  // members (sequences s .. s+m-1)
+  if (M > 1 && L >= t0 + p.part_tokens) {  // workgroup-uniform: only a filled partition is shared
+    const int w0 = s - s % M;
+    const int lo = max(s - 1, w0);
+    const int hi = min(w0 + M, p.num_seqs);
+    const int E = p.part_tokens / BS;  // table entries of the partition
+    for (int c = lo + int(threadIdx.x); c < hi; c += kThreads)
+      differs[c - lo] = clamp_len(p, p.context_lens[c]) < t0 + p.part_tokens;
+    __syncthreads();
+    const int32_t* mine = p.block_tables + size_t(s) * p.bt_s + t0 / BS;
+    for (int idx = threadIdx.x; idx < (hi - lo) * E; idx += kThreads) {
+      const int c = lo + idx / E;
+      const int e = idx - (c - lo) * E;
+      if (c != s && p.block_tables[size_t(c) * p.bt_s + t0 / BS + e] != mine[e]) differs[c - lo] = 1;
+    }
+    __syncthreads();
+    if (lo < s && differs[0] == 0) return;  // s-1 computes this partition for s
+    for (int c = s + 1; c < hi && differs[c - lo] == 0; ++c) ++m;
+  }
+  const int ncols = m * G;
+
+  // column r: member r / G, head r % G
+  const int ci = r / G;
+  const int qh = kvh * G + (r - ci * G);
+  u32x4 q[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    q[c] = u32x4{0u, 0u, 0u, 0u};
+    if (r < ncols) q[c] = load16(p.q + size_t(s + ci) * p.q_s + size_t(qh) * p.q_h + 8 * (g4 + 4 * c));
+  }
+  MfmaAcc<D> acc;
+  mfma_reset(acc);
+  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
+                                [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    mfma_tile<D>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
+  });
+
+  // combine the waves; column c goes to sequence s + c / G, head kvh * G + c % G
+  float l = acc.l;
+  l += shfl_xor(l, 16);
+  l += shfl_xor(l, 32);
+  if (g4 == 0) {
+    sm.m[wave][r] = acc.m;
+    sm.l[wave][r] = l;
+  }
+  if (r < ncols) {
+#pragma unroll
+    for (int mm = 0; mm < D / 16; ++mm)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
+    const int col = idx / D;
+    const int d = idx - col * D;
+    float M_ = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, sm.m[w][col]);
+    float o = 0.f, lsum = 0.f;
+    if (M_ != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float e = exp2f(sm.m[w][col] - M_);
+        o += sm.o[w][d][col] * e;
+        lsum += sm.l[w][col] * e;
+      }
+    }
+    const int sc = s + col / G;
+    const int h = kvh * G + col % G;
+    if (partitions(p, p.context_lens[sc]) <= 1) {
+      store_out(p, sc, h, d, lsum > 0.f ? o / lsum : 0.f);
+    } else {
+      const size_t wrow = (size_t(sc) * p.num_q_heads + h) * p.max_parts + part;
+      p.ws_o[wrow * D + d] = o / lsum;
+      if (d == 0) {
+        p.ws_ml[wrow * 2 + 0] = M_;
+        p.ws_ml[wrow * 2 + 1] = lsum;
+      }
+    }
+  }
+}
+
 template <int D, int BS, int VG>
 __global__ __launch_bounds__(kThreads, BS == 8 || VG == 2 ? 1 : 2) void decode_valu(DecodeParams p) {
   constexpr int NC = D / 32;
@@ -1660,9 +1781,12 @@ template <int D, int BS>
 hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx& c) {
   static_assert(kDeepSlots > kPipeSlots, "");
   hipError_t e;
-  if (path == Path::Mfma)
-    e = deep_pipeline(p, c) ? launch_rows(decode_mfma<D, BS, kDeepSlots>, p, p.num_kv_heads * p.head_groups, c)
-                            : launch_rows(decode_mfma<D, BS, kPipeSlots>, p, p.num_kv_heads * p.head_groups, c);
+  if (path == Path::Mfma && deep_pipeline(p, c))
+    e = launch_rows(decode_mfma<D, BS, kDeepSlots>, p, p.num_kv_heads * p.head_groups, c);
+  else if (path == Path::Mfma && p.max_parts > 1 && p.group <= 16)
+    e = launch_rows(decode_shared<D, BS>, p, p.num_kv_heads, c);  // split: shared partitions read once
+  else if (path == Path::Mfma)
+    e = launch_rows(decode_mfma<D, BS, kPipeSlots>, p, p.num_kv_heads * p.head_groups, c);
   else if (p.group == 1)
     e = launch_rows(decode_valu<D, BS, 1>, p, p.num_kv_heads, c);
   else
