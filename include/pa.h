@@ -150,7 +150,11 @@ int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* bloc
  *                                   (batches of more than 8192 sequences:
  *                                   partitions of 512 tokens).
  * A second kernel combines the partial results of a split context in
- * ascending token order with a log-sum-exp reduce.  The partial results live in a
+ * ascending token order with a log-sum-exp reduce.  Under partitions, a
+ * partition that consecutive sequences fill with the same physical blocks (a
+ * shared prefix, "PagedAttention from First Principles", section 9) is read
+ * once for up to 16/G of them: keep sequences that share a prefix adjacent.
+ * The results do not depend on it.  The partial results live in a
  * library-owned workspace on the current device, grown with hipMalloc when a
  * call needs more (never during stream capture: that returns PA_ERR_WORKSPACE;
  * use pa_decode_ex there).  Calls that need the workspace may not overlap on
