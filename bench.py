@@ -36,17 +36,21 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 
 # HBM bytes per launch of a step's main kernel, from two rocprofv3
 # --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by what
-# the counter reads for a plain copy of known size in the same run.  Valid only
+# the counter reads for a plain copy of known size in the same run, and the
+# kernel's MFMA busy share of SIMD cycles from a third.  Valid only
 # for the kernel sources they were taken on (sha256 of the files below);
 # reported as null once those change.
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "6ec9d10421af3516b3a8d6d57c383abafc236105bc9a8314ef807648279ba0d8",
-    # the step's one launch: FETCH_SIZE 134430.5 KiB x 1.9999, WRITE_SIZE 1280.2 KiB x 1.0
-    "llama3_8b_b64 decode_multi<128,16,1>": {"fetch_bytes": 275297179, "write_bytes": 1310965},
-    # the verification batch: FETCH_SIZE 141223.4 KiB x 1.9999, WRITE_SIZE 4353.6 KiB x 1.0
-    "llama3_8b_verify5_b64 decode_multi<128,16,2>": {"fetch_bytes": 289208279, "write_bytes": 4458062},
+    "sources_sha256": "8cffc51e7da12e524f841c72117505c407193202524e02ca435eb7686ae08e99",
+    # the step's one launch: FETCH_SIZE 134433.6 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.68 %
+    "llama3_8b_b64 decode_multi<128,16,1>": {"fetch_bytes": 275303450, "write_bytes": 1310859,
+                                             "mfma_busy_pct": 4.68},
+    # the verification batch: FETCH_SIZE 141217.2 KiB x 1.9999, WRITE_SIZE 4353.7 KiB x 1.0; MfmaUtil 8.92 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2>": {"fetch_bytes": 289195580, "write_bytes": 4458217,
+                                                     "mfma_busy_pct": 8.92},
 }
 
 
@@ -123,12 +127,23 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(config, kernel):
+def measured(config, kernel):
+    """The counter figures for this workload's kernel, if taken on these sources."""
     t = MEASURED_TRAFFIC
     key = f"{config} {kernel}"
     if key not in t or t["sources_sha256"] != sources_sha256():
         return None
-    return t[key]["fetch_bytes"] + t[key]["write_bytes"]
+    return t[key]
+
+
+def measured_traffic(config, kernel):
+    m = measured(config, kernel)
+    return None if m is None else m["fetch_bytes"] + m["write_bytes"]
+
+
+def measured_mfma(config, kernel):
+    m = measured(config, kernel)
+    return None if m is None else m.get("mfma_busy_pct")
 
 
 def decode_kernels(w, part, cus):
@@ -222,6 +237,7 @@ def multi_query_leg(steps, warmup, tev, stream, flush):
         "achieved_gbs": round(algo / t / 1e9, 2),
         "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic(w.name, "decode_multi<128,16,2>"),
+        "mfma_busy_pct": measured_mfma(w.name, "decode_multi<128,16,2>"),
         "tokens_per_s": round(T / t, 1),
         "single_token_decode_same_pools_call_ms": round(mean(single_ms), 5),
         "note": "pa_decode_multi (append fused, causal over cached + drafted tokens) vs pa_decode of "
@@ -506,6 +522,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(w.name, kernels[0]),
+            "mfma_busy_pct": measured_mfma(w.name, kernels[0]),
             "kernels": kernels,
             "algorithmic_bytes": algo_bytes,
             "timed": f"HIP events (created with hipEventDisableSystemFence) stamped by the GPU "

@@ -643,6 +643,8 @@ int multi_params(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, con
   m.vn_t = v_new->stride[0];
   m.vn_h = v_new->stride[1];
   m.slots = static_cast<const int64_t*>(slot_mapping->data);
+  m.k_store = static_cast<uint16_t*>(k_cache->data);
+  m.v_store = static_cast<uint16_t*>(v_cache->data);
   m.query_start = query_start ? static_cast<const int32_t*>(query_start->data) : nullptr;
   m.num_rows = int(T);
   m.max_query_len = max_query_len;

@@ -82,6 +82,8 @@ struct MultiParams {
   const uint16_t* v_new;
   int64_t kn_t, kn_h, vn_t, vn_h;  // element strides of k_new, v_new rows
   const int64_t* slots;
+  uint16_t* k_store;               // the pools again, written by the append
+  uint16_t* v_store;
   const int32_t* query_start;      // [S + 1], or null: row s is sequence s's one new token
   int num_rows;                    // T
   int max_query_len;               // rows per sequence the grid covers

@@ -1,5 +1,8 @@
 // HIP kernels for gfx950 (CDNA4): slot-mapped KV append, paged decode
-// attention, and the split-K log-sum-exp combine.
+// attention, the split-K log-sum-exp combine, batched copy-on-write block
+// copies, and attention for several new tokens per sequence with their
+// append fused in (chunked prefill, speculative verification, and the
+// one-launch decode step).
 //
 // Method: one query token per sequence attends to its cached tokens, which
 // live in fixed-size physical blocks reached through a per-sequence block
@@ -17,17 +20,19 @@
 //   matrix cores without LDS staging or shuffles.
 // * Loads are buffer loads through a resource descriptor built per tile in
 //   scalar registers from the block-table entry, with the non-temporal bit
-//   (the pools are read once per step).  Each wave keeps the next three tiles'
-//   loads in flight while it computes on the current one (two where registers
-//   would otherwise halve occupancy); past its last tile a zero-record
-//   descriptor turns the padding loads into free zero loads, so the loop never
-//   branches around a load and the compiler waits only for the tile it is
-//   about to use.
+//   (the pools are read once per step).  Each wave keeps the next tile's loads
+//   in flight while it computes on the current one (the next three on grids
+//   of fewer workgroups than compute units, which are latency-bound); past its
+//   last tile a zero-record descriptor turns the padding loads into free zero
+//   loads, so the loop never branches around a load and the compiler waits
+//   only for the tile it is about to use.
 // * Partitioned schedule: a grid of (pair, partition) workgroups of 4 waves,
 //   each wave walking every 4th tile of its partition.  Unsplit grids hand
 //   their rows to the sequences by rank of context length (longest first, or
 //   long paired with short on each compute unit when the whole grid is
 //   resident), so no compute unit is left with the longest work at the end.
+//   Split grids read a partition that neighbouring sequences fill with the
+//   same blocks (a shared prefix) once, for all of them.
 // * Stream-K schedule (few long contexts): the tiles of all pairs, in
 //   (sequence, head, tile) order, are cut into one equal contiguous range per
 //   wave of a persistent grid (a few workgroups per CU), so every wave streams
@@ -43,8 +48,11 @@
 //   placed in the two halves of each lane's eight k values against the same
 //   four V values twice, so the PV product keeps ~16 significant bits of P at
 //   one MFMA per accumulator.
-// * MHA path (1 or 2 q heads per KV head): fp32 FMAs on the same loads,
-//   cross-lane sums with wave shuffles.
+// * MHA path (1 or 2 q heads per KV head, unsplit): fp32 FMAs on the same
+//   loads, cross-lane sums with wave shuffles.
+// * Several new tokens per sequence: MFMA columns are (new token, query head)
+//   pairs, causal among the new tokens, whose K/V are read from the inputs
+//   and stored to their slots after the cached context has been read.
 // * The softmax reference max is raised lazily: only when a tile's max
 //   exceeds it by more than 2^8 in probability, so the accumulator rescale
 //   runs on a handful of tiles instead of every tile.  Numerator and
@@ -1562,8 +1570,8 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
     app_v = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
   }
   auto append = [&]() {
-    uint16_t* kc = const_cast<uint16_t*>(p.k_cache);
-    uint16_t* vc = const_cast<uint16_t*>(p.v_cache);
+    uint16_t* kc = mp.k_store;
+    uint16_t* vc = mp.v_store;
     if (int(threadIdx.x) < staged && app_slot >= 0 && app_slot < mp.num_slots)
       write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, app_slot, kvh, threadIdx.x % (D / 8), app_k, app_v);
     for (int u = threadIdx.x + staged; u < units; u += kThreads) {
