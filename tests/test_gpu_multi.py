@@ -161,3 +161,27 @@ def test_multi_debug_contracts():
             assert e.value.code == pa.PA_ERR_CONTRACT, kw
     finally:
         pa.set_debug(old)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_multi_random_batches(seed):
+    """Seeded random batches: geometry (grouping 1..16, D, B), cached lengths
+    (0 .. 700) and new-token counts (0 .. 40, so one or two column sets and
+    several new tiles), max_query_len with slack; pools bit-exact and every row
+    against the oracle."""
+    rng = np.random.default_rng(4000 + seed)
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    b = int(rng.choice([8, 16, 32]))
+    S = int(rng.integers(1, 7))
+    old = rng.integers(0, 700, size=S).tolist()
+    new = rng.integers(0, 41, size=S).tolist()
+    new = [max(n, 1 if o == 0 else 0) for o, n in zip(old, new)]  # no empty sequences
+    w = workloads.multi_query_workload(5000 + seed, old, new, num_q_heads=g * hkv, num_kv_heads=hkv,
+                                       head_dim=d, block_size=b, name=f"random{seed}")
+    print(f"[random{seed}] G={g} Hkv={hkv} D={d} B={b} old={old} new={new}", flush=True)
+    kst, vst, ref = oracle_multi(w)
+    got, dw = run_multi(w, out_f32=True, max_query_len=max(new) + int(rng.integers(0, 5)))
+    check_pools(w, dw, kst, vst)
+    assert_close(got, ref, f"random{seed}")

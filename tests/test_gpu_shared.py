@@ -83,3 +83,34 @@ def test_shared_partitions_parity(case):
     assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks)
     a, r = assert_close(out.double().cpu().numpy(), ref, name)
     print(f"[{name}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_shared_random_batches(seed):
+    """Seeded random forked batches: group sizes 1..20, prompt lengths that end
+    on or inside a block, grouping 1..16, partition 256..1024."""
+    rng = np.random.default_rng(6000 + seed)
+    hkv = int(rng.choice([1, 2, 4]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    b = int(rng.choice([8, 16, 32]))
+    part = int(rng.choice([256, 512, 1024]))
+    groups = rng.integers(1, 21, size=int(rng.integers(1, 4))).tolist()
+    prompt = int(rng.choice([part, 2 * part, part + 37, 3 * part // 2]))
+    w = shared_workload(f"shared{seed}", 7000 + seed, groups, prompt, 300, hq=g * hkv, hkv=hkv, d=d, b=b)
+    print(f"[shared{seed}] G={g} Hkv={hkv} D={d} B={b} groups={groups} prompt={prompt} part={part}", flush=True)
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+    dw = dev.upload(w)
+    kst, vst, ref = oracle_step(w)
+    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies)
+    pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
+    maxlen = w.table_width * w.block_size
+    nb = pa.workspace_bytes(w.num_seqs, g * hkv, hkv, d, maxlen, part)
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size,
+                 partition_tokens=part, workspace=ws)
+    torch.cuda.synchronize()
+    assert_close(out.double().cpu().numpy(), ref, f"shared{seed}")
