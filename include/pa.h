@@ -316,7 +316,9 @@ int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, con
  * no cached position read by the call (t < L_s - n_s of any sequence) lies in
  * a slot it writes.  Rows outside every sequence's range are not written; a
  * sequence's rows past its context length (n_s > L_s) are written as zeros.
- * S == 0, T == 0 or max_query_len == 0 is a no-op.
+ * S == 0, T == 0 or max_query_len == 0 is a no-op.  With few sequences the
+ * cached context is split into partitions joined by a log-sum-exp combine, in
+ * the library-owned workspace of pa_decode (same growth and threading rules).
  */
 int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
                     const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,

@@ -783,6 +783,25 @@ PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tenso
   if ((rc = multi_params(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
                          context_lens, g, scale, max_query_len, &m)) != PA_OK)
     return rc;
+  // Split the cached context when the grid would leave the GPU half empty:
+  // partitions (multiples of 256 tokens, at least 512) so that the
+  // workgroups cover it about twice; the pieces go to the library workspace.
+  const int64_t pairs = S * g.kv_heads * m.col_groups, max_len = W * g.block_size;
+  if (pairs < kFullGpuPairs) {
+    const int64_t want = (kFullGpuPairs + pairs - 1) / pairs;
+    int64_t part = std::max<int64_t>(512, ((max_len + want - 1) / want + 255) / 256 * 256);
+    while ((max_len + part - 1) / part > 65535) part *= 2;
+    if (part < max_len) {
+      const int64_t parts = (max_len + part - 1) / part;
+      const pa::WorkspaceLayout wl = pa::workspace_layout(T, Hq, D, parts);
+      void* ws = nullptr;
+      if ((rc = owned_workspace(wl.total, stream, &ws)) != PA_OK) return rc;
+      m.d.part_tokens = int(part);
+      m.d.max_parts = int(parts);
+      m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
+      m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
+    }
+  }
   int cus = 0;
   if ((rc = device_cus(&cus)) != PA_OK) return rc;
   const pa::LaunchCtx ctx{stream, nullptr, nullptr, cus};

@@ -1111,6 +1111,12 @@ __device__ __forceinline__ void mfma_finish(const DecodeParams& p, Smem<D>& sm, 
   finish_partition<D>(p, sm, s, h0, ncols, part, nparts);
 }
 
+// Partitions of a multi-token sequence with L_old cached tokens: the new
+// tokens join the last (at least one partition, also with nothing cached).
+__device__ __forceinline__ int multi_parts(const DecodeParams& p, int L_old) {
+  return max(1, min((L_old + p.part_tokens - 1) / p.part_tokens, p.max_parts));
+}
+
 // Partitions of sequence s that this launch covers (clamping keeps the
 // partition count consistent with the grid for over-long contexts).
 __device__ __forceinline__ int partitions(const DecodeParams& p, int L) {
@@ -1532,8 +1538,13 @@ __device__ __forceinline__ void mfma_tile_causal(MfmaAcc<D>& a, const u32x4 (&q)
 
 // A workgroup computes NS sets of 16 columns against each tile it loads, so
 // a (sequence, KV head) with up to 16 * NS columns reads its context once.
-template <int D, int BS, int NS>
-__global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode_multi(MultiParams mp) {
+// Split: the cached context is cut into partitions (grid z), whose pieces the
+// combine kernel joins; the unsplit kernel carries none of that (at D = 128,
+// B = 16 and one column set its registers leave room for a third workgroup
+// per compute unit, which the split kernel's do not).
+template <int D, int BS, int NS, bool Split>
+__global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2))
+void decode_multi(MultiParams mp) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
   const DecodeParams& p = mp.d;
@@ -1552,13 +1563,21 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
   const int L = clamp_len(p, p.context_lens[s]);
   const int n = min(min(r1 - r0, L), mp.max_query_len);
   const int L_old = L - n;
+  // split schedule: partition `part` of the cached tokens; the new tokens
+  // belong to the last partition, whose workgroups also append them
+  const int part = Split ? int(blockIdx.z) : 0;
+  const int nparts = Split ? multi_parts(p, L_old) : 1;
+  if (part >= nparts) return;  // workgroup-uniform
+  const bool last = part == nparts - 1;
+  const int t0 = Split ? part * p.part_tokens : 0;
+  const int t1 = Split ? min(L_old, t0 + p.part_tokens) : L_old;
 
   // The column-group-0 workgroup appends this head's new tokens: its loads
   // are issued first and its pool stores come after the walk, since pool
   // stores ahead of it would hold the walk's pool loads back (loads are not
   // moved across stores that may alias them).  One 16-byte piece per thread
   // here; pieces past the first kThreads are copied at the end.
-  const int units = cg == 0 ? n * (D / 8) : 0;
+  const int units = cg == 0 && last ? n * (D / 8) : 0;
   const int staged = min(units, kThreads);
   u32x4 app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
   int64_t app_slot = -1;
@@ -1584,7 +1603,7 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
       write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, slot, kvh, piece, kv, vv);
     }
   };
-  if (cg == 0) {  // rows past the context (a sequence with no tokens) read as empty: zeros
+  if (cg == 0 && part == 0) {  // rows past the context (a sequence with no tokens) read as empty: zeros
     const int rows = min(r1 - r0, mp.max_query_len);
     for (int idx = threadIdx.x; idx < (rows - n) * G * D; idx += kThreads) {
       const int i = idx / (G * D);
@@ -1600,7 +1619,7 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
   }
 
   const auto row = table_row(p, s, BS);
-  const TableCache first = fetch_table<BS>(row, 0, wave, 0, lane);
+  const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
   // column set cs: columns col0 + 16 cs + r; columns past the last query
   // compute with a zero query (never stored) and see every new token
   u32x4 q[NS][NC];
@@ -1620,13 +1639,13 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
   MfmaAcc<D> acc[NS];
 #pragma unroll
   for (int cs = 0; cs < NS; ++cs) mfma_reset(acc[cs]);
-  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, 0, L_old, wave, lane,
+  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
                                            [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-    mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, L_old, lane, kt, vt);
+    mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
   });
-  // the new tiles continue the cached tiles' round robin over the waves
-  const int old_tiles = (L_old + 15) >> 4;
-  for (int u = (wave + kWaves - old_tiles % kWaves) % kWaves; 16 * u < n; u += kWaves) {
+  // the new tiles (last partition) continue the cached tiles' round robin over the waves
+  const int old_tiles = (t1 - t0 + 15) >> 4;
+  for (int u = (wave + kWaves - old_tiles % kWaves) % kWaves; last && 16 * u < n; u += kWaves) {
     u32x4 kt[NC], vt[NC];
     load_new_tile<D>(mp, r0, n, u, kvh, lane, kt, vt);
 #pragma unroll
@@ -1674,8 +1693,40 @@ __global__ __launch_bounds__(kThreads, (BS == 8 && NS == 2 ? 1 : 2)) void decode
       }
       const int cc = cbase + col;
       const int i = cc / G;
-      store_out(p, r0 + i, kvh * G + (cc - i * G), d, lsum > 0.f ? o / lsum : 0.f);
+      const int h = kvh * G + (cc - i * G);
+      if (!Split || nparts <= 1) {
+        store_out(p, r0 + i, h, d, lsum > 0.f ? o / lsum : 0.f);
+      } else {  // this partition's piece of row r0 + i for the combine
+        const size_t wrow = (size_t(r0 + i) * p.num_q_heads + h) * p.max_parts + part;
+        p.ws_o[wrow * D + d] = lsum > 0.f ? o / lsum : 0.f;
+        if (d == 0) {
+          p.ws_ml[wrow * 2 + 0] = M;
+          p.ws_ml[wrow * 2 + 1] = lsum;
+        }
+      }
     }
+  }
+}
+
+// Pieces of each new token's row, combined in ascending token order.  One
+// thread per (head, dim) of a sequence, looping over its rows.
+template <int D>
+__global__ __launch_bounds__(256) void combine_rows(MultiParams mp) {
+  const DecodeParams& p = mp.d;
+  const int s = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= p.num_q_heads * D) return;
+  const int r0 = mp.query_start ? min(max(mp.query_start[s], 0), mp.num_rows) : min(s, mp.num_rows);
+  const int r1 = mp.query_start ? min(max(mp.query_start[s + 1], r0), mp.num_rows) : min(s + 1, mp.num_rows);
+  const int L = clamp_len(p, p.context_lens[s]);
+  const int n = min(min(r1 - r0, L), mp.max_query_len);
+  const int nparts = multi_parts(p, L - n);
+  if (nparts <= 1) return;  // the kernel wrote these rows directly
+  const int h = idx / D;
+  const int d = idx - h * D;
+  for (int i = 0; i < n; ++i) {
+    const size_t row0 = (size_t(r0 + i) * p.num_q_heads + h) * p.max_parts;
+    store_out(p, r0 + i, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
   }
 }
 
@@ -1884,23 +1935,34 @@ hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCt
 template <typename K>
 hipError_t launch_multi_k(K kernel, MultiParams p, const LaunchCtx& c) {
   const int row_wgs = p.d.num_kv_heads * p.col_groups;
-  p.d.rank_split = rank_split_for(kernel, p.d, row_wgs, c);
-  return launch_main(kernel, dim3(row_wgs, p.d.num_seqs), dim3(kThreads), c, p);
+  p.d.rank_split = p.d.max_parts == 1 ? rank_split_for(kernel, p.d, row_wgs, c) : p.d.num_seqs;
+  return launch_main(kernel, dim3(row_wgs, p.d.num_seqs, p.d.max_parts), dim3(kThreads), c, p);
 }
 
-template <int D, int NS>
-hipError_t launch_multi_ns(const MultiParams& p, int block_size, const LaunchCtx& c) {
+template <int D, int NS, bool Split>
+hipError_t launch_multi_split(const MultiParams& p, int block_size, const LaunchCtx& c) {
   switch (block_size) {
-    case 8: return launch_multi_k(decode_multi<D, 8, NS>, p, c);
-    case 16: return launch_multi_k(decode_multi<D, 16, NS>, p, c);
-    case 32: return launch_multi_k(decode_multi<D, 32, NS>, p, c);
+    case 8: return launch_multi_k(decode_multi<D, 8, NS, Split>, p, c);
+    case 16: return launch_multi_k(decode_multi<D, 16, NS, Split>, p, c);
+    case 32: return launch_multi_k(decode_multi<D, 32, NS, Split>, p, c);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int D, int NS>
+hipError_t launch_multi_ns(const MultiParams& p, int block_size, const LaunchCtx& c) {
+  return p.d.max_parts > 1 ? launch_multi_split<D, NS, true>(p, block_size, c)
+                           : launch_multi_split<D, NS, false>(p, block_size, c);
+}
+
 template <int D>
 hipError_t launch_multi_d(const MultiParams& p, int block_size, const LaunchCtx& c) {
-  return p.col_sets == 1 ? launch_multi_ns<D, 1>(p, block_size, c) : launch_multi_ns<D, 2>(p, block_size, c);
+  const hipError_t e =
+      p.col_sets == 1 ? launch_multi_ns<D, 1>(p, block_size, c) : launch_multi_ns<D, 2>(p, block_size, c);
+  if (e != hipSuccess || p.d.max_parts <= 1) return e;
+  const dim3 cgrid((p.d.num_q_heads * D + 255) / 256, p.d.num_seqs);
+  hipLaunchKernelGGL((combine_rows<D>), cgrid, dim3(256), 0, c.stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_multi(const MultiParams& p, int head_dim, int block_size, const LaunchCtx& c) {

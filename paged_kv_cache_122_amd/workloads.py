@@ -376,6 +376,14 @@ def llama3_8b_verify5():
                                 width=blocks_for_tokens(2048 + 5, 16))
 
 
+def long32k_verify5():
+    """Speculative verification over long contexts: 8 seqs x 32,763 cached tokens,
+    each verifying 5 drafted tokens (32 q / 8 kv heads, D 128, B 16)."""
+    seed = 1010
+    return multi_query_workload(seed, [32768 - 5] * 8, [5] * 8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                block_size=16, name="long32k_verify5_b16")
+
+
 def long_context(block_size):
     """8 seqs x 32,768 tokens, 32 q / 8 kv heads, D 128, B in {8, 16, 32},
     random placement, pool needed + 10 %."""
@@ -401,6 +409,7 @@ CONFIGS = {
     "long32k_b32": lambda: long_context(32),
     "opt13b_cow_fork_b128": opt13b_cow_fork,
     "llama3_8b_verify5_b64": llama3_8b_verify5,
+    "long32k_verify5_b16": long32k_verify5,
 }
 
 

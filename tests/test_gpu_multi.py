@@ -185,3 +185,37 @@ def test_multi_random_batches(seed):
     got, dw = run_multi(w, out_f32=True, max_query_len=max(new) + int(rng.integers(0, 5)))
     check_pools(w, dw, kst, vst)
     assert_close(got, ref, f"random{seed}")
+
+
+def test_multi_split_long_contexts():
+    """Few sequences with long contexts: the cached context is split into
+    partitions whose pieces a combine kernel joins.  The 32k-token verification
+    batch (8 x 5 drafted tokens), every row against the oracle."""
+    w = workloads.make("long32k_verify5_b16")
+    print(f"[long32k_verify5] T={w.q.shape[0]}", flush=True)
+    kst, vst, ref = oracle_multi(w)
+    got, dw = run_multi(w, out_f32=True)
+    check_pools(w, dw, kst, vst)
+    a, r = assert_close(got, ref, "long32k_verify5")
+    print(f"[long32k_verify5] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+
+
+# small batches of long-ish contexts, so that the schedule splits (partitions of
+# 512 tokens): nothing cached, no new token, cached lengths on partition
+# boundaries, one and two column sets, B 8 / 32, D 64
+SPLIT = [
+    ("split_mixed", [3000, 2559, 0, 1024, 700], [1, 7, 20, 0, 3], 8, 2, 128, 16),
+    ("split_b8_d64_mha", [5000, 1200], [2, 33], 4, 4, 64, 8),
+    ("split_b32_gqa8", [4100, 4096], [16, 1], 16, 2, 128, 32),
+]
+
+
+@pytest.mark.parametrize("name,old,new,hq,hkv,d,b", SPLIT, ids=[c[0] for c in SPLIT])
+def test_multi_split_edges(name, old, new, hq, hkv, d, b):
+    w = workloads.multi_query_workload(8000 + len(name), old, new, num_q_heads=hq, num_kv_heads=hkv,
+                                       head_dim=d, block_size=b, name=name)
+    print(f"[{name}] old={old} new={new}", flush=True)
+    kst, vst, ref = oracle_multi(w)
+    got, dw = run_multi(w, out_f32=True)
+    check_pools(w, dw, kst, vst)
+    assert_close(got, ref, name)
