@@ -17,7 +17,8 @@ that the GPU stamps at its start and end, against 8 TB/s.  ``two_call_step``
 times the same step as pa_cache_append + pa_decode.  ``paging_control``
 times the same decode over an unpaged copy of the cache; ``multi_query`` times
 pa_decode_multi (several new tokens per sequence: speculative verification)
-on the Llama-3-8B-shaped batch with 5 drafted tokens per sequence.  ``cpu_baseline`` is the fp64 oracle on a bounded
+on the Llama-3-8B-shaped batch with 5 drafted tokens per sequence, and
+``multi_query_long`` on 8 sequences of 32k tokens with 5 drafted tokens each.  ``cpu_baseline`` is the fp64 oracle on a bounded
 sample of the same workload, on this host's CPU.
 """
 
@@ -43,14 +44,18 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "8cffc51e7da12e524f841c72117505c407193202524e02ca435eb7686ae08e99",
-    # the step's one launch: FETCH_SIZE 134433.6 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.68 %
-    "llama3_8b_b64 decode_multi<128,16,1>": {"fetch_bytes": 275303450, "write_bytes": 1310859,
-                                             "mfma_busy_pct": 4.68},
-    # the verification batch: FETCH_SIZE 141217.2 KiB x 1.9999, WRITE_SIZE 4353.7 KiB x 1.0; MfmaUtil 8.92 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2>": {"fetch_bytes": 289195580, "write_bytes": 4458217,
-                                                     "mfma_busy_pct": 8.92},
+    "sources_sha256": "82241145f750b13071a26ccbb0ce898343faad0a290d26930a08f474209f1f09",
+    # the step's one launch: FETCH_SIZE 134436.6 KiB x 1.9999, WRITE_SIZE 1280.0 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.70 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 275307621, "write_bytes": 1310752,
+                                                   "mfma_busy_pct": 4.70},
+    # the verification batch: FETCH_SIZE 141226.9 KiB x 1.9999, WRITE_SIZE 4354.8 KiB x 1.0; MfmaUtil 9.12 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 289213176, "write_bytes": 4459310,
+                                                           "mfma_busy_pct": 9.12},
+    # long-context verification (split): FETCH_SIZE 524913.7 KiB x 1.9999, WRITE_SIZE 5426.8 KiB x 1.0;
+    # MfmaUtil 11.51 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074950617, "write_bytes": 5557079,
+                                                        "mfma_busy_pct": 11.51},
 }
 
 
@@ -167,14 +172,16 @@ def decode_kernels(w, part, cus):
     return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
 
 
-MULTI_CONFIG = "llama3_8b_verify5_b64"
+MULTI_CONFIGS = (("llama3_8b_verify5_b64", "decode_multi<128,16,2,false>"),
+                 ("long32k_verify5_b16", "decode_multi<128,16,2,true>"))
 
 
-def multi_query_leg(steps, warmup, tev, stream, flush):
-    """pa_decode_multi on the verification batch (64 sequences, 5 drafted tokens
-    each): the append of the drafted tokens and their causal attention, one
-    launch.  Beside it, pa_decode of one token per sequence over the same pools
-    (same KV bytes).  Each call after a cache flush, timed by events around it."""
+def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
+    """pa_decode_multi on a verification batch (5 drafted tokens per sequence):
+    the append of the drafted tokens and their causal attention, one launch
+    (and a combine when the context is split).  Beside it, pa_decode of one
+    token per sequence over the same pools (same KV bytes).  Each call after a
+    cache flush, timed by events around it."""
     import numpy as np
     import torch
 
@@ -182,7 +189,7 @@ def multi_query_leg(steps, warmup, tev, stream, flush):
     from paged_kv_cache_122_amd import device as dev
     from paged_kv_cache_122_amd import workloads
 
-    w = workloads.make(MULTI_CONFIG)
+    w = workloads.make(config)
     dw = dev.upload(w, "cuda:0")
     counts = np.diff(w.query_start)
     mql = int(counts.max())
@@ -236,8 +243,9 @@ def multi_query_leg(steps, warmup, tev, stream, flush):
         "algorithmic_bytes": algo,
         "achieved_gbs": round(algo / t / 1e9, 2),
         "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(w.name, "decode_multi<128,16,2>"),
-        "mfma_busy_pct": measured_mfma(w.name, "decode_multi<128,16,2>"),
+        "kernel": kernel,
+        "traffic": measured_traffic(w.name, kernel),
+        "mfma_busy_pct": measured_mfma(w.name, kernel),
         "tokens_per_s": round(T / t, 1),
         "single_token_decode_same_pools_call_ms": round(mean(single_ms), 5),
         "note": "pa_decode_multi (append fused, causal over cached + drafted tokens) vs pa_decode of "
@@ -251,7 +259,7 @@ def fused_step(w, part):
     MFMA schedule), and that kernel's name."""
     g = w.num_q_heads // w.num_kv_heads
     unsplit = part == -1 or part >= w.block_tables.shape[1] * w.block_size
-    return g >= 3 and unsplit, f"decode_multi<{w.head_dim},{w.block_size},{2 if g > 16 else 1}>"
+    return g >= 3 and unsplit, f"decode_multi<{w.head_dim},{w.block_size},{2 if g > 16 else 1},false>"
 
 
 def percentile(xs, q):
@@ -455,9 +463,9 @@ def main():
             unsplit_ms = [tev.elapsed_ms(c, d) for _, _, c, d in cev]
             del kc, vc, out_c
 
-        multi = None
+        multi = []
         if not args.no_multi:
-            multi = multi_query_leg(args.steps, args.warmup, tev, stream, flush)
+            multi = [multi_query_leg(c, k, args.steps, args.warmup, tev, stream, flush) for c, k in MULTI_CONFIGS]
 
         tev.close()
 
@@ -553,7 +561,8 @@ def main():
                 "pa_decode (the append kernel, then the decode schedule), flushed, events around the calls",
     }
     if multi:
-        line["multi_query"] = multi
+        line["multi_query"] = multi[0]
+        line["multi_query_long"] = multi[1]
     if hot_ms:
         line["unflushed_step_ms"] = {"mean": round(mean(hot_ms), 5),
                                      "p50": round(percentile(hot_ms, 50), 5),
