@@ -44,18 +44,18 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "82241145f750b13071a26ccbb0ce898343faad0a290d26930a08f474209f1f09",
-    # the step's one launch: FETCH_SIZE 134436.6 KiB x 1.9999, WRITE_SIZE 1280.0 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.70 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 275307621, "write_bytes": 1310752,
-                                                   "mfma_busy_pct": 4.70},
-    # the verification batch: FETCH_SIZE 141226.9 KiB x 1.9999, WRITE_SIZE 4354.8 KiB x 1.0; MfmaUtil 9.12 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 289213176, "write_bytes": 4459310,
-                                                           "mfma_busy_pct": 9.12},
-    # long-context verification (split): FETCH_SIZE 524913.7 KiB x 1.9999, WRITE_SIZE 5426.8 KiB x 1.0;
-    # MfmaUtil 11.51 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074950617, "write_bytes": 5557079,
-                                                        "mfma_busy_pct": 11.51},
+    "sources_sha256": "9c32feba3a559d78d9c1a3662ac9f0df8e1ac4619baa8ae1e9440c7c083e85da",
+    # the step's one launch: FETCH_SIZE 133775.6 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.63 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273958745, "write_bytes": 1310832,
+                                                   "mfma_busy_pct": 4.63},
+    # the verification batch: FETCH_SIZE 140611.9 KiB x 1.9999, WRITE_SIZE 4353.7 KiB x 1.0; MfmaUtil 9.04 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287958803, "write_bytes": 4458158,
+                                                           "mfma_busy_pct": 9.04},
+    # long-context verification (split): FETCH_SIZE 524888.0 KiB x 1.9999, WRITE_SIZE 5426.7 KiB x 1.0;
+    # MfmaUtil 11.50 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074917373, "write_bytes": 5556969,
+                                                        "mfma_busy_pct": 11.50},
 }
 
 

@@ -204,12 +204,18 @@ __device__ __forceinline__ LaneOffsets<D, BS> lane_offsets(int lane) {
 }
 
 // Load the tile starting at token ts of KV head kvh whose physical block(s)
-// are phys0 / phys1, or zeros without any memory access when !valid.
+// are phys0 / phys1, or zeros without any memory access when !valid.  Lanes
+// whose tokens (K row, or first token of the V quad) lie at or past t1 load
+// zeros through an out-of-range offset, so the last tile of a context reads
+// only its live rows.
 template <int D, int BS>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, int kvh, int phys0, int phys1,
-                                          int ts, bool valid, const LaneOffsets<D, BS>& lo,
+                                          int ts, int t1, bool valid, const LaneOffsets<D, BS>& lo,
                                           u32x4 (&k)[D / 32], u32x4 (&v)[D / 32]) {
   constexpr int kTileBytes = BS * D * 2;
+  const int lane = __lane_id();
+  const uint32_t kx = ts + (lane & 15) >= t1 ? kOutOfRange : 0u;
+  const uint32_t vx = ts + 4 * (lane >> 4) >= t1 ? kOutOfRange : 0u;
   const size_t blk_elems = size_t(p.num_kv_heads) * BS * D;
   const size_t head_off = size_t(kvh) * BS * D;
   const int bytes = valid ? kTileBytes : 0;
@@ -220,18 +226,18 @@ __device__ __forceinline__ void load_tile(const DecodeParams& p, int kvh, int ph
     const auto v1 = make_rsrc(p.v_cache + size_t(phys1) * blk_elems + head_off, bytes);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      k[c] = stream_load16(k0, lo.k0 + c * 4 * BS * 16) | stream_load16(k1, lo.k1 + c * 4 * BS * 16);
+      k[c] = stream_load16(k0, (lo.k0 + c * 4 * BS * 16) | kx) | stream_load16(k1, (lo.k1 + c * 4 * BS * 16) | kx);
 #pragma unroll
     for (int c = 0; c < D / 32; ++c)
-      v[c] = stream_load16(v0, lo.v0 + c * 256) | stream_load16(v1, lo.v1 + c * 256);
+      v[c] = stream_load16(v0, (lo.v0 + c * 256) | vx) | stream_load16(v1, (lo.v1 + c * 256) | vx);
   } else {
     // B = 32 holds two tiles per block: the second half starts 16 tokens in
     const uint32_t khalf = BS == 32 ? uint32_t(((ts >> 4) & 1) * 16 * 8 * 2) : 0u;
     const uint32_t vhalf = BS == 32 ? uint32_t(((ts >> 4) & 1) * 4 * D * 4 * 2) : 0u;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) k[c] = stream_load16(k0, lo.k0 + khalf + c * 4 * BS * 16);
+    for (int c = 0; c < D / 32; ++c) k[c] = stream_load16(k0, (lo.k0 + khalf + c * 4 * BS * 16) | kx);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) v[c] = stream_load16(v0, lo.v0 + vhalf + c * 256);
+    for (int c = 0; c < D / 32; ++c) v[c] = stream_load16(v0, (lo.v0 + vhalf + c * 256) | vx);
   }
 }
 
@@ -735,7 +741,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_sk(DecodeParams p, Strea
       int kvh, h0, ncols;
       head_span(p, u.hg, kvh, h0, ncols);
       const bool opens = j < m && (u.t == 0 || base + jj == rg.T0);
-      load_tile<D, BS>(p, kvh, u.b0, u.b1, 16 * u.t, j < m, lo, kt, vt);
+      load_tile<D, BS>(p, kvh, u.b0, u.b1, 16 * u.t, u.L, j < m, lo, kt, vt);
       load_q_operand<D>(p, u.s, u.hg, opens, lane, qt);
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -800,7 +806,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_sk(DecodeParams p, Strea
     auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
       const int jj = min(j, m - 1);
       const Uniform u = read_meta(meta, jj);
-      load_tile<D, BS>(p, u.hg, u.b0, u.b1, 16 * u.t, j < m, lo, kt, vt);
+      load_tile<D, BS>(p, u.hg, u.b0, u.b1, 16 * u.t, u.L, j < m, lo, kt, vt);
       __builtin_amdgcn_sched_barrier(0);
     };
     auto compute = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
@@ -976,7 +982,7 @@ __device__ __forceinline__ void walk_tiles(const DecodeParams& p, __amdgpu_buffe
         b1 = __builtin_amdgcn_readlane(tc.e1, jj);
         b1 = start(jj) + 8 < t1 ? b1 : b0;
       }
-      load_tile<D, BS>(p, kvh, b0, b1, start(jj), j < m, lo, kt, vt);
+      load_tile<D, BS>(p, kvh, b0, b1, start(jj), t1, j < m, lo, kt, vt);
       __builtin_amdgcn_sched_barrier(0);
     };
     // The trip count is rounded up to whole rounds of S tiles: the extra tiles
@@ -1366,14 +1372,18 @@ __device__ __forceinline__ void walk_contiguous(const DecodeParams& p, int s, in
     const auto k_r = valid ? rk : rz;
     const auto v_r = valid ? rv : rz;
     const int toff = valid ? (wave + kWaves * j) * kTileBytes : 0;
+    // rows past t1 load zeros, as in the paged walk
+    const int ts = kTileTokens * (wave + kWaves * j);
+    const uint32_t kx = ts + (lane & 15) >= t1 ? kOutOfRange : 0u;
+    const uint32_t vx = ts + 4 * (lane >> 4) >= t1 ? kOutOfRange : 0u;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       kt[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            k_r, int(lo.k0 + c * 4 * kTileTokens * 16), toff, kStreamingLoad));
+                                            k_r, int((lo.k0 + c * 4 * kTileTokens * 16) | kx), toff, kStreamingLoad));
 #pragma unroll
     for (int c = 0; c < NC; ++c)
       vt[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                            v_r, int(lo.v0 + c * 256), toff, kStreamingLoad));
+                                            v_r, int((lo.v0 + c * 256) | vx), toff, kStreamingLoad));
     __builtin_amdgcn_sched_barrier(0);
   };
   const int rounds = (n + S - 1) / S;
