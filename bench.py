@@ -44,18 +44,18 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "9c32feba3a559d78d9c1a3662ac9f0df8e1ac4619baa8ae1e9440c7c083e85da",
-    # the step's one launch: FETCH_SIZE 133775.6 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.63 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273958745, "write_bytes": 1310832,
-                                                   "mfma_busy_pct": 4.63},
-    # the verification batch: FETCH_SIZE 140611.9 KiB x 1.9999, WRITE_SIZE 4353.7 KiB x 1.0; MfmaUtil 9.04 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287958803, "write_bytes": 4458158,
-                                                           "mfma_busy_pct": 9.04},
-    # long-context verification (split): FETCH_SIZE 524888.0 KiB x 1.9999, WRITE_SIZE 5426.7 KiB x 1.0;
-    # MfmaUtil 11.50 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074917373, "write_bytes": 5556969,
-                                                        "mfma_busy_pct": 11.50},
+    "sources_sha256": "417c0057640aaf91b8b27c77c23cc50c08be83817039e17d75f48627c7de0bfb",
+    # the step's one launch: FETCH_SIZE 133783.6 KiB x 1.9999, WRITE_SIZE 1280.0 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.61 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273970292, "write_bytes": 1310741,
+                                                   "mfma_busy_pct": 4.61},
+    # the verification batch: FETCH_SIZE 140626.4 KiB x 1.9999, WRITE_SIZE 4353.9 KiB x 1.0; MfmaUtil 8.58 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287983335, "write_bytes": 4458345,
+                                                           "mfma_busy_pct": 8.58},
+    # long-context verification (split): FETCH_SIZE 524893.6 KiB x 1.9999, WRITE_SIZE 5426.5 KiB x 1.0;
+    # MfmaUtil 11.49 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074909379, "write_bytes": 5556754,
+                                                        "mfma_busy_pct": 11.49},
 }
 
 
@@ -328,6 +328,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from paged_kv_cache_122_amd import _lib as pa
@@ -373,9 +374,14 @@ def main():
     ws_bytes = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, 0)
     ws = pa.alloc_workspace(ws_bytes, "cuda:0") if ws_bytes else None
 
+    # the host copy of the lengths that a serving engine keeps (it computes
+    # them); unsplit schedules rank the sequences from it on the host
+    host_lens = np.asarray(w.context_lens, dtype=np.int32)
+
     def decode(kernel_events=None):
         pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                     w.block_size, workspace=ws, kernel_events=kernel_events, stream=stream)
+                     w.block_size, workspace=ws, kernel_events=kernel_events, host_context_lens=host_lens,
+                     stream=stream)
 
     def step(kernel_events=None):
         # the step's copy-on-write copies (if any), then append + decode in one call
@@ -383,7 +389,7 @@ def main():
             pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
         pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
                          dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=ws,
-                         kernel_events=kernel_events, stream=stream)
+                         kernel_events=kernel_events, host_context_lens=host_lens, stream=stream)
 
     tev = TimingEvents()
     E = tev.create
@@ -512,7 +518,8 @@ def main():
             "step": ("pa_copy_blocks (copy-on-write) + " if has_copies else "")
                     + "pa_append_decode (" + ("one launch: the new token stored and attended"
                                               if fused else "append kernel, then the decode schedule")
-                    + "), caches flushed before each step",
+                    + "), with a host copy of the lengths (the sequences ranked on the host), "
+                    "caches flushed before each step",
             "cow_copies": int(w.copies.shape[0]),
             "schedule": schedule,
         },

@@ -185,6 +185,17 @@ typedef struct {
   hipEvent_t kernel_stop;    /* they then record the start and the end of the
                                 main decode kernel alone (not the combine), as
                                 timed by the GPU (hipExtLaunchKernel) */
+  const int32_t* host_context_lens; /* NULL, or HOST memory holding a copy of
+                                context_lens ([num_seqs] int32), read during
+                                the call only.  Unsplit schedules then rank the
+                                sequences on the host and pass the order with
+                                the kernel's arguments, instead of every
+                                workgroup loading and ranking the lengths
+                                first.  It steers only which workgroup takes
+                                which sequence: results are the same with or
+                                without it, and with lengths that differ from
+                                the device's (a contract violation, reported
+                                as PA_ERR_CONTRACT under pa_set_debug(1)) */
 } pa_decode_opts;
 
 /* Bytes of workspace pa_decode_ex needs for these sizes (0 when nothing is split). */

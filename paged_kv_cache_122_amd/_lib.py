@@ -10,6 +10,8 @@ runtime torch already loaded (both carry the soname libamdhip64.so.7).
 import ctypes
 import os
 
+import numpy as np
+
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
@@ -35,7 +37,7 @@ class PaDecodeOpts(ctypes.Structure):
     _fields_ = [("partition_tokens", ctypes.c_int32), ("path", ctypes.c_int32),
                 ("max_context_len", ctypes.c_int64), ("workgroups_per_cu", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("kernel_start", ctypes.c_void_p),
-                ("kernel_stop", ctypes.c_void_p)]
+                ("kernel_stop", ctypes.c_void_p), ("host_context_lens", ctypes.c_void_p)]
 
 
 class PaError(RuntimeError):
@@ -210,25 +212,47 @@ def _event_handle(e):
     return h
 
 
+def _host_lens(host_context_lens, context_lens):
+    """A host copy of context_lens as a contiguous int32 array (kept alive by the caller
+    for the call), or None."""
+    if host_context_lens is None:
+        return None
+    if isinstance(host_context_lens, torch.Tensor):
+        if host_context_lens.device.type != "cpu":
+            raise ValueError("host_context_lens must live in host memory")
+        host_context_lens = host_context_lens.numpy()
+    a = np.ascontiguousarray(host_context_lens, dtype=np.int32)
+    if a.ndim != 1 or a.shape[0] != context_lens.shape[0]:
+        raise ValueError(f"host_context_lens: {context_lens.shape[0]} entries expected, got shape {a.shape}")
+    return a
+
+
+def _opts(partition_tokens, path, max_context_len, workgroups_per_cu, kernel_events, host_lens):
+    ev = (None, None)
+    if kernel_events is not None:
+        ev = tuple(_event_handle(e) for e in kernel_events)
+    return PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0,
+                        ev[0], ev[1], None if host_lens is None else host_lens.ctypes.data)
+
+
 def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, *,
               partition_tokens=0, path=0, max_context_len=0, workgroups_per_cu=0, workspace=None,
-              kernel_events=None, stream=None):
+              kernel_events=None, host_context_lens=None, stream=None):
     """pa_decode_ex: decode with options and a caller-owned workspace.
 
     kernel_events: optional (start, stop) pair of timing events (torch.cuda.Event with
     enable_timing=True, or raw hipEvent_t handles) that then time the main decode
     kernel alone on the GPU.
+    host_context_lens: optional host copy of context_lens (numpy / list / CPU tensor);
+    unsplit schedules then rank the sequences on the host.
     """
     lib = load()
     ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),
                                            (v_cache, "v_cache"), (block_tables, "block_tables"),
                                            (context_lens, "context_lens"))]
     ds = [describe(x) for x in ts]
-    ev = (None, None)
-    if kernel_events is not None:
-        ev = tuple(_event_handle(e) for e in kernel_events)
-    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0,
-                        ev[0], ev[1])
+    hl = _host_lens(host_context_lens, context_lens)
+    opts = _opts(partition_tokens, path, max_context_len, workgroups_per_cu, kernel_events, hl)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -240,7 +264,7 @@ def decode_ex(out, q, k_cache, v_cache, block_tables, context_lens, scale, block
 
 def append_decode(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                   *, partition_tokens=0, path=0, max_context_len=0, workgroups_per_cu=0, workspace=None,
-                  kernel_events=None, stream=None):
+                  kernel_events=None, host_context_lens=None, stream=None):
     """pa_append_decode: this step's k/v [S, Hkv, D] appended at slot_mapping [S], then the
     decode of q [S, Hq, D], as one call (one launch where the schedule is unsplit MFMA)."""
     lib = load()
@@ -248,11 +272,8 @@ def append_decode(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, co
         (out, "out"), (q, "q"), (k, "k"), (v, "v"), (slot_mapping, "slot_mapping"), (k_cache, "k_cache"),
         (v_cache, "v_cache"), (block_tables, "block_tables"), (context_lens, "context_lens"))]
     ds = [describe(x) for x in ts]
-    ev = (None, None)
-    if kernel_events is not None:
-        ev = tuple(_event_handle(e) for e in kernel_events)
-    opts = PaDecodeOpts(int(partition_tokens), int(path), int(max_context_len), int(workgroups_per_cu), 0,
-                        ev[0], ev[1])
+    hl = _host_lens(host_context_lens, context_lens)
+    opts = _opts(partition_tokens, path, max_context_len, workgroups_per_cu, kernel_events, hl)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()

@@ -365,7 +365,8 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
 }
 
 int debug_check_decode(const DecodePlan& pl, const pa_tensor* block_tables,
-                       const pa_tensor* context_lens, int64_t max_len, hipStream_t stream) {
+                       const pa_tensor* context_lens, int64_t max_len, const int32_t* host_lens,
+                       hipStream_t stream) {
   std::vector<int32_t> lens, bt;
   int rc;
   if ((rc = copy_to_host(&lens, context_lens->data, size_t(pl.S), stream)) != PA_OK) return rc;
@@ -374,6 +375,9 @@ int debug_check_decode(const DecodePlan& pl, const pa_tensor* block_tables,
     return rc;
   for (int64_t s = 0; s < pl.S; ++s) {
     const int64_t L = lens[s];
+    if (host_lens && host_lens[s] != L)
+      return fail(PA_ERR_CONTRACT, "opts.host_context_lens[%lld] = %lld, but context_lens[%lld] = %lld",
+                  (long long)s, (long long)host_lens[s], (long long)s, (long long)L);
     if (L < 0 || L > pl.W * pl.B)
       return fail(PA_ERR_CONTRACT, "context_lens[%lld] = %lld outside [0, width*block_size = %lld]",
                   (long long)s, (long long)L, (long long)(pl.W * pl.B));
@@ -402,7 +406,8 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   if (pl.S == 0) return PA_OK;
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "scale must be finite");
   const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
-  if (debug && (rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK)
+  if (debug && (rc = debug_check_decode(pl, block_tables, context_lens, max_len,
+                                                   opts ? opts->host_context_lens : nullptr, stream)) != PA_OK)
     return rc;
 
   char* ws = nullptr;  // partial results of split contexts
@@ -446,7 +451,8 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   int cus = 0;
   if ((rc = device_cus(&cus)) != PA_OK) return rc;
   const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr,
-                          opts ? opts->kernel_stop : nullptr, cus};
+                          opts ? opts->kernel_stop : nullptr, cus,
+                          opts ? opts->host_context_lens : nullptr};
   hipError_t e;
   if (pl.stream) {
     pa::StreamParams sk{};
@@ -904,7 +910,8 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
   }
   const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
   if (g_debug.load()) {
-    if ((rc = debug_check_decode(pl, block_tables, context_lens, max_len, stream)) != PA_OK) return rc;
+    if ((rc = debug_check_decode(pl, block_tables, context_lens, max_len,
+                                                   opts ? opts->host_context_lens : nullptr, stream)) != PA_OK) return rc;
     std::vector<int32_t> lens, bt;
     std::vector<int64_t> slots;
     const size_t stride = size_t(block_tables->stride[0]);
@@ -937,7 +944,8 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
       return rc;
     int cus = 0;
     if ((rc = device_cus(&cus)) != PA_OK) return rc;
-    const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus};
+    const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus,
+                            opts ? opts->host_context_lens : nullptr};
     const hipError_t e = pa::launch_multi(m, int(pl.D), int(pl.B), ctx);
     if (e != hipSuccess) return hip_fail(e, "fused append + decode launch");
     return PA_OK;

@@ -50,6 +50,10 @@ struct DecodeParams {
                         // order, the rows from it on the rest from the shortest up
   float* ws_o;          // [S, Hq, max_parts, D]  normalised partial outputs
   float* ws_ml;         // [S, Hq, max_parts, 2]  (reference max in log2 units, sum)
+  // unsplit grids: the sequence of each row, ranked on the host from a host
+  // copy of context_lens (has_order != 0), else ranked by each workgroup
+  int has_order;
+  uint16_t order[kMaxRankedSeqs];
 };
 
 // stream-K schedule: plan = {tiles per wave, total tiles, -, -, prefix[S + 1]}
@@ -118,6 +122,7 @@ struct LaunchCtx {
   hipEvent_t start;
   hipEvent_t stop;
   int cus;  // compute units of the device
+  const int32_t* host_lens = nullptr;  // host copy of context_lens [S], or null
 };
 
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,

@@ -1067,6 +1067,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
 // more than kMaxRankedSeqs sequences or with table spans of 2^22 tokens or more.
 __device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
   const int S = p.num_seqs;
+  if (p.has_order) return p.order[y];  // ranked on the host: no round trip to the lengths
   if (p.max_parts > 1 || S > kMaxRankedSeqs || p.max_len >= (1 << 22)) return y;
   __shared__ uint32_t keys[kMaxRankedSeqs];
   __shared__ int pick;
@@ -1586,7 +1587,11 @@ void decode_multi(MultiParams mp) {
   // are issued first and its pool stores come after the walk, since pool
   // stores ahead of it would hold the walk's pool loads back (loads are not
   // moved across stores that may alias them).  One 16-byte piece per thread
-  // here; pieces past the first kThreads are copied at the end.
+  // here, parked in LDS during the walk (only the thread that loaded a piece
+  // reads it back, so no barrier); pieces past the first kThreads are copied
+  // at the end.
+  __shared__ u32x4 park_k[kThreads], park_v[kThreads];
+  __shared__ int64_t park_slot[kThreads];
   const int units = cg == 0 && last ? n * (D / 8) : 0;
   const int staged = min(units, kThreads);
   u32x4 app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
@@ -1598,11 +1603,11 @@ void decode_multi(MultiParams mp) {
     app_k = load16(mp.k_new + size_t(r0 + i) * mp.kn_t + size_t(kvh) * mp.kn_h + piece * 8);
     app_v = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
   }
-  auto append = [&]() {
+  auto append = [&](u32x4 k0, u32x4 v0, int64_t slot0) {
     uint16_t* kc = mp.k_store;
     uint16_t* vc = mp.v_store;
-    if (int(threadIdx.x) < staged && app_slot >= 0 && app_slot < mp.num_slots)
-      write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, app_slot, kvh, threadIdx.x % (D / 8), app_k, app_v);
+    if (int(threadIdx.x) < staged && slot0 >= 0 && slot0 < mp.num_slots)
+      write_slot_piece<D, BS>(kc, vc, p.num_kv_heads, slot0, kvh, threadIdx.x % (D / 8), k0, v0);
     for (int u = threadIdx.x + staged; u < units; u += kThreads) {
       const int i = u / (D / 8);
       const int piece = u - i * (D / 8);
@@ -1624,7 +1629,7 @@ void decode_multi(MultiParams mp) {
   const int cols = n * G;             // (query, head) columns of this KV head
   const int col0 = 16 * NS * cg;      // first column of this workgroup
   if (col0 >= cols) {                 // workgroup-uniform; column group 0 only when n == 0
-    append();
+    append(app_k, app_v, app_slot);
     return;
   }
 
@@ -1649,6 +1654,12 @@ void decode_multi(MultiParams mp) {
   MfmaAcc<D> acc[NS];
 #pragma unroll
   for (int cs = 0; cs < NS; ++cs) mfma_reset(acc[cs]);
+  // after the table and query loads, so that its wait covers the append's loads only
+  if (int(threadIdx.x) < staged) {
+    park_k[threadIdx.x] = app_k;
+    park_v[threadIdx.x] = app_v;
+    park_slot[threadIdx.x] = app_slot;
+  }
   walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
                                            [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
@@ -1662,7 +1673,11 @@ void decode_multi(MultiParams mp) {
     for (int cs = 0; cs < NS; ++cs)
       mfma_tile_causal<D>(acc[cs], q[cs], p.scale_log2, 16 * u, qi[cs], lane, kt, vt);
   }
-  append();  // every pool read of this workgroup is done
+  // every pool read of this workgroup is done
+  if (int(threadIdx.x) < staged)
+    append(park_k[threadIdx.x], park_v[threadIdx.x], park_slot[threadIdx.x]);
+  else
+    append(app_k, app_v, -1);
 
   // combine the waves set by set; column (i, g) goes to row r0 + i, head kvh * G + g
 #pragma unroll
@@ -1835,9 +1850,27 @@ int rank_split_for(K kernel, const DecodeParams& p, int row_wgs, const LaunchCtx
   return int(std::min<int64_t>(p.num_seqs, (c.cus + row_wgs - 1) / row_wgs));
 }
 
+// The same ranking as ranked_seq's, on the host from a host copy of the
+// lengths: clamped length, longest first, equal lengths by index; rows below
+// rank_split take the ranks in order, the rest from the shortest up.  The
+// order is a permutation whatever the lengths say, so lengths that differ
+// from the device's change only the placement, never a result.
+inline void fill_order(DecodeParams& p, const LaunchCtx& c) {
+  p.has_order = 0;
+  const int S = p.num_seqs;
+  if (!c.host_lens || p.max_parts > 1 || S > kMaxRankedSeqs || p.max_len >= (1 << 22)) return;
+  int idx[kMaxRankedSeqs];
+  for (int i = 0; i < S; ++i) idx[i] = i;
+  auto len = [&](int i) { return std::min(std::max(c.host_lens[i], 0), p.max_len); };
+  std::stable_sort(idx, idx + S, [&](int a, int b) { return len(a) > len(b); });
+  for (int r = 0; r < S; ++r) p.order[r < p.rank_split ? r : S - 1 - (r - p.rank_split)] = uint16_t(idx[r]);
+  p.has_order = 1;
+}
+
 template <typename K>
 hipError_t launch_rows(K kernel, DecodeParams p, int row_wgs, const LaunchCtx& c) {
   p.rank_split = p.max_parts == 1 ? rank_split_for(kernel, p, row_wgs, c) : p.num_seqs;
+  fill_order(p, c);
   return launch_main(kernel, dim3(row_wgs, p.num_seqs, p.max_parts), dim3(kThreads), c, p);
 }
 
@@ -1946,6 +1979,7 @@ template <typename K>
 hipError_t launch_multi_k(K kernel, MultiParams p, const LaunchCtx& c) {
   const int row_wgs = p.d.num_kv_heads * p.col_groups;
   p.d.rank_split = p.d.max_parts == 1 ? rank_split_for(kernel, p.d, row_wgs, c) : p.d.num_seqs;
+  fill_order(p.d, c);
   return launch_main(kernel, dim3(row_wgs, p.d.num_seqs, p.d.max_parts), dim3(kThreads), c, p);
 }
 

@@ -297,3 +297,27 @@ def test_append_decode_validation(lib):
     assert call(decode_args(W=128), opts=pa.PaDecodeOpts(512, 0, 0)) == pa.PA_ERR_WORKSPACE
     assert call(decode_args(W=128), opts=pa.PaDecodeOpts(512, 0, 0), ws=ctypes.c_void_p(FAKE),
                 ws_bytes=100) == pa.PA_ERR_WORKSPACE
+
+
+def test_host_context_lens_marshalling():
+    """opts.host_context_lens: the binding hands the library a contiguous int32
+    host array with one entry per sequence, or NULL."""
+    import numpy as np
+    import torch
+
+    lens = torch.zeros(4, dtype=torch.int32)
+    assert pa._host_lens(None, lens) is None
+    a = pa._host_lens([3, 1, 4, 1], lens)
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"] and a.tolist() == [3, 1, 4, 1]
+    b = pa._host_lens(torch.tensor([5, 9, 2, 6], dtype=torch.int64), lens)
+    assert b.dtype == np.int32 and b.tolist() == [5, 9, 2, 6]
+    strided = np.arange(8, dtype=np.int32)[::2]
+    assert pa._host_lens(strided, lens).tolist() == [0, 2, 4, 6]
+    with pytest.raises(ValueError):
+        pa._host_lens([1, 2, 3], lens)
+    with pytest.raises(ValueError):
+        pa._host_lens(np.zeros((2, 2), dtype=np.int32), lens)
+    o = pa._opts(0, 0, 0, 0, None, a)
+    assert o.host_context_lens == a.ctypes.data
+    assert pa._opts(0, 0, 0, 0, None, None).host_context_lens is None
+    assert ctypes.sizeof(pa.PaDecodeOpts) == 48

@@ -1,0 +1,95 @@
+"""GPU checks of opts.host_context_lens: with a host copy of the lengths the
+unsplit schedules rank the sequences on the host and pass the order with the
+kernel's arguments.  Only the placement of the workgroups changes, so the
+outputs (and the appended pools) are bit-identical to the device-ranked call,
+also when the host copy is wrong (the order is still a permutation); under
+pa_set_debug(1) a wrong copy is refused.  The host-ranked step also matches the
+fp64 oracle (max|err| <= 1e-2, relative RMS <= 2e-3)."""
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, need_gpu, oracle_step, sample_seqs
+from paged_kv_cache_122_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+# (config, decode options); every case takes an unsplit schedule
+CASES = [
+    ("tiny_gqa4_d64", {}),
+    ("llama3_8b_b64", {}),
+    ("llama3_70b_b256", {}),
+    ("llama3_8b_b64", {"partition_tokens": -1, "path": 2}),
+    ("opt13b_mha_prefix_b128", {"partition_tokens": -1, "path": 1}),  # VALU, one head per KV head
+]
+
+
+def _wrong_lens(w):
+    """Lengths that rank the sequences in a different order than the true ones."""
+    rng = np.random.default_rng(7)
+    return rng.permutation(np.asarray(w.context_lens, dtype=np.int32))
+
+
+@pytest.mark.parametrize("name,opts", CASES, ids=[f"{c[0]}-{c[1]}" for c in CASES])
+def test_host_order_bit_identical(name, opts):
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.make(name)
+    print(f"[{name} {opts}] S={w.num_seqs}", flush=True)
+    dw = dev.upload(w)
+    true_lens = np.asarray(w.context_lens, dtype=np.int32)
+    outs = {}
+    for label, hl in (("device", None), ("host", true_lens), ("wrong", _wrong_lens(w))):
+        o_step = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+        o_dec = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+        pa.append_decode(o_step, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                         dw.block_tables, dw.context_lens, w.scale, w.block_size, host_context_lens=hl, **opts)
+        pa.decode_ex(o_dec, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                     w.block_size, host_context_lens=hl, **opts)
+        torch.cuda.synchronize()
+        outs[label] = (o_step.cpu().numpy(), o_dec.cpu().numpy())
+    for label in ("host", "wrong"):
+        for i, what in enumerate(("append_decode", "decode_ex")):
+            assert np.array_equal(outs[label][i].view(np.uint32), outs["device"][i].view(np.uint32)), \
+                f"{name} {what}: {label}-ranked output differs from the device-ranked one"
+    # the appended pools and the step's attention against the oracle
+    seqs = sample_seqs(w, 12)
+    kst, vst, ref = oracle_step(w, seqs)
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+    a, r = assert_close(outs["host"][0].astype(np.float64)[seqs], ref[seqs], name)
+    print(f"[{name} {opts}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+    del dw
+    torch.cuda.empty_cache()
+
+
+def test_host_order_debug_contract():
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.make("tiny_gqa4_d64")
+    dw = dev.upload(w)
+    out = torch.empty_like(dw.q)
+    lens = np.asarray(w.context_lens, dtype=np.int32)
+    bad = lens.copy()
+    bad[1] += 1
+    old = pa.set_debug(True)
+    try:
+        pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                     w.block_size, host_context_lens=lens)
+        for call in (
+            lambda: pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                                 w.block_size, host_context_lens=bad),
+            lambda: pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                                     dw.block_tables, dw.context_lens, w.scale, w.block_size,
+                                     host_context_lens=bad)):
+            with pytest.raises(pa.PaError) as e:
+                call()
+            assert e.value.code == pa.PA_ERR_CONTRACT
+            assert "host_context_lens" in str(e.value)
+    finally:
+        pa.set_debug(old)
+    torch.cuda.synchronize()
