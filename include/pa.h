@@ -187,15 +187,20 @@ typedef struct {
                                 timed by the GPU (hipExtLaunchKernel) */
   const int32_t* host_context_lens; /* NULL, or HOST memory holding a copy of
                                 context_lens ([num_seqs] int32), read during
-                                the call only.  Unsplit schedules then rank the
-                                sequences on the host and pass the order with
-                                the kernel's arguments, instead of every
-                                workgroup loading and ranking the lengths
-                                first.  It steers only which workgroup takes
-                                which sequence: results are the same with or
-                                without it, and with lengths that differ from
-                                the device's (a contract violation, reported
-                                as PA_ERR_CONTRACT under pa_set_debug(1)) */
+                                the call only; it must equal the device's
+                                lengths (a precondition, reported as
+                                PA_ERR_CONTRACT under pa_set_debug(1)).
+                                Unsplit schedules then rank the sequences on
+                                the host and pass the order with the kernel's
+                                arguments, instead of every workgroup loading
+                                and ranking the lengths first; there it steers
+                                only placement, and results are identical with
+                                or without it.  pa_append_decode also uses it
+                                where the automatic schedule is stream-K (few
+                                long contexts, MFMA path): partitions sized on
+                                the lengths so that the workgroups share the
+                                tokens evenly, only those holding tokens
+                                launched, the append fused into that launch */
 } pa_decode_opts;
 
 /* Bytes of workspace pa_decode_ex needs for these sizes (0 when nothing is split). */
@@ -268,7 +273,10 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * fused to cut launches; "PagedAttention from First Principles", section 5).
  * Where the decode schedule is unsplit on the MFMA path, one kernel does both:
  * it stores the new token and takes its K/V from k / v for the attention.
- * Otherwise the append kernel runs, then the decode the schedule chooses.
+ * Where it is stream-K and opts carries host_context_lens, the multi-token
+ * kernel does both over partitions sized on those lengths (in the workspace),
+ * and a second kernel combines each row's partitions.  Otherwise the append
+ * kernel runs, then the decode the schedule chooses.
  *
  *   out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
  *   opts, workspace, workspace_bytes: as for pa_decode_ex (kernel events in
@@ -278,7 +286,8 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  *   slot_mapping  int64 [S]: the slot of that position.
  *
  * The result equals pa_cache_append followed by pa_decode_ex with the same
- * options.  Preconditions (debug mode checks them, with pa_decode's): for
+ * options (up to the rounding of a different split where host lengths pick
+ * the partitions).  Preconditions (debug mode checks them, with pa_decode's): for
  * every sequence with L_s > 0, slot_mapping[s] is the slot its block table
  * gives position L_s - 1; a sequence with L_s == 0 has no new token and a
  * negative slot.  Every argument, the workspace included, is checked

@@ -934,6 +934,62 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     }
   }
 
+  if (pl.stream && pl.path == pa::Path::Mfma && opts && opts->host_context_lens) {
+    // Few long contexts whose lengths the host knows: the multi-token
+    // kernel's partitions, sized on those lengths so that about
+    // kFullGpuPairs workgroups share the tokens evenly, with the append
+    // fused and each row's partitions combined after (in the caller's
+    // workspace).  The grid covers the table width whatever the copy says,
+    // so a wrong copy changes only the partition size.
+    const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
+    pa::MultiParams m;
+    if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
+                           g, scale, 1, &m)) != PA_OK)
+      return rc;
+    const int64_t span = pl.W * pl.B;
+    int64_t tokens = 0;
+    for (int64_t s = 0; s < pl.S; ++s)
+      tokens += std::min<int64_t>(std::max<int64_t>(opts->host_context_lens[s], 0), span);
+    const int64_t row_wgs = pl.Hkv * m.col_groups;
+    int64_t part = std::max<int64_t>(512, ((tokens * row_wgs + kFullGpuPairs - 1) / kFullGpuPairs + 255) / 256 * 256);
+    while ((span + part - 1) / part > 65535) part *= 2;
+    const int64_t parts = (span + part - 1) / part;
+    const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, parts);
+    if (parts > 1 && wl.total <= workspace_bytes) {
+      m.d.part_tokens = int(part);
+      m.d.max_parts = int(parts);
+      m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+      m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+      // Launch only the partitions that hold tokens, longest contexts first
+      // (a grid over every sequence's table span leaves most workgroups of
+      // an uneven batch with nothing to do but load their length and leave).
+      // Each sequence's count is the kernel's: its cached tokens (all but the
+      // new one) in partitions of `part`, at least one.
+      if (pl.S <= pa::kMaxRankedSeqs && parts <= 256) {
+        std::vector<int> idx(size_t(pl.S));
+        for (int64_t i = 0; i < pl.S; ++i) idx[size_t(i)] = int(i);
+        auto len = [&](int i) { return std::min<int64_t>(std::max<int64_t>(opts->host_context_lens[i], 0), span); };
+        std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return len(x) > len(y); });
+        int items = 0;
+        for (const int sq : idx) {
+          const int64_t cached = std::max<int64_t>(len(sq) - 1, 0);
+          const int64_t np = std::min<int64_t>(std::max<int64_t>((cached + part - 1) / part, 1), parts);
+          if (items + np > pa::kMaxRankedSeqs) { items = -1; break; }
+          for (int64_t j = 0; j < np; ++j) m.d.order[items++] = uint16_t((sq << 8) | int(j));
+        }
+        if (items > 0) {
+          m.d.has_order = 2;
+          m.num_items = items;
+        }
+      }
+      int cus = 0;
+      if ((rc = device_cus(&cus)) != PA_OK) return rc;
+      const pa::LaunchCtx ctx{stream, opts->kernel_start, opts->kernel_stop, cus, opts->host_context_lens};
+      const hipError_t e = pa::launch_multi(m, int(pl.D), int(pl.B), ctx);
+      if (e != hipSuccess) return hip_fail(e, "fused append + split decode launch");
+      return PA_OK;
+    }
+  }
   if (!pl.stream && pl.max_parts == 1 && pl.path == pa::Path::Mfma) {
     // unsplit MFMA schedule: the multi-token kernel with one new token per
     // sequence stores it and attends in one launch

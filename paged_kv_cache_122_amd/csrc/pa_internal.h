@@ -50,8 +50,10 @@ struct DecodeParams {
                         // order, the rows from it on the rest from the shortest up
   float* ws_o;          // [S, Hq, max_parts, D]  normalised partial outputs
   float* ws_ml;         // [S, Hq, max_parts, 2]  (reference max in log2 units, sum)
-  // unsplit grids: the sequence of each row, ranked on the host from a host
-  // copy of context_lens (has_order != 0), else ranked by each workgroup
+  // has_order 1 (unsplit grids): order[row] is the row's sequence, ranked on
+  // the host from a host copy of context_lens (0: ranked by each workgroup).
+  // has_order 2 (split multi-token grid): order[y] = sequence << 8 | partition,
+  // the grid's rows listing only the partitions that hold tokens.
   int has_order;
   uint16_t order[kMaxRankedSeqs];
 };
@@ -94,6 +96,7 @@ struct MultiParams {
   int col_sets;                    // 16-column MFMA sets per workgroup (1 or 2)
   int col_groups;                  // workgroups per KV head: ceil(max_query_len * G / (16 * col_sets))
   int64_t num_slots;               // num_blocks * block_size
+  int num_items;                   // > 0: grid rows from d.order (has_order 2), one partition each
 };
 
 struct CopyParams {

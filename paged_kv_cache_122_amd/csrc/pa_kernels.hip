@@ -1067,7 +1067,7 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
 // more than kMaxRankedSeqs sequences or with table spans of 2^22 tokens or more.
 __device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
   const int S = p.num_seqs;
-  if (p.has_order) return p.order[y];  // ranked on the host: no round trip to the lengths
+  if (p.has_order == 1) return p.order[y];  // ranked on the host: no round trip to the lengths
   if (p.max_parts > 1 || S > kMaxRankedSeqs || p.max_len >= (1 << 22)) return y;
   __shared__ uint32_t keys[kMaxRankedSeqs];
   __shared__ int pick;
@@ -1565,7 +1565,20 @@ void decode_multi(MultiParams mp) {
   const int g4 = lane >> 4;
   const int kvh = blockIdx.x / mp.col_groups;
   const int cg = blockIdx.x - kvh * mp.col_groups;
-  const int s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
+  int s, part;
+  if constexpr (Split) {
+    if (p.has_order == 2) {  // the host's list of (sequence, partition) items
+      const int item = p.order[blockIdx.y];
+      s = item >> 8;
+      part = item & 255;
+    } else {
+      s = blockIdx.y;
+      part = blockIdx.z;
+    }
+  } else {
+    s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
+    part = 0;
+  }
   const int G = p.group;
   // this sequence's rows, kept inside [0, T); at most max_query_len of them
   // (no query_start: row s, one new token per sequence)
@@ -1576,7 +1589,6 @@ void decode_multi(MultiParams mp) {
   const int L_old = L - n;
   // split schedule: partition `part` of the cached tokens; the new tokens
   // belong to the last partition, whose workgroups also append them
-  const int part = Split ? int(blockIdx.z) : 0;
   const int nparts = Split ? multi_parts(p, L_old) : 1;
   if (part >= nparts) return;  // workgroup-uniform
   const bool last = part == nparts - 1;
@@ -1734,7 +1746,8 @@ void decode_multi(MultiParams mp) {
 }
 
 // Pieces of each new token's row, combined in ascending token order.  One
-// thread per (head, dim) of a sequence, looping over its rows.
+// thread per (head, dim) of a sequence's row: grid z strides over the rows, so
+// that the rows' round trips to the workspace overlap instead of queueing.
 template <int D>
 __global__ __launch_bounds__(256) void combine_rows(MultiParams mp) {
   const DecodeParams& p = mp.d;
@@ -1749,7 +1762,7 @@ __global__ __launch_bounds__(256) void combine_rows(MultiParams mp) {
   if (nparts <= 1) return;  // the kernel wrote these rows directly
   const int h = idx / D;
   const int d = idx - h * D;
-  for (int i = 0; i < n; ++i) {
+  for (int i = blockIdx.z; i < n; i += gridDim.z) {
     const size_t row0 = (size_t(r0 + i) * p.num_q_heads + h) * p.max_parts;
     store_out(p, r0 + i, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
   }
@@ -1978,6 +1991,8 @@ hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCt
 template <typename K>
 hipError_t launch_multi_k(K kernel, MultiParams p, const LaunchCtx& c) {
   const int row_wgs = p.d.num_kv_heads * p.col_groups;
+  if (p.num_items > 0)  // split over the host's (sequence, partition) list
+    return launch_main(kernel, dim3(row_wgs, p.num_items, 1), dim3(kThreads), c, p);
   p.d.rank_split = p.d.max_parts == 1 ? rank_split_for(kernel, p.d, row_wgs, c) : p.d.num_seqs;
   fill_order(p.d, c);
   return launch_main(kernel, dim3(row_wgs, p.d.num_seqs, p.d.max_parts), dim3(kThreads), c, p);
@@ -2004,7 +2019,7 @@ hipError_t launch_multi_d(const MultiParams& p, int block_size, const LaunchCtx&
   const hipError_t e =
       p.col_sets == 1 ? launch_multi_ns<D, 1>(p, block_size, c) : launch_multi_ns<D, 2>(p, block_size, c);
   if (e != hipSuccess || p.d.max_parts <= 1) return e;
-  const dim3 cgrid((p.d.num_q_heads * D + 255) / 256, p.d.num_seqs);
+  const dim3 cgrid((p.d.num_q_heads * D + 255) / 256, p.d.num_seqs, std::min(p.max_query_len, 65535));
   hipLaunchKernelGGL((combine_rows<D>), cgrid, dim3(256), 0, c.stream, p);
   return hipGetLastError();
 }

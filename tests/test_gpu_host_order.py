@@ -93,3 +93,49 @@ def test_host_order_debug_contract():
     finally:
         pa.set_debug(old)
     torch.cuda.synchronize()
+
+
+# Few long contexts (the automatic schedule is stream-K): with host lengths
+# pa_append_decode runs the multi-token kernel over partitions sized on them,
+# launching only the partitions that hold tokens.  (name, lengths or None for
+# a named config, q heads, kv heads, head dim, block size)
+SPLIT_CASES = [
+    ("long32k_b16", None, 0, 0, 0, 0),
+    ("long32k_b8", None, 0, 0, 0, 0),
+    ("halving", [16384 >> i for i in range(8)], 32, 8, 128, 16),
+    ("one_long", [16384] + [300] * 15, 32, 8, 128, 16),
+    ("odd_lengths", [1, 5000, 2, 4097, 12000, 17], 32, 8, 128, 32),
+    ("d64_b8_gqa8", [20000, 700, 20001], 16, 2, 64, 8),
+]
+
+
+@pytest.mark.parametrize("name,lens,hq,hkv,d,b", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_host_lens_split_step(name, lens, hq, hkv, d, b):
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    if lens is None:
+        w = workloads.make(name)
+    else:
+        w = workloads.random_workload(6100 + len(name), lens, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                                      block_size=b, name=name)
+    maxlen = w.table_width * w.block_size
+    assert pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, maxlen) == -2, "expected a stream-K batch"
+    print(f"[{name}] S={w.num_seqs} lens={list(w.context_lens)[:8]}", flush=True)
+    dw = dev.upload(w)
+    nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen, 0)
+    ws = pa.alloc_workspace(nb, "cuda")
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, dw.block_tables,
+                     dw.context_lens, w.scale, w.block_size, workspace=ws,
+                     host_context_lens=np.asarray(w.context_lens, dtype=np.int32))
+    torch.cuda.synchronize()
+    seqs = sample_seqs(w, 8)
+    kst, vst, ref = oracle_step(w, seqs)
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+    a, r = assert_close(out.double().cpu().numpy()[seqs], ref[seqs], name)
+    print(f"[{name}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+    del dw
+    torch.cuda.empty_cache()
