@@ -44,18 +44,18 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "417c0057640aaf91b8b27c77c23cc50c08be83817039e17d75f48627c7de0bfb",
-    # the step's one launch: FETCH_SIZE 133783.6 KiB x 1.9999, WRITE_SIZE 1280.0 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.61 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273970292, "write_bytes": 1310741,
-                                                   "mfma_busy_pct": 4.61},
-    # the verification batch: FETCH_SIZE 140626.4 KiB x 1.9999, WRITE_SIZE 4353.9 KiB x 1.0; MfmaUtil 8.58 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287983335, "write_bytes": 4458345,
-                                                           "mfma_busy_pct": 8.58},
-    # long-context verification (split): FETCH_SIZE 524893.6 KiB x 1.9999, WRITE_SIZE 5426.5 KiB x 1.0;
-    # MfmaUtil 11.49 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074909379, "write_bytes": 5556754,
-                                                        "mfma_busy_pct": 11.49},
+    "sources_sha256": "0e190abc206144c68e397ce9c6eb41957486094075969ad8ffd316faaf23f8bf",
+    # the step's one launch: FETCH_SIZE 133788.0 KiB x 1.9999, WRITE_SIZE 1280.0 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.77 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273979414, "write_bytes": 1310720,
+                                                   "mfma_busy_pct": 4.77},
+    # the verification batch: FETCH_SIZE 140618.8 KiB x 1.9999, WRITE_SIZE 4353.5 KiB x 1.0; MfmaUtil 8.53 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287967930, "write_bytes": 4457961,
+                                                           "mfma_busy_pct": 8.53},
+    # long-context verification (split): FETCH_SIZE 524891.1 KiB x 1.9999, WRITE_SIZE 5426.4 KiB x 1.0;
+    # MfmaUtil 11.54 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074904608, "write_bytes": 5556599,
+                                                        "mfma_busy_pct": 11.54},
 }
 
 
@@ -255,11 +255,27 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
 
 
 def fused_step(w, part):
-    """Whether pa_append_decode runs this workload as one launch (the unsplit
-    MFMA schedule), and that kernel's name."""
+    """How pa_append_decode (given the host copy of the lengths) runs this
+    workload: (append fused into the attention launch, its kernels, what the
+    schedule is).  The unsplit MFMA schedule is one launch; a stream-K batch
+    on the MFMA path runs the multi-token kernel over partitions sized on the
+    lengths (so that about 512 workgroups share the tokens), then the row
+    combine; anything else appends first and decodes as pa_decode_ex does."""
     g = w.num_q_heads // w.num_kv_heads
-    unsplit = part == -1 or part >= w.block_tables.shape[1] * w.block_size
-    return g >= 3 and unsplit, f"decode_multi<{w.head_dim},{w.block_size},{2 if g > 16 else 1},false>"
+    sets = 2 if g > 16 else 1
+    span = w.block_tables.shape[1] * w.block_size
+    unsplit = part == -1 or part >= span
+    if g >= 3 and unsplit:
+        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},false>"], \
+            "one launch: the new token stored and attended"
+    if g >= 3 and part == -2:
+        row_wgs = w.num_kv_heads * -(-g // (16 * sets))
+        tokens = int(sum(min(max(int(x), 0), span) for x in w.context_lens))
+        p = max(512, -(-(-(-tokens * row_wgs // 512)) // 256) * 256)
+        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},true>", f"combine_rows<{w.head_dim}>"], \
+            f"partitions of {p} tokens sized on the host's lengths, only those holding tokens launched, " \
+            "the new token stored by the last one; then the row combine"
+    return False, [], "append kernel, then the decode schedule"
 
 
 def percentile(xs, q):
@@ -351,11 +367,11 @@ def main():
     max_len = int(w.block_tables.shape[1]) * w.block_size
     part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
     kernels, schedule = decode_kernels(w, part, torch.cuda.get_device_properties(0).multi_processor_count)
-    fused, fused_kernel = fused_step(w, part)
+    fused, fused_kernels, step_kind = fused_step(w, part)
     new_kv_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
     if fused:
-        # one launch reads the context (the new token from k / v) and writes the new token
-        kernels, schedule = [fused_kernel], schedule + "; append fused into the decode launch"
+        # the main launch reads the context (the new token from k / v) and writes the new token
+        kernels, schedule = fused_kernels, step_kind
         algo_bytes += new_kv_bytes
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.Stream()  # default priority
@@ -516,8 +532,7 @@ def main():
             "unique_kv_bytes": w.unique_kv_bytes(),
             "seed": w.seed,
             "step": ("pa_copy_blocks (copy-on-write) + " if has_copies else "")
-                    + "pa_append_decode (" + ("one launch: the new token stored and attended"
-                                              if fused else "append kernel, then the decode schedule")
+                    + "pa_append_decode (" + step_kind
                     + "), with a host copy of the lengths (the sequences ranked on the host), "
                     "caches flushed before each step",
             "cow_copies": int(w.copies.shape[0]),
