@@ -106,6 +106,9 @@ SPLIT_CASES = [
     ("one_long", [16384] + [300] * 15, 32, 8, 128, 16),
     ("odd_lengths", [1, 5000, 2, 4097, 12000, 17], 32, 8, 128, 32),
     ("d64_b8_gqa8", [20000, 700, 20001], 16, 2, 64, 8),
+    ("gqa32_two_sets", [30000, 20000], 64, 2, 128, 16),
+    # more items than the kernel arguments list: the grid spans every table
+    ("many_items", [1500 + (37 * i) % 1000 for i in range(300)], 4, 1, 128, 16),
 ]
 
 
