@@ -142,7 +142,11 @@ int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* bloc
  * block_size):
  *   P >= 512, G >= 3, Lmax <= 8192  one workgroup per pair, no split;
  *   P >= 512 otherwise              partitions of 1024 tokens;
- *   P * ceil(Lmax / 16) <= 4096     one workgroup per pair (tiny batch);
+ *   Lmax <= 1024                    one workgroup per pair (short tables);
+ *   P * ceil(Lmax / 512) <= 2048    partitions of 512 tokens (few pairs with
+ *                                   long tables: the grid still fits the GPU
+ *                                   about once, so the partitions a shorter
+ *                                   context leaves empty cost little);
  *   otherwise                       stream-K: the 16-token tiles of all pairs
  *                                   are cut into equal contiguous ranges, one
  *                                   per wave of a persistent grid, and a
@@ -196,11 +200,11 @@ typedef struct {
                                 and ranking the lengths first; there it steers
                                 only placement, and results are identical with
                                 or without it.  pa_append_decode also uses it
-                                where the automatic schedule is stream-K (few
-                                long contexts, MFMA path): partitions sized on
-                                the lengths so that the workgroups share the
-                                tokens evenly, only those holding tokens
-                                launched, the append fused into that launch */
+                                where the automatic schedule splits with few
+                                pairs (MFMA path): partitions sized on the
+                                lengths so that the workgroups share the tokens
+                                evenly, only those holding tokens launched, the
+                                append fused into that launch */
 } pa_decode_opts;
 
 /* Bytes of workspace pa_decode_ex needs for these sizes (0 when nothing is split). */
@@ -273,10 +277,12 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * fused to cut launches; "PagedAttention from First Principles", section 5).
  * Where the decode schedule is unsplit on the MFMA path, one kernel does both:
  * it stores the new token and takes its K/V from k / v for the attention.
- * Where it is stream-K and opts carries host_context_lens, the multi-token
+ * Where the automatic schedule splits with fewer than 512 pairs (stream-K or
+ * 512-token partitions) and opts carries host_context_lens, the multi-token
  * kernel does both over partitions sized on those lengths (in the workspace),
- * and a second kernel combines each row's partitions.  Otherwise the append
- * kernel runs, then the decode the schedule chooses.
+ * and a second kernel combines each row's partitions; where those lengths
+ * fit one partition each, the unsplit fused kernel runs.  Otherwise the
+ * append kernel runs, then the decode the schedule chooses.
  *
  *   out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
  *   opts, workspace, workspace_bytes: as for pa_decode_ex (kernel events in

@@ -214,8 +214,13 @@ bool stream_fits(int64_t S, int64_t pairs, int64_t max_len) {
 //  * tiny batches -> one workgroup per pair (the launch cost dominates);
 //  * otherwise (few, long contexts) -> stream-K.
 constexpr int64_t kFullGpuPairs = 512;
-constexpr int64_t kTinyTiles = 4096;
 constexpr int64_t kNoSplitMaxLen = 8192;
+// Few pairs: tables up to this many tokens stay unsplit; longer ones take
+// partitions of kDefaultPartition tokens while their grid has at most
+// kMaxPartitionGrid workgroups (most of it resident at once, so partitions a
+// short context leaves empty cost little), and stream-K beyond.
+constexpr int64_t kSmallNoSplitLen = 1024;
+constexpr int64_t kMaxPartitionGrid = 2048;
 
 struct Schedule {
   bool stream;
@@ -226,7 +231,10 @@ Schedule auto_schedule(int64_t S, int64_t pairs, int64_t group, int64_t max_len)
   const int64_t tiles = (max_len + pa::kTileTokens - 1) / pa::kTileTokens;
   if (pairs >= kFullGpuPairs)
     return {false, group <= 2 ? 1024 : (max_len <= kNoSplitMaxLen ? -1 : 1024)};
-  if (pairs * tiles <= kTinyTiles) return {false, -1};
+  (void)tiles;
+  if (max_len <= kSmallNoSplitLen) return {false, -1};
+  const int64_t parts = (max_len + pa::kDefaultPartition - 1) / pa::kDefaultPartition;
+  if (pairs * parts <= kMaxPartitionGrid) return {false, pa::kDefaultPartition};
   if (stream_fits(S, pairs, max_len)) return {true, 0};
   return {false, pa::kDefaultPartition};
 }
@@ -934,13 +942,16 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     }
   }
 
-  if (pl.stream && pl.path == pa::Path::Mfma && opts && opts->host_context_lens) {
-    // Few long contexts whose lengths the host knows: the multi-token
-    // kernel's partitions, sized on those lengths so that about
+  const int64_t pairs = pl.S * pl.Hkv * ((pl.Hq / pl.Hkv + 15) / 16);
+  bool fuse_unsplit = !pl.stream && pl.max_parts == 1 && pl.path == pa::Path::Mfma;
+  if ((pl.stream || (pl.max_parts > 1 && pairs < kFullGpuPairs)) && pl.path == pa::Path::Mfma && opts &&
+      opts->host_context_lens && opts->partition_tokens == 0) {  // an automatic schedule only
+    // Few pairs with long contexts, whose lengths the host knows: the
+    // multi-token kernel's partitions, sized on those lengths so that about
     // kFullGpuPairs workgroups share the tokens evenly, with the append
     // fused and each row's partitions combined after (in the caller's
-    // workspace).  The grid covers the table width whatever the copy says,
-    // so a wrong copy changes only the partition size.
+    // workspace); where every context fits one partition, the unsplit fused
+    // kernel instead.
     const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
     pa::MultiParams m;
     if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
@@ -954,8 +965,12 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     int64_t part = std::max<int64_t>(512, ((tokens * row_wgs + kFullGpuPairs - 1) / kFullGpuPairs + 255) / 256 * 256);
     while ((span + part - 1) / part > 65535) part *= 2;
     const int64_t parts = (span + part - 1) / part;
+    int64_t longest = 0;
+    for (int64_t s = 0; s < pl.S; ++s) longest = std::max<int64_t>(longest, opts->host_context_lens[s]);
     const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, parts);
-    if (parts > 1 && wl.total <= workspace_bytes) {
+    if (std::min(longest, span) - 1 <= part) {
+      fuse_unsplit = true;
+    } else if (parts > 1 && wl.total <= workspace_bytes) {
       m.d.part_tokens = int(part);
       m.d.max_parts = int(parts);
       m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
@@ -990,7 +1005,7 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
       return PA_OK;
     }
   }
-  if (!pl.stream && pl.max_parts == 1 && pl.path == pa::Path::Mfma) {
+  if (fuse_unsplit) {
     // unsplit MFMA schedule: the multi-token kernel with one new token per
     // sequence stores it and attends in one launch
     const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};

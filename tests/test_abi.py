@@ -181,6 +181,11 @@ def test_schedule_query(lib):
     assert s(128, 40, 40, 2048) == 1024      # MHA with many pairs: 1024-token partitions
     assert s(64, 32, 8, 16384) == 1024       # long contexts, many pairs
     assert s(4, 8, 2, 912) == -1             # tiny batch
+    assert s(60, 32, 8, 1024) == -1         # few pairs, short tables: no split
+    assert s(1, 32, 8, 8192) == 512          # one long context: 512-token partitions (128 workgroups)
+    assert s(32, 32, 8, 2048) == 512         # 256 pairs x 4 partitions
+    assert s(16, 32, 8, 6016) == 512         # 1536 workgroups
+    assert s(16, 32, 8, 32768) == -2         # 8192 workgroups of 512 tokens: stream-K
     assert s(8, 32, 8, 32768) == -2          # few long contexts: stream-K
     assert s(9000, 64, 8, 1024) == -1        # 72000 pairs
     assert s(9000, 2, 1, 1 << 20) == 1024
@@ -188,7 +193,8 @@ def test_schedule_query(lib):
         s(4, 6, 4, 100)
     assert e.value.code == pa.PA_ERR_INVALID
     # every automatic choice is consistent with the workspace size query
-    for args in ((64, 32, 8, 2048), (128, 40, 40, 2048), (8, 32, 8, 32768), (64, 32, 8, 16384)):
+    for args in ((64, 32, 8, 2048), (128, 40, 40, 2048), (8, 32, 8, 32768), (64, 32, 8, 16384),
+                 (1, 32, 8, 8192), (16, 32, 8, 6016)):
         S, Hq, Hkv, L = args
         assert lib.pa_decode_workspace_bytes(S, Hq, Hkv, 128, L, 0) == \
             lib.pa_decode_workspace_bytes(S, Hq, Hkv, 128, L, s(*args))
