@@ -194,6 +194,9 @@ typedef struct {
                                 the call only; it must equal the device's
                                 lengths (a precondition, reported as
                                 PA_ERR_CONTRACT under pa_set_debug(1)).
+                                Where max_context_len is 0, the longest of
+                                them bounds the launch in its place (tables
+                                are often sized for a model's maximum context).
                                 Unsplit schedules then rank the sequences on
                                 the host and pass the order with the kernel's
                                 arguments, instead of every workgroup loading

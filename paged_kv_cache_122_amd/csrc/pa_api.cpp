@@ -313,6 +313,13 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
 
   int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : W * g.block_size;
   if (opts && opts->max_context_len < 0) return fail(PA_ERR_INVALID, "opts.max_context_len < 0");
+  if (opts && opts->max_context_len == 0 && opts->host_context_lens && S > 0) {
+    // the longest context bounds the launch, not the table width (engines
+    // often size tables for the model's maximum context)
+    int64_t longest = 1;
+    for (int64_t s = 0; s < S; ++s) longest = std::max<int64_t>(longest, opts->host_context_lens[s]);
+    max_len = std::min(longest, max_len);
+  }
   if (W * g.block_size > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "table width * block_size >= 2^31");
   const int pt_opt = opts ? opts->partition_tokens : 0;
   const int wpc = opts ? opts->workgroups_per_cu : 0;
