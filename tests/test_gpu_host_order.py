@@ -209,3 +209,44 @@ def test_host_lens_bound_wide_tables():
     assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
     assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
     assert_close(outs[0].astype(np.float64)[seqs], ref[seqs], "wide_tables")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_host_lens_random_steps(seed):
+    """Seeded random batches through pa_append_decode with host lengths, so
+    that every route is taken somewhere (fused unsplit, host-length partitions,
+    the one-partition fallback, append + partitioned decode for G <= 2):
+    grouping 1 .. 16, D 64 / 128, B 8 / 16 / 32, 1 .. 40 sequences, lengths
+    from 1 token to 12k; pools bit-exact and sampled rows against the oracle."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    rng = np.random.default_rng(6400 + seed)
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    b = int(rng.choice([8, 16, 32]))
+    S = int(rng.integers(1, 41))
+    top = int(rng.choice([600, 3000, 12000]))
+    lens = rng.integers(1, top + 1, size=S).tolist()
+    w = workloads.random_workload(6500 + seed, lens, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, block_size=b,
+                                  name=f"host_random{seed}")
+    maxlen = w.table_width * w.block_size
+    sched = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, maxlen)
+    print(f"[host_random{seed}] G={g} Hkv={hkv} D={d} B={b} S={S} max={max(lens)} schedule={sched}", flush=True)
+    dw = dev.upload(w)
+    nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen, 0)
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, dw.block_tables,
+                     dw.context_lens, w.scale, w.block_size, workspace=ws,
+                     host_context_lens=np.asarray(w.context_lens, dtype=np.int32))
+    torch.cuda.synchronize()
+    seqs = sample_seqs(w, 8)
+    kst, vst, ref = oracle_step(w, seqs)
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+    assert_close(out.double().cpu().numpy()[seqs], ref[seqs], f"host_random{seed}")
+    del dw
+    torch.cuda.empty_cache()
