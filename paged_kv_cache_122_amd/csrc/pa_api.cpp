@@ -893,6 +893,104 @@ int cache_append_impl(const pa_tensor* k, const pa_tensor* v, const pa_tensor* s
 
 }  // namespace
 
+namespace {
+
+// pa_append_decode's slot contract (debug mode): the slot of a sequence with
+// tokens is its table's slot of position L - 1; an empty sequence has none.
+int debug_check_append_slots(const DecodePlan& pl, const pa_tensor* slot_mapping, const pa_tensor* block_tables,
+                             const pa_tensor* context_lens, hipStream_t stream) {
+  std::vector<int32_t> lens, bt;
+  std::vector<int64_t> slots;
+  const size_t stride = size_t(block_tables->stride[0]);
+  int rc;
+  if ((rc = copy_to_host(&lens, context_lens->data, size_t(pl.S), stream)) != PA_OK) return rc;
+  if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(pl.S), stream)) != PA_OK) return rc;
+  if ((rc = copy_to_host(&bt, block_tables->data, size_t(pl.S - 1) * stride + size_t(pl.W), stream)) != PA_OK)
+    return rc;
+  for (int64_t s = 0; s < pl.S; ++s) {
+    const int64_t L = lens[size_t(s)];
+    if (L == 0) {
+      if (slots[size_t(s)] >= 0)
+        return fail(PA_ERR_CONTRACT, "sequence %lld has no token (context length 0) but slot %lld",
+                    (long long)s, (long long)slots[size_t(s)]);
+      continue;
+    }
+    const int64_t want = int64_t(bt[size_t(s) * stride + size_t((L - 1) / pl.B)]) * pl.B + (L - 1) % pl.B;
+    if (slots[size_t(s)] != want)
+      return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld, but position %lld of sequence %lld is slot %lld",
+                  (long long)s, (long long)slots[size_t(s)], (long long)(L - 1), (long long)s, (long long)want);
+  }
+  return PA_OK;
+}
+
+// Partitions of the multi-token kernel sized on the host's lengths, so that
+// about kFullGpuPairs workgroups share the tokens evenly: their size, count
+// and, within the limits of the kernel-argument list, the (sequence,
+// partition) items that hold tokens, longest contexts first.  Returns false
+// where every context fits one partition (then the unsplit kernel is the
+// better launch).  A grid over every sequence's table span would leave most
+// workgroups of an uneven batch with nothing to do but load their length and
+// leave; each sequence's count is the kernel's (its cached tokens, all but the
+// new one, in partitions of `part`, at least one).
+bool host_length_split(const DecodePlan& pl, const int32_t* host_lens, pa::MultiParams* m) {
+  const int64_t span = pl.W * pl.B;
+  auto len = [&](int64_t i) { return std::min<int64_t>(std::max<int64_t>(host_lens[i], 0), span); };
+  int64_t tokens = 0, longest = 0;
+  for (int64_t s = 0; s < pl.S; ++s) {
+    tokens += len(s);
+    longest = std::max(longest, len(s));
+  }
+  const int64_t row_wgs = pl.Hkv * m->col_groups;
+  int64_t part = std::max<int64_t>(512, ((tokens * row_wgs + kFullGpuPairs - 1) / kFullGpuPairs + 255) / 256 * 256);
+  while ((span + part - 1) / part > 65535) part *= 2;
+  if (longest - 1 <= part) return false;
+  const int64_t parts = (span + part - 1) / part;
+  m->d.part_tokens = int(part);
+  m->d.max_parts = int(parts);
+  if (pl.S <= pa::kMaxRankedSeqs && parts <= 256) {
+    std::vector<int> idx(size_t(pl.S));
+    for (int64_t i = 0; i < pl.S; ++i) idx[size_t(i)] = int(i);
+    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return len(x) > len(y); });
+    int items = 0;
+    for (const int sq : idx) {
+      const int64_t cached = std::max<int64_t>(len(sq) - 1, 0);
+      const int64_t np = std::min<int64_t>(std::max<int64_t>((cached + part - 1) / part, 1), parts);
+      if (items + np > pa::kMaxRankedSeqs) {
+        items = -1;
+        break;
+      }
+      for (int64_t j = 0; j < np; ++j) m->d.order[items++] = uint16_t((sq << 8) | int(j));
+    }
+    if (items > 0) {
+      m->d.has_order = 2;
+      m->num_items = items;
+    }
+  }
+  return true;
+}
+
+// One launch of the multi-token kernel for the step (one new token per
+// sequence): it stores the new token and attends, taking its K/V from k and
+// v; split (m->d.max_parts > 1, pieces in the workspace) a combine follows.
+int launch_fused_step(const DecodePlan& pl, pa::MultiParams* m, const pa_decode_opts* opts, void* workspace,
+                      hipStream_t stream) {
+  int rc;
+  if (m->d.max_parts > 1) {
+    const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, m->d.max_parts);
+    m->d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+    m->d.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+  }
+  int cus = 0;
+  if ((rc = device_cus(&cus)) != PA_OK) return rc;
+  const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus,
+                          opts ? opts->host_context_lens : nullptr};
+  const hipError_t e = pa::launch_multi(*m, int(pl.D), int(pl.B), ctx);
+  if (e != hipSuccess) return hip_fail(e, "fused append + decode launch");
+  return PA_OK;
+}
+
+}  // namespace
+
 PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
                                const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
                                const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
@@ -923,113 +1021,32 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     if (reinterpret_cast<uintptr_t>(workspace) & 255u)
       return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   }
-  const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
+  const int32_t* host_lens = opts ? opts->host_context_lens : nullptr;
   if (g_debug.load()) {
-    if ((rc = debug_check_decode(pl, block_tables, context_lens, max_len,
-                                                   opts ? opts->host_context_lens : nullptr, stream)) != PA_OK) return rc;
-    std::vector<int32_t> lens, bt;
-    std::vector<int64_t> slots;
-    const size_t stride = size_t(block_tables->stride[0]);
-    if ((rc = copy_to_host(&lens, context_lens->data, size_t(pl.S), stream)) != PA_OK) return rc;
-    if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(pl.S), stream)) != PA_OK) return rc;
-    if ((rc = copy_to_host(&bt, block_tables->data, size_t(pl.S - 1) * stride + size_t(pl.W), stream)) != PA_OK)
-      return rc;
-    for (int64_t s = 0; s < pl.S; ++s) {
-      const int64_t L = lens[size_t(s)];
-      if (L == 0) {
-        if (slots[size_t(s)] >= 0)
-          return fail(PA_ERR_CONTRACT, "sequence %lld has no token (context length 0) but slot %lld",
-                      (long long)s, (long long)slots[size_t(s)]);
-        continue;
-      }
-      const int64_t want = int64_t(bt[size_t(s) * stride + size_t((L - 1) / pl.B)]) * pl.B + (L - 1) % pl.B;
-      if (slots[size_t(s)] != want)
-        return fail(PA_ERR_CONTRACT, "slot_mapping[%lld] = %lld, but position %lld of sequence %lld is slot %lld",
-                    (long long)s, (long long)slots[size_t(s)], (long long)(L - 1), (long long)s, (long long)want);
-    }
+    const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
+    if ((rc = debug_check_decode(pl, block_tables, context_lens, max_len, host_lens, stream)) != PA_OK) return rc;
+    if ((rc = debug_check_append_slots(pl, slot_mapping, block_tables, context_lens, stream)) != PA_OK) return rc;
   }
 
+  // Route: the multi-token kernel in one launch where the schedule is unsplit
+  // on the MFMA path; with host lengths, also where the automatic schedule
+  // splits few pairs (partitions sized on those lengths, or unsplit where
+  // every context fits one); otherwise the append kernel, then the decode.
   const int64_t pairs = pl.S * pl.Hkv * ((pl.Hq / pl.Hkv + 15) / 16);
-  bool fuse_unsplit = !pl.stream && pl.max_parts == 1 && pl.path == pa::Path::Mfma;
-  if ((pl.stream || (pl.max_parts > 1 && pairs < kFullGpuPairs)) && pl.path == pa::Path::Mfma && opts &&
-      opts->host_context_lens && opts->partition_tokens == 0) {  // an automatic schedule only
-    // Few pairs with long contexts, whose lengths the host knows: the
-    // multi-token kernel's partitions, sized on those lengths so that about
-    // kFullGpuPairs workgroups share the tokens evenly, with the append
-    // fused and each row's partitions combined after (in the caller's
-    // workspace); where every context fits one partition, the unsplit fused
-    // kernel instead.
+  const bool mfma = pl.path == pa::Path::Mfma;
+  const bool unsplit = !pl.stream && pl.max_parts == 1;
+  const bool host_split = mfma && !unsplit && host_lens && opts->partition_tokens == 0 &&
+                          (pl.stream || pairs < kFullGpuPairs);
+  if ((mfma && unsplit) || host_split) {
     const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
     pa::MultiParams m;
     if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
                            g, scale, 1, &m)) != PA_OK)
       return rc;
-    const int64_t span = pl.W * pl.B;
-    int64_t tokens = 0;
-    for (int64_t s = 0; s < pl.S; ++s)
-      tokens += std::min<int64_t>(std::max<int64_t>(opts->host_context_lens[s], 0), span);
-    const int64_t row_wgs = pl.Hkv * m.col_groups;
-    int64_t part = std::max<int64_t>(512, ((tokens * row_wgs + kFullGpuPairs - 1) / kFullGpuPairs + 255) / 256 * 256);
-    while ((span + part - 1) / part > 65535) part *= 2;
-    const int64_t parts = (span + part - 1) / part;
-    int64_t longest = 0;
-    for (int64_t s = 0; s < pl.S; ++s) longest = std::max<int64_t>(longest, opts->host_context_lens[s]);
-    const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, parts);
-    if (std::min(longest, span) - 1 <= part) {
-      fuse_unsplit = true;
-    } else if (parts > 1 && wl.total <= workspace_bytes) {
-      m.d.part_tokens = int(part);
-      m.d.max_parts = int(parts);
-      m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
-      m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
-      // Launch only the partitions that hold tokens, longest contexts first
-      // (a grid over every sequence's table span leaves most workgroups of
-      // an uneven batch with nothing to do but load their length and leave).
-      // Each sequence's count is the kernel's: its cached tokens (all but the
-      // new one) in partitions of `part`, at least one.
-      if (pl.S <= pa::kMaxRankedSeqs && parts <= 256) {
-        std::vector<int> idx(size_t(pl.S));
-        for (int64_t i = 0; i < pl.S; ++i) idx[size_t(i)] = int(i);
-        auto len = [&](int i) { return std::min<int64_t>(std::max<int64_t>(opts->host_context_lens[i], 0), span); };
-        std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return len(x) > len(y); });
-        int items = 0;
-        for (const int sq : idx) {
-          const int64_t cached = std::max<int64_t>(len(sq) - 1, 0);
-          const int64_t np = std::min<int64_t>(std::max<int64_t>((cached + part - 1) / part, 1), parts);
-          if (items + np > pa::kMaxRankedSeqs) { items = -1; break; }
-          for (int64_t j = 0; j < np; ++j) m.d.order[items++] = uint16_t((sq << 8) | int(j));
-        }
-        if (items > 0) {
-          m.d.has_order = 2;
-          m.num_items = items;
-        }
-      }
-      int cus = 0;
-      if ((rc = device_cus(&cus)) != PA_OK) return rc;
-      const pa::LaunchCtx ctx{stream, opts->kernel_start, opts->kernel_stop, cus, opts->host_context_lens};
-      const hipError_t e = pa::launch_multi(m, int(pl.D), int(pl.B), ctx);
-      if (e != hipSuccess) return hip_fail(e, "fused append + split decode launch");
-      return PA_OK;
-    }
+    if (!host_split || !host_length_split(pl, host_lens, &m) ||
+        pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts).total <= workspace_bytes)
+      return launch_fused_step(pl, &m, opts, workspace, stream);
   }
-  if (fuse_unsplit) {
-    // unsplit MFMA schedule: the multi-token kernel with one new token per
-    // sequence stores it and attends in one launch
-    const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
-    pa::MultiParams m;
-    if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
-                           g, scale, 1, &m)) != PA_OK)
-      return rc;
-    int cus = 0;
-    if ((rc = device_cus(&cus)) != PA_OK) return rc;
-    const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus,
-                            opts ? opts->host_context_lens : nullptr};
-    const hipError_t e = pa::launch_multi(m, int(pl.D), int(pl.B), ctx);
-    if (e != hipSuccess) return hip_fail(e, "fused append + decode launch");
-    return PA_OK;
-  }
-  // otherwise the append kernel, then the decode the plan chose (contracts
-  // were checked above)
   if ((rc = cache_append_impl(k, v, slot_mapping, k_cache, v_cache, false, stream)) != PA_OK) return rc;
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, opts, false,
                        workspace, workspace_bytes, false, stream);
