@@ -22,6 +22,8 @@
  *   pa_decode_multi  several new tokens per sequence (chunked prefill,
  *                    speculative verification): their append and their causal
  *                    attention in one launch.
+ *   pa_decode_multi_ex, pa_decode_multi_workspace_bytes  the same with
+ *                    options and the caller's workspace (no allocation).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -353,6 +355,52 @@ int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, 
                     const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,
                     pa_tensor* v_cache, const pa_tensor* block_tables, const pa_tensor* context_lens,
                     float scale, int32_t block_size, int32_t max_query_len, hipStream_t stream);
+
+/*
+ * pa_decode_multi_ex -- pa_decode_multi with options and the caller's
+ * workspace: it allocates nothing, so it may be captured into a HIP graph.
+ *
+ *   opts          NULL (as pa_decode_multi) or pa_decode_opts:
+ *                   partition_tokens  0 automatic (as pa_decode_multi), -1
+ *                                     never split, else partitions of this
+ *                                     many cached tokens (a positive multiple
+ *                                     of 32); -2 (stream-K) is
+ *                                     PA_ERR_UNSUPPORTED here;
+ *                   path              0 or 2 (the multi-token kernels are
+ *                                     MFMA only; 1 is PA_ERR_UNSUPPORTED);
+ *                   max_context_len   0, or a bound on every context_lens[s]
+ *                                     that sizes a split;
+ *                   workgroups_per_cu, reserved  must be 0;
+ *                   kernel_start, kernel_stop  as for pa_decode_ex (the main
+ *                                     kernel, not the combine);
+ *                   host_context_lens as for pa_decode_ex: unsplit launches
+ *                                     rank the sequences on the host, and
+ *                                     where max_context_len is 0 the longest
+ *                                     of them bounds a split.
+ *   workspace, workspace_bytes  device memory, 256-byte aligned, of at least
+ *                 pa_decode_multi_workspace_bytes(T, num_seqs, num_q_heads,
+ *                 num_kv_heads, head_dim, max_query_len, bound,
+ *                 opts->partition_tokens) bytes, bound being the split's
+ *                 bound above (or anything larger); NULL / 0 when that is 0.
+ *                 PA_ERR_WORKSPACE if too small or misaligned.  Calls that
+ *                 share a workspace must be ordered on one stream.
+ *
+ * Everything else (arguments, preconditions, results) is pa_decode_multi's;
+ * with the same split the two give identical bits.
+ */
+int pa_decode_multi_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
+                       const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,
+                       pa_tensor* v_cache, const pa_tensor* block_tables, const pa_tensor* context_lens,
+                       float scale, int32_t block_size, int32_t max_query_len, const pa_decode_opts* opts,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes pa_decode_multi_ex needs for num_rows (T) new tokens of
+ * num_seqs sequences, max_query_len rows per sequence at most, cached
+ * contexts bounded by max_context_len, and opts.partition_tokens as given
+ * (0 = automatic).  0 when the launch does not split (or for sizes <= 0). */
+size_t pa_decode_multi_workspace_bytes(int64_t num_rows, int64_t num_seqs, int64_t num_q_heads,
+                                       int64_t num_kv_heads, int64_t head_dim, int32_t max_query_len,
+                                       int64_t max_context_len, int32_t partition_tokens);
 
 /* Message of the last failed call on this thread (valid until the next pa_* call). */
 const char* pa_last_error(void);

@@ -22,7 +22,7 @@ MAX_DIMS = 5
 
 EXPORTED = ("pa_append_decode", "pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous",
             "pa_decode_ex",
-            "pa_decode_multi", "pa_decode_workspace_bytes",
+            "pa_decode_multi", "pa_decode_multi_ex", "pa_decode_multi_workspace_bytes", "pa_decode_workspace_bytes",
             "pa_decode_schedule", "pa_last_error", "pa_set_debug")
 
 _DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.int32: PA_I32, torch.int64: PA_I64}
@@ -64,6 +64,13 @@ def load(path=None):
     lib.pa_copy_blocks.argtypes = [P, P, P, ctypes.c_void_p]
     lib.pa_decode_contiguous.argtypes = [P, P, P, P, P, ctypes.c_float, ctypes.c_void_p]
     lib.pa_decode_multi.argtypes = [P] * 10 + [ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    lib.pa_decode_multi_ex.argtypes = [P] * 10 + [ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.POINTER(PaDecodeOpts), ctypes.c_void_p, ctypes.c_size_t,
+                                                  ctypes.c_void_p]
+    lib.pa_decode_multi_ex.restype = ctypes.c_int
+    lib.pa_decode_multi_workspace_bytes.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int32, ctypes.c_int64,
+                                                                           ctypes.c_int32]
+    lib.pa_decode_multi_workspace_bytes.restype = ctypes.c_size_t
     lib.pa_decode_contiguous.restype = ctypes.c_int
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
@@ -157,6 +164,35 @@ def decode_multi(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cac
     _check(lib, lib.pa_decode_multi(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
                                     ctypes.c_int32(block_size), ctypes.c_int32(max_query_len),
                                     _stream(stream)))
+
+
+def decode_multi_ex(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
+                    context_lens, scale, block_size, max_query_len, *, partition_tokens=0, path=0,
+                    max_context_len=0, workspace=None, kernel_events=None, host_context_lens=None, stream=None):
+    """pa_decode_multi_ex: pa_decode_multi with options and a caller-owned workspace (no allocation)."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in (
+        (out, "out"), (q, "q"), (k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),
+        (query_start, "query_start"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+        (block_tables, "block_tables"), (context_lens, "context_lens"))]
+    ds = [describe(x) for x in ts]
+    hl = _host_lens(host_context_lens, context_lens)
+    opts = _opts(partition_tokens, path, max_context_len, 0, kernel_events, hl)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib, lib.pa_decode_multi_ex(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
+                                       ctypes.c_int32(block_size), ctypes.c_int32(max_query_len), ctypes.byref(opts),
+                                       ctypes.c_void_p(ws_ptr) if ws_ptr else None, ctypes.c_size_t(ws_bytes),
+                                       _stream(stream)))
+
+
+def multi_workspace_bytes(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim, max_query_len,
+                          max_context_len, partition_tokens=0):
+    """pa_decode_multi_workspace_bytes."""
+    return int(load().pa_decode_multi_workspace_bytes(int(num_rows), int(num_seqs), int(num_q_heads),
+                                                      int(num_kv_heads), int(head_dim), int(max_query_len),
+                                                      int(max_context_len), int(partition_tokens)))
 
 
 def copy_blocks(k_cache, v_cache, block_pairs, stream=None):

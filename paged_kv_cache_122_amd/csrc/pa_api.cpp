@@ -624,15 +624,23 @@ namespace {
 
 // Kernel arguments of the multi-token kernel (shapes already validated);
 // query_start may be NULL: one new token per sequence, row s.
+// MFMA column sets and groups of a multi-token launch: columns are (new
+// token, query head) pairs, at most 16 per set and two sets per workgroup.
+void multi_columns(int64_t max_query_len, int64_t G, int* col_sets, int64_t* col_groups) {
+  const int64_t cols = max_query_len * G;
+  *col_sets = cols > 16 ? 2 : 1;
+  *col_groups = (cols + 16 * *col_sets - 1) / (16 * *col_sets);
+}
+
 int multi_params(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
                  const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,
                  pa_tensor* v_cache, const pa_tensor* block_tables, const pa_tensor* context_lens,
                  const CacheGeom& g, float scale, int32_t max_query_len, pa::MultiParams* mp) {
   const int64_t T = q->shape[0], Hq = q->shape[1], S = context_lens->shape[0];
   const int64_t G = Hq / g.kv_heads, W = block_tables->shape[1];
-  const int64_t cols = int64_t(max_query_len) * G;  // MFMA columns per (sequence, KV head)
-  const int col_sets = cols > 16 ? 2 : 1;
-  const int64_t col_groups = (cols + 16 * col_sets - 1) / (16 * col_sets);
+  int col_sets = 1;
+  int64_t col_groups = 1;
+  multi_columns(max_query_len, G, &col_sets, &col_groups);
   if (g.kv_heads * col_groups > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "grid too large");
   pa::MultiParams m{};
   pa::DecodeParams& p = m.d;
@@ -736,12 +744,26 @@ int debug_check_multi(const pa_tensor* slot_mapping, const pa_tensor* query_star
 
 }  // namespace
 
-PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new,
-                              const pa_tensor* v_new, const pa_tensor* slot_mapping,
-                              const pa_tensor* query_start, pa_tensor* k_cache, pa_tensor* v_cache,
-                              const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
-                              int32_t block_size, int32_t max_query_len, hipStream_t stream) {
-  g_error.clear();
+namespace {
+
+// The automatic split of a multi-token launch: when its grid would fill less
+// than half the GPU, partitions (multiples of 256 tokens, at least 512) so
+// that the workgroups cover the cached context about twice; 0 = no split.
+int64_t multi_auto_part(int64_t pairs, int64_t max_len) {
+  if (pairs >= kFullGpuPairs) return 0;
+  const int64_t want = (kFullGpuPairs + pairs - 1) / pairs;
+  int64_t part = std::max<int64_t>(512, ((max_len + want - 1) / want + 255) / 256 * 256);
+  while ((max_len + part - 1) / part > 65535) part *= 2;
+  return part < max_len ? part : 0;
+}
+
+// pa_decode_multi and pa_decode_multi_ex: `owned` takes the library
+// workspace, else the caller's.
+int multi_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, const pa_tensor* v_new,
+                 const pa_tensor* slot_mapping, const pa_tensor* query_start, pa_tensor* k_cache,
+                 pa_tensor* v_cache, const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                 int32_t block_size, int32_t max_query_len, const pa_decode_opts* opts, bool owned,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
   int rc;
   CacheGeom g;
   if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
@@ -800,35 +822,119 @@ PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tenso
                               g.block_size, g.num_blocks, max_query_len, stream)) != PA_OK)
     return rc;
 
+  if (opts) {
+    if (opts->reserved != 0) return fail(PA_ERR_INVALID, "opts.reserved must be 0");
+    if (opts->path == 1) return fail(PA_ERR_UNSUPPORTED, "the multi-token path runs on MFMA only (opts.path 0 or 2)");
+    if (opts->path != 0 && opts->path != 2) return fail(PA_ERR_INVALID, "opts.path %d (expected 0 or 2)", opts->path);
+    if (opts->workgroups_per_cu != 0) return fail(PA_ERR_INVALID, "opts.workgroups_per_cu must be 0 here");
+    if (opts->partition_tokens == -2) return fail(PA_ERR_UNSUPPORTED, "no stream-K schedule for several new tokens");
+    if (opts->partition_tokens < -2 || (opts->partition_tokens > 0 && opts->partition_tokens % 32))
+      return fail(PA_ERR_INVALID, "opts.partition_tokens %d (0, -1 or a positive multiple of 32)",
+                  opts->partition_tokens);
+    if (opts->max_context_len < 0) return fail(PA_ERR_INVALID, "opts.max_context_len < 0");
+    if ((opts->kernel_start == nullptr) != (opts->kernel_stop == nullptr))
+      return fail(PA_ERR_INVALID, "opts.kernel_start and opts.kernel_stop: both or neither");
+  }
+  const int32_t* host_lens = opts ? opts->host_context_lens : nullptr;
+  if (S == 0 || T == 0 || max_query_len == 0) return PA_OK;
+  if (g_debug.load()) {
+    if ((rc = debug_check_multi(slot_mapping, query_start, block_tables, context_lens, S, T, W, g.block_size,
+                                g.num_blocks, max_query_len, stream)) != PA_OK)
+      return rc;
+    if (host_lens) {
+      std::vector<int32_t> lens;
+      if ((rc = copy_to_host(&lens, context_lens->data, size_t(S), stream)) != PA_OK) return rc;
+      for (int64_t s = 0; s < S; ++s)
+        if (host_lens[s] != lens[size_t(s)])
+          return fail(PA_ERR_CONTRACT, "opts.host_context_lens[%lld] = %lld, but context_lens[%lld] = %lld",
+                      (long long)s, (long long)host_lens[s], (long long)s, (long long)lens[size_t(s)]);
+    }
+  }
+
   pa::MultiParams m;
   if ((rc = multi_params(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
                          context_lens, g, scale, max_query_len, &m)) != PA_OK)
     return rc;
-  // Split the cached context when the grid would leave the GPU half empty:
-  // partitions (multiples of 256 tokens, at least 512) so that the
-  // workgroups cover it about twice; the pieces go to the library workspace.
-  const int64_t pairs = S * g.kv_heads * m.col_groups, max_len = W * g.block_size;
-  if (pairs < kFullGpuPairs) {
-    const int64_t want = (kFullGpuPairs + pairs - 1) / pairs;
-    int64_t part = std::max<int64_t>(512, ((max_len + want - 1) / want + 255) / 256 * 256);
-    while ((max_len + part - 1) / part > 65535) part *= 2;
-    if (part < max_len) {
-      const int64_t parts = (max_len + part - 1) / part;
-      const pa::WorkspaceLayout wl = pa::workspace_layout(T, Hq, D, parts);
-      void* ws = nullptr;
+  // the bound on the cached context that sizes a split: opts, else the
+  // longest host length, else the table width
+  int64_t max_len = W * g.block_size;
+  if (opts && opts->max_context_len > 0) {
+    max_len = opts->max_context_len;
+  } else if (host_lens) {
+    int64_t longest = 1;
+    for (int64_t s = 0; s < S; ++s) longest = std::max<int64_t>(longest, host_lens[s]);
+    max_len = std::min(longest, max_len);
+  }
+  const int64_t pairs = S * g.kv_heads * m.col_groups;
+  const int32_t want = opts ? opts->partition_tokens : 0;
+  int64_t part = want == 0 ? multi_auto_part(pairs, max_len) : (want > 0 && want < max_len ? want : 0);
+  if (part > 0) {
+    const int64_t parts = (max_len + part - 1) / part;
+    if (parts > 65535) return fail(PA_ERR_INVALID, "opts.partition_tokens %lld: more than 65535 partitions", (long long)part);
+    const pa::WorkspaceLayout wl = pa::workspace_layout(T, Hq, D, parts);
+    void* ws = nullptr;
+    if (owned) {
       if ((rc = owned_workspace(wl.total, stream, &ws)) != PA_OK) return rc;
-      m.d.part_tokens = int(part);
-      m.d.max_parts = int(parts);
-      m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
-      m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
+    } else {
+      if (!workspace || workspace_bytes < wl.total)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, wl.total);
+      if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+      ws = workspace;
     }
+    m.d.part_tokens = int(part);
+    m.d.max_parts = int(parts);
+    m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
+    m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
   }
   int cus = 0;
   if ((rc = device_cus(&cus)) != PA_OK) return rc;
-  const pa::LaunchCtx ctx{stream, nullptr, nullptr, cus};
+  const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus,
+                          host_lens};
   const hipError_t e = pa::launch_multi(m, int(D), int(g.block_size), ctx);
   if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
   return PA_OK;
+}
+
+}  // namespace
+
+PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new,
+                              const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                              const pa_tensor* query_start, pa_tensor* k_cache, pa_tensor* v_cache,
+                              const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                              int32_t block_size, int32_t max_query_len, hipStream_t stream) {
+  g_error.clear();
+  return multi_common(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
+                      context_lens, scale, block_size, max_query_len, nullptr, true, nullptr, 0, stream);
+}
+
+PA_EXPORT int pa_decode_multi_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new,
+                                 const pa_tensor* v_new, const pa_tensor* slot_mapping,
+                                 const pa_tensor* query_start, pa_tensor* k_cache, pa_tensor* v_cache,
+                                 const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
+                                 int32_t block_size, int32_t max_query_len, const pa_decode_opts* opts,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_error.clear();
+  return multi_common(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
+                      context_lens, scale, block_size, max_query_len, opts, false, workspace, workspace_bytes,
+                      stream);
+}
+
+PA_EXPORT size_t pa_decode_multi_workspace_bytes(int64_t num_rows, int64_t num_seqs, int64_t num_q_heads,
+                                                 int64_t num_kv_heads, int64_t head_dim, int32_t max_query_len,
+                                                 int64_t max_context_len, int32_t partition_tokens) {
+  if (num_rows <= 0 || num_seqs <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
+      max_query_len <= 0 || max_context_len <= 0 || head_dim <= 0)
+    return 0;
+  int col_sets = 1;
+  int64_t col_groups = 1;
+  multi_columns(max_query_len, num_q_heads / num_kv_heads, &col_sets, &col_groups);
+  const int64_t pairs = num_seqs * num_kv_heads * col_groups;
+  const int64_t part = partition_tokens == 0 ? multi_auto_part(pairs, max_context_len)
+                                             : (partition_tokens > 0 && partition_tokens < max_context_len
+                                                    ? partition_tokens : 0);
+  if (part <= 0) return 0;
+  return pa::workspace_layout(num_rows, num_q_heads, head_dim, (max_context_len + part - 1) / part).total;
 }
 
 namespace {

@@ -327,3 +327,52 @@ def test_host_context_lens_marshalling():
     assert o.host_context_lens == a.ctypes.data
     assert pa._opts(0, 0, 0, 0, None, None).host_context_lens is None
     assert ctypes.sizeof(pa.PaDecodeOpts) == 48
+
+
+def test_decode_multi_ex_validation(lib):
+    """pa_decode_multi_ex checks its options and the workspace before any launch
+    (fake pointers: every call fails validation or is a no-op)."""
+    r = ctypes.byref
+
+    def call(opts=None, ws=None, ws_bytes=0, S=4, T=10, W=8, Hq=8, Hkv=2, D=128, B=16, NB=64, mql=5):
+        out, q = T_([T, Hq, D], pa.PA_BF16), T_([T, Hq, D], pa.PA_BF16)
+        k_new, v_new = T_([T, Hkv, D], pa.PA_BF16), T_([T, Hkv, D], pa.PA_BF16)
+        sl, qst = T_([T], pa.PA_I64), T_([S + 1], pa.PA_I32)
+        kc, vc = T_([NB, Hkv, D // 8, B, 8], pa.PA_BF16), T_([NB, Hkv, B // 4, D, 4], pa.PA_BF16)
+        bt, ln = T_([S, W], pa.PA_I32), T_([S], pa.PA_I32)
+        return lib.pa_decode_multi_ex(r(out), r(q), r(k_new), r(v_new), r(sl), r(qst), r(kc), r(vc), r(bt), r(ln),
+                                      0.1, B, mql, r(opts) if opts is not None else None, ws, ws_bytes, None)
+
+    O = pa.PaDecodeOpts
+    assert call(O(0, 1, 0)) == pa.PA_ERR_UNSUPPORTED          # VALU: the multi-token kernels are MFMA only
+    assert call(O(0, 3, 0)) == pa.PA_ERR_INVALID
+    assert call(O(-2, 0, 0)) == pa.PA_ERR_UNSUPPORTED         # no stream-K for several new tokens
+    assert call(O(48, 0, 0)) == pa.PA_ERR_INVALID             # not a multiple of 32
+    assert call(O(-3, 0, 0)) == pa.PA_ERR_INVALID
+    assert call(O(0, 0, -1)) == pa.PA_ERR_INVALID             # max_context_len < 0
+    assert call(O(0, 0, 0, 1)) == pa.PA_ERR_INVALID           # workgroups_per_cu
+    assert call(O(0, 0, 0, 0, 1)) == pa.PA_ERR_INVALID        # reserved
+    assert call(O(0, 0, 0, 0, 0, 0x1000, None)) == pa.PA_ERR_INVALID
+    assert call(O(0, 0, 0), S=0) == pa.PA_OK                  # nothing to do
+    # 8 (sequence, KV head) pairs over 8192-token tables split: the workspace is checked
+    need = lib.pa_decode_multi_workspace_bytes(10, 4, 8, 2, 128, 5, 512 * 16, 0)
+    assert need > 0
+    assert call(O(0, 0, 0), W=512) == pa.PA_ERR_WORKSPACE
+    assert call(O(0, 0, 0), W=512, ws=0x1000, ws_bytes=need - 256) == pa.PA_ERR_WORKSPACE
+    assert call(O(0, 0, 0), W=512, ws=0x1010, ws_bytes=need) == pa.PA_ERR_WORKSPACE   # not 256-byte aligned
+    assert call(None, W=512) == pa.PA_ERR_WORKSPACE
+
+
+def test_multi_workspace_bytes(lib):
+    f = lib.pa_decode_multi_workspace_bytes
+    up = lambda x: (x + 255) // 256 * 256
+    # 8 seqs x 5 rows (40), 32 q / 8 kv heads: 20 columns in one workgroup per KV head, 64 pairs; the
+    # automatic split cuts 32k-token contexts into partitions of 4096 (about 512 workgroups)
+    assert f(40, 8, 32, 8, 128, 5, 32768, 0) == up(4 * 2 * 40 * 32 * 8) + up(4 * 40 * 32 * 8 * 128)
+    assert f(40, 8, 32, 8, 128, 5, 32768, 2048) == up(4 * 2 * 40 * 32 * 16) + up(4 * 40 * 32 * 16 * 128)
+    assert f(40, 8, 32, 8, 128, 5, 32768, -1) == 0            # never split
+    assert f(320, 64, 32, 8, 128, 5, 2048, 0) == 0            # 512 pairs: no split
+    assert f(40, 8, 32, 8, 128, 5, 512, 0) == 0               # one partition: no split
+    assert f(40, 8, 32, 8, 128, 5, 1024, 1024) == 0           # partition as long as the bound
+    assert f(0, 8, 32, 8, 128, 5, 32768, 0) == 0
+    assert f(40, 8, 30, 8, 128, 5, 32768, 0) == 0             # heads not a multiple

@@ -1,7 +1,8 @@
 """GPU check that the entry points which take the caller's workspace allocate
 nothing and can be captured into a HIP graph: pa_append_decode (the fused
 one-launch step, the host-length split step with its row combine, and the
-append-then-partitioned step with its combine) and pa_decode_ex (stream-K).
+append-then-partitioned step with its combine), pa_decode_ex (stream-K) and
+pa_decode_multi_ex (several new tokens, split, with the row combine).
 Each graph is replayed several times, with eager work and a synchronisation
 between replays, and every replay's output must equal the eager call's bit for
 bit (the kernels are deterministic and the step's append is idempotent)."""
@@ -19,6 +20,7 @@ CASES = [
     ("long32k_b16", "append_decode"),             # host-length partitions + row combine
     ("opt13b_mha_prefix_b128", "append_decode"),  # append kernel, shared partitions, combine
     ("long32k_b16", "decode_ex"),                 # stream-K + its combine
+    ("long32k_verify5_b16", "decode_multi_ex"),   # several new tokens, split + row combine
 ]
 
 
@@ -32,7 +34,12 @@ def test_graph_replay_matches_eager(name, call):
     print(f"[{name} {call}] S={w.num_seqs}", flush=True)
     dw = dev.upload(w)
     maxlen = w.table_width * w.block_size
-    nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen, 0)
+    if call == "decode_multi_ex":
+        mql = int(np.diff(w.query_start).max())
+        nb = pa.multi_workspace_bytes(w.q.shape[0], w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, mql,
+                                      maxlen, 0)
+    else:
+        nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen, 0)
     ws = pa.alloc_workspace(nb, "cuda") if nb else None
     hl = np.asarray(w.context_lens, dtype=np.int32)
     out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
@@ -42,6 +49,10 @@ def test_graph_replay_matches_eager(name, call):
             pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
                              dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=ws,
                              host_context_lens=hl)
+        elif call == "decode_multi_ex":
+            pa.decode_multi_ex(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache,
+                               dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size, mql,
+                               workspace=ws)
         else:
             pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
                          w.block_size, workspace=ws)

@@ -219,3 +219,52 @@ def test_multi_split_edges(name, old, new, hq, hkv, d, b):
     got, dw = run_multi(w, out_f32=True)
     check_pools(w, dw, kst, vst)
     assert_close(got, ref, name)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_verify5_b64", "long32k_verify5_b16"])
+def test_multi_ex_matches_multi(name):
+    """pa_decode_multi_ex with the caller's workspace (sized by
+    pa_decode_multi_workspace_bytes) equals pa_decode_multi bit for bit on the
+    same split, also with host lengths (placement only here); explicit
+    partitions and never-split runs match the oracle; kernel events time the
+    main kernel."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.make(name)
+    print(f"[{name}] T={w.q.shape[0]} S={w.num_seqs}", flush=True)
+    dw = dev.upload(w)
+    T = w.q.shape[0]
+    mql = int(np.diff(w.query_start).max())
+    span = w.table_width * w.block_size
+    hl = np.asarray(w.context_lens, dtype=np.int32)
+
+    def run(ex, **kw):
+        out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+        args = (out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache, dw.v_cache,
+                dw.block_tables, dw.context_lens, w.scale, w.block_size, mql)
+        if ex:
+            bound = kw.pop("bound", span)
+            nb = pa.multi_workspace_bytes(T, w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, mql, bound,
+                                          kw.get("partition_tokens", 0))
+            ws = pa.alloc_workspace(nb, "cuda") if nb else None
+            pa.decode_multi_ex(*args, workspace=ws, **kw)
+        else:
+            pa.decode_multi(*args)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    ref_bits = run(False)
+    for kw in ({}, {"host_context_lens": hl, "bound": int(hl.max())}):
+        got = run(True, **kw)
+        assert np.array_equal(got.view(np.uint32), ref_bits.view(np.uint32)), f"{name} {list(kw)}"
+    _, _, ref = oracle_multi(w)
+    assert_close(run(True, partition_tokens=1024), ref, f"{name} partitions of 1024")
+    assert_close(run(True, partition_tokens=-1), ref, f"{name} never split")
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    run(True, kernel_events=(a, b))
+    assert a.elapsed_time(b) > 0
+    del dw
+    torch.cuda.empty_cache()
