@@ -225,14 +225,29 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
     stream.synchronize()
     multi_ms = [tev.elapsed_ms(a, b) for a, b, _, _ in ev]
     single_ms = [tev.elapsed_ms(c, d) for _, _, c, d in ev]
+    # the main kernel alone: pa_decode_multi_ex with the caller's workspace,
+    # the host copy of the lengths and GPU-stamped events around the kernel
     T = int(w.q.shape[0])
+    span = int(w.block_tables.shape[1]) * w.block_size
+    nb = pa.multi_workspace_bytes(T, w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, mql, span, 0)
+    ws = pa.alloc_workspace(nb, "cuda:0") if nb else None
+    host_lens = np.asarray(w.context_lens, dtype=np.int32)
+    kev = [(E(), E()) for _ in range(steps)]
+    for a, b in kev:
+        flush.zero_()
+        pa.decode_multi_ex(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache,
+                           dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size, mql,
+                           workspace=ws, kernel_events=(a, b), host_context_lens=host_lens, stream=stream)
+    stream.synchronize()
+    kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
     new_kv = T * w.num_kv_heads * w.head_dim * 2 * 2
     # K/V of every context token read once (cached ones from the pool, new ones
     # from k_new / v_new), the new K/V written, q read and out written
     algo = w.unique_kv_bytes() + new_kv + 2 * T * w.num_q_heads * w.head_dim * 2
     mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     t = mean(multi_ms) / 1e3
-    del dw
+    tk = mean(kernel_ms) / 1e3
+    del dw, ws
     return {
         "workload": w.name,
         "num_seqs": w.num_seqs,
@@ -244,13 +259,17 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
         "achieved_gbs": round(algo / t / 1e9, 2),
         "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
         "kernel": kernel,
+        "kernel_ms": {"mean": round(mean(kernel_ms), 5), "p50": round(percentile(kernel_ms, 50), 5)},
+        "kernel_achieved_gbs": round(algo / tk / 1e9, 2),
+        "kernel_hbm_frac": round(algo / tk / 1e9 / HBM_PEAK_GBS, 4),
         "traffic": measured_traffic(w.name, kernel),
         "mfma_busy_pct": measured_mfma(w.name, kernel),
         "tokens_per_s": round(T / t, 1),
         "single_token_decode_same_pools_call_ms": round(mean(single_ms), 5),
         "note": "pa_decode_multi (append fused, causal over cached + drafted tokens) vs pa_decode of "
                 "one token per sequence on the same pools, alternating, each after a cache flush, "
-                "events around the call (launch included)",
+                "events around the call (launch included); kernel_ms: the main kernel alone through "
+                "pa_decode_multi_ex (caller workspace, host lengths), GPU-stamped events",
     }
 
 
