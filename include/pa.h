@@ -374,7 +374,11 @@ int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, 
  *                   kernel_start, kernel_stop  as for pa_decode_ex (the main
  *                                     kernel, not the combine);
  *                   host_context_lens as for pa_decode_ex: unsplit launches
- *                                     rank the sequences on the host, and
+ *                                     rank the sequences on the host; an
+ *                                     automatic split with few pairs is sized
+ *                                     on them, launching only the partitions
+ *                                     that hold tokens (within the workspace
+ *                                     given; else the shape-only split), and
  *                                     where max_context_len is 0 the longest
  *                                     of them bounds a split.
  *   workspace, workspace_bytes  device memory, 256-byte aligned, of at least

@@ -746,6 +746,54 @@ int debug_check_multi(const pa_tensor* slot_mapping, const pa_tensor* query_star
 
 namespace {
 
+// Partitions of the multi-token kernel sized on the host's lengths, so that
+// about kFullGpuPairs workgroups share the tokens evenly: their size, count
+// and, within the limits of the kernel-argument list, the (sequence,
+// partition) items that hold tokens, longest contexts first.  Returns false
+// where every context fits one partition (then the unsplit kernel is the
+// better launch).  A grid over every sequence's table span would leave most
+// workgroups of an uneven batch with nothing to do but load their length and
+// leave.  Each sequence's count is the kernel's: its cached tokens (all but
+// its `new_tokens` new ones) in partitions of `part`, at least one; with
+// new_tokens 0 (counts unknown to the host) an upper bound, whose surplus
+// items find no tokens and leave.
+bool host_length_split(int64_t S, int64_t Hkv, int64_t span, const int32_t* host_lens, int64_t new_tokens,
+                       pa::MultiParams* m) {
+  auto len = [&](int64_t i) { return std::min<int64_t>(std::max<int64_t>(host_lens[i], 0), span); };
+  int64_t tokens = 0, longest = 0;
+  for (int64_t s = 0; s < S; ++s) {
+    tokens += len(s);
+    longest = std::max(longest, len(s));
+  }
+  const int64_t row_wgs = Hkv * m->col_groups;
+  int64_t part = std::max<int64_t>(512, ((tokens * row_wgs + kFullGpuPairs - 1) / kFullGpuPairs + 255) / 256 * 256);
+  while ((span + part - 1) / part > 65535) part *= 2;
+  if (longest - new_tokens <= part) return false;
+  const int64_t parts = (span + part - 1) / part;
+  m->d.part_tokens = int(part);
+  m->d.max_parts = int(parts);
+  if (S <= pa::kMaxRankedSeqs && parts <= 256) {
+    std::vector<int> idx(static_cast<size_t>(S));
+    for (int64_t i = 0; i < S; ++i) idx[size_t(i)] = int(i);
+    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return len(x) > len(y); });
+    int items = 0;
+    for (const int sq : idx) {
+      const int64_t cached = std::max<int64_t>(len(sq) - new_tokens, 0);
+      const int64_t np = std::min<int64_t>(std::max<int64_t>((cached + part - 1) / part, 1), parts);
+      if (items + np > pa::kMaxRankedSeqs) {
+        items = -1;
+        break;
+      }
+      for (int64_t j = 0; j < np; ++j) m->d.order[items++] = uint16_t((sq << 8) | int(j));
+    }
+    if (items > 0) {
+      m->d.has_order = 2;
+      m->num_items = items;
+    }
+  }
+  return true;
+}
+
 // The automatic split of a multi-token launch: when its grid would fill less
 // than half the GPU, partitions (multiples of 256 tokens, at least 512) so
 // that the workgroups cover the cached context about twice; 0 = no split.
@@ -755,6 +803,19 @@ int64_t multi_auto_part(int64_t pairs, int64_t max_len) {
   int64_t part = std::max<int64_t>(512, ((max_len + want - 1) / want + 255) / 256 * 256);
   while ((max_len + part - 1) / part > 65535) part *= 2;
   return part < max_len ? part : 0;
+}
+
+// The multi-token launch as planned (with the caller's timing events).
+int launch_multi_plan(const pa::MultiParams& m, const pa_decode_opts* opts, int64_t D, int64_t B,
+                      const int32_t* host_lens, hipStream_t stream) {
+  int cus = 0;
+  int rc;
+  if ((rc = device_cus(&cus)) != PA_OK) return rc;
+  const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus,
+                          host_lens};
+  const hipError_t e = pa::launch_multi(m, int(D), int(B), ctx);
+  if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
+  return PA_OK;
 }
 
 // pa_decode_multi and pa_decode_multi_ex: `owned` takes the library
@@ -867,6 +928,27 @@ int multi_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, con
   }
   const int64_t pairs = S * g.kv_heads * m.col_groups;
   const int32_t want = opts ? opts->partition_tokens : 0;
+  if (host_lens && want == 0 && pairs < kFullGpuPairs) {
+    // automatic split with the host's lengths: partitions sized on them and
+    // only those holding tokens launched (as pa_append_decode), or no split
+    // where every context fits one; the shape-only split below where the
+    // caller's workspace is too small for that plan
+    pa::MultiParams hm = m;
+    if (!host_length_split(S, g.kv_heads, W * g.block_size, host_lens, 0, &hm))
+      return launch_multi_plan(m, opts, D, g.block_size, host_lens, stream);
+    const pa::WorkspaceLayout wl = pa::workspace_layout(T, Hq, D, hm.d.max_parts);
+    void* ws = nullptr;
+    if (owned) {
+      if ((rc = owned_workspace(wl.total, stream, &ws)) != PA_OK) return rc;
+    } else if (workspace && workspace_bytes >= wl.total && !(reinterpret_cast<uintptr_t>(workspace) & 255u)) {
+      ws = workspace;
+    }
+    if (ws) {
+      hm.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
+      hm.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
+      return launch_multi_plan(hm, opts, D, g.block_size, host_lens, stream);
+    }
+  }
   int64_t part = want == 0 ? multi_auto_part(pairs, max_len) : (want > 0 && want < max_len ? want : 0);
   if (part > 0) {
     const int64_t parts = (max_len + part - 1) / part;
@@ -887,13 +969,7 @@ int multi_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, con
     m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.ml_off);
     m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.o_off);
   }
-  int cus = 0;
-  if ((rc = device_cus(&cus)) != PA_OK) return rc;
-  const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr, cus,
-                          host_lens};
-  const hipError_t e = pa::launch_multi(m, int(D), int(g.block_size), ctx);
-  if (e != hipSuccess) return hip_fail(e, "multi-token decode launch");
-  return PA_OK;
+  return launch_multi_plan(m, opts, D, g.block_size, host_lens, stream);
 }
 
 }  // namespace
@@ -1029,52 +1105,6 @@ int debug_check_append_slots(const DecodePlan& pl, const pa_tensor* slot_mapping
   return PA_OK;
 }
 
-// Partitions of the multi-token kernel sized on the host's lengths, so that
-// about kFullGpuPairs workgroups share the tokens evenly: their size, count
-// and, within the limits of the kernel-argument list, the (sequence,
-// partition) items that hold tokens, longest contexts first.  Returns false
-// where every context fits one partition (then the unsplit kernel is the
-// better launch).  A grid over every sequence's table span would leave most
-// workgroups of an uneven batch with nothing to do but load their length and
-// leave; each sequence's count is the kernel's (its cached tokens, all but the
-// new one, in partitions of `part`, at least one).
-bool host_length_split(const DecodePlan& pl, const int32_t* host_lens, pa::MultiParams* m) {
-  const int64_t span = pl.W * pl.B;
-  auto len = [&](int64_t i) { return std::min<int64_t>(std::max<int64_t>(host_lens[i], 0), span); };
-  int64_t tokens = 0, longest = 0;
-  for (int64_t s = 0; s < pl.S; ++s) {
-    tokens += len(s);
-    longest = std::max(longest, len(s));
-  }
-  const int64_t row_wgs = pl.Hkv * m->col_groups;
-  int64_t part = std::max<int64_t>(512, ((tokens * row_wgs + kFullGpuPairs - 1) / kFullGpuPairs + 255) / 256 * 256);
-  while ((span + part - 1) / part > 65535) part *= 2;
-  if (longest - 1 <= part) return false;
-  const int64_t parts = (span + part - 1) / part;
-  m->d.part_tokens = int(part);
-  m->d.max_parts = int(parts);
-  if (pl.S <= pa::kMaxRankedSeqs && parts <= 256) {
-    std::vector<int> idx(size_t(pl.S));
-    for (int64_t i = 0; i < pl.S; ++i) idx[size_t(i)] = int(i);
-    std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return len(x) > len(y); });
-    int items = 0;
-    for (const int sq : idx) {
-      const int64_t cached = std::max<int64_t>(len(sq) - 1, 0);
-      const int64_t np = std::min<int64_t>(std::max<int64_t>((cached + part - 1) / part, 1), parts);
-      if (items + np > pa::kMaxRankedSeqs) {
-        items = -1;
-        break;
-      }
-      for (int64_t j = 0; j < np; ++j) m->d.order[items++] = uint16_t((sq << 8) | int(j));
-    }
-    if (items > 0) {
-      m->d.has_order = 2;
-      m->num_items = items;
-    }
-  }
-  return true;
-}
-
 // One launch of the multi-token kernel for the step (one new token per
 // sequence): it stores the new token and attends, taking its K/V from k and
 // v; split (m->d.max_parts > 1, pieces in the workspace) a combine follows.
@@ -1149,7 +1179,7 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
                            g, scale, 1, &m)) != PA_OK)
       return rc;
-    if (!host_split || !host_length_split(pl, host_lens, &m) ||
+    if (!host_split || !host_length_split(pl.S, pl.Hkv, pl.W * pl.B, host_lens, 1, &m) ||
         pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts).total <= workspace_bytes)
       return launch_fused_step(pl, &m, opts, workspace, stream);
   }

@@ -268,3 +268,31 @@ def test_multi_ex_matches_multi(name):
     assert a.elapsed_time(b) > 0
     del dw
     torch.cuda.empty_cache()
+
+
+def test_multi_ex_host_lens_uneven():
+    """Uneven contexts with several new tokens each, through pa_decode_multi_ex
+    with host lengths: partitions sized on them, only those holding tokens
+    launched (the counts from whole lengths, an upper bound); pools bit-exact
+    and every row against the oracle."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    w = workloads.multi_query_workload(8800, [20000, 300, 300, 8000, 50, 4100], [5, 3, 1, 4, 2, 16],
+                                       num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                                       name="multi_uneven")
+    kst, vst, ref = oracle_multi(w)
+    dw = dev.upload(w)
+    T = w.q.shape[0]
+    mql = int(np.diff(w.query_start).max())
+    span = w.table_width * w.block_size
+    nb = pa.multi_workspace_bytes(T, w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, mql, span, 0)
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    pa.decode_multi_ex(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache, dw.v_cache,
+                       dw.block_tables, dw.context_lens, w.scale, w.block_size, mql, workspace=ws,
+                       host_context_lens=np.asarray(w.context_lens, dtype=np.int32))
+    torch.cuda.synchronize()
+    check_pools(w, dw, kst, vst)
+    assert_close(out.double().cpu().numpy(), ref, "multi_uneven")
