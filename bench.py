@@ -44,18 +44,18 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "0e190abc206144c68e397ce9c6eb41957486094075969ad8ffd316faaf23f8bf",
-    # the step's one launch: FETCH_SIZE 133788.0 KiB x 1.9999, WRITE_SIZE 1280.0 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.77 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273979414, "write_bytes": 1310720,
-                                                   "mfma_busy_pct": 4.77},
-    # the verification batch: FETCH_SIZE 140618.8 KiB x 1.9999, WRITE_SIZE 4353.5 KiB x 1.0; MfmaUtil 8.53 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287967930, "write_bytes": 4457961,
-                                                           "mfma_busy_pct": 8.53},
-    # long-context verification (split): FETCH_SIZE 524891.1 KiB x 1.9999, WRITE_SIZE 5426.4 KiB x 1.0;
-    # MfmaUtil 11.54 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074904608, "write_bytes": 5556599,
-                                                        "mfma_busy_pct": 11.54},
+    "sources_sha256": "1507643c2b78e3bcd8f4080c0e4a21870bb7302308cd563e50d64b08bdf72d8b",
+    # the step's one launch: FETCH_SIZE 133788.0 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.73 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273982224, "write_bytes": 1310773,
+                                                   "mfma_busy_pct": 4.73},
+    # the verification batch: FETCH_SIZE 140627.5 KiB x 1.9999, WRITE_SIZE 4353.2 KiB x 1.0; MfmaUtil 8.46 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287988687, "write_bytes": 4457682,
+                                                           "mfma_busy_pct": 8.46},
+    # long-context verification (split): FETCH_SIZE 524893.8 KiB x 1.9999, WRITE_SIZE 5426.9 KiB x 1.0;
+    # MfmaUtil 11.41 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074921405, "write_bytes": 5557138,
+                                                        "mfma_busy_pct": 11.41},
 }
 
 

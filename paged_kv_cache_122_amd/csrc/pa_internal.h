@@ -97,6 +97,8 @@ struct MultiParams {
   int col_groups;                  // workgroups per KV head: ceil(max_query_len * G / (16 * col_sets))
   int64_t num_slots;               // num_blocks * block_size
   int num_items;                   // > 0: grid rows from d.order (has_order 2), one partition each
+  int append_rows;                 // > 0 (unsplit grids larger than the GPU holds at once): rows
+                                   // after the sequences' rows that only append, started last
 };
 
 struct CopyParams {

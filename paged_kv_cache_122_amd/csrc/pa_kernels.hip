@@ -1443,6 +1443,46 @@ __device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_
   }
 }
 
+// Piece u of a multi-token call's append: row u / (Hkv * D/8), then the head
+// and 8 dims.  The row is stored where decode_multi's attention workgroups
+// would store it: it lies among the first n of its sequence's rows (n as
+// there), and its slot is in the pool (a negative slot skips the store).
+template <int D, int BS>
+__device__ __forceinline__ void append_piece(const MultiParams& mp, int64_t u) {
+  const DecodeParams& p = mp.d;
+  const int per_row = p.num_kv_heads * (D / 8);
+  const int64_t i64 = u / per_row;
+  if (i64 >= mp.num_rows) return;
+  const int i = int(i64);
+  int s = i, r0 = i, r1 = i + 1;  // no query_start: row s is sequence s's one new token
+  if (mp.query_start) {
+    // the last sequence whose rows start at or before row i (query_start is
+    // non-decreasing), with the kernel's clamping to [0, T)
+    auto start = [&](int k) { return min(max(mp.query_start[k], 0), mp.num_rows); };
+    if (start(0) > i) return;
+    int lo = 0, hi = p.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (start(mid) <= i) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    r0 = start(s);
+    r1 = max(start(s + 1), r0);
+  } else if (i >= p.num_seqs) {
+    return;
+  }
+  const int n = min(min(r1 - r0, clamp_len(p, p.context_lens[s])), mp.max_query_len);
+  if (i - r0 >= n) return;
+  const int rem = int(u - i64 * per_row);
+  const int h = rem / (D / 8);
+  const int piece = rem - h * (D / 8);
+  const int64_t slot = mp.slots[i];
+  if (slot < 0 || slot >= mp.num_slots) return;
+  const u32x4 kv = load16(mp.k_new + size_t(i) * mp.kn_t + size_t(h) * mp.kn_h + piece * 8);
+  const u32x4 vv = load16(mp.v_new + size_t(i) * mp.vn_t + size_t(h) * mp.vn_h + piece * 8);
+  write_slot_piece<D, BS>(mp.k_store, mp.v_store, mp.d.num_kv_heads, slot, h, piece, kv, vv);
+}
+
 // ---------------------------------------------------------------------------
 // several new tokens per sequence (chunked prefill, speculative verification)
 //
@@ -1576,6 +1616,16 @@ void decode_multi(MultiParams mp) {
       part = blockIdx.z;
     }
   } else {
+    // Grids larger than the GPU holds at once end in rows that only append:
+    // the dispatcher starts them last, as slots free up, so that no
+    // attention workgroup holds its slot until its stores are acknowledged
+    // while the reads still saturate the memory (one-wave grids store at the
+    // end of each walk instead).
+    if (int(blockIdx.y) >= p.num_seqs) {
+      append_piece<D, BS>(mp, (int64_t(blockIdx.y) - p.num_seqs) * gridDim.x * kThreads +
+                                  int64_t(blockIdx.x) * kThreads + threadIdx.x);
+      return;
+    }
     s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
     part = 0;
   }
@@ -1604,7 +1654,7 @@ void decode_multi(MultiParams mp) {
   // at the end.
   __shared__ u32x4 park_k[kThreads], park_v[kThreads];
   __shared__ int64_t park_slot[kThreads];
-  const int units = cg == 0 && last ? n * (D / 8) : 0;
+  const int units = cg == 0 && last && mp.append_rows == 0 ? n * (D / 8) : 0;
   const int staged = min(units, kThreads);
   u32x4 app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
   int64_t app_slot = -1;
@@ -1849,15 +1899,20 @@ hipError_t launch_main(K kernel, dim3 grid, dim3 block, const LaunchCtx& c, A...
   return hipGetLastError();
 }
 
-// Split row for ranked_seq: the rows whose workgroups the dispatcher places
-// first, one per compute unit, when the whole grid fits on the machine at
-// once (resident workgroups per compute unit from the kernel's occupancy);
-// else every row, which is plain longest-first.
+// Workgroups of a kernel that one compute unit holds at once (its occupancy).
 template <typename K>
-int rank_split_for(K kernel, const DecodeParams& p, int row_wgs, const LaunchCtx& c) {
+int resident_per_cu(K kernel) {
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0) != hipSuccess || occ < 1)
     occ = 1;
+  return occ;
+}
+
+// Split row for ranked_seq: the rows whose workgroups the dispatcher places
+// first, one per compute unit, when the whole grid fits on the machine at
+// once (occ resident workgroups per compute unit); else every row, which is
+// plain longest-first.
+inline int rank_split_of(const DecodeParams& p, int row_wgs, int occ, const LaunchCtx& c) {
   const int64_t wgs = int64_t(row_wgs) * p.num_seqs;
   if (wgs > int64_t(c.cus) * occ) return p.num_seqs;
   return int(std::min<int64_t>(p.num_seqs, (c.cus + row_wgs - 1) / row_wgs));
@@ -1882,7 +1937,7 @@ inline void fill_order(DecodeParams& p, const LaunchCtx& c) {
 
 template <typename K>
 hipError_t launch_rows(K kernel, DecodeParams p, int row_wgs, const LaunchCtx& c) {
-  p.rank_split = p.max_parts == 1 ? rank_split_for(kernel, p, row_wgs, c) : p.num_seqs;
+  p.rank_split = p.max_parts == 1 ? rank_split_of(p, row_wgs, resident_per_cu(kernel), c) : p.num_seqs;
   fill_order(p, c);
   return launch_main(kernel, dim3(row_wgs, p.num_seqs, p.max_parts), dim3(kThreads), c, p);
 }
@@ -1989,21 +2044,32 @@ hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCt
 }
 
 template <typename K>
-hipError_t launch_multi_k(K kernel, MultiParams p, const LaunchCtx& c) {
+hipError_t launch_multi_k(K kernel, MultiParams p, int head_dim, const LaunchCtx& c) {
   const int row_wgs = p.d.num_kv_heads * p.col_groups;
   if (p.num_items > 0)  // split over the host's (sequence, partition) list
     return launch_main(kernel, dim3(row_wgs, p.num_items, 1), dim3(kThreads), c, p);
-  p.d.rank_split = p.d.max_parts == 1 ? rank_split_for(kernel, p.d, row_wgs, c) : p.d.num_seqs;
+  const int occ = p.d.max_parts == 1 ? resident_per_cu(kernel) : 1;
+  p.d.rank_split = p.d.max_parts == 1 ? rank_split_of(p.d, row_wgs, occ, c) : p.d.num_seqs;
   fill_order(p.d, c);
-  return launch_main(kernel, dim3(row_wgs, p.d.num_seqs, p.d.max_parts), dim3(kThreads), c, p);
+  // unsplit grids that the GPU cannot hold at once append from rows of their own, started last
+  p.append_rows = 0;
+  if (p.d.max_parts == 1) {
+    if (int64_t(row_wgs) * p.d.num_seqs > int64_t(c.cus) * occ) {
+      const int64_t pieces = int64_t(p.num_rows) * p.d.num_kv_heads * (head_dim / 8);
+      const int64_t per_row = int64_t(row_wgs) * kThreads;
+      const int64_t rows = (pieces + per_row - 1) / per_row;
+      if (p.d.num_seqs + rows <= 65535) p.append_rows = int(rows);
+    }
+  }
+  return launch_main(kernel, dim3(row_wgs, p.d.num_seqs + p.append_rows, p.d.max_parts), dim3(kThreads), c, p);
 }
 
 template <int D, int NS, bool Split>
 hipError_t launch_multi_split(const MultiParams& p, int block_size, const LaunchCtx& c) {
   switch (block_size) {
-    case 8: return launch_multi_k(decode_multi<D, 8, NS, Split>, p, c);
-    case 16: return launch_multi_k(decode_multi<D, 16, NS, Split>, p, c);
-    case 32: return launch_multi_k(decode_multi<D, 32, NS, Split>, p, c);
+    case 8: return launch_multi_k(decode_multi<D, 8, NS, Split>, p, D, c);
+    case 16: return launch_multi_k(decode_multi<D, 16, NS, Split>, p, D, c);
+    case 32: return launch_multi_k(decode_multi<D, 32, NS, Split>, p, D, c);
     default: return hipErrorInvalidValue;
   }
 }
