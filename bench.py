@@ -44,18 +44,18 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "1507643c2b78e3bcd8f4080c0e4a21870bb7302308cd563e50d64b08bdf72d8b",
+    "sources_sha256": "a35779ae562e1edf4bfc0223704e10d86089b742f519cea4ec777c2e6a9b6663",
     # the step's one launch: FETCH_SIZE 133788.0 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.73 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273982224, "write_bytes": 1310773,
-                                                   "mfma_busy_pct": 4.73},
-    # the verification batch: FETCH_SIZE 140627.5 KiB x 1.9999, WRITE_SIZE 4353.2 KiB x 1.0; MfmaUtil 8.46 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287988687, "write_bytes": 4457682,
-                                                           "mfma_busy_pct": 8.46},
-    # long-context verification (split): FETCH_SIZE 524893.8 KiB x 1.9999, WRITE_SIZE 5426.9 KiB x 1.0;
-    # MfmaUtil 11.41 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074921405, "write_bytes": 5557138,
-                                                        "mfma_busy_pct": 11.41},
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.67 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273979013, "write_bytes": 1310843,
+                                                   "mfma_busy_pct": 4.67},
+    # the verification batch: FETCH_SIZE 140627.3 KiB x 1.9999, WRITE_SIZE 4354.1 KiB x 1.0; MfmaUtil 8.59 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287985108, "write_bytes": 4458592,
+                                                           "mfma_busy_pct": 8.59},
+    # long-context verification (split): FETCH_SIZE 524893.6 KiB x 1.9999, WRITE_SIZE 5426.8 KiB x 1.0;
+    # MfmaUtil 11.44 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074908696, "write_bytes": 5557006,
+                                                        "mfma_busy_pct": 11.44},
 }
 
 
@@ -167,7 +167,7 @@ def decode_kernels(w, part, cus):
         return [core + tmpl], "one workgroup per (sequence, head group), no split"
     wgs = w.num_seqs * w.num_kv_heads * -(-g // 16) * parts
     if g <= 16 and wgs >= cus:  # split schedules read shared partitions once
-        return ([f"decode_shared<{w.head_dim},{w.block_size}>", f"combine_parts<{w.head_dim}>"],
+        return ([f"decode_shared<{w.head_dim},{w.block_size},false>", f"combine_parts<{w.head_dim}>"],
                 f"partitions of {part} tokens, shared partitions read once")
     return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
 
@@ -273,28 +273,35 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
     }
 
 
-def fused_step(w, part):
+def fused_step(w, part, cus):
     """How pa_append_decode (given the host copy of the lengths) runs this
-    workload: (append fused into the attention launch, its kernels, what the
-    schedule is).  The unsplit MFMA schedule is one launch; a stream-K batch
-    on the MFMA path runs the multi-token kernel over partitions sized on the
-    lengths (so that about 512 workgroups share the tokens), then the row
-    combine; anything else appends first and decodes as pa_decode_ex does."""
+    workload: (append fused into the decode, its kernels, what the schedule
+    is, whether the main kernel writes the new tokens).  The unsplit MFMA
+    schedule is one launch; a stream-K batch on the MFMA path runs the
+    multi-token kernel over partitions sized on the lengths (so that about 512
+    workgroups share the tokens), then the row combine; a partitioned batch
+    whose grid fills the GPU runs the shared-partition kernel, which takes the
+    new token from k / v, and a combine that stores it; anything else appends
+    first and decodes as pa_decode_ex does."""
     g = w.num_q_heads // w.num_kv_heads
     sets = 2 if g > 16 else 1
     span = w.block_tables.shape[1] * w.block_size
     unsplit = part == -1 or part >= span
     if g >= 3 and unsplit:
         return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},false>"], \
-            "one launch: the new token stored and attended"
+            "one launch: the new token stored and attended", True
     if g >= 3 and part == -2:
         row_wgs = w.num_kv_heads * -(-g // (16 * sets))
         tokens = int(sum(min(max(int(x), 0), span) for x in w.context_lens))
         p = max(512, -(-(-(-tokens * row_wgs // 512)) // 256) * 256)
         return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},true>", f"combine_rows<{w.head_dim}>"], \
             f"partitions of {p} tokens sized on the host's lengths, only those holding tokens launched, " \
-            "the new token stored by the last one; then the row combine"
-    return False, [], "append kernel, then the decode schedule"
+            "the new token stored by the last one; then the row combine", True
+    if part > 0 and not unsplit and g <= 16 and w.num_seqs * w.num_kv_heads * -(-span // part) >= cus:
+        return True, [f"decode_shared<{w.head_dim},{w.block_size},true>", f"combine_append<{w.head_dim},{w.block_size}>"], \
+            f"partitions of {part} tokens, shared partitions read once, the new token taken from k / v by its " \
+            "last partition; then the combine, which stores the new tokens", False
+    return False, [], "append kernel, then the decode schedule", False
 
 
 def percentile(xs, q):
@@ -385,13 +392,16 @@ def main():
     algo_bytes = w.unique_kv_bytes()
     max_len = int(w.block_tables.shape[1]) * w.block_size
     part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
-    kernels, schedule = decode_kernels(w, part, torch.cuda.get_device_properties(0).multi_processor_count)
-    fused, fused_kernels, step_kind = fused_step(w, part)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    kernels, schedule = decode_kernels(w, part, cus)
+    fused, fused_kernels, step_kind, writes_new = fused_step(w, part, cus)
     new_kv_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
     if fused:
-        # the main launch reads the context (the new token from k / v) and writes the new token
+        # the main launch reads the context (the new token from k / v); in one-launch steps it
+        # also writes the new token (else the combine that follows does)
         kernels, schedule = fused_kernels, step_kind
-        algo_bytes += new_kv_bytes
+        if writes_new:
+            algo_bytes += new_kv_bytes
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.Stream()  # default priority
     torch.cuda.synchronize()
@@ -552,8 +562,10 @@ def main():
             "seed": w.seed,
             "step": ("pa_copy_blocks (copy-on-write) + " if has_copies else "")
                     + "pa_append_decode (" + step_kind
-                    + "), with a host copy of the lengths (the sequences ranked on the host), "
-                    "caches flushed before each step",
+                    + "), with a host copy of the lengths"
+                    + (" (the sequences ranked on the host)" if kernels[0].endswith(",false>") and "multi" in kernels[0]
+                       else "")
+                    + ", caches flushed before each step",
             "cow_copies": int(w.copies.shape[0]),
             "schedule": schedule,
         },

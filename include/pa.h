@@ -286,8 +286,15 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * 512-token partitions) and opts carries host_context_lens, the multi-token
  * kernel does both over partitions sized on those lengths (in the workspace),
  * and a second kernel combines each row's partitions; where those lengths
- * fit one partition each, the unsplit fused kernel runs.  Otherwise the
- * append kernel runs, then the decode the schedule chooses.
+ * fit one partition each, the unsplit fused kernel runs.  Where the
+ * schedule is partitioned on the MFMA path (grouping <= 16) and the grid
+ * fills the GPU, the step takes two launches instead of three: the workgroup
+ * of a sequence's last partition in the shared-partition kernel reads the
+ * pool up to the new position and folds the new token in from k / v, and the
+ * combine kernel that follows also stores the new tokens.  Otherwise the
+ * append kernel runs, then the decode the schedule chooses (outputs then
+ * equal the two calls' bit for bit; the fused kernels differ from them only
+ * in rounding).
  *
  *   out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
  *   opts, workspace, workspace_bytes: as for pa_decode_ex (kernel events in
@@ -297,8 +304,8 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  *   slot_mapping  int64 [S]: the slot of that position.
  *
  * The result equals pa_cache_append followed by pa_decode_ex with the same
- * options (up to the rounding of a different split where host lengths pick
- * the partitions).  Preconditions (debug mode checks them, with pa_decode's): for
+ * options, up to rounding where a fused kernel runs or host lengths pick the
+ * partitions.  Preconditions (debug mode checks them, with pa_decode's): for
  * every sequence with L_s > 0, slot_mapping[s] is the slot its block table
  * gives position L_s - 1; a sequence with L_s == 0 has no new token and a
  * negative slot.  Every argument, the workspace included, is checked

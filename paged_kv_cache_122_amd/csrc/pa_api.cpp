@@ -1183,6 +1183,30 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
         pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts).total <= workspace_bytes)
       return launch_fused_step(pl, &m, opts, workspace, stream);
   }
+  if (mfma && !pl.stream && pl.max_parts > 1) {
+    // partitioned: where the schedule runs the shared-partition kernel, it
+    // takes the append too (its last partitions read the new token from k / v)
+    const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
+    pa::MultiParams m;
+    if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,
+                           g, scale, 1, &m)) != PA_OK)
+      return rc;
+    m.d.head_groups = (m.d.group + 15) / 16;
+    m.d.part_tokens = pl.part_tokens;
+    m.d.max_parts = pl.max_parts;
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != PA_OK) return rc;
+    const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr,
+                            cus, host_lens};
+    if (pa::shared_step_applies(m.d, pl.path, ctx)) {
+      const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts);
+      m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+      m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+      const hipError_t e = pa::launch_shared_step(m, int(pl.D), int(pl.B), ctx);
+      if (e != hipSuccess) return hip_fail(e, "fused append + shared-partition decode launch");
+      return PA_OK;
+    }
+  }
   if ((rc = cache_append_impl(k, v, slot_mapping, k_cache, v_cache, false, stream)) != PA_OK) return rc;
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, opts, false,
                        workspace, workspace_bytes, false, stream);

@@ -135,6 +135,12 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
 hipError_t launch_copy(const CopyParams& p, hipStream_t stream);
 hipError_t launch_multi(const MultiParams& p, int head_dim, int block_size, const LaunchCtx& c);
+// A decode step on the partitioned schedule (m.d's partitions, one new token
+// per sequence in m): true where that schedule runs the shared-partition
+// kernel, which then takes the append too (launch_shared_step: one launch and
+// the combine; hipErrorInvalidValue where it does not apply).
+bool shared_step_applies(const DecodeParams& p, Path path, const LaunchCtx& c);
+hipError_t launch_shared_step(const MultiParams& m, int head_dim, int block_size, const LaunchCtx& c);
 // Contiguous control: k_cache / v_cache hold one region of max_len tokens per
 // (sequence, KV head); MFMA path, no split.
 hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCtx& ctx);

@@ -1171,6 +1171,23 @@ __global__ __launch_bounds__(kThreads, (SL == kPipeSlots ? 2 : 1)) void decode_m
   mfma_finish<D>(p, sm, acc, s, h0, ncols, part, nparts, wave, lane);
 }
 
+// Dims 8*piece .. +7 of one token's K and V (kv, vv) into slot `slot` of head h.
+template <int D, int BS>
+__device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_cache, int num_kv_heads,
+                                                 int64_t slot, int h, int piece, u32x4 kv, u32x4 vv) {
+  const int64_t blk = slot / BS;
+  const int off = int(slot - blk * BS);
+  const size_t tile = (size_t(blk) * num_kv_heads + h) * (BS * D);
+  store16(k_cache + tile + (piece * BS + off) * 8, kv);
+  uint16_t* vt = v_cache + tile + ((off >> 2) * D + piece * 8) * 4 + (off & 3);
+  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vt[(2 * e) * 4] = uint16_t(w[e] & 0xffffu);
+    vt[(2 * e + 1) * 4] = uint16_t(w[e] >> 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // shared partitions (partitioned schedule, G <= 16)
 //
@@ -1184,14 +1201,26 @@ __global__ __launch_bounds__(kThreads, (SL == kPipeSlots ? 2 : 1)) void decode_m
 // looks inside the window: s-1 (is s a follower?) and s+1 ... (members).
 // Each member's partial result goes where its own workgroup would have put
 // it, and the combine kernel is unchanged.
+//
+// Fused (a decode step, one new token per sequence, in mp's k_new / v_new /
+// slots): the last token of a sequence's last partition is that token.  The
+// workgroup of the partition walks the pool up to it and folds the new token
+// in from k_new / v_new when it joins the waves; combine_append stores it in
+// the pools afterwards (no workgroup of this kernel reads its slot), so the
+// step needs no append launch before the decode, and no attention workgroup
+// waits at its end for store acknowledgements while the reads saturate the
+// memory.  The new token's block is the sequence's own (it is written), so
+// the workgroup of a last partition carries no other member.
 // ---------------------------------------------------------------------------
 constexpr int kMaxShare = 16;  // members per workgroup at G = 1
 
-template <int D, int BS>
-__global__ __launch_bounds__(kThreads, 2) void decode_shared(DecodeParams p) {
+template <int D, int BS, bool Fused>
+__global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
   __shared__ int differs[kMaxShare + 1];  // window members from s-1: 1 = not sharing s's partition
+  __shared__ float x_new[16];             // fused: the new token's scores (log2 units), by column
+  const DecodeParams& p = mp.d;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int r = lane & 15;
@@ -1209,6 +1238,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(DecodeParams p) {
   const int nparts = partitions(p, L);
   if (part >= (nparts > 0 ? nparts : 1)) return;
   const int t1 = min(L, t0 + p.part_tokens);
+  const bool own_new = Fused && L > 0 && part == nparts - 1;  // workgroup-uniform
+  const int t_walk = own_new ? t1 - 1 : t1;                   // the pool's tokens read here
 
   int m = 1;  // members (sequences s .. s+m-1)
   if (M > 1 && L >= t0 + p.part_tokens) {  // workgroup-uniform: only a filled partition is shared
@@ -1242,10 +1273,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(DecodeParams p) {
   }
   MfmaAcc<D> acc;
   mfma_reset(acc);
-  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
+  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t_walk, wave, lane,
                                 [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-    mfma_tile<D>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
+    mfma_tile<D>(acc, q, p.scale_log2, ts, t_walk, lane, kt, vt);
   });
+
+  if (Fused && own_new) {
+    // the new token's score for s's columns (heads kvh * G + c, c < G):
+    // 16 threads per column, 8 dims each
+    const int c = threadIdx.x >> 4;
+    const int j = threadIdx.x & 15;
+    float dot = 0.f;
+    if (c < G && 8 * j < D) {
+      const u32x4 qv = load16(p.q + size_t(s) * p.q_s + size_t(kvh * G + c) * p.q_h + 8 * j);
+      const u32x4 kv = load16(mp.k_new + size_t(s) * mp.kn_t + size_t(kvh) * mp.kn_h + 8 * j);
+      const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dot = fmaf(bf_lo(qa[e]), bf_lo(ka[e]), dot);
+        dot = fmaf(bf_hi(qa[e]), bf_hi(ka[e]), dot);
+      }
+    }
+    dot += shfl_xor(dot, 1);
+    dot += shfl_xor(dot, 2);
+    dot += shfl_xor(dot, 4);
+    dot += shfl_xor(dot, 8);
+    if (j == 0 && c < G) x_new[c] = dot * p.scale_log2;
+  }
 
   // combine the waves; column c goes to sequence s + c / G, head kvh * G + c % G
   float l = acc.l;
@@ -1276,6 +1330,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(DecodeParams p) {
         o += sm.o[w][d][col] * e;
         lsum += sm.l[w][col] * e;
       }
+    }
+    if (Fused && own_new && col < G) {  // fold in the new token: score x_new[col], value v_new[s, kvh, d]
+      const float x = x_new[col];
+      const float M2 = fmaxf(M_, x);
+      const float a = exp2f(M_ - M2);  // 0 where no pool token was read (M_ = -inf)
+      const float b = exp2f(x - M2);
+      const float v = bf16_value(mp.v_new[size_t(s) * mp.vn_t + size_t(kvh) * mp.vn_h + d]);
+      o = o * a + b * v;
+      lsum = lsum * a + b;
+      M_ = M2;
     }
     const int sc = s + col / G;
     const int h = kvh * G + col % G;
@@ -1424,23 +1488,6 @@ __global__ __launch_bounds__(kThreads, (SL == kPipeSlots ? 2 : 1)) void decode_m
     mfma_tile<D>(acc, q, p.scale_log2, ts, L, lane, kt, vt);
   });
   mfma_finish<D>(p, sm, acc, s, h0, ncols, 0, 1, wave, lane);
-}
-
-// Dims 8*piece .. +7 of one token's K and V (kv, vv) into slot `slot` of head h.
-template <int D, int BS>
-__device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_cache, int num_kv_heads,
-                                                 int64_t slot, int h, int piece, u32x4 kv, u32x4 vv) {
-  const int64_t blk = slot / BS;
-  const int off = int(slot - blk * BS);
-  const size_t tile = (size_t(blk) * num_kv_heads + h) * (BS * D);
-  store16(k_cache + tile + (piece * BS + off) * 8, kv);
-  uint16_t* vt = v_cache + tile + ((off >> 2) * D + piece * 8) * 4 + (off & 3);
-  const uint32_t w[4] = {vv.x, vv.y, vv.z, vv.w};
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    vt[(2 * e) * 4] = uint16_t(w[e] & 0xffffu);
-    vt[(2 * e + 1) * 4] = uint16_t(w[e] >> 16);
-  }
 }
 
 // Piece u of a multi-token call's append: row u / (Hkv * D/8), then the head
@@ -1832,6 +1879,33 @@ __global__ __launch_bounds__(256) void combine_parts(DecodeParams p) {
   store_out(p, s, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
 }
 
+// The same combine after decode_shared's fused step, which also stores the
+// step's new tokens (one per sequence, from mp's k_new / v_new) at their
+// slots: one 16-byte piece of sequence s's token per thread of its row.
+template <int D, int BS>
+__global__ __launch_bounds__(256) void combine_append(MultiParams mp) {
+  const DecodeParams& p = mp.d;
+  const int s = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < p.num_kv_heads * (D / 8)) {
+    const int64_t slot = mp.slots[s];
+    if (slot >= 0 && slot < mp.num_slots) {
+      const int h = idx / (D / 8);
+      const int piece = idx - h * (D / 8);
+      const u32x4 kv = load16(mp.k_new + size_t(s) * mp.kn_t + size_t(h) * mp.kn_h + piece * 8);
+      const u32x4 vv = load16(mp.v_new + size_t(s) * mp.vn_t + size_t(h) * mp.vn_h + piece * 8);
+      write_slot_piece<D, BS>(mp.k_store, mp.v_store, p.num_kv_heads, slot, h, piece, kv, vv);
+    }
+  }
+  if (idx >= p.num_q_heads * D) return;
+  const int nparts = partitions(p, p.context_lens[s]);
+  if (nparts <= 1) return;  // the decode kernel wrote this row directly
+  const int h = idx / D;
+  const int d = idx - h * D;
+  const size_t row0 = (size_t(s) * p.num_q_heads + h) * p.max_parts;
+  store_out(p, s, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
+}
+
 // ---------------------------------------------------------------------------
 // slot-mapped append
 // ---------------------------------------------------------------------------
@@ -1954,7 +2028,8 @@ hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx&
   if (path == Path::Mfma && deep_pipeline(p, c))
     e = launch_rows(decode_mfma<D, BS, kDeepSlots>, p, p.num_kv_heads * p.head_groups, c);
   else if (path == Path::Mfma && p.max_parts > 1 && p.group <= 16)
-    e = launch_rows(decode_shared<D, BS>, p, p.num_kv_heads, c);  // split: shared partitions read once
+    e = launch_main(decode_shared<D, BS, false>, dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c,
+                    MultiParams{p});  // split: shared partitions read once (no ranking)
   else if (path == Path::Mfma)
     e = launch_rows(decode_mfma<D, BS, kPipeSlots>, p, p.num_kv_heads * p.head_groups, c);
   else if (p.group == 1)
@@ -1964,6 +2039,21 @@ hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx&
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
   hipLaunchKernelGGL((combine_parts<D>), cgrid, dim3(256), 0, c.stream, p);
+  return hipGetLastError();
+}
+
+// The partitioned schedule's decode_shared launch with the step's new tokens
+// (one per sequence in m) read from k_new / v_new, then the combine, which
+// stores them.
+template <int D, int BS>
+hipError_t launch_shared_step_d(const MultiParams& m, const LaunchCtx& c) {
+  const DecodeParams& p = m.d;
+  hipError_t e = launch_main(decode_shared<D, BS, true>, dim3(p.num_kv_heads, p.num_seqs, p.max_parts),
+                             dim3(kThreads), c, m);
+  if (e != hipSuccess) return e;
+  // num_kv_heads * D / 8 <= num_q_heads * D: the combine's rows cover the pieces
+  const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
+  hipLaunchKernelGGL((combine_append<D, BS>), cgrid, dim3(256), 0, c.stream, m);
   return hipGetLastError();
 }
 
@@ -2026,6 +2116,23 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
   if (head_dim == 64) return launch_decode_d<64>(p, sk, block_size, path, ctx);
   if (head_dim == 128) return launch_decode_d<128>(p, sk, block_size, path, ctx);
   return hipErrorInvalidValue;
+}
+
+bool shared_step_applies(const DecodeParams& p, Path path, const LaunchCtx& c) {
+  return path == Path::Mfma && p.max_parts > 1 && p.group <= 16 && !deep_pipeline(p, c);
+}
+
+hipError_t launch_shared_step(const MultiParams& m, int head_dim, int block_size, const LaunchCtx& c) {
+  if (!shared_step_applies(m.d, Path::Mfma, c)) return hipErrorInvalidValue;
+  switch (head_dim * 100 + block_size) {
+    case 6408: return launch_shared_step_d<64, 8>(m, c);
+    case 6416: return launch_shared_step_d<64, 16>(m, c);
+    case 6432: return launch_shared_step_d<64, 32>(m, c);
+    case 12808: return launch_shared_step_d<128, 8>(m, c);
+    case 12816: return launch_shared_step_d<128, 16>(m, c);
+    case 12832: return launch_shared_step_d<128, 32>(m, c);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCtx& ctx) {

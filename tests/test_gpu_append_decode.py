@@ -1,8 +1,10 @@
 """GPU checks of pa_append_decode, the decode step in one call: the appended
 pools are bit-exact against the oracle's append, the attention matches the fp64
 oracle (max|err| <= 1e-2, relative RMS <= 2e-3), on the fused one-launch path
-(unsplit MFMA schedules) and on the append-then-decode path (VALU, split and
-stream-K schedules), where it equals pa_cache_append + pa_decode_ex bit for bit."""
+(unsplit MFMA schedules), on the partitioned schedule whose shared-partition
+kernel takes the append (one launch and the combine), and on the
+append-then-decode path (VALU, small split batches, stream-K), where it equals
+pa_cache_append + pa_decode_ex bit for bit."""
 
 import numpy as np
 import pytest
@@ -58,14 +60,15 @@ def test_append_decode_parity(name, opts, n_check):
 
 
 def test_append_decode_equals_two_calls_where_unfused():
-    """Split and VALU schedules run the append kernel, then pa_decode_ex's own
-    kernels: the output equals the two separate calls bit for bit."""
+    """Stream-K, VALU and small partitioned batches (the deep pipeline) run the
+    append kernel, then pa_decode_ex's own kernels: the output equals the two
+    separate calls bit for bit."""
     torch = need_gpu()
     from paged_kv_cache_122_amd import _lib as pa
     from paged_kv_cache_122_amd import device as dev
 
-    for name, opts in (("llama3_8b_b64", {"partition_tokens": 512}), ("opt13b_mha_prefix_b128", {}),
-                       ("long32k_b16", {})):
+    for name, opts in (("opt13b_mha_prefix_b128", {"path": 1}),
+                       ("tiny_gqa4_d64", {"partition_tokens": 32}), ("long32k_b16", {})):
         w = workloads.make(name)
         dw1, dw2 = dev.upload(w), dev.upload(w)
         o1, o2 = torch.empty_like(dw1.q), torch.empty_like(dw2.q)
@@ -165,3 +168,36 @@ def test_append_decode_block_sizes(b, d, hq, hkv):
     assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks)
     assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks)
     assert_close(out.double().cpu().numpy(), ref, f"ad_b{b}")
+
+
+@pytest.mark.parametrize("g,d,b", [(1, 128, 16), (4, 64, 8), (16, 128, 32)], ids=["mha", "gqa4_d64_b8", "gqa16_b32"])
+def test_append_decode_shared_step_edges(g, d, b):
+    """The partitioned step whose shared-partition kernel takes the append, at
+    partitions of 256 tokens: contexts of one token (nothing read from the
+    pool), lengths on and either side of partition boundaries (the new token
+    alone in the last partition, or ending it), empty sequences (slot -1) and
+    random ones; 40 sequences x 8 KV heads, so the schedule does not take the
+    deep pipeline.  Pools bit-exact, every row against the oracle."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    rng = np.random.Generator(np.random.PCG64(1300 + g + d + b))
+    edges = [1, 2, 255, 256, 257, 511, 512, 513, 768, 1024, 0, 0, 16, 17]
+    lens = edges + rng.integers(1, 1100, size=40 - len(edges), endpoint=True).tolist()
+    nb = int(1.2 * sum(-(-L // b) for L in lens)) + 4
+    _, tables = workloads.place_independent(rng, lens, b, nb)
+    w = workloads.build_workload(f"shared_step_g{g}", 1300 + g, rng, num_q_heads=8 * g, num_kv_heads=8, head_dim=d,
+                                 block_size=b, num_blocks=nb, tables=tables, context_lens=lens,
+                                 width=max(len(t) for t in tables))
+    print(f"[shared_step G={g} D={d} B={b}] S={w.num_seqs}", flush=True)
+    dw = dev.upload(w)
+    kst, vst, ref = oracle_step(w)
+    out = torch.full(dw.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    _run(pa, dw, w, out, {"partition_tokens": 256})
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+    got = out.double().cpu().numpy()
+    assert np.all(got[[10, 11]] == 0.0)
+    a, r = assert_close(got, ref, f"shared_step_g{g}")
+    print(f"[shared_step G={g}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)

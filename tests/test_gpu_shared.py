@@ -4,8 +4,11 @@ same physical blocks, all of them filled) once for all of them.  Forked
 prompts in groups of several sizes (some crossing the aligned window of 16/G
 sequences), prompts that end inside a block (copy-on-write), members too short
 to fill a shared partition, and an interleaved order where nothing is shared
-consecutively.  Each case against the fp64 oracle: max|err| <= 1e-2, relative
-RMS <= 2e-3 (f32 outputs)."""
+consecutively.  Each case runs as two calls (pa_cache_append, then
+pa_decode_ex) and as one pa_append_decode, whose shared-partition kernel takes
+the append (the last partition of each sequence reads its new token from k / v
+and stores it); pools bit-exact and every row against the fp64 oracle:
+max|err| <= 1e-2, relative RMS <= 2e-3 (f32 outputs)."""
 
 import numpy as np
 import pytest
@@ -48,6 +51,36 @@ def shared_workload(name, seed, groups, prompt, tail_max, *, hq, hkv, d, b, inte
                                     copies=list(pool.pending_copies))
 
 
+def run_step(w, part, fused):
+    """Copy-on-write copies, then the step's append and decode on partitions of
+    `part` tokens (two calls, or pa_append_decode); returns (out f64, device workload)."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    dw = dev.upload(w)
+    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies)
+    maxlen = w.table_width * w.block_size
+    nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen, part)
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    if fused:
+        pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, dw.block_tables,
+                         dw.context_lens, w.scale, w.block_size, partition_tokens=part, workspace=ws)
+    else:
+        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
+        pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size,
+                     partition_tokens=part, workspace=ws)
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy(), dw
+
+
+def check_pools(w, dw, kst, vst):
+    from paged_kv_cache_122_amd import device as dev
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
+
+
 # (name, seed, groups, prompt, tail_max, Hq, Hkv, D, B, partition tokens, interleave)
 CASES = [
     ("mha_windows", 3001, [8, 3, 1, 20], 1024, 300, 4, 4, 128, 16, 512, False),
@@ -59,34 +92,23 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "append_decode"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_shared_partitions_parity(case):
-    torch = need_gpu()
-    from paged_kv_cache_122_amd import _lib as pa
-    from paged_kv_cache_122_amd import device as dev
-
+def test_shared_partitions_parity(case, fused):
     name, seed, groups, prompt, tail_max, hq, hkv, d, b, part, inter = case
     w = shared_workload(name, seed, groups, prompt, tail_max, hq=hq, hkv=hkv, d=d, b=b, interleave=inter)
-    print(f"[{name}] S={w.num_seqs} lens {int(w.context_lens.min())}..{int(w.context_lens.max())} "
+    print(f"[{name} fused={fused}] S={w.num_seqs} lens {int(w.context_lens.min())}..{int(w.context_lens.max())} "
           f"copies {len(w.copies)} partition {part}", flush=True)
-    dw = dev.upload(w)
     kst, vst, ref = oracle_step(w)
-    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies)
-    pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
-    maxlen = w.table_width * w.block_size
-    nb = pa.workspace_bytes(w.num_seqs, hq, hkv, d, maxlen, part)
-    ws = pa.alloc_workspace(nb, "cuda") if nb else None
-    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
-    pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size,
-                 partition_tokens=part, workspace=ws)
-    torch.cuda.synchronize()
-    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks)
-    a, r = assert_close(out.double().cpu().numpy(), ref, name)
+    got, dw = run_step(w, part, fused)
+    check_pools(w, dw, kst, vst)
+    a, r = assert_close(got, ref, name)
     print(f"[{name}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "append_decode"])
 @pytest.mark.parametrize("seed", range(5))
-def test_shared_random_batches(seed):
+def test_shared_random_batches(seed, fused):
     """Seeded random forked batches: group sizes 1..20, prompt lengths that end
     on or inside a block, grouping 1..16, partition 256..1024."""
     rng = np.random.default_rng(6000 + seed)
@@ -98,19 +120,9 @@ def test_shared_random_batches(seed):
     groups = rng.integers(1, 21, size=int(rng.integers(1, 4))).tolist()
     prompt = int(rng.choice([part, 2 * part, part + 37, 3 * part // 2]))
     w = shared_workload(f"shared{seed}", 7000 + seed, groups, prompt, 300, hq=g * hkv, hkv=hkv, d=d, b=b)
-    print(f"[shared{seed}] G={g} Hkv={hkv} D={d} B={b} groups={groups} prompt={prompt} part={part}", flush=True)
-    torch = need_gpu()
-    from paged_kv_cache_122_amd import _lib as pa
-    from paged_kv_cache_122_amd import device as dev
-    dw = dev.upload(w)
+    print(f"[shared{seed} fused={fused}] G={g} Hkv={hkv} D={d} B={b} groups={groups} prompt={prompt} "
+          f"part={part}", flush=True)
     kst, vst, ref = oracle_step(w)
-    pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies)
-    pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
-    maxlen = w.table_width * w.block_size
-    nb = pa.workspace_bytes(w.num_seqs, g * hkv, hkv, d, maxlen, part)
-    ws = pa.alloc_workspace(nb, "cuda") if nb else None
-    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
-    pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size,
-                 partition_tokens=part, workspace=ws)
-    torch.cuda.synchronize()
-    assert_close(out.double().cpu().numpy(), ref, f"shared{seed}")
+    got, dw = run_step(w, part, fused)
+    check_pools(w, dw, kst, vst)
+    assert_close(got, ref, f"shared{seed}")
