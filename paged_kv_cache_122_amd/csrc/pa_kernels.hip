@@ -1881,17 +1881,19 @@ __global__ __launch_bounds__(256) void combine_parts(DecodeParams p) {
 
 // The same combine after decode_shared's fused step, which also stores the
 // step's new tokens (one per sequence, from mp's k_new / v_new) at their
-// slots: one 16-byte piece of sequence s's token per thread of its row.
+// slots: one 16-byte piece of sequence s's token per thread, dealt over all
+// workgroups of its row, so that each holds only a few stores.
 template <int D, int BS>
 __global__ __launch_bounds__(256) void combine_append(MultiParams mp) {
   const DecodeParams& p = mp.d;
   const int s = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < p.num_kv_heads * (D / 8)) {
+  const int u = threadIdx.x * gridDim.x + blockIdx.x;
+  if (u < p.num_kv_heads * (D / 8)) {
     const int64_t slot = mp.slots[s];
     if (slot >= 0 && slot < mp.num_slots) {
-      const int h = idx / (D / 8);
-      const int piece = idx - h * (D / 8);
+      const int h = u / (D / 8);
+      const int piece = u - h * (D / 8);
       const u32x4 kv = load16(mp.k_new + size_t(s) * mp.kn_t + size_t(h) * mp.kn_h + piece * 8);
       const u32x4 vv = load16(mp.v_new + size_t(s) * mp.vn_t + size_t(h) * mp.vn_h + piece * 8);
       write_slot_piece<D, BS>(mp.k_store, mp.v_store, p.num_kv_heads, slot, h, piece, kv, vv);
