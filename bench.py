@@ -44,18 +44,26 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "a35779ae562e1edf4bfc0223704e10d86089b742f519cea4ec777c2e6a9b6663",
-    # the step's one launch: FETCH_SIZE 133788.0 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.67 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273979013, "write_bytes": 1310843,
-                                                   "mfma_busy_pct": 4.67},
-    # the verification batch: FETCH_SIZE 140627.3 KiB x 1.9999, WRITE_SIZE 4354.1 KiB x 1.0; MfmaUtil 8.59 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287985108, "write_bytes": 4458592,
-                                                           "mfma_busy_pct": 8.59},
-    # long-context verification (split): FETCH_SIZE 524893.6 KiB x 1.9999, WRITE_SIZE 5426.8 KiB x 1.0;
-    # MfmaUtil 11.44 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074908696, "write_bytes": 5557006,
-                                                        "mfma_busy_pct": 11.44},
+    "sources_sha256": "dda88c1be23a894d5f48580224cc48df885709af8c29550d23978e4a1f8933a8",
+    # the step's one launch: FETCH_SIZE 133788.2 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
+    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.66 %
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273979547, "write_bytes": 1310784,
+                                                   "mfma_busy_pct": 4.66},
+    # the verification batch: FETCH_SIZE 140627.6 KiB x 1.9999, WRITE_SIZE 4353.6 KiB x 1.0; MfmaUtil 8.56 %
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287985629, "write_bytes": 4458048,
+                                                           "mfma_busy_pct": 8.56},
+    # long-context verification (split): FETCH_SIZE 524893.5 KiB x 1.9999, WRITE_SIZE 5426.6 KiB x 1.0;
+    # MfmaUtil 11.59 %
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074908611, "write_bytes": 5556827,
+                                                        "mfma_busy_pct": 11.59},
+    # the --config steps' main kernels (bench.py --config X --steps 5 --warmup 2 --no-cpu-baseline
+    # --no-control --no-multi --copy-calibration 256, one counter per run):
+    # Llama-3-70B-shaped: FETCH_SIZE 442993.4 KiB x 1.9999, WRITE_SIZE 7168.0 KiB x 1.0
+    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907196049, "write_bytes": 7340032},
+    # OPT-13B-shaped prefix sharing: FETCH_SIZE 852223.5 KiB x 1.9999, WRITE_SIZE 5380.3 KiB x 1.0
+    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745252744, "write_bytes": 5509477},
+    # 8 x 32k tokens, B 16: FETCH_SIZE 524706.4 KiB x 1.9999, WRITE_SIZE 1136.2 KiB x 1.0
+    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074533797, "write_bytes": 1163493},
 }
 
 
