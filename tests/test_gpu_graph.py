@@ -1,8 +1,9 @@
 """GPU check that the entry points which take the caller's workspace allocate
 nothing and can be captured into a HIP graph: pa_append_decode (the fused
 one-launch step, the host-length split step with its row combine, and the
-append-then-partitioned step with its combine), pa_decode_ex (stream-K) and
-pa_decode_multi_ex (several new tokens, split, with the row combine).
+partitioned step whose shared-partition kernel takes the new token, with the
+combine that stores it), pa_decode_ex (stream-K) and pa_decode_multi_ex
+(several new tokens, split, with the row combine).
 Each graph is replayed several times, with eager work and a synchronisation
 between replays, and every replay's output must equal the eager call's bit for
 bit (the kernels are deterministic and the step's append is idempotent)."""
@@ -18,7 +19,7 @@ pytestmark = pytest.mark.gpu
 CASES = [
     ("llama3_8b_b64", "append_decode"),           # one fused launch
     ("long32k_b16", "append_decode"),             # host-length partitions + row combine
-    ("opt13b_mha_prefix_b128", "append_decode"),  # append kernel, shared partitions, combine
+    ("opt13b_mha_prefix_b128", "append_decode"),  # shared partitions (new token from k / v), combine + append
     ("long32k_b16", "decode_ex"),                 # stream-K + its combine
     ("long32k_verify5_b16", "decode_multi_ex"),   # several new tokens, split + row combine
 ]
