@@ -329,31 +329,32 @@ def test_multi_ex_debug_refuses_wrong_host_lens():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("hq,new_max", [(32, 4), (64, 3)], ids=["g4", "g8_two_groups"])
-def test_multi_grid_larger_than_gpu(hq, new_max):
-    """300 sequences x 8 KV heads (one or two column groups each): the unsplit
-    grid is larger than the GPU holds at once, so the append runs from rows of
-    its own at the end of the grid.  Some sequences bring no token; rows past
-    query_start[S] carry slots in an unowned block, which must stay untouched.
-    Pools bit-exact, every row against the oracle."""
+@pytest.mark.parametrize("hq,new_max,d,b", [(32, 4, 128, 16), (64, 3, 128, 16), (16, 2, 64, 8), (32, 20, 128, 32)],
+                         ids=["g4", "g8_two_groups", "g2_d64_b8", "g4_two_sets_b32"])
+def test_multi_grid_larger_than_gpu(hq, new_max, d, b):
+    """300 sequences x 8 KV heads (one or two column groups or sets each): the
+    unsplit grid is larger than the GPU holds at once, so the append runs from
+    rows of its own at the end of the grid.  Some sequences bring no token;
+    rows past query_start[S] carry slots in an unowned block, which must stay
+    untouched.  Pools bit-exact, every row against the oracle."""
     torch = need_gpu()
     from paged_kv_cache_122_amd import _lib as pa
     from paged_kv_cache_122_amd import device as dev
 
-    rng = np.random.default_rng(9100 + hq)
+    rng = np.random.default_rng(9100 + hq + d + b)
     S = 300
     old = rng.integers(0, 400, size=S).tolist()
     new = rng.integers(0, new_max + 1, size=S).tolist()
     new = [max(n, 1 if o == 0 else 0) for o, n in zip(old, new)]
-    w = workloads.multi_query_workload(9200 + hq, old, new, num_q_heads=hq, num_kv_heads=8, head_dim=128,
-                                       block_size=16, name=f"many_seqs_g{hq // 8}")
+    w = workloads.multi_query_workload(9200 + hq + d + b, old, new, num_q_heads=hq, num_kv_heads=8, head_dim=d,
+                                       block_size=b, name=f"many_seqs_g{hq // 8}")
     print(f"[many_seqs G={hq // 8}] T={w.q.shape[0]} S={S}", flush=True)
     kst, vst, ref = oracle_multi(w)
     dw = dev.upload(w)
     T, slack = w.q.shape[0], 5
     free = sorted(set(range(w.num_blocks)) - {int(b) for b in w.owned})
     assert free, "the pool has no unowned block"
-    slots = torch.cat([dw.slot_mapping, torch.arange(slack, dtype=torch.int64, device="cuda") + free[0] * 16])
+    slots = torch.cat([dw.slot_mapping, torch.arange(slack, dtype=torch.int64, device="cuda") + free[0] * b])
 
     def pad(t):
         return torch.cat([t, torch.ones((slack,) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)])
