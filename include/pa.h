@@ -244,6 +244,38 @@ int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
                  const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
                  hipStream_t stream);
 
+/* Bytes of device memory the library reserves, once per GPU it runs on, for
+ * pa_decode_noalloc's partial results (held until the process ends). */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc.
+ *
+ * Arguments, schedule, preconditions and results are pa_decode's; the outputs
+ * equal pa_decode's bit for bit.  A split schedule keeps its partial results
+ * (the only memory beyond the inputs and outputs) in a fixed array of
+ * PA_NOALLOC_SCRATCH_BYTES that the library holds per GPU, instead of
+ * pa_decode's growable workspace.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its first call on a device looks up
+ * that device's copy of the array.
+ *
+ * A call whose schedule needs more than PA_NOALLOC_SCRATCH_BYTES
+ * (pa_decode_workspace_bytes with max_context_len = table width * block_size
+ * and partition_tokens 0) returns PA_ERR_WORKSPACE before launching anything;
+ * use pa_decode_ex with a workspace of that size instead.  Every call on a GPU
+ * shares that GPU's array, and a call does not depend on what an earlier one
+ * left in it (each split call writes every entry before its combine reads
+ * it).  Calls that may overlap on one GPU (different streams, or different
+ * host threads without ordering) race on the array: order them on one
+ * stream.
+ */
+int pa_decode_noalloc(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                      const pa_tensor* v_cache, const pa_tensor* block_tables,
+                      const pa_tensor* context_lens, float scale, int32_t block_size,
+                      hipStream_t stream);
+
 /*
  * pa_decode_contiguous -- the control for paging: the same decode over a cache
  * that is not paged.

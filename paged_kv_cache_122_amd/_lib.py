@@ -21,7 +21,7 @@ PA_BF16, PA_F32, PA_I32, PA_I64 = 1, 2, 3, 4
 MAX_DIMS = 5
 
 EXPORTED = ("pa_append_decode", "pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous",
-            "pa_decode_ex",
+            "pa_decode_ex", "pa_decode_noalloc",
             "pa_decode_multi", "pa_decode_multi_ex", "pa_decode_multi_workspace_bytes", "pa_decode_workspace_bytes",
             "pa_decode_schedule", "pa_last_error", "pa_set_debug")
 
@@ -75,6 +75,8 @@ def load(path=None):
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_decode.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
     lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p]
+    lib.pa_decode_noalloc.restype = ctypes.c_int
     lib.pa_decode_ex.argtypes = [P, P, P, P, P, P, ctypes.c_float, ctypes.c_int32,
                                  ctypes.POINTER(PaDecodeOpts), ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p]
@@ -213,6 +215,21 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_si
     ds = [describe(x) for x in ts]
     _check(lib, lib.pa_decode(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
                               ctypes.c_int32(block_size), _stream(stream)))
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, stream=None):
+    """pa_decode_noalloc: pa_decode with its partial results in the library's fixed
+    per-GPU scratch array (no allocation)."""
+    lib = load()
+    ts = [_device_tensor(x, n) for x, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"),
+                                           (v_cache, "v_cache"), (block_tables, "block_tables"),
+                                           (context_lens, "context_lens"))]
+    ds = [describe(x) for x in ts]
+    _check(lib, lib.pa_decode_noalloc(*[ctypes.byref(d) for d in ds], ctypes.c_float(scale),
+                                      ctypes.c_int32(block_size), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # PA_NOALLOC_SCRATCH_BYTES in include/pa.h
 
 
 def workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

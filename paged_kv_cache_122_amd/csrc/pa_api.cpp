@@ -551,6 +551,30 @@ PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* 
                        false, workspace, workspace_bytes, g_debug.load() != 0, stream);
 }
 
+PA_EXPORT int pa_decode_noalloc(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
+                                const pa_tensor* v_cache, const pa_tensor* block_tables,
+                                const pa_tensor* context_lens, float scale, int32_t block_size,
+                                hipStream_t stream) {
+  g_error.clear();
+  // the size check comes before any device call: an oversized call launches nothing
+  DecodePlan pl;
+  int rc = plan_decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size, nullptr, &pl);
+  if (rc != PA_OK) return rc;
+  if (pl.ws.total > PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_noalloc: this schedule needs %zu bytes of partial results, the library's "
+                "fixed scratch holds %zu; use pa_decode_ex with a workspace",
+                pl.ws.total, size_t(PA_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (pl.S > 0 && pl.ws.total > 0) {
+    const hipError_t e = pa::noalloc_scratch(&ws, &ws_bytes);
+    if (e != hipSuccess) return hip_fail(e, "looking up the scratch array of this device");
+  }
+  return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, nullptr,
+                       false, ws, ws_bytes, g_debug.load() != 0, stream);
+}
+
 PA_EXPORT int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
                                    const pa_tensor* v, const pa_tensor* context_lens, float scale,
                                    hipStream_t stream) {

@@ -132,6 +132,9 @@ struct LaunchCtx {
 
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
                          Path path, const LaunchCtx& ctx);
+// Address of the current device's copy of the library's fixed scratch array
+// (PA_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream);
 hipError_t launch_copy(const CopyParams& p, hipStream_t stream);
 hipError_t launch_multi(const MultiParams& p, int head_dim, int block_size, const LaunchCtx& c);

@@ -64,10 +64,39 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
+#include <unordered_map>
 
+#include "pa.h"
 #include "pa_internal.h"
 
+// Partial results of pa_decode_noalloc's split schedules: each GPU the library
+// runs on holds its own copy until the process ends.  In host code the name
+// stands for no device address; the launchers use the address that
+// noalloc_scratch() looks up per device.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 namespace pa {
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  static std::mutex mu;
+  static std::unordered_map<int, void*> addr;  // device -> its copy of the array
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  *bytes = PA_NOALLOC_SCRATCH_BYTES;
+  return hipSuccess;
+}
 
 WorkspaceLayout workspace_layout(int64_t num_seqs, int64_t num_q_heads, int64_t head_dim,
                                  int64_t max_parts) {

@@ -376,3 +376,31 @@ def test_multi_workspace_bytes(lib):
     assert f(40, 8, 32, 8, 128, 5, 1024, 1024) == 0           # partition as long as the bound
     assert f(0, 8, 32, 8, 128, 5, 32768, 0) == 0
     assert f(40, 8, 30, 8, 128, 5, 32768, 0) == 0             # heads not a multiple
+
+
+def test_decode_noalloc_validation(lib):
+    """pa_decode_noalloc validates like pa_decode and refuses, before any device
+    call, a schedule whose partial results exceed its fixed scratch (fake
+    pointers: every call below fails validation)."""
+    r = ctypes.byref
+
+    def call(a, block_size=16):
+        return lib.pa_decode_noalloc(r(a["out"]), r(a["q"]), r(a["k"]), r(a["v"]), r(a["bt"]), r(a["lens"]),
+                                     0.1, block_size, None)
+
+    assert call(decode_args(Hq=7)) == pa.PA_ERR_INVALID
+    assert call(decode_args(D=96)) == pa.PA_ERR_UNSUPPORTED
+    assert call(decode_args(), block_size=8) == pa.PA_ERR_INVALID
+    # 4096 sequences in 32k-token tables: 32 partitions of 1024 tokens per (sequence, q head)
+    big = decode_args(S=4096, Hq=32, Hkv=8, W=2048)
+    need = lib.pa_decode_workspace_bytes(4096, 32, 8, 128, 2048 * 16, 0)
+    assert need > pa.NOALLOC_SCRATCH_BYTES
+    assert call(big) == pa.PA_ERR_WORKSPACE
+    assert b"scratch" in lib.pa_last_error()
+    assert call(decode_args(S=0)) == pa.PA_OK  # nothing to do, no scratch needed
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pa.NOALLOC_SCRATCH_BYTES

@@ -1,0 +1,77 @@
+"""pa_decode_noalloc: pa_decode with its partial results in the library's fixed
+per-GPU scratch array.  Through the C ABI, two calls in a row (the second on a
+smaller batch) on each split schedule that uses the scratch (512-token
+partitions, stream-K), each equal to pa_decode bit for bit and to the fp64
+oracle within the attention bounds; a schedule that needs more than the array
+holds is refused before anything runs."""
+
+import numpy as np
+import pytest
+
+import oracle
+from paged_kv_cache_122_amd import device as dev
+from paged_kv_cache_122_amd import workloads
+from tests.gpu_util import assert_close_bf16, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+# (name, lengths of the first call, lengths of the second, smaller call, schedule both take)
+CASES = [
+    ("partitions", [8192, 5000, 3000, 700], [3000, 1500], 512),
+    ("stream_k", np.random.default_rng(7).integers(2000, 8192, size=20, endpoint=True).tolist(),
+     np.random.default_rng(8).integers(1000, 8192, size=17, endpoint=True).tolist(), -2),
+]
+
+
+def _workload(seed, lens):
+    return workloads.random_workload(seed, lens, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                                     block_size=16, width=512, name=f"noalloc_{seed}")
+
+
+@pytest.mark.parametrize("name,first,second,sched", CASES, ids=[c[0] for c in CASES])
+def test_noalloc_equals_decode(name, first, second, sched):
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+
+    for call, (seed, lens) in enumerate([(71, first), (72, second)]):
+        w = _workload(seed + (0 if sched > 0 else 10), lens)
+        assert pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.table_width * w.block_size) == sched
+        need = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                                  w.table_width * w.block_size, 0)
+        assert 0 < need <= pa.NOALLOC_SCRATCH_BYTES
+        dw = dev.upload(w, "cuda:0")
+        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
+        out_na = torch.full_like(dw.q, float("nan"))
+        out_ref = torch.full_like(dw.q, float("nan"))
+        print(f"noalloc {name} call {call}: S={w.num_seqs} need={need}", flush=True)
+        pa.decode_noalloc(out_na, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                          w.block_size)
+        pa.decode(out_ref, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                  w.block_size)
+        torch.cuda.synchronize()
+        got = dev.bf16_bits(out_na)
+        assert np.array_equal(got, dev.bf16_bits(out_ref)), f"{name} call {call}: differs from pa_decode"
+        kst, vst = w.stores()
+        oracle.cache_append(w.k_new, w.v_new, w.slot_mapping, kst, vst, w.block_size)
+        ref = oracle.paged_decode(w.q, kst, vst, w.block_tables, w.context_lens, w.scale, w.block_size)
+        assert_close_bf16(oracle.bf16_bits_to_f64(got), ref, f"{name} call {call}")
+
+
+def test_noalloc_refuses_more_than_the_scratch_holds():
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+
+    # 4096 sequences x 32 q heads in 32k-token tables: 32 partitions of 1024
+    # tokens, 2.2 GB of partial results
+    S, Hq, Hkv, D, B, W = 4096, 32, 8, 128, 16, 2048
+    assert pa.workspace_bytes(S, Hq, Hkv, D, W * B, 0) > pa.NOALLOC_SCRATCH_BYTES
+    q = torch.zeros((S, Hq, D), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.full_like(q, 7.0)
+    k, v = dev.alloc_pools(4, Hkv, D, B, "cuda:0", fill=0.0)
+    bt = torch.zeros((S, W), dtype=torch.int32, device="cuda:0")
+    lens = torch.ones(S, dtype=torch.int32, device="cuda:0")
+    with pytest.raises(pa.PaError) as e:
+        pa.decode_noalloc(out, q, k, v, bt, lens, 0.1, B)
+    assert e.value.code == pa.PA_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all()), "a refused call wrote its output"
