@@ -1,25 +1,30 @@
 """Benchmark of one paged-decode layer step on one MI355X: slot-mapped append of
 this step's K/V and paged decode attention, as one pa_append_decode call (one
-launch where the decode schedule is unsplit MFMA, else the append kernel and
-then the decode schedule).
+launch where the decode schedule is unsplit MFMA; the shared-partition kernel
+and a combine on partitioned batches; the split multi-token kernel and a row
+combine on few long contexts).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+                    [--configs all|none|NAME,...] [--no-cpu-baseline]
 
-Prints ONE JSON line.  ``value`` is effective KV-read GB/s of the whole step
-(sum_s L_s * Hkv * D * 2 (K and V) * 2 bytes, divided by the event-timed step).  Inputs are resident in HBM; before every timed step a
-1 GiB buffer is written so that neither L2 nor the 256 MB Infinity Cache
-still holds the pools (the flush is outside the timed region).  All work runs
-on one stream of this process and the HIP events are recorded on it; they are
-created with hipEventDisableSystemFence, so recording them flushes no cache.
-``roofline`` is the step's main kernel alone (on the default workload the
-only kernel of the step), timed in as many further flushed steps by events
-that the GPU stamps at its start and end, against 8 TB/s.  ``two_call_step``
-times the same step as pa_cache_append + pa_decode.  ``paging_control``
-times the same decode over an unpaged copy of the cache; ``multi_query`` times
-pa_decode_multi (several new tokens per sequence: speculative verification)
-on the Llama-3-8B-shaped batch with 5 drafted tokens per sequence, and
-``multi_query_long`` on 8 sequences of 32k tokens with 5 drafted tokens each.  ``cpu_baseline`` is the fp64 oracle on a bounded
-sample of the same workload, on this host's CPU.
+Prints ONE JSON line.  The headline (``value``, ``roofline``) is the
+Llama-3-8B-shaped batch (``--config`` changes it); ``configs`` holds one row per
+seeded configuration, every one timed the same way in the same run.  ``value`` is
+effective KV-read GB/s of the whole step (sum_s L_s * Hkv * D * 2 (K and V) * 2
+bytes, divided by the event-timed step).  Inputs are resident in HBM; before
+every timed step a 1 GiB buffer is written so that neither L2 nor the 256 MB
+Infinity Cache still holds the pools (the flush is outside the timed region).
+All work runs on one stream of this process and the HIP events are recorded on
+it; they are created with hipEventDisableSystemFence, so recording them flushes
+no cache.  ``roofline`` is the step's main kernel alone, timed in as many
+further flushed steps by events that the GPU stamps at its start and end,
+against 8 TB/s.  ``two_call_step`` times the headline step as pa_cache_append +
+pa_decode.  ``paging_control`` times the same decode over an unpaged copy of the
+cache; ``multi_query`` times pa_decode_multi (several new tokens per sequence:
+speculative verification) on the Llama-3-8B-shaped batch with 5 drafted tokens
+per sequence, and ``multi_query_long`` on 8 sequences of 32k tokens with 5
+drafted tokens each.  ``cpu_baseline`` is the fp64 oracle on a bounded sample of
+the headline workload, in worker processes on this host's cores.
 """
 
 import argparse
@@ -34,36 +39,26 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 DEFAULT_CONFIG = "llama3_8b_b64"
+# every seeded configuration, one row each in ``configs``
+CONFIG_ROWS = ("tiny_gqa4_d64", "llama3_8b_b64", "llama3_70b_b256", "opt13b_mha_prefix_b128",
+               "long32k_b8", "long32k_b16", "long32k_b32", "opt13b_cow_fork_b128")
+# worker processes of the CPU baseline: this host's cores, at most the share
+# of one GPU's host on the GPU machines
+CPU_WORKERS_MAX = 16
 
-# HBM bytes per launch of a step's main kernel, from two rocprofv3
-# --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by what
-# the counter reads for a plain copy of known size in the same run, and the
-# kernel's MFMA busy share of SIMD cycles from a third.  Valid only
-# for the kernel sources they were taken on (sha256 of the files below);
-# reported as null once those change.
+# HBM bytes per launch of a step's main kernel, from two rocprofv3 --pmc runs
+# of this script (FETCH_SIZE, then WRITE_SIZE), each scaled by what the counter
+# reads for a plain copy of known size in the same run, and the kernel's MFMA
+# busy share of SIMD cycles from a third.  They are copied here from the
+# summaries under profiles/ (named per entry), not measured in the run that
+# prints them, and hold only for the sources they were taken on (sha256 of the
+# files below, which include the host code that picks the schedule); reported
+# as null once those change.
 KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
-                  "paged_kv_cache_122_amd/csrc/pa_internal.h")
+                  "paged_kv_cache_122_amd/csrc/pa_internal.h",
+                  "paged_kv_cache_122_amd/csrc/pa_api.cpp")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "dda88c1be23a894d5f48580224cc48df885709af8c29550d23978e4a1f8933a8",
-    # the step's one launch: FETCH_SIZE 133788.2 KiB x 1.9999, WRITE_SIZE 1280.1 KiB x 1.0;
-    # MfmaUtil (SQ_VALU_MFMA_BUSY_CYCLES over SIMD cycles) 4.66 %
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273979547, "write_bytes": 1310784,
-                                                   "mfma_busy_pct": 4.66},
-    # the verification batch: FETCH_SIZE 140627.6 KiB x 1.9999, WRITE_SIZE 4353.6 KiB x 1.0; MfmaUtil 8.56 %
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287985629, "write_bytes": 4458048,
-                                                           "mfma_busy_pct": 8.56},
-    # long-context verification (split): FETCH_SIZE 524893.5 KiB x 1.9999, WRITE_SIZE 5426.6 KiB x 1.0;
-    # MfmaUtil 11.59 %
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074908611, "write_bytes": 5556827,
-                                                        "mfma_busy_pct": 11.59},
-    # the --config steps' main kernels (bench.py --config X --steps 5 --warmup 2 --no-cpu-baseline
-    # --no-control --no-multi --copy-calibration 256, one counter per run):
-    # Llama-3-70B-shaped: FETCH_SIZE 442993.4 KiB x 1.9999, WRITE_SIZE 7168.0 KiB x 1.0
-    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907196049, "write_bytes": 7340032},
-    # OPT-13B-shaped prefix sharing: FETCH_SIZE 852223.5 KiB x 1.9999, WRITE_SIZE 5380.3 KiB x 1.0
-    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745252744, "write_bytes": 5509477},
-    # 8 x 32k tokens, B 16: FETCH_SIZE 524706.4 KiB x 1.9999, WRITE_SIZE 1136.2 KiB x 1.0
-    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074533797, "write_bytes": 1163493},
+    "sources_sha256": None,
 }
 
 
@@ -72,10 +67,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default=DEFAULT_CONFIG)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, help="the headline workload")
+    ap.add_argument("--configs", default="all",
+                    help="rows of the configs object: all, none, or a comma-separated list")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="seconds each CPU baseline worker spends on the oracle")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the multi-token (speculative verification) leg")
     ap.add_argument("--no-control", action="store_true",
@@ -149,21 +146,39 @@ def measured(config, kernel):
     return t[key]
 
 
-def measured_traffic(config, kernel):
+def counter_fields(config, kernel):
+    """traffic (fetched + written bytes per launch), MFMA busy share and where
+    they come from, or nulls when no summary holds them for these sources."""
     m = measured(config, kernel)
-    return None if m is None else m["fetch_bytes"] + m["write_bytes"]
+    if m is None:
+        return {"traffic": None, "mfma_busy_pct": None, "traffic_source": None}
+    return {"traffic": m["fetch_bytes"] + m["write_bytes"], "mfma_busy_pct": m.get("mfma_busy_pct"),
+            "traffic_source": m["source"] + " (rocprofv3 counter passes, copied here; not measured in this run)"}
 
 
-def measured_mfma(config, kernel):
-    m = measured(config, kernel)
-    return None if m is None else m.get("mfma_busy_pct")
+def mean(xs):
+    return sum(xs) / len(xs)
+
+
+def percentile(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return float("nan")
+    k = (len(xs) - 1) * q / 100.0
+    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
+
+
+def stats_us(ms):
+    return {"mean": round(mean(ms) * 1e3, 2), "p10": round(percentile(ms, 10) * 1e3, 2),
+            "p50": round(percentile(ms, 50) * 1e3, 2), "p90": round(percentile(ms, 90) * 1e3, 2)}
 
 
 def decode_kernels(w, part, cus):
     """Kernels one automatic pa_decode call launches on this workload."""
     g = w.num_q_heads // w.num_kv_heads
     core = f"decode_{'mfma' if g >= 3 else 'valu'}"
-    tmpl = f"<{w.head_dim},{w.block_size}>"
+    tmpl = f"<{w.head_dim},{w.block_size}>" if g >= 3 else f"<{w.head_dim},{w.block_size},{g}>"
     if part == -2:
         return [core + "_sk" + tmpl, f"combine_sk<{w.head_dim}>"], "stream-K"
     max_len = w.block_tables.shape[1] * w.block_size
@@ -178,6 +193,155 @@ def decode_kernels(w, part, cus):
         return ([f"decode_shared<{w.head_dim},{w.block_size},false>", f"combine_parts<{w.head_dim}>"],
                 f"partitions of {part} tokens, shared partitions read once")
     return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
+
+
+def fused_step(w, part, cus):
+    """How pa_append_decode (given the host copy of the lengths) runs this
+    workload: (append fused into the decode, its kernels, what the schedule
+    is, whether the main kernel writes the new tokens).  The unsplit MFMA
+    schedule is one launch; a stream-K batch on the MFMA path runs the
+    multi-token kernel over partitions sized on the lengths (so that about 512
+    workgroups share the tokens), then the row combine; a partitioned batch
+    whose grid fills the GPU runs the shared-partition kernel, which takes the
+    new token from k / v, and a combine that stores it; anything else appends
+    first and decodes as pa_decode_ex does."""
+    g = w.num_q_heads // w.num_kv_heads
+    sets = 2 if g > 16 else 1
+    span = w.block_tables.shape[1] * w.block_size
+    unsplit = part == -1 or part >= span
+    if g >= 3 and unsplit:
+        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},false>"], \
+            "one launch: the new token stored and attended", True
+    if g >= 3 and part == -2:
+        row_wgs = w.num_kv_heads * -(-g // (16 * sets))
+        tokens = int(sum(min(max(int(x), 0), span) for x in w.context_lens))
+        p = max(512, -(-(-(-tokens * row_wgs // 512)) // 256) * 256)
+        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},true>", f"combine_rows<{w.head_dim}>"], \
+            f"partitions of {p} tokens sized on the host's lengths, only those holding tokens launched, " \
+            "the new token stored by the last one; then the row combine", True
+    if part > 0 and not unsplit and g <= 16 and w.num_seqs * w.num_kv_heads * -(-span // part) >= cus:
+        return True, [f"decode_shared<{w.head_dim},{w.block_size},true>", f"combine_append<{w.head_dim},{w.block_size}>"], \
+            f"partitions of {part} tokens, shared partitions read once, the new token taken from k / v by its " \
+            "last partition; then the combine, which stores the new tokens", False
+    return False, [], "append kernel, then the decode schedule", False
+
+
+class Step:
+    """One layer step of a workload on the GPU, as a serving engine would run
+    it: the step's copy-on-write copies (if any), then pa_append_decode with the
+    caller's workspace and a host copy of the lengths."""
+
+    def __init__(self, w, cus, stream):
+        import numpy as np
+        import torch
+
+        from paged_kv_cache_122_amd import _lib as pa
+        from paged_kv_cache_122_amd import device as dev
+
+        self.pa, self.w, self.stream = pa, w, stream
+        self.dw = dev.upload(w, "cuda:0")
+        self.out = torch.empty_like(self.dw.q)
+        self.has_copies = int(w.copies.shape[0]) > 0
+        max_len = int(w.block_tables.shape[1]) * w.block_size
+        self.part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
+        self.kernels, self.schedule = decode_kernels(w, self.part, cus)
+        fused, fk, kind, writes_new = fused_step(w, self.part, cus)
+        # bytes the main kernel must move: a physical block shared by several
+        # sequences (a common prefix) counts once; in one-launch steps the
+        # kernel also writes the new token (else the combine that follows does)
+        self.algo_bytes = w.unique_kv_bytes()
+        if fused:
+            self.kernels, self.schedule = fk, kind
+            if writes_new:
+                self.algo_bytes += w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
+        nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, 0)
+        self.ws = pa.alloc_workspace(nb, "cuda:0") if nb else None
+        self.host_lens = np.asarray(w.context_lens, dtype=np.int32)
+
+    def copies(self):
+        if self.has_copies:
+            self.pa.copy_blocks(self.dw.k_cache, self.dw.v_cache, self.dw.copies, stream=self.stream)
+
+    def __call__(self, kernel_events=None):
+        dw, w = self.dw, self.w
+        self.copies()
+        self.pa.append_decode(self.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                              dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=self.ws,
+                              kernel_events=kernel_events, host_context_lens=self.host_lens, stream=self.stream)
+
+    def append(self):
+        dw = self.dw
+        self.copies()
+        self.pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, stream=self.stream)
+
+    def decode(self):
+        """The call pa_decode makes (same schedule), with the step's workspace."""
+        dw, w = self.dw, self.w
+        self.pa.decode_ex(self.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
+                          w.block_size, workspace=self.ws, host_context_lens=self.host_lens, stream=self.stream)
+
+    def step_desc(self):
+        return (("pa_copy_blocks (copy-on-write) + " if self.has_copies else "")
+                + "pa_append_decode (" + self.schedule + "), with a host copy of the lengths"
+                + (" (the sequences ranked on the host)"
+                   if self.kernels[0].endswith(",false>") and "multi" in self.kernels[0] else "")
+                + ", caches flushed before each step")
+
+
+def time_steps(st, steps, warmup, tev, flush):
+    """(step ms, main-kernel ms) over `steps` flushed steps each: the step
+    between events around the call, then the main kernel alone between events
+    the GPU stamps at its start and end (a launch that carries them costs the
+    stream a few microseconds more, so it is kept out of the step timing)."""
+    stream = st.stream
+    for _ in range(warmup):
+        flush.zero_()
+        st()
+    stream.synchronize()
+    ev = [(tev.create(), tev.create()) for _ in range(steps)]
+    kev = [(tev.create(), tev.create()) for _ in range(steps)]
+    for a, b in ev:
+        flush.zero_()
+        tev.record(a, stream)
+        st()
+        tev.record(b, stream)
+    stream.synchronize()
+    step_ms = [tev.elapsed_ms(a, b) for a, b in ev]
+    for k in kev:
+        flush.zero_()
+        st(kernel_events=k)
+    stream.synchronize()
+    kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
+    return step_ms, kernel_ms
+
+
+def config_row(st, step_ms, kernel_ms):
+    """One row of ``configs``: the step of this workload and its main kernel."""
+    w = st.w
+    eff = w.effective_kv_bytes()
+    t, tk = mean(step_ms) / 1e3, mean(kernel_ms) / 1e3
+    row = {
+        "num_seqs": w.num_seqs, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+        "head_dim": w.head_dim, "block_size": w.block_size,
+        "context_tokens": int(w.context_lens.sum()), "max_context_len": int(w.context_lens.max()),
+        "step_us": stats_us(step_ms),
+        "value": round(eff / t / 1e9, 2),
+        "unit": "GB/s",
+        "seqs_per_s": round(w.num_seqs / t, 1),
+        "kernel": st.kernels[0],
+        "kernels": st.kernels,
+        "kernel_us": stats_us(kernel_ms),
+        "effective_kv_bytes": eff,
+        "unique_kv_bytes": w.unique_kv_bytes(),
+        "algorithmic_bytes": st.algo_bytes,
+        "kernel_gbs": round(st.algo_bytes / tk / 1e9, 2),
+        "kernel_frac": round(st.algo_bytes / tk / 1e9 / HBM_PEAK_GBS, 4),
+        "step_frac_unique": round(w.unique_kv_bytes() / t / 1e9 / HBM_PEAK_GBS, 4),
+        "schedule": st.schedule,
+        "cow_copies": int(w.copies.shape[0]),
+    }
+    row.update(counter_fields(w.name, st.kernels[0]))
+    return row
 
 
 MULTI_CONFIGS = (("llama3_8b_verify5_b64", "decode_multi<128,16,2,false>"),
@@ -252,121 +416,118 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
     # K/V of every context token read once (cached ones from the pool, new ones
     # from k_new / v_new), the new K/V written, q read and out written
     algo = w.unique_kv_bytes() + new_kv + 2 * T * w.num_q_heads * w.head_dim * 2
-    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     t = mean(multi_ms) / 1e3
     tk = mean(kernel_ms) / 1e3
     del dw, ws
-    return {
+    row = {
         "workload": w.name,
         "num_seqs": w.num_seqs,
         "new_tokens": T,
         "max_query_len": mql,
         "context_tokens": int(w.context_lens.sum()),
-        "call_ms": {"mean": round(mean(multi_ms), 5), "p50": round(percentile(multi_ms, 50), 5)},
+        "call_us": stats_us(multi_ms),
         "algorithmic_bytes": algo,
         "achieved_gbs": round(algo / t / 1e9, 2),
         "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
         "kernel": kernel,
-        "kernel_ms": {"mean": round(mean(kernel_ms), 5), "p50": round(percentile(kernel_ms, 50), 5)},
+        "kernel_us": stats_us(kernel_ms),
         "kernel_achieved_gbs": round(algo / tk / 1e9, 2),
         "kernel_hbm_frac": round(algo / tk / 1e9 / HBM_PEAK_GBS, 4),
-        "traffic": measured_traffic(w.name, kernel),
-        "mfma_busy_pct": measured_mfma(w.name, kernel),
         "tokens_per_s": round(T / t, 1),
-        "single_token_decode_same_pools_call_ms": round(mean(single_ms), 5),
+        "single_token_decode_same_pools_call_us": round(mean(single_ms) * 1e3, 2),
         "note": "pa_decode_multi (append fused, causal over cached + drafted tokens) vs pa_decode of "
                 "one token per sequence on the same pools, alternating, each after a cache flush, "
-                "events around the call (launch included); kernel_ms: the main kernel alone through "
+                "events around the call (launch included); kernel_us: the main kernel alone through "
                 "pa_decode_multi_ex (caller workspace, host lengths), GPU-stamped events",
     }
+    row.update(counter_fields(w.name, kernel))
+    return row
 
 
-def fused_step(w, part, cus):
-    """How pa_append_decode (given the host copy of the lengths) runs this
-    workload: (append fused into the decode, its kernels, what the schedule
-    is, whether the main kernel writes the new tokens).  The unsplit MFMA
-    schedule is one launch; a stream-K batch on the MFMA path runs the
-    multi-token kernel over partitions sized on the lengths (so that about 512
-    workgroups share the tokens), then the row combine; a partitioned batch
-    whose grid fills the GPU runs the shared-partition kernel, which takes the
-    new token from k / v, and a combine that stores it; anything else appends
-    first and decodes as pa_decode_ex does."""
-    g = w.num_q_heads // w.num_kv_heads
-    sets = 2 if g > 16 else 1
-    span = w.block_tables.shape[1] * w.block_size
-    unsplit = part == -1 or part >= span
-    if g >= 3 and unsplit:
-        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},false>"], \
-            "one launch: the new token stored and attended", True
-    if g >= 3 and part == -2:
-        row_wgs = w.num_kv_heads * -(-g // (16 * sets))
-        tokens = int(sum(min(max(int(x), 0), span) for x in w.context_lens))
-        p = max(512, -(-(-(-tokens * row_wgs // 512)) // 256) * 256)
-        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},true>", f"combine_rows<{w.head_dim}>"], \
-            f"partitions of {p} tokens sized on the host's lengths, only those holding tokens launched, " \
-            "the new token stored by the last one; then the row combine", True
-    if part > 0 and not unsplit and g <= 16 and w.num_seqs * w.num_kv_heads * -(-span // part) >= cus:
-        return True, [f"decode_shared<{w.head_dim},{w.block_size},true>", f"combine_append<{w.head_dim},{w.block_size}>"], \
-            f"partitions of {part} tokens, shared partitions read once, the new token taken from k / v by its " \
-            "last partition; then the combine, which stores the new tokens", False
-    return False, [], "append kernel, then the decode schedule", False
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle in worker processes forked before this process
+# touches the GPU; each inherits the headline workload and times the oracle's
+# append + decode on its share of the sequences.
+# ---------------------------------------------------------------------------
+_CPU_WORKLOAD = None
 
 
-def percentile(xs, q):
-    xs = sorted(xs)
-    if not xs:
-        return float("nan")
-    k = (len(xs) - 1) * q / 100.0
-    lo, hi = int(k), min(int(k) + 1, len(xs) - 1)
-    return xs[lo] + (xs[hi] - xs[lo]) * (k - lo)
-
-
-def cpu_baseline(w, budget_s):
-    """Time the fp64 oracle (append + decode), one sequence at a time, in passes
-    over the batch, until about budget_s seconds of CPU time are spent."""
-    import oracle
+def _cpu_worker_init():
     try:
         from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)  # one BLAS thread per worker process
     except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        pass
 
-    order = list(range(w.num_seqs))
-    kst, vst = w.stores()
-    t_total, tokens, done = 0.0, 0, 0
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        if ctx:
-            ctx.__enter__()
-        passes = 0
-        while t_total < budget_s:
-            passes += 1
+
+def _cpu_share(job):
+    """Oracle append + decode over this worker's sequences, in passes, until
+    `budget` seconds are spent; returns (context tokens, sequence-steps, seconds)."""
+    import oracle
+    from paged_kv_cache_122_amd.workloads import BlockStore
+
+    seqs, budget = job
+    w = _CPU_WORKLOAD
+    # this process's own (copy-on-write) view of the pools: re-appending a token
+    # writes the same value again
+    kst = BlockStore(w.owned, w.k_blocks, w.num_blocks)
+    vst = BlockStore(w.owned, w.v_blocks, w.num_blocks)
+    spent, tokens, done = 0.0, 0, 0
+    if len(w.copies):
+        oracle.copy_blocks(w.copies, kst, vst)
+    while spent < budget and seqs:
+        for s in seqs:
             t0 = time.perf_counter()
-            oracle.copy_blocks(w.copies, kst, vst)  # the step's copy-on-write copies, if any
-            t_total += time.perf_counter() - t0
-            for s in order:
-                t0 = time.perf_counter()
-                oracle.cache_append(w.k_new[s:s + 1], w.v_new[s:s + 1], w.slot_mapping[s:s + 1], kst, vst,
-                                    w.block_size)
-                oracle.paged_decode(w.q, kst, vst, w.block_tables, w.context_lens, w.scale, w.block_size,
-                                    seqs=[s])
-                t_total += time.perf_counter() - t0
-                tokens += int(w.context_lens[s])
-                done += 1
-                if t_total >= budget_s:
-                    break
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    kv_bytes = tokens * w.num_kv_heads * w.head_dim * 2 * 2
+            oracle.cache_append(w.k_new[s:s + 1], w.v_new[s:s + 1], w.slot_mapping[s:s + 1], kst, vst,
+                                w.block_size)
+            oracle.paged_decode(w.q, kst, vst, w.block_tables, w.context_lens, w.scale, w.block_size, seqs=[s])
+            spent += time.perf_counter() - t0
+            tokens += int(w.context_lens[s])
+            done += 1
+            if spent >= budget:
+                break
+    return tokens, done, spent
+
+
+def start_cpu_pool(w):
+    """Fork the baseline's worker processes now, before the GPU is initialised
+    in this process (they never touch it)."""
+    import multiprocessing
+
+    global _CPU_WORKLOAD
+    _CPU_WORKLOAD = w
+    affinity = len(os.sched_getaffinity(0))
+    n = max(1, min(affinity, CPU_WORKERS_MAX, w.num_seqs))
+    pool = multiprocessing.get_context("fork").Pool(n, initializer=_cpu_worker_init)
+    return pool, n, affinity
+
+
+def cpu_baseline(pool, n, affinity, w, budget_s):
+    """Sequences dealt round robin over the workers; each worker loops over its
+    share for budget_s seconds.  Rate = sum over workers of their own rates
+    (they run at the same time, one per core)."""
+    jobs = [(list(range(i, w.num_seqs, n)), budget_s) for i in range(n)]
+    wall0 = time.perf_counter()
+    res = pool.map(_cpu_share, jobs)
+    wall = time.perf_counter() - wall0
+    pool.close()
+    pool.join()
+    bpt = w.num_kv_heads * w.head_dim * 2 * 2
+    gbs = sum(tok * bpt / t for tok, _, t in res if t > 0) / 1e9
+    seqs_s = sum(d / t for _, d, t in res if t > 0)
+    done = sum(d for _, d, _ in res)
+    tokens = sum(tok for tok, _, _ in res)
     return {
-        "value": round(kv_bytes / t_total / 1e9, 6),
+        "value": round(gbs, 6),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": n,
         "kind": "oracle",
-        "seqs_per_s": round(done / t_total, 4),
-        "sample": f"{done} sequence-steps ({passes} pass(es) over the {w.num_seqs}-sequence batch, "
-                  f"{tokens} context tokens), fp64 numpy oracle append + decode, one BLAS thread, "
-                  f"{t_total:.1f} s",
+        "seqs_per_s": round(seqs_s, 3),
+        "host_affinity_cores": affinity,
+        "sample": f"{done} sequence-steps of the {w.num_seqs}-sequence {w.name} batch ({tokens} context "
+                  f"tokens): fp64 numpy oracle append + decode, one sequence at a time, in {n} worker "
+                  f"processes with one BLAS thread each, the sequences dealt round robin, about "
+                  f"{budget_s:.0f} s per worker ({wall:.1f} s wall); rate = sum of the workers' rates",
     }
 
 
@@ -378,111 +539,56 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    from paged_kv_cache_122_amd import workloads
+
+    if args.configs == "all":
+        rows = list(CONFIG_ROWS)
+    elif args.configs == "none":
+        rows = []
+    else:
+        rows = [c for c in args.configs.split(",") if c]
+        bad = [c for c in rows if c not in workloads.CONFIGS]
+        if bad:
+            print(f"bench.py: unknown configs {bad}", file=sys.stderr)
+            sys.exit(2)
+
+    w = workloads.make(args.config)
+    pool = None
+    if not args.no_cpu_baseline:
+        pool, n_workers, affinity = start_cpu_pool(w)
+
     import torch
 
     from paged_kv_cache_122_amd import _lib as pa
     from paged_kv_cache_122_amd import device as dev
-    from paged_kv_cache_122_amd import workloads
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     pa.load()
     torch.cuda.set_device(0)
-
-    w = workloads.make(args.config)
-    dw = dev.upload(w, "cuda:0")
-    out = torch.empty_like(dw.q)
-    eff_bytes = w.effective_kv_bytes()
-    # bytes the kernel must bring from HBM: a physical block shared by several
-    # sequences (a common prefix) counts once
-    algo_bytes = w.unique_kv_bytes()
-    max_len = int(w.block_tables.shape[1]) * w.block_size
-    part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    kernels, schedule = decode_kernels(w, part, cus)
-    fused, fused_kernels, step_kind, writes_new = fused_step(w, part, cus)
-    new_kv_bytes = w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
-    if fused:
-        # the main launch reads the context (the new token from k / v); in one-launch steps it
-        # also writes the new token (else the combine that follows does)
-        kernels, schedule = fused_kernels, step_kind
-        if writes_new:
-            algo_bytes += new_kv_bytes
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.Stream()  # default priority
     torch.cuda.synchronize()
-
-    has_copies = int(w.copies.shape[0]) > 0
-
-    def append():
-        # the step's copy-on-write copies (if any) go first, then the append
-        if has_copies:
-            pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
-        pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, stream=stream)
-
-    # the call pa_decode makes, with a workspace of our own so that the main
-    # kernel can be bracketed by GPU-timed events
-    ws_bytes = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, 0)
-    ws = pa.alloc_workspace(ws_bytes, "cuda:0") if ws_bytes else None
-
-    # the host copy of the lengths that a serving engine keeps (it computes
-    # them); unsplit schedules rank the sequences from it on the host
-    host_lens = np.asarray(w.context_lens, dtype=np.int32)
-
-    def decode(kernel_events=None):
-        pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                     w.block_size, workspace=ws, kernel_events=kernel_events, host_context_lens=host_lens,
-                     stream=stream)
-
-    def step(kernel_events=None):
-        # the step's copy-on-write copies (if any), then append + decode in one call
-        if has_copies:
-            pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies, stream=stream)
-        pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
-                         dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=ws,
-                         kernel_events=kernel_events, host_context_lens=host_lens, stream=stream)
+    eff_bytes = w.effective_kv_bytes()
 
     tev = TimingEvents()
     E = tev.create
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            flush.zero_()
-            step()
-        stream.synchronize()
-
-        ev = [(E(), E()) for _ in range(args.steps)]
-        kev = [(E(), E()) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        for e0, e1 in ev:
-            flush.zero_()
-            tev.record(e0, stream)
-            step()
-            tev.record(e1, stream)
-        stream.synchronize()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        step_ms = [tev.elapsed_ms(a, b) for a, b in ev]
-
-        # the same steps again with the main kernel bracketed by events that the
-        # GPU stamps at its own start and end (such a launch costs the stream a
-        # few microseconds more, so it is kept out of the steps above)
-        for k in kev:
-            flush.zero_()
-            step(kernel_events=k)
-        stream.synchronize()
-        kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
+        st = Step(w, cus, stream)
+        step_ms, kernel_ms = time_steps(st, args.steps, args.warmup, tev, flush)
+        print(f"bench: {w.name} step {mean(step_ms) * 1e3:.1f} us, kernel {mean(kernel_ms) * 1e3:.1f} us",
+              file=sys.stderr, flush=True)
 
         # the step as two calls: pa_cache_append, then pa_decode's schedule
         tw = [(E(), E(), E()) for _ in range(args.steps)]
         for e0, e1, e2 in tw:
             flush.zero_()
             tev.record(e0, stream)
-            append()
+            st.append()
             tev.record(e1, stream)
-            decode()
+            st.decode()
             tev.record(e2, stream)
         stream.synchronize()
         append_ms = [tev.elapsed_ms(a, b) for a, b, _ in tw]
@@ -494,7 +600,7 @@ def main():
             hot = [(E(), E()) for _ in range(args.steps)]
             for a, b in hot:
                 tev.record(a, stream)
-                step()
+                st()
                 tev.record(b, stream)
             stream.synchronize()
             hot_ms = [tev.elapsed_ms(a, b) for a, b in hot]
@@ -504,8 +610,9 @@ def main():
         # way as the paged call above
         contig_ms, unsplit_ms = [], []
         if not args.no_control:
-            kc, vc = dev.contiguous_copy(dw, w)
-            out_c = torch.empty_like(out)
+            kc, vc = dev.contiguous_copy(st.dw, w)
+            out_c = torch.empty_like(st.out)
+            dw = st.dw
             cev = [(E(), E(), E(), E()) for _ in range(args.steps)]
             for a, b, c, d in cev:
                 flush.zero_()
@@ -521,10 +628,30 @@ def main():
             contig_ms = [tev.elapsed_ms(a, b) for a, b, _, _ in cev]
             unsplit_ms = [tev.elapsed_ms(c, d) for _, _, c, d in cev]
             del kc, vc, out_c
+        head_row = config_row(st, step_ms, kernel_ms)
+        head_kernels, head_schedule, head_algo, head_desc = st.kernels, st.schedule, st.algo_bytes, st.step_desc()
+        del st
+        torch.cuda.empty_cache()
 
         multi = []
         if not args.no_multi:
             multi = [multi_query_leg(c, k, args.steps, args.warmup, tev, stream, flush) for c, k in MULTI_CONFIGS]
+            torch.cuda.empty_cache()
+
+        # every seeded configuration, timed the same way
+        configs = {}
+        for name in rows:
+            if name == w.name:
+                configs[name] = head_row
+                continue
+            cw = workloads.make(name)
+            cst = Step(cw, cus, stream)
+            sm, km = time_steps(cst, args.steps, args.warmup, tev, flush)
+            configs[name] = config_row(cst, sm, km)
+            print(f"bench: {name} step {mean(sm) * 1e3:.1f} us, kernel {mean(km) * 1e3:.1f} us",
+                  file=sys.stderr, flush=True)
+            del cst, cw
+            torch.cuda.empty_cache()
 
         tev.close()
 
@@ -537,11 +664,11 @@ def main():
             stream.synchronize()
             del src, dst
 
-    mean = lambda xs: sum(xs) / len(xs)  # noqa: E731
     t_step = mean(step_ms) / 1e3
     t_kernel = mean(kernel_ms) / 1e3
     value = eff_bytes / t_step / 1e9
-    achieved = algo_bytes / t_kernel / 1e9
+    achieved = head_algo / t_kernel / 1e9
+    cf = counter_fields(w.name, head_kernels[0])
     line = {
         "metric": "paged decode-attention effective KV GB/s vs HBM peak; seqs/s per layer-step",
         "value": round(value, 2),
@@ -568,14 +695,9 @@ def main():
             "effective_kv_bytes": eff_bytes,
             "unique_kv_bytes": w.unique_kv_bytes(),
             "seed": w.seed,
-            "step": ("pa_copy_blocks (copy-on-write) + " if has_copies else "")
-                    + "pa_append_decode (" + step_kind
-                    + "), with a host copy of the lengths"
-                    + (" (the sequences ranked on the host)" if kernels[0].endswith(",false>") and "multi" in kernels[0]
-                       else "")
-                    + ", caches flushed before each step",
+            "step": head_desc,
             "cow_copies": int(w.copies.shape[0]),
-            "schedule": schedule,
+            "schedule": head_schedule,
         },
         "seqs_per_s": round(w.num_seqs / t_step, 1),
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
@@ -583,53 +705,58 @@ def main():
                            "p10": round(percentile(kernel_ms, 10), 5),
                            "p50": round(percentile(kernel_ms, 50), 5),
                            "p90": round(percentile(kernel_ms, 90), 5)},
-        "wall_ms_per_step_incl_flush": round(wall / args.steps * 1e3, 4),
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(w.name, kernels[0]),
-            "mfma_busy_pct": measured_mfma(w.name, kernels[0]),
-            "kernels": kernels,
-            "algorithmic_bytes": algo_bytes,
+            "traffic": cf["traffic"],
+            "traffic_source": cf["traffic_source"],
+            "mfma_busy_pct": cf["mfma_busy_pct"],
+            "kernels": head_kernels,
+            "algorithmic_bytes": head_algo,
             "timed": f"HIP events (created with hipEventDisableSystemFence) stamped by the GPU "
-                     f"at the start and end of {kernels[0]} (hipExtLaunchKernel), {args.steps} "
+                     f"at the start and end of {head_kernels[0]} (hipExtLaunchKernel), {args.steps} "
                      "further steps, caches flushed",
         },
     }
     if contig_ms:
         line["paging_control"] = {
-            "contiguous_call_ms": round(mean(contig_ms), 5),
-            "paged_same_schedule_call_ms": round(mean(unsplit_ms), 5),
+            "contiguous_call_us": round(mean(contig_ms) * 1e3, 2),
+            "paged_same_schedule_call_us": round(mean(unsplit_ms) * 1e3, 2),
             "paged_over_contiguous": round(mean(unsplit_ms) / mean(contig_ms) - 1.0, 4),
-            "paged_auto_call_ms": round(mean(decode_ms), 5),
+            "paged_auto_call_us": round(mean(decode_ms) * 1e3, 2),
             "note": "pa_decode_contiguous on an unpaged copy of the cache (per sequence and KV head a "
                     "run of 16-token tiles, no block table) vs the paged kernel with the same "
                     "schedule (one workgroup per sequence and head group, MFMA), alternating, each "
                     "after a cache flush and timed by events around the call",
         }
     line["two_call_step"] = {
-        "step_ms": {"mean": round(mean(two_ms), 5), "p50": round(percentile(two_ms, 50), 5)},
+        "step_us": stats_us(two_ms),
         "value": round(eff_bytes / (mean(two_ms) / 1e3) / 1e9, 2),
         "unit": "GB/s",
-        "append_call_ms": {"mean": round(mean(append_ms), 5), "p50": round(percentile(append_ms, 50), 5)},
-        "decode_call_ms": {"mean": round(mean(decode_ms), 5), "p10": round(percentile(decode_ms, 10), 5),
-                           "p50": round(percentile(decode_ms, 50), 5),
-                           "p90": round(percentile(decode_ms, 90), 5)},
-        "note": "the same step as " + ("pa_copy_blocks + " if has_copies else "") + "pa_cache_append + "
+        "append_call_us": stats_us(append_ms),
+        "decode_call_us": stats_us(decode_ms),
+        "note": "the same step as " + ("pa_copy_blocks + " if int(w.copies.shape[0]) else "") + "pa_cache_append + "
                 "pa_decode (the append kernel, then the decode schedule), flushed, events around the calls",
     }
     if multi:
         line["multi_query"] = multi[0]
         line["multi_query_long"] = multi[1]
     if hot_ms:
-        line["unflushed_step_ms"] = {"mean": round(mean(hot_ms), 5),
-                                     "p50": round(percentile(hot_ms, 50), 5),
-                                     "gbs": round(eff_bytes / (mean(hot_ms) / 1e3) / 1e9, 2)}
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["unflushed_step_us"] = {**stats_us(hot_ms), "gbs": round(eff_bytes / (mean(hot_ms) / 1e3) / 1e9, 2)}
+    if configs:
+        line["configs"] = configs
+        line["configs_note"] = (
+            "every seeded configuration, each step (pa_append_decode with the caller's workspace and a host "
+            "copy of the lengths, after the step's copy-on-write copies) timed by events around it over "
+            f"{args.steps} flushed steps after {args.warmup} warm-up steps, and its main kernel alone by "
+            "GPU-stamped events over as many more; value = effective (logical) KV bytes / step; kernel_frac "
+            "= algorithmic bytes (unique KV bytes, plus the new tokens where that kernel writes them) / "
+            "kernel time / 8 TB/s")
+    if pool is not None:
+        line["cpu_baseline"] = cpu_baseline(pool, n_workers, affinity, w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

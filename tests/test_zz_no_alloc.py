@@ -11,7 +11,7 @@ import pytest
 import oracle
 from paged_kv_cache_122_amd import device as dev
 from paged_kv_cache_122_amd import workloads
-from tests.gpu_util import assert_close_bf16, need_gpu
+from gpu_util import assert_close_bf16, need_gpu
 
 pytestmark = pytest.mark.gpu
 
