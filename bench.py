@@ -244,19 +244,29 @@ class Step:
         self.has_copies = int(w.copies.shape[0]) > 0
         max_len = int(w.block_tables.shape[1]) * w.block_size
         self.part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
-        self.kernels, self.schedule = decode_kernels(w, self.part, cus)
-        fused, fk, kind, writes_new = fused_step(w, self.part, cus)
-        # bytes the main kernel must move: a physical block shared by several
-        # sequences (a common prefix) counts once; in one-launch steps the
-        # kernel also writes the new token (else the combine that follows does)
-        self.algo_bytes = w.unique_kv_bytes()
+        _, self.schedule = decode_kernels(w, self.part, cus)
+        fused, _, kind, _ = fused_step(w, self.part, cus)
         if fused:
-            self.kernels, self.schedule = fk, kind
-            if writes_new:
-                self.algo_bytes += w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
+            self.schedule = kind
         nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, 0)
         self.ws = pa.alloc_workspace(nb, "cuda:0") if nb else None
         self.host_lens = np.asarray(w.context_lens, dtype=np.int32)
+        # the kernels the step launches, as the library reports them (one
+        # call; the bench's warm-up repeats it); the main kernel is the first
+        # one after the copy-on-write copies and a separate append
+        self()
+        launched = pa.last_launch()
+        self.kernels = [k for k in launched if not k.startswith(("copy_kernel", "append_kernel"))]
+        if not self.kernels:
+            raise RuntimeError(f"{w.name}: the step launched no decode kernel ({launched})")
+        self.kernels_all = launched
+        # bytes the main kernel must move: a physical block shared by several
+        # sequences (a common prefix) counts once; the multi-token kernel also
+        # writes the new tokens (a separate append kernel, or the combine after
+        # the shared-partition kernel, writes them otherwise)
+        self.algo_bytes = w.unique_kv_bytes()
+        if self.kernels[0].startswith("decode_multi"):
+            self.algo_bytes += w.num_seqs * w.num_kv_heads * w.head_dim * 2 * 2
 
     def copies(self):
         if self.has_copies:
@@ -264,7 +274,7 @@ class Step:
 
     def __call__(self, kernel_events=None):
         dw, w = self.dw, self.w
-        self.copies()
+        self.copies()  # pa_last_launch then names the step's own call alone
         self.pa.append_decode(self.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
                               dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=self.ws,
                               kernel_events=kernel_events, host_context_lens=self.host_lens, stream=self.stream)
@@ -329,7 +339,7 @@ def config_row(st, step_ms, kernel_ms):
         "unit": "GB/s",
         "seqs_per_s": round(w.num_seqs / t, 1),
         "kernel": st.kernels[0],
-        "kernels": st.kernels,
+        "kernels": st.kernels_all,
         "kernel_us": stats_us(kernel_ms),
         "effective_kv_bytes": eff,
         "unique_kv_bytes": w.unique_kv_bytes(),
@@ -344,11 +354,10 @@ def config_row(st, step_ms, kernel_ms):
     return row
 
 
-MULTI_CONFIGS = (("llama3_8b_verify5_b64", "decode_multi<128,16,2,false>"),
-                 ("long32k_verify5_b16", "decode_multi<128,16,2,true>"))
+MULTI_CONFIGS = ("llama3_8b_verify5_b64", "long32k_verify5_b16")
 
 
-def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
+def multi_query_leg(config, steps, warmup, tev, stream, flush):
     """pa_decode_multi on a verification batch (5 drafted tokens per sequence):
     the append of the drafted tokens and their causal attention, one launch
     (and a combine when the context is split).  Beside it, pa_decode of one
@@ -412,6 +421,7 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
                            workspace=ws, kernel_events=(a, b), host_context_lens=host_lens, stream=stream)
     stream.synchronize()
     kernel_ms = [tev.elapsed_ms(a, b) for a, b in kev]
+    kernels = pa.last_launch()
     new_kv = T * w.num_kv_heads * w.head_dim * 2 * 2
     # K/V of every context token read once (cached ones from the pool, new ones
     # from k_new / v_new), the new K/V written, q read and out written
@@ -429,7 +439,8 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
         "algorithmic_bytes": algo,
         "achieved_gbs": round(algo / t / 1e9, 2),
         "hbm_frac": round(algo / t / 1e9 / HBM_PEAK_GBS, 4),
-        "kernel": kernel,
+        "kernel": kernels[0],
+        "kernels": kernels,
         "kernel_us": stats_us(kernel_ms),
         "kernel_achieved_gbs": round(algo / tk / 1e9, 2),
         "kernel_hbm_frac": round(algo / tk / 1e9 / HBM_PEAK_GBS, 4),
@@ -440,7 +451,7 @@ def multi_query_leg(config, kernel, steps, warmup, tev, stream, flush):
                 "events around the call (launch included); kernel_us: the main kernel alone through "
                 "pa_decode_multi_ex (caller workspace, host lengths), GPU-stamped events",
     }
-    row.update(counter_fields(w.name, kernel))
+    row.update(counter_fields(w.name, kernels[0]))
     return row
 
 
@@ -629,13 +640,14 @@ def main():
             unsplit_ms = [tev.elapsed_ms(c, d) for _, _, c, d in cev]
             del kc, vc, out_c
         head_row = config_row(st, step_ms, kernel_ms)
-        head_kernels, head_schedule, head_algo, head_desc = st.kernels, st.schedule, st.algo_bytes, st.step_desc()
+        head_kernels, head_schedule, head_algo, head_desc = st.kernels_all, st.schedule, st.algo_bytes, st.step_desc()
+        head_main = st.kernels[0]
         del st
         torch.cuda.empty_cache()
 
         multi = []
         if not args.no_multi:
-            multi = [multi_query_leg(c, k, args.steps, args.warmup, tev, stream, flush) for c, k in MULTI_CONFIGS]
+            multi = [multi_query_leg(c, args.steps, args.warmup, tev, stream, flush) for c in MULTI_CONFIGS]
             torch.cuda.empty_cache()
 
         # every seeded configuration, timed the same way
@@ -668,7 +680,7 @@ def main():
     t_kernel = mean(kernel_ms) / 1e3
     value = eff_bytes / t_step / 1e9
     achieved = head_algo / t_kernel / 1e9
-    cf = counter_fields(w.name, head_kernels[0])
+    cf = counter_fields(w.name, head_main)
     line = {
         "metric": "paged decode-attention effective KV GB/s vs HBM peak; seqs/s per layer-step",
         "value": round(value, 2),
@@ -716,8 +728,9 @@ def main():
             "mfma_busy_pct": cf["mfma_busy_pct"],
             "kernels": head_kernels,
             "algorithmic_bytes": head_algo,
+            "kernel": head_main,
             "timed": f"HIP events (created with hipEventDisableSystemFence) stamped by the GPU "
-                     f"at the start and end of {head_kernels[0]} (hipExtLaunchKernel), {args.steps} "
+                     f"at the start and end of {head_main} (hipExtLaunchKernel), {args.steps} "
                      "further steps, caches flushed",
         },
     }

@@ -340,8 +340,11 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * partitions.  Preconditions (debug mode checks them, with pa_decode's): for
  * every sequence with L_s > 0, slot_mapping[s] is the slot its block table
  * gives position L_s - 1; a sequence with L_s == 0 has no new token and a
- * negative slot.  Every argument, the workspace included, is checked
- * before anything is launched.  S == 0 is a no-op.
+ * negative slot; no sequence reads a slot that receives another sequence's
+ * new token (copy-on-write has made the block that receives a new token
+ * private to its sequence; the fused kernels read the pools before the new
+ * tokens are stored, the two calls after).  Every argument, the workspace
+ * included, is checked before anything is launched.  S == 0 is a no-op.
  */
 int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k, const pa_tensor* v,
                      const pa_tensor* slot_mapping, pa_tensor* k_cache, pa_tensor* v_cache,
@@ -447,6 +450,15 @@ size_t pa_decode_multi_workspace_bytes(int64_t num_rows, int64_t num_seqs, int64
 
 /* Message of the last failed call on this thread (valid until the next pa_* call). */
 const char* pa_last_error(void);
+
+/*
+ * The kernels the last call of an entry point that takes a stream enqueued on
+ * this thread, in launch order, separated by spaces, each as its template
+ * instantiation (for instance "decode_shared<128,16,true> combine_append<128,16>");
+ * empty if it launched nothing.  For tests and benchmarks that need to know
+ * which schedule ran.  Valid until the next pa_* call on this thread.
+ */
+const char* pa_last_launch(void);
 
 /*
  * Debug mode (process-wide, off by default).  When on, the entry points that

@@ -23,7 +23,7 @@ MAX_DIMS = 5
 EXPORTED = ("pa_append_decode", "pa_cache_append", "pa_copy_blocks", "pa_decode", "pa_decode_contiguous",
             "pa_decode_ex", "pa_decode_noalloc",
             "pa_decode_multi", "pa_decode_multi_ex", "pa_decode_multi_workspace_bytes", "pa_decode_workspace_bytes",
-            "pa_decode_schedule", "pa_last_error", "pa_set_debug")
+            "pa_decode_schedule", "pa_last_error", "pa_last_launch", "pa_set_debug")
 
 _DTYPES = {torch.bfloat16: PA_BF16, torch.float32: PA_F32, torch.int32: PA_I32, torch.int64: PA_I64}
 
@@ -90,6 +90,8 @@ def load(path=None):
     lib.pa_decode_schedule.restype = ctypes.c_int
     lib.pa_last_error.argtypes = []
     lib.pa_last_error.restype = ctypes.c_char_p
+    lib.pa_last_launch.argtypes = []
+    lib.pa_last_launch.restype = ctypes.c_char_p
     lib.pa_set_debug.argtypes = [ctypes.c_int]
     lib.pa_set_debug.restype = ctypes.c_int
     if path is None:
@@ -334,6 +336,11 @@ def append_decode(out, q, k, v, slot_mapping, k_cache, v_cache, block_tables, co
                                      ctypes.c_int32(block_size), ctypes.byref(opts),
                                      ctypes.c_void_p(ws_ptr) if ws_ptr else None,
                                      ctypes.c_size_t(ws_bytes), _stream(stream)))
+
+
+def last_launch():
+    """Kernels the last library call on this thread enqueued (pa_last_launch), as a list."""
+    return load().pa_last_launch().decode().split()
 
 
 def set_debug(on):

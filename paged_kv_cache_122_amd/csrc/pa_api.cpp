@@ -24,7 +24,14 @@
 namespace {
 
 thread_local std::string g_error;
+thread_local std::string g_launch;  // kernels the last entry point enqueued on this thread
 std::atomic<int> g_debug{0};
+
+// Start of every entry point: no message, no launch yet.
+void begin_call() {
+  g_error.clear();
+  g_launch.clear();
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -492,6 +499,8 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
 
 PA_EXPORT const char* pa_last_error(void) { return g_error.c_str(); }
 
+PA_EXPORT const char* pa_last_launch(void) { return g_launch.c_str(); }
+
 PA_EXPORT int pa_set_debug(int on) { return g_debug.exchange(on ? 1 : 0); }
 
 PA_EXPORT size_t pa_decode_workspace_bytes(int64_t num_seqs, int64_t num_q_heads,
@@ -536,7 +545,7 @@ PA_EXPORT int pa_decode(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_c
                         const pa_tensor* v_cache, const pa_tensor* block_tables,
                         const pa_tensor* context_lens, float scale, int32_t block_size,
                         hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size,
                        nullptr, true, nullptr, 0, g_debug.load() != 0, stream);
 }
@@ -546,7 +555,7 @@ PA_EXPORT int pa_decode_ex(pa_tensor* out, const pa_tensor* q, const pa_tensor* 
                            const pa_tensor* context_lens, float scale, int32_t block_size,
                            const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
                            hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   return decode_common(out, q, k_cache, v_cache, block_tables, context_lens, scale, block_size, opts,
                        false, workspace, workspace_bytes, g_debug.load() != 0, stream);
 }
@@ -555,7 +564,7 @@ PA_EXPORT int pa_decode_noalloc(pa_tensor* out, const pa_tensor* q, const pa_ten
                                 const pa_tensor* v_cache, const pa_tensor* block_tables,
                                 const pa_tensor* context_lens, float scale, int32_t block_size,
                                 hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   // the size check comes before any device call: an oversized call launches nothing
   DecodePlan pl;
   int rc = plan_decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size, nullptr, &pl);
@@ -578,7 +587,7 @@ PA_EXPORT int pa_decode_noalloc(pa_tensor* out, const pa_tensor* q, const pa_ten
 PA_EXPORT int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
                                    const pa_tensor* v, const pa_tensor* context_lens, float scale,
                                    hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   int rc;
   if ((rc = check_desc(k, "k", PA_BF16, 5)) != PA_OK) return rc;
   if ((rc = check_desc(v, "v", PA_BF16, 5)) != PA_OK) return rc;
@@ -901,12 +910,6 @@ int multi_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_new, con
   if (S > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs %lld > 65535", (long long)S);
   if (T > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "too many rows");
   if (W * g.block_size > 0x7fffffff) return fail(PA_ERR_UNSUPPORTED, "table width * block_size >= 2^31");
-  if (S == 0 || T == 0 || max_query_len == 0) return PA_OK;
-  if (g_debug.load() &&
-      (rc = debug_check_multi(slot_mapping, query_start, block_tables, context_lens, S, T, W,
-                              g.block_size, g.num_blocks, max_query_len, stream)) != PA_OK)
-    return rc;
-
   if (opts) {
     if (opts->reserved != 0) return fail(PA_ERR_INVALID, "opts.reserved must be 0");
     if (opts->path == 1) return fail(PA_ERR_UNSUPPORTED, "the multi-token path runs on MFMA only (opts.path 0 or 2)");
@@ -1003,7 +1006,7 @@ PA_EXPORT int pa_decode_multi(pa_tensor* out, const pa_tensor* q, const pa_tenso
                               const pa_tensor* query_start, pa_tensor* k_cache, pa_tensor* v_cache,
                               const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
                               int32_t block_size, int32_t max_query_len, hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   return multi_common(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
                       context_lens, scale, block_size, max_query_len, nullptr, true, nullptr, 0, stream);
 }
@@ -1014,7 +1017,7 @@ PA_EXPORT int pa_decode_multi_ex(pa_tensor* out, const pa_tensor* q, const pa_te
                                  const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
                                  int32_t block_size, int32_t max_query_len, const pa_decode_opts* opts,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   return multi_common(out, q, k_new, v_new, slot_mapping, query_start, k_cache, v_cache, block_tables,
                       context_lens, scale, block_size, max_query_len, opts, false, workspace, workspace_bytes,
                       stream);
@@ -1129,6 +1132,36 @@ int debug_check_append_slots(const DecodePlan& pl, const pa_tensor* slot_mapping
   return PA_OK;
 }
 
+// pa_append_decode's read contract (debug mode): no sequence reads a slot
+// that this call writes for another sequence (a block receiving a new token
+// is private to its sequence, as copy-on-write leaves it).
+int debug_check_append_reads(const DecodePlan& pl, const pa_tensor* slot_mapping, const pa_tensor* block_tables,
+                             const pa_tensor* context_lens, hipStream_t stream) {
+  std::vector<int32_t> lens, bt;
+  std::vector<int64_t> slots;
+  const size_t stride = size_t(block_tables->stride[0]);
+  int rc;
+  if ((rc = copy_to_host(&lens, context_lens->data, size_t(pl.S), stream)) != PA_OK) return rc;
+  if ((rc = copy_to_host(&slots, slot_mapping->data, size_t(pl.S), stream)) != PA_OK) return rc;
+  if ((rc = copy_to_host(&bt, block_tables->data, size_t(pl.S - 1) * stride + size_t(pl.W), stream)) != PA_OK)
+    return rc;
+  std::unordered_map<int64_t, int64_t> writer;  // slot -> the sequence whose new token it receives
+  for (int64_t s = 0; s < pl.S; ++s)
+    if (slots[size_t(s)] >= 0) writer[slots[size_t(s)]] = s;
+  for (int64_t c = 0; c < pl.S && !writer.empty(); ++c) {
+    const int64_t L = std::min<int64_t>(std::max<int32_t>(lens[size_t(c)], 0), pl.W * pl.B);
+    for (int64_t pos = 0; pos < L; ++pos) {
+      const int64_t sl = int64_t(bt[size_t(c) * stride + size_t(pos / pl.B)]) * pl.B + pos % pl.B;
+      const auto it = writer.find(sl);
+      if (it != writer.end() && it->second != c)
+        return fail(PA_ERR_CONTRACT,
+                    "sequence %lld reads slot %lld (position %lld), which receives the new token of sequence %lld",
+                    (long long)c, (long long)sl, (long long)pos, (long long)it->second);
+    }
+  }
+  return PA_OK;
+}
+
 // One launch of the multi-token kernel for the step (one new token per
 // sequence): it stores the new token and attends, taking its K/V from k and
 // v; split (m->d.max_parts > 1, pieces in the workspace) a combine follows.
@@ -1156,7 +1189,7 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
                                const pa_tensor* block_tables, const pa_tensor* context_lens, float scale,
                                int32_t block_size, const pa_decode_opts* opts, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   int rc;
   DecodePlan pl;
   if ((rc = plan_decode(out, q, k_cache, v_cache, block_tables, context_lens, block_size, opts, &pl)) != PA_OK)
@@ -1186,6 +1219,7 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     const int64_t max_len = (opts && opts->max_context_len > 0) ? opts->max_context_len : pl.W * pl.B;
     if ((rc = debug_check_decode(pl, block_tables, context_lens, max_len, host_lens, stream)) != PA_OK) return rc;
     if ((rc = debug_check_append_slots(pl, slot_mapping, block_tables, context_lens, stream)) != PA_OK) return rc;
+    if ((rc = debug_check_append_reads(pl, slot_mapping, block_tables, context_lens, stream)) != PA_OK) return rc;
   }
 
   // Route: the multi-token kernel in one launch where the schedule is unsplit
@@ -1238,7 +1272,7 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
 
 PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* block_pairs,
                              hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   int rc;
   CacheGeom g;
   if ((rc = check_caches(k_cache, v_cache, &g)) != PA_OK) return rc;
@@ -1285,6 +1319,15 @@ PA_EXPORT int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_te
 
 PA_EXPORT int pa_cache_append(const pa_tensor* k, const pa_tensor* v, const pa_tensor* slot_mapping,
                               pa_tensor* k_cache, pa_tensor* v_cache, hipStream_t stream) {
-  g_error.clear();
+  begin_call();
   return cache_append_impl(k, v, slot_mapping, k_cache, v_cache, g_debug.load() != 0, stream);
 }
+
+namespace pa {
+
+void note_launch(const char* name) {
+  if (!g_launch.empty()) g_launch += ' ';
+  g_launch += name;
+}
+
+}  // namespace pa

@@ -132,6 +132,8 @@ struct LaunchCtx {
 
 hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head_dim, int block_size,
                          Path path, const LaunchCtx& ctx);
+// Records a kernel the current entry point enqueued (pa_last_launch).
+void note_launch(const char* name);
 // Address of the current device's copy of the library's fixed scratch array
 // (PA_NOALLOC_SCRATCH_BYTES, 256-byte aligned), looked up once per device.
 hipError_t noalloc_scratch(void** ptr, size_t* bytes);

@@ -64,7 +64,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdio>
 #include <mutex>
+#include <string>
 #include <unordered_map>
 
 #include "pa.h"
@@ -1238,8 +1240,10 @@ __device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_
 // the pools afterwards (no workgroup of this kernel reads its slot), so the
 // step needs no append launch before the decode, and no attention workgroup
 // waits at its end for store acknowledgements while the reads saturate the
-// memory.  The new token's block is the sequence's own (it is written), so
-// the workgroup of a last partition carries no other member.
+// memory.  A partition that is the last of the leader or of a member holds a
+// new token that is not in the pools yet, so it is never shared: its
+// sequence computes it alone (after copy-on-write the new token's block is
+// the sequence's own anyway, and no other table names it).
 // ---------------------------------------------------------------------------
 constexpr int kMaxShare = 16;  // members per workgroup at G = 1
 
@@ -1270,14 +1274,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   const bool own_new = Fused && L > 0 && part == nparts - 1;  // workgroup-uniform
   const int t_walk = own_new ? t1 - 1 : t1;                   // the pool's tokens read here
 
+  // Only a filled partition is shared; in a decode step also only one that
+  // holds none of its sequences' new tokens (a sequence's last token lies in
+  // its last partition): those are not in the pools yet when this kernel
+  // reads them.
+  const int share_len = t0 + p.part_tokens + (Fused ? 1 : 0);
   int m = 1;  // members (sequences s .. s+m-1)
-  if (M > 1 && L >= t0 + p.part_tokens) {  // workgroup-uniform: only a filled partition is shared
+  if (M > 1 && L >= share_len) {  // workgroup-uniform
     const int w0 = s - s % M;
     const int lo = max(s - 1, w0);
     const int hi = min(w0 + M, p.num_seqs);
     const int E = p.part_tokens / BS;  // table entries of the partition
     for (int c = lo + int(threadIdx.x); c < hi; c += kThreads)
-      differs[c - lo] = clamp_len(p, p.context_lens[c]) < t0 + p.part_tokens;
+      differs[c - lo] = clamp_len(p, p.context_lens[c]) < share_len;
     __syncthreads();
     const int32_t* mine = p.block_tables + size_t(s) * p.bt_s + t0 / BS;
     for (int idx = threadIdx.x; idx < (hi - lo) * E; idx += kThreads) {
@@ -1994,14 +2003,32 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyParams p) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Name of a kernel instantiation, as pa_last_launch reports it.
+std::string kname(const char* fmt, int a = 0, int b = 0, int c = 0) {
+  char buf[96];
+  snprintf(buf, sizeof(buf), fmt, a, b, c);
+  return buf;
+}
+
+std::string multi_name(int d, int bs, int ns, bool split) {
+  return kname(split ? "decode_multi<%d,%d,%d,true>" : "decode_multi<%d,%d,%d,false>", d, bs, ns);
+}
+
+// The status of the launch just made; a successful one is recorded for pa_last_launch.
+hipError_t launched(const std::string& name) {
+  const hipError_t e = hipGetLastError();
+  if (e == hipSuccess) note_launch(name.c_str());
+  return e;
+}
+
 // The main decode kernel of a call, optionally bracketed by timing events.
 template <typename K, typename... A>
-hipError_t launch_main(K kernel, dim3 grid, dim3 block, const LaunchCtx& c, A... args) {
+hipError_t launch_main(const std::string& name, K kernel, dim3 grid, dim3 block, const LaunchCtx& c, A... args) {
   if (c.start && c.stop)
     hipExtLaunchKernelGGL(kernel, grid, block, 0, c.stream, c.start, c.stop, 0, args...);
   else
     hipLaunchKernelGGL(kernel, grid, block, 0, c.stream, args...);
-  return hipGetLastError();
+  return launched(name);
 }
 
 // Workgroups of a kernel that one compute unit holds at once (its occupancy).
@@ -2041,10 +2068,10 @@ inline void fill_order(DecodeParams& p, const LaunchCtx& c) {
 }
 
 template <typename K>
-hipError_t launch_rows(K kernel, DecodeParams p, int row_wgs, const LaunchCtx& c) {
+hipError_t launch_rows(const std::string& name, K kernel, DecodeParams p, int row_wgs, const LaunchCtx& c) {
   p.rank_split = p.max_parts == 1 ? rank_split_of(p, row_wgs, resident_per_cu(kernel), c) : p.num_seqs;
   fill_order(p, c);
-  return launch_main(kernel, dim3(row_wgs, p.num_seqs, p.max_parts), dim3(kThreads), c, p);
+  return launch_main(name, kernel, dim3(row_wgs, p.num_seqs, p.max_parts), dim3(kThreads), c, p);
 }
 
 // Fewer MFMA workgroups than compute units: take the deep pipeline.
@@ -2057,20 +2084,23 @@ hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx&
   static_assert(kDeepSlots > kPipeSlots, "");
   hipError_t e;
   if (path == Path::Mfma && deep_pipeline(p, c))
-    e = launch_rows(decode_mfma<D, BS, kDeepSlots>, p, p.num_kv_heads * p.head_groups, c);
+    e = launch_rows(kname("decode_mfma<%d,%d,%d>", D, BS, kDeepSlots), decode_mfma<D, BS, kDeepSlots>, p,
+                    p.num_kv_heads * p.head_groups, c);
   else if (path == Path::Mfma && p.max_parts > 1 && p.group <= 16)
-    e = launch_main(decode_shared<D, BS, false>, dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c,
+    e = launch_main(kname("decode_shared<%d,%d,false>", D, BS), decode_shared<D, BS, false>,
+                    dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c,
                     MultiParams{p});  // split: shared partitions read once (no ranking)
   else if (path == Path::Mfma)
-    e = launch_rows(decode_mfma<D, BS, kPipeSlots>, p, p.num_kv_heads * p.head_groups, c);
+    e = launch_rows(kname("decode_mfma<%d,%d,%d>", D, BS, kPipeSlots), decode_mfma<D, BS, kPipeSlots>, p,
+                    p.num_kv_heads * p.head_groups, c);
   else if (p.group == 1)
-    e = launch_rows(decode_valu<D, BS, 1>, p, p.num_kv_heads, c);
+    e = launch_rows(kname("decode_valu<%d,%d,1>", D, BS), decode_valu<D, BS, 1>, p, p.num_kv_heads, c);
   else
-    e = launch_rows(decode_valu<D, BS, 2>, p, p.num_kv_heads, c);
+    e = launch_rows(kname("decode_valu<%d,%d,2>", D, BS), decode_valu<D, BS, 2>, p, p.num_kv_heads, c);
   if (e != hipSuccess || p.max_parts <= 1) return e;
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
   hipLaunchKernelGGL((combine_parts<D>), cgrid, dim3(256), 0, c.stream, p);
-  return hipGetLastError();
+  return launched(kname("combine_parts<%d>", D));
 }
 
 // The partitioned schedule's decode_shared launch with the step's new tokens
@@ -2079,40 +2109,41 @@ hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx&
 template <int D, int BS>
 hipError_t launch_shared_step_d(const MultiParams& m, const LaunchCtx& c) {
   const DecodeParams& p = m.d;
-  hipError_t e = launch_main(decode_shared<D, BS, true>, dim3(p.num_kv_heads, p.num_seqs, p.max_parts),
-                             dim3(kThreads), c, m);
+  hipError_t e = launch_main(kname("decode_shared<%d,%d,true>", D, BS), decode_shared<D, BS, true>,
+                             dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c, m);
   if (e != hipSuccess) return e;
   // num_kv_heads * D / 8 <= num_q_heads * D: the combine's rows cover the pieces
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
   hipLaunchKernelGGL((combine_append<D, BS>), cgrid, dim3(256), 0, c.stream, m);
-  return hipGetLastError();
+  return launched(kname("combine_append<%d,%d>", D, BS));
 }
 
 // Persistent grid: as many workgroups as can be resident at once (all waves
 // stream concurrently; a second round would repeat the start-up latency).
 template <typename K>
-hipError_t launch_persistent(K kernel, const DecodeParams& p, const StreamParams& sk, const LaunchCtx& c) {
+hipError_t launch_persistent(const std::string& name, K kernel, const DecodeParams& p, const StreamParams& sk,
+                             const LaunchCtx& c) {
   int occ = 0;
   hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kThreads, 0);
   if (e != hipSuccess) return e;
   const int per_cu = std::max(1, std::min(sk.workgroups_per_cu, occ));
   const int wgs = std::min(sk.cus * per_cu, kMaxStreamWaves / kWaves);
-  return launch_main(kernel, dim3(wgs), dim3(kThreads), c, p, sk);
+  return launch_main(name, kernel, dim3(wgs), dim3(kThreads), c, p, sk);
 }
 
 template <int D, int BS>
 hipError_t launch_stream(const DecodeParams& p, const StreamParams& sk, Path path, const LaunchCtx& c) {
   hipError_t e;
   if (path == Path::Mfma)
-    e = launch_persistent(decode_mfma_sk<D, BS>, p, sk, c);
+    e = launch_persistent(kname("decode_mfma_sk<%d,%d>", D, BS), decode_mfma_sk<D, BS>, p, sk, c);
   else if (p.group == 1)
-    e = launch_persistent(decode_valu_sk<D, BS, 1>, p, sk, c);
+    e = launch_persistent(kname("decode_valu_sk<%d,%d,1>", D, BS), decode_valu_sk<D, BS, 1>, p, sk, c);
   else
-    e = launch_persistent(decode_valu_sk<D, BS, 2>, p, sk, c);
+    e = launch_persistent(kname("decode_valu_sk<%d,%d,2>", D, BS), decode_valu_sk<D, BS, 2>, p, sk, c);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((combine_sk<D>), dim3(p.num_seqs * p.num_kv_heads * p.head_groups), dim3(512), 0,
                      c.stream, p, sk);
-  return hipGetLastError();
+  return launched(kname("combine_sk<%d>", D));
 }
 
 template <int D>
@@ -2137,7 +2168,7 @@ hipError_t launch_append_d(const AppendParams& p, int block_size, hipStream_t st
     case 32: hipLaunchKernelGGL((append_kernel<D, 32>), grid, block, 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return launched(kname("append_kernel<%d,%d>", D, block_size));
 }
 
 }  // namespace
@@ -2173,19 +2204,23 @@ hipError_t launch_contiguous(const DecodeParams& p, int head_dim, const LaunchCt
   // the pipeline depth the paged kernel takes for the same grid
   const bool deep = deep_pipeline(q, ctx);
   if (head_dim == 64)
-    return deep ? launch_rows(decode_mfma_contiguous<64, kDeepSlots>, q, row_wgs, ctx)
-                : launch_rows(decode_mfma_contiguous<64, kPipeSlots>, q, row_wgs, ctx);
+    return deep ? launch_rows(kname("decode_mfma_contiguous<64,%d>", kDeepSlots),
+                              decode_mfma_contiguous<64, kDeepSlots>, q, row_wgs, ctx)
+                : launch_rows(kname("decode_mfma_contiguous<64,%d>", kPipeSlots),
+                              decode_mfma_contiguous<64, kPipeSlots>, q, row_wgs, ctx);
   if (head_dim == 128)
-    return deep ? launch_rows(decode_mfma_contiguous<128, kDeepSlots>, q, row_wgs, ctx)
-                : launch_rows(decode_mfma_contiguous<128, kPipeSlots>, q, row_wgs, ctx);
+    return deep ? launch_rows(kname("decode_mfma_contiguous<128,%d>", kDeepSlots),
+                              decode_mfma_contiguous<128, kDeepSlots>, q, row_wgs, ctx)
+                : launch_rows(kname("decode_mfma_contiguous<128,%d>", kPipeSlots),
+                              decode_mfma_contiguous<128, kPipeSlots>, q, row_wgs, ctx);
   return hipErrorInvalidValue;
 }
 
 template <typename K>
-hipError_t launch_multi_k(K kernel, MultiParams p, int head_dim, const LaunchCtx& c) {
+hipError_t launch_multi_k(const std::string& name, K kernel, MultiParams p, int head_dim, const LaunchCtx& c) {
   const int row_wgs = p.d.num_kv_heads * p.col_groups;
   if (p.num_items > 0)  // split over the host's (sequence, partition) list
-    return launch_main(kernel, dim3(row_wgs, p.num_items, 1), dim3(kThreads), c, p);
+    return launch_main(name, kernel, dim3(row_wgs, p.num_items, 1), dim3(kThreads), c, p);
   const int occ = p.d.max_parts == 1 ? resident_per_cu(kernel) : 1;
   p.d.rank_split = p.d.max_parts == 1 ? rank_split_of(p.d, row_wgs, occ, c) : p.d.num_seqs;
   fill_order(p.d, c);
@@ -2199,15 +2234,16 @@ hipError_t launch_multi_k(K kernel, MultiParams p, int head_dim, const LaunchCtx
       if (p.d.num_seqs + rows <= 65535) p.append_rows = int(rows);
     }
   }
-  return launch_main(kernel, dim3(row_wgs, p.d.num_seqs + p.append_rows, p.d.max_parts), dim3(kThreads), c, p);
+  return launch_main(name, kernel, dim3(row_wgs, p.d.num_seqs + p.append_rows, p.d.max_parts), dim3(kThreads), c,
+                     p);
 }
 
 template <int D, int NS, bool Split>
 hipError_t launch_multi_split(const MultiParams& p, int block_size, const LaunchCtx& c) {
   switch (block_size) {
-    case 8: return launch_multi_k(decode_multi<D, 8, NS, Split>, p, D, c);
-    case 16: return launch_multi_k(decode_multi<D, 16, NS, Split>, p, D, c);
-    case 32: return launch_multi_k(decode_multi<D, 32, NS, Split>, p, D, c);
+    case 8: return launch_multi_k(multi_name(D, 8, NS, Split), decode_multi<D, 8, NS, Split>, p, D, c);
+    case 16: return launch_multi_k(multi_name(D, 16, NS, Split), decode_multi<D, 16, NS, Split>, p, D, c);
+    case 32: return launch_multi_k(multi_name(D, 32, NS, Split), decode_multi<D, 32, NS, Split>, p, D, c);
     default: return hipErrorInvalidValue;
   }
 }
@@ -2225,7 +2261,7 @@ hipError_t launch_multi_d(const MultiParams& p, int block_size, const LaunchCtx&
   if (e != hipSuccess || p.d.max_parts <= 1) return e;
   const dim3 cgrid((p.d.num_q_heads * D + 255) / 256, p.d.num_seqs, std::min(p.max_query_len, 65535));
   hipLaunchKernelGGL((combine_rows<D>), cgrid, dim3(256), 0, c.stream, p);
-  return hipGetLastError();
+  return launched(kname("combine_rows<%d>", D));
 }
 
 hipError_t launch_multi(const MultiParams& p, int head_dim, int block_size, const LaunchCtx& c) {
@@ -2238,7 +2274,7 @@ hipError_t launch_copy(const CopyParams& p, hipStream_t stream) {
   const int64_t gx = 2 * ((p.block_units + kCopyChunk - 1) / kCopyChunk);
   const dim3 grid(unsigned(gx), unsigned(std::min(p.num_pairs, 65535)));
   hipLaunchKernelGGL(copy_kernel, grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return launched("copy_kernel");
 }
 
 hipError_t launch_append(const AppendParams& p, int head_dim, int block_size, hipStream_t stream) {

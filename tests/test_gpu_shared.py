@@ -8,7 +8,10 @@ consecutively.  Each case runs as two calls (pa_cache_append, then
 pa_decode_ex) and as one pa_append_decode, whose shared-partition kernel takes
 the append (the last partition of each sequence reads its new token from k / v
 and stores it); pools bit-exact and every row against the fp64 oracle:
-max|err| <= 1e-2, relative RMS <= 2e-3 (f32 outputs)."""
+max|err| <= 1e-2, relative RMS <= 2e-3 (f32 outputs).  Every batch is grown
+(its groups repeated) until its grid holds a workgroup per compute unit, and
+each call is checked to have run the shared-partition kernel (pa_last_launch):
+smaller grids take the deep-pipeline kernel, which shares nothing."""
 
 import numpy as np
 import pytest
@@ -51,9 +54,37 @@ def shared_workload(name, seed, groups, prompt, tail_max, *, hq, hkv, d, b, inte
                                     copies=list(pool.pending_copies))
 
 
+GRID_MIN = 256  # workgroups: the split schedule takes decode_shared from one per compute unit
+
+
+def grown_workload(name, seed, groups, prompt, tail_max, part, **kw):
+    """shared_workload with its groups repeated until (KV heads x sequences x
+    partitions) reaches GRID_MIN."""
+    reps = 1
+    while True:
+        w = shared_workload(name, seed, list(groups) * reps, prompt, tail_max, **kw)
+        parts = -(-(w.table_width * w.block_size) // part)
+        if w.num_kv_heads * w.num_seqs * parts >= GRID_MIN:
+            return w
+        reps *= 2
+
+
+_REFS = {}
+
+
+def reference(w):
+    """The oracle's step, its decode computed once per workload of this module."""
+    key = (w.name, w.seed, w.num_seqs)
+    kst, vst, ref = oracle_step(w, seqs=[] if key in _REFS else None)
+    if key not in _REFS:
+        _REFS[key] = ref
+    return kst, vst, _REFS[key]
+
+
 def run_step(w, part, fused):
     """Copy-on-write copies, then the step's append and decode on partitions of
-    `part` tokens (two calls, or pa_append_decode); returns (out f64, device workload)."""
+    `part` tokens (two calls, or pa_append_decode); returns (out f64, device
+    workload).  Checks that the decode ran the shared-partition kernel."""
     torch = need_gpu()
     from paged_kv_cache_122_amd import _lib as pa
     from paged_kv_cache_122_amd import device as dev
@@ -64,13 +95,17 @@ def run_step(w, part, fused):
     nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, maxlen, part)
     ws = pa.alloc_workspace(nb, "cuda") if nb else None
     out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    d, b = w.head_dim, w.block_size
     if fused:
         pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, dw.block_tables,
                          dw.context_lens, w.scale, w.block_size, partition_tokens=part, workspace=ws)
+        want = [f"decode_shared<{d},{b},true>", f"combine_append<{d},{b}>"]
     else:
         pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
         pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size,
                      partition_tokens=part, workspace=ws)
+        want = [f"decode_shared<{d},{b},false>", f"combine_parts<{d}>"]
+    assert pa.last_launch() == want, f"route {pa.last_launch()}, expected {want}"
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), dw
 
@@ -96,10 +131,10 @@ CASES = [
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_shared_partitions_parity(case, fused):
     name, seed, groups, prompt, tail_max, hq, hkv, d, b, part, inter = case
-    w = shared_workload(name, seed, groups, prompt, tail_max, hq=hq, hkv=hkv, d=d, b=b, interleave=inter)
+    w = grown_workload(name, seed, groups, prompt, tail_max, part, hq=hq, hkv=hkv, d=d, b=b, interleave=inter)
     print(f"[{name} fused={fused}] S={w.num_seqs} lens {int(w.context_lens.min())}..{int(w.context_lens.max())} "
           f"copies {len(w.copies)} partition {part}", flush=True)
-    kst, vst, ref = oracle_step(w)
+    kst, vst, ref = reference(w)
     got, dw = run_step(w, part, fused)
     check_pools(w, dw, kst, vst)
     a, r = assert_close(got, ref, name)
@@ -119,10 +154,37 @@ def test_shared_random_batches(seed, fused):
     part = int(rng.choice([256, 512, 1024]))
     groups = rng.integers(1, 21, size=int(rng.integers(1, 4))).tolist()
     prompt = int(rng.choice([part, 2 * part, part + 37, 3 * part // 2]))
-    w = shared_workload(f"shared{seed}", 7000 + seed, groups, prompt, 300, hq=g * hkv, hkv=hkv, d=d, b=b)
-    print(f"[shared{seed} fused={fused}] G={g} Hkv={hkv} D={d} B={b} groups={groups} prompt={prompt} "
+    w = grown_workload(f"shared{seed}", 7000 + seed, groups, prompt, 300, part, hq=g * hkv, hkv=hkv, d=d, b=b)
+    print(f"[shared{seed} fused={fused}] G={g} Hkv={hkv} D={d} B={b} S={w.num_seqs} prompt={prompt} "
           f"part={part}", flush=True)
-    kst, vst, ref = oracle_step(w)
+    kst, vst, ref = reference(w)
     got, dw = run_step(w, part, fused)
     check_pools(w, dw, kst, vst)
     assert_close(got, ref, f"shared{seed}")
+
+
+def test_append_decode_refuses_reads_of_another_sequences_new_slot():
+    """Debug mode: a step whose new token lands in a slot another sequence reads
+    (a shared block written without copy-on-write) is refused before any launch."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    # two sequences on one block: sequence 0 (5 tokens) writes position 4, which
+    # sequence 1 (6 tokens) reads as its own position 4
+    w = workloads.build_workload("shared_slot", 9001, np.random.Generator(np.random.PCG64(9001)),
+                                 num_q_heads=8, num_kv_heads=2, head_dim=64, block_size=16, num_blocks=4,
+                                 tables=[[2], [2]], context_lens=[5, 6], width=1)
+    dw = dev.upload(w)
+    out = torch.empty_like(dw.q)
+    before = dev.bf16_bits(dw.k_cache).copy()
+    prev = pa.set_debug(True)
+    try:
+        with pytest.raises(pa.PaError) as e:
+            pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                             dw.block_tables, dw.context_lens, w.scale, w.block_size)
+    finally:
+        pa.set_debug(prev)
+    assert e.value.code == pa.PA_ERR_CONTRACT and "new token of sequence 0" in str(e.value)
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.bf16_bits(dw.k_cache), before), "a refused call wrote the pool"
