@@ -26,7 +26,7 @@ Host bookkeeping only; it never touches K/V values.
 import hashlib
 import struct
 
-from .blockpool import Sequence, allocate_tokens
+from .blockpool import Sequence, reserve_slots
 
 ROOT_HASH = bytes(32)
 
@@ -45,7 +45,7 @@ class PrefixCache:
         self.pool = pool
         self.by_hash = {}   # hash -> physical block
         self.hash_of = {}   # physical block -> hash
-        pool.on_allocate = self._forget
+        pool.on_take = self._forget
 
     def _forget(self, b):
         """The pool reused block b: its old contents, and so its hash, are gone."""
@@ -57,7 +57,7 @@ class PrefixCache:
         if self.pool.ref.get(b, 0) == 0:
             self.pool.revive(b)
         else:
-            self.pool.incref(b)
+            self.pool.share(b)
 
     def allocate_prompt(self, token_ids, salt=b""):
         """A sequence holding ``token_ids``: full blocks through the cache, the
@@ -73,11 +73,11 @@ class PrefixCache:
                 self._share(b)
                 hits += 1
             else:
-                b = self.pool.allocate()
+                b = self.pool.take()
                 self.by_hash[h] = b
                 self.hash_of[b] = h
             seq.table.append(b)
             seq.length += B
             parent = h
-        allocate_tokens(self.pool, seq, len(token_ids) - seq.length)
+        reserve_slots(self.pool, seq, len(token_ids) - seq.length)
         return seq, hits

@@ -29,7 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import layout
-from .blockpool import BlockPool, Sequence, allocate_tokens, append_token, fork, free, slot_of_position
+from .blockpool import BlockPool, Sequence, fork, free, reserve_slot, reserve_slots, slot_of_position
 from .sizing import blocks_for_tokens, effective_kv_bytes
 
 NAN_BF16 = 0x7FC0
@@ -225,7 +225,7 @@ def place_independent(rng, context_lens, block_size, num_blocks):
     tables = []
     for L in context_lens:
         seq = Sequence()
-        allocate_tokens(pool, seq, int(L))
+        reserve_slots(pool, seq, int(L))
         tables.append(seq.table)
     return pool, tables
 
@@ -300,11 +300,11 @@ def opt13b_prefix_sharing():
     tables, lens = [], []
     for g in range(groups):
         parent = Sequence()
-        allocate_tokens(pool, parent, prompt)
+        reserve_slots(pool, parent, prompt)
         children = [fork(pool, parent) for _ in range(per)]
         free(pool, parent)
         for j, child in enumerate(children):
-            allocate_tokens(pool, child, tails[g * per + j])
+            reserve_slots(pool, child, tails[g * per + j])
             tables.append(child.table)
             lens.append(child.length)
     if pool.pending_copies:
@@ -331,11 +331,11 @@ def opt13b_cow_fork():
     tables, lens = [], []
     for _ in range(groups):
         parent = Sequence()
-        allocate_tokens(pool, parent, prompt)
+        reserve_slots(pool, parent, prompt)
         children = [fork(pool, parent) for _ in range(per)]
         free(pool, parent)
         for child in children:
-            append_token(pool, child)  # this step's token
+            reserve_slot(pool, child)  # this step's token
             tables.append(child.table)
             lens.append(child.length)
     copies = list(pool.pending_copies)
