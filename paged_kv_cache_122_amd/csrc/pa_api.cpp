@@ -805,7 +805,7 @@ bool host_length_split(int64_t S, int64_t Hkv, int64_t span, const int32_t* host
   const int64_t parts = (span + part - 1) / part;
   m->d.part_tokens = int(part);
   m->d.max_parts = int(parts);
-  if (S <= pa::kMaxRankedSeqs && parts <= 256) {
+  if (S <= pa::kMaxItemSeqs && parts <= 256) {
     std::vector<int> idx(static_cast<size_t>(S));
     for (int64_t i = 0; i < S; ++i) idx[size_t(i)] = int(i);
     std::stable_sort(idx.begin(), idx.end(), [&](int x, int y) { return len(x) > len(y); });
@@ -813,7 +813,7 @@ bool host_length_split(int64_t S, int64_t Hkv, int64_t span, const int32_t* host
     for (const int sq : idx) {
       const int64_t cached = std::max<int64_t>(len(sq) - new_tokens, 0);
       const int64_t np = std::min<int64_t>(std::max<int64_t>((cached + part - 1) / part, 1), parts);
-      if (items + np > pa::kMaxRankedSeqs) {
+      if (items + np > pa::kMaxOrder) {
         items = -1;
         break;
       }

@@ -16,7 +16,15 @@ constexpr int kDefaultPartition = 512;  // tokens per partition on the partition
 // stream-K schedule limits: the per-workgroup tile prefix lives in LDS, and
 // partial results are sized for at most this many waves
 constexpr int kMaxStreamSeqs = 8192;
-constexpr int kMaxRankedSeqs = 256;      // partitioned grids order at most this many sequences
+// Ordering the rows of an unsplit grid by context length: each workgroup ranks
+// up to kMaxDeviceRanked sequences itself (keys in LDS); a host copy of the
+// lengths lets the host rank up to kMaxOrder, passed in the kernel arguments
+// (the order array keeps every parameter struct within 4 KiB of kernel
+// arguments).  Larger batches keep index order.
+constexpr int kMaxDeviceRanked = 256;
+constexpr int kMaxOrder = 1536;
+// The split multi-token grid's (sequence, partition) list: 8 bits each.
+constexpr int kMaxItemSeqs = 256;
 constexpr int kMaxStreamWaves = 4096;
 constexpr int kDefaultWorkgroupsPerCu = 2;
 constexpr int kPlanHeader = 4;  // ints before the tile prefix in the stream-K plan
@@ -55,7 +63,7 @@ struct DecodeParams {
   // has_order 2 (split multi-token grid): order[y] = sequence << 8 | partition,
   // the grid's rows listing only the partitions that hold tokens.
   int has_order;
-  uint16_t order[kMaxRankedSeqs];
+  uint16_t order[kMaxOrder];
 };
 
 // stream-K schedule: plan = {tiles per wave, total tiles, -, -, prefix[S + 1]}
@@ -100,6 +108,9 @@ struct MultiParams {
   int append_rows;                 // > 0 (unsplit grids larger than the GPU holds at once): rows
                                    // after the sequences' rows that only append, started last
 };
+
+static_assert(sizeof(MultiParams) + sizeof(StreamParams) <= 4096,
+              "kernel arguments stay within 4 KiB");
 
 struct CopyParams {
   const int64_t* pairs;  // [N, 2] (src, dst) physical block ids

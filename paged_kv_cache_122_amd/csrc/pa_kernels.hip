@@ -1095,12 +1095,13 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
 // the partition, and neighbouring sequences, which often share prefix blocks
 // (parallel samples of one prompt), stay close in time so that the shared
 // blocks are still cached when the next one reads them.  So do batches of
-// more than kMaxRankedSeqs sequences or with table spans of 2^22 tokens or more.
+// more than kMaxDeviceRanked sequences or with table spans of 2^22 tokens or
+// more, unless the host ranked them (has_order 1).
 __device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
   const int S = p.num_seqs;
   if (p.has_order == 1) return p.order[y];  // ranked on the host: no round trip to the lengths
-  if (p.max_parts > 1 || S > kMaxRankedSeqs || p.max_len >= (1 << 22)) return y;
-  __shared__ uint32_t keys[kMaxRankedSeqs];
+  if (p.max_parts > 1 || S > kMaxDeviceRanked || p.max_len >= (1 << 22)) return y;
+  __shared__ uint32_t keys[kMaxDeviceRanked];
   __shared__ int pick;
   const int S16 = (S + 15) & ~15;  // zero keys pad to whole 16-key steps
   for (int u = threadIdx.x; u < S16; u += blockDim.x)
@@ -2058,8 +2059,8 @@ inline int rank_split_of(const DecodeParams& p, int row_wgs, int occ, const Laun
 inline void fill_order(DecodeParams& p, const LaunchCtx& c) {
   p.has_order = 0;
   const int S = p.num_seqs;
-  if (!c.host_lens || p.max_parts > 1 || S > kMaxRankedSeqs || p.max_len >= (1 << 22)) return;
-  int idx[kMaxRankedSeqs];
+  if (!c.host_lens || p.max_parts > 1 || S > kMaxOrder) return;
+  int idx[kMaxOrder];
   for (int i = 0; i < S; ++i) idx[i] = i;
   auto len = [&](int i) { return std::min(std::max(c.host_lens[i], 0), p.max_len); };
   std::stable_sort(idx, idx + S, [&](int a, int b) { return len(a) > len(b); });

@@ -250,3 +250,40 @@ def test_host_lens_random_steps(seed):
     assert_close(out.double().cpu().numpy()[seqs], ref[seqs], f"host_random{seed}")
     del dw
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S", [600, 1536, 1600])
+def test_host_order_large_batches(S):
+    """Batches past what a workgroup ranks itself (256 sequences): the host ranks
+    up to 1536 and passes the order in the kernel arguments; 1600 keeps index
+    order.  Outputs and pools bit-identical with and without the host copy (and
+    with a wrong one), every row against the oracle."""
+    torch = need_gpu()
+    from gpu_util import oracle_reference
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    rng = np.random.default_rng(8100 + S)
+    lens = rng.integers(16, 640, size=S, endpoint=True).tolist()
+    w = workloads.random_workload(8100 + S, lens, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16,
+                                  width=40, name=f"large_batch_{S}")
+    print(f"[large_batch_{S}] schedule {pa.schedule(S, 32, 8, 640)}", flush=True)
+    outs = {}
+    for label, hl in (("device", None), ("host", np.asarray(w.context_lens, dtype=np.int32)),
+                      ("wrong", _wrong_lens(w))):
+        dw = dev.upload(w)
+        out = torch.empty_like(dw.q)
+        pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
+                         dw.block_tables, dw.context_lens, w.scale, w.block_size, host_context_lens=hl)
+        assert pa.last_launch() == ["decode_multi<128,16,1,false>"], pa.last_launch()
+        torch.cuda.synchronize()
+        outs[label] = (dev.bf16_bits(out), dev.bf16_bits(dw.k_cache[dw.owned]), dev.bf16_bits(dw.v_cache[dw.owned]))
+        del dw
+    for label in ("host", "wrong"):
+        for a, b in zip(outs[label], outs["device"]):
+            assert np.array_equal(a, b), f"S={S}: {label}-ranked step differs from the device-ordered one"
+    kst, vst, ref = oracle_reference(w)
+    assert np.array_equal(outs["host"][1], kst.blocks) and np.array_equal(outs["host"][2], vst.blocks)
+    import oracle
+    a, r = assert_close(oracle.bf16_bits_to_f64(outs["host"][0]), ref, f"large_batch_{S}")
+    print(f"[large_batch_{S}] all rows: max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
