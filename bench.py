@@ -231,7 +231,7 @@ class Step:
     it: the step's copy-on-write copies (if any), then pa_append_decode with the
     caller's workspace and a host copy of the lengths."""
 
-    def __init__(self, w, cus, stream):
+    def __init__(self, w, cus, stream, partition_tokens=0):
         import numpy as np
         import torch
 
@@ -239,6 +239,7 @@ class Step:
         from paged_kv_cache_122_amd import device as dev
 
         self.pa, self.w, self.stream = pa, w, stream
+        self.partition_tokens = partition_tokens  # 0: the automatic schedule
         self.dw = dev.upload(w, "cuda:0")
         self.out = torch.empty_like(self.dw.q)
         self.has_copies = int(w.copies.shape[0]) > 0
@@ -248,7 +249,7 @@ class Step:
         fused, _, kind, _ = fused_step(w, self.part, cus)
         if fused:
             self.schedule = kind
-        nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, 0)
+        nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, partition_tokens)
         self.ws = pa.alloc_workspace(nb, "cuda:0") if nb else None
         self.host_lens = np.asarray(w.context_lens, dtype=np.int32)
         # the kernels the step launches, as the library reports them (one
@@ -277,7 +278,8 @@ class Step:
         self.copies()  # pa_last_launch then names the step's own call alone
         self.pa.append_decode(self.out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache,
                               dw.block_tables, dw.context_lens, w.scale, w.block_size, workspace=self.ws,
-                              kernel_events=kernel_events, host_context_lens=self.host_lens, stream=self.stream)
+                              kernel_events=kernel_events, host_context_lens=self.host_lens,
+                              partition_tokens=self.partition_tokens, stream=self.stream)
 
     def append(self):
         dw = self.dw
@@ -288,7 +290,8 @@ class Step:
         """The call pa_decode makes (same schedule), with the step's workspace."""
         dw, w = self.dw, self.w
         self.pa.decode_ex(self.out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale,
-                          w.block_size, workspace=self.ws, host_context_lens=self.host_lens, stream=self.stream)
+                          w.block_size, workspace=self.ws, host_context_lens=self.host_lens,
+                          partition_tokens=self.partition_tokens, stream=self.stream)
 
     def step_desc(self):
         return (("pa_copy_blocks (copy-on-write) + " if self.has_copies else "")

@@ -156,11 +156,16 @@ int pa_copy_blocks(pa_tensor* k_cache, pa_tensor* v_cache, const pa_tensor* bloc
  *                                   (batches of more than 8192 sequences:
  *                                   partitions of 512 tokens).
  * A second kernel combines the partial results of a split context in
- * ascending token order with a log-sum-exp reduce.  Under partitions, a
- * partition that consecutive sequences fill with the same physical blocks (a
- * shared prefix, "PagedAttention from First Principles", section 9) is read
- * once for up to 16/G of them: keep sequences that share a prefix adjacent.
- * The results do not depend on it.  The partial results live in a
+ * ascending token order with a log-sum-exp reduce.  Blocks that consecutive
+ * sequences hold in common (a shared prefix, "PagedAttention from First
+ * Principles", section 9) are read once for a run of up to 16/G of them, by
+ * the shared-partition kernel: under partitions with G <= 16, and on the
+ * automatic unsplit schedule with G <= 2, wherever the grid holds a
+ * workgroup per compute unit.  Within
+ * a partition a run reads the members' common leading blocks once, then each
+ * member's own; it grows member by member while the own 16-token tiles do
+ * not outnumber the common ones.  Keep sequences that share a prefix
+ * adjacent; the results do not depend on it.  The partial results live in a
  * library-owned workspace on the current device, grown with hipMalloc when a
  * call needs more (never during stream capture: that returns PA_ERR_WORKSPACE;
  * use pa_decode_ex there).  Calls that need the workspace may not overlap on
@@ -319,8 +324,9 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * kernel does both over partitions sized on those lengths (in the workspace),
  * and a second kernel combines each row's partitions; where those lengths
  * fit one partition each, the unsplit fused kernel runs.  Where the
- * schedule is partitioned on the MFMA path (grouping <= 16) and the grid
- * fills the GPU, the step takes two launches instead of three: the workgroup
+ * schedule is partitioned on the MFMA path (grouping <= 16), or unsplit with
+ * grouping <= 2, and the grid fills the GPU, the step takes two launches
+ * instead of three: the workgroup
  * of a sequence's last partition in the shared-partition kernel reads the
  * pool up to the new position and folds the new token in from k / v, and the
  * combine kernel that follows also stores the new tokens.  Otherwise the

@@ -196,6 +196,7 @@ int owned_workspace(size_t need, hipStream_t stream, void** out) {
 struct DecodePlan {
   int64_t S, Hq, Hkv, D, B, W, NB;
   int part_tokens, max_parts;
+  bool share_unsplit;   // automatic VALU path, unsplit: the shared-partition kernel where the grid fills the GPU
   bool stream;          // stream-K schedule (else partitioned)
   int workgroups_per_cu;
   pa::Path path;
@@ -363,6 +364,7 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
     pl->stream = true;
     pl->part_tokens = 0;
     pl->max_parts = 1;
+    pl->share_unsplit = false;
     pl->ws = pa::stream_workspace_layout(S, pairs, D);
     return PA_OK;
   }
@@ -381,6 +383,11 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
   // grouping up to 16: it reads a partition that consecutive sequences share
   // (a common prefix) once for all of them, which the VALU kernel cannot.
   if (want == 0 && max_parts > 1 && G <= 16) pl->path = pa::Path::Mfma;
+  // Unsplit with one or two q heads per KV head: where the grid fills the GPU
+  // the shared-partition kernel takes it (one partition spanning the table),
+  // so that prefix blocks neighbouring sequences share (parallel samples of
+  // a prompt) are read once; smaller grids keep the VALU kernel.
+  pl->share_unsplit = want == 0 && max_parts == 1 && G <= 2;
   pl->ws = pa::workspace_layout(S, Hq, D, max_parts);
   if (max_parts == 1) pl->ws.total = 0;
   return PA_OK;
@@ -470,6 +477,7 @@ int decode_common(pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cache,
   p.scale_log2 = float(double(scale) * 1.4426950408889634);
   p.part_tokens = pl.part_tokens;
   p.max_parts = pl.max_parts;
+  p.share_unsplit = pl.share_unsplit;
   int cus = 0;
   if ((rc = device_cus(&cus)) != PA_OK) return rc;
   const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr,
@@ -1241,7 +1249,7 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
         pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts).total <= workspace_bytes)
       return launch_fused_step(pl, &m, opts, workspace, stream);
   }
-  if (mfma && !pl.stream && pl.max_parts > 1) {
+  if (!pl.stream && ((mfma && pl.max_parts > 1) || pl.share_unsplit)) {
     // partitioned: where the schedule runs the shared-partition kernel, it
     // takes the append too (its last partitions read the new token from k / v)
     const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
@@ -1252,14 +1260,17 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
     m.d.head_groups = (m.d.group + 15) / 16;
     m.d.part_tokens = pl.part_tokens;
     m.d.max_parts = pl.max_parts;
+    m.d.share_unsplit = pl.share_unsplit;
     int cus = 0;
     if ((rc = device_cus(&cus)) != PA_OK) return rc;
     const pa::LaunchCtx ctx{stream, opts ? opts->kernel_start : nullptr, opts ? opts->kernel_stop : nullptr,
                             cus, host_lens};
     if (pa::shared_step_applies(m.d, pl.path, ctx)) {
-      const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts);
-      m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
-      m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+      if (m.d.max_parts > 1) {  // split: pieces in the workspace (unsplit rows are written directly)
+        const pa::WorkspaceLayout wl = pa::workspace_layout(pl.S, pl.Hq, pl.D, m.d.max_parts);
+        m.d.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.ml_off);
+        m.d.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.o_off);
+      }
       const hipError_t e = pa::launch_shared_step(m, int(pl.D), int(pl.B), ctx);
       if (e != hipSuccess) return hip_fail(e, "fused append + shared-partition decode launch");
       return PA_OK;

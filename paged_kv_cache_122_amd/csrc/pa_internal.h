@@ -63,6 +63,10 @@ struct DecodeParams {
   // has_order 2 (split multi-token grid): order[y] = sequence << 8 | partition,
   // the grid's rows listing only the partitions that hold tokens.
   int has_order;
+  // automatic path, one partition per sequence, 1-2 q heads per KV head: a
+  // grid that fills the GPU runs the shared-partition kernel (prefixes that
+  // neighbouring sequences share are read once) instead of the VALU kernel
+  int share_unsplit;
   uint16_t order[kMaxOrder];
 };
 

@@ -423,6 +423,78 @@ __device__ __forceinline__ void mfma_tile_sets(MfmaAcc<D> (&a)[NS], const u32x4 
   }
 }
 
+// mfma_probs with a per-column limit: token tok0 + 4*g4 + j counts for this
+// lane's column when it is at most climit (new tokens: the column's query
+// index; a run's tile: the tile's end for the columns it counts for, -1 for
+// the others).  Masked scores contribute exactly zero even before the column
+// has seen a token.
+template <int D>
+__device__ __forceinline__ u32x4 mfma_probs_limit(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
+                                                  int tok0, int climit, int lane, const u32x4 (&kt)[D / 32]) {
+  constexpr int NC = D / 32;
+  const int g4 = lane >> 4;
+  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < NC; c += 2) {
+    s0 = mfma_16x16x32(kt[c], q[c], s0);
+    s1 = mfma_16x16x32(kt[c + 1], q[c + 1], s1);
+  }
+  const f32x4 sacc = s0 + s1;
+  float sc[4];
+  bool vis[4];
+  float mt = kNegInf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vis[j] = tok0 + 4 * g4 + j <= climit;
+    sc[j] = vis[j] ? sacc[j] * scale_log2 : kNegInf;
+    mt = fmaxf(mt, sc[j]);
+  }
+  if (__any(mt > a.m + kRescaleSlack)) {
+    mt = fmaxf(mt, shfl_xor(mt, 16));
+    mt = fmaxf(mt, shfl_xor(mt, 32));
+    const float m_new = fmaxf(a.m, mt);
+    const float alpha = a.m == kNegInf ? 0.f : exp2_ftz(a.m - m_new);
+    a.l *= alpha;
+#pragma unroll
+    for (int i = 0; i < 2 * NC; ++i) a.o[i] *= alpha;
+    a.m = m_new;
+  }
+  float pr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    pr[j] = vis[j] ? exp2_ftz(sc[j] - a.m) : 0.f;
+    a.l += pr[j];
+  }
+  uint32_t hb[4], lb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hb[j] = bf16_bits(pr[j]);
+    lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
+  }
+  return u32x4{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)};
+}
+
+// o += P V for one tile, P as mfma_probs returns it (hi + lo bf16).
+template <int D>
+__device__ __forceinline__ void mfma_pv(MfmaAcc<D>& a, u32x4 pb, const u32x4 (&vt)[D / 32]) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};
+    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};
+    a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
+    a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
+  }
+}
+
+// mfma_tile with a per-column limit (mfma_probs_limit).  V past the tile's
+// tokens must be finite (zeros).
+template <int D>
+__device__ __forceinline__ void mfma_tile_causal(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
+                                                 int tok0, int climit, int lane, const u32x4 (&kt)[D / 32],
+                                                 const u32x4 (&vt)[D / 32]) {
+  mfma_pv<D>(a, mfma_probs_limit<D>(a, q, scale_log2, tok0, climit, lane, kt), vt);
+}
+
 // ---------------------------------------------------------------------------
 // per-tile math, MHA path (VALU)
 //
@@ -1223,37 +1295,129 @@ __device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_
 // ---------------------------------------------------------------------------
 // shared partitions (partitioned schedule, G <= 16)
 //
-// Sequences that share a prefix hold the same physical blocks for it.  When
-// consecutive sequences s, s+1, ... all fill partition j and their tables name
-// the same blocks there, the workgroup of the first computes partition j for
-// all of them: its MFMA columns are (member, query head) pairs, member i's
-// column i*G + g holding sequence s+i's query head kvh*G + g, so each shared
-// tile is read once.  The others skip partition j.  Runs are cut at aligned
-// windows of 16/G sequences (the columns of one workgroup), so the test only
-// looks inside the window: s-1 (is s a follower?) and s+1 ... (members).
-// Each member's partial result goes where its own workgroup would have put
-// it, and the combine kernel is unchanged.
+// Sequences that share a prefix hold the same physical blocks for it.  Inside
+// an aligned window of 16/G consecutive sequences (the columns of one
+// workgroup), a run of sequences whose tables for partition j begin with the
+// same blocks is computed by the workgroup of its first sequence, the leader:
+// its MFMA columns are (member, query head) pairs, member i's column i*G + g
+// holding sequence s+i's query head kvh*G + g.  The tiles the members have in
+// common are read once for all columns; then each member's own tiles of the
+// partition (a copy-on-write block and what the member wrote since, say) are
+// read once, counting for that member's columns only.  The other members'
+// workgroups skip partition j.  A run grows only while the members' own tiles
+// together stay within the common ones, so a leader reads at most twice a
+// partition's tiles.  Every workgroup of the window derives the same runs from
+// the same table entries and lengths.  Each member's partial result goes
+// where its own workgroup would have put it, and the combine kernel is
+// unchanged.
 //
 // Fused (a decode step, one new token per sequence, in mp's k_new / v_new /
-// slots): the last token of a sequence's last partition is that token.  The
-// workgroup of the partition walks the pool up to it and folds the new token
-// in from k_new / v_new when it joins the waves; combine_append stores it in
-// the pools afterwards (no workgroup of this kernel reads its slot), so the
-// step needs no append launch before the decode, and no attention workgroup
-// waits at its end for store acknowledgements while the reads saturate the
-// memory.  A partition that is the last of the leader or of a member holds a
-// new token that is not in the pools yet, so it is never shared: its
-// sequence computes it alone (after copy-on-write the new token's block is
-// the sequence's own anyway, and no other table names it).
+// slots): a sequence's last token, in its last partition, is the new one and
+// is not in the pools yet.  The walk reads a member's pool tokens up to it,
+// and the new token is folded in from k_new / v_new when the waves are
+// joined; combine_append stores it in the pools afterwards (no workgroup of
+// this kernel reads its slot), so the step needs no append launch before the
+// decode, and no attention workgroup waits at its end for store
+// acknowledgements while the reads saturate the memory.
 // ---------------------------------------------------------------------------
 constexpr int kMaxShare = 16;  // members per workgroup at G = 1
+
+// Walk a run's nv tiles, tiles wave, wave + 4, ... of it in this wave, with
+// the next S - 1 tiles' loads issued before the current one is computed (as
+// walk_tiles).  Tiles [0, n_sh) are the common tokens [t0, sh_end) of every
+// member, whose block-table entries come from the leader's row (`first`
+// holds the wave's first 64, fetched before the plan was known).  The rest are
+// the members' own tokens: member c's [t_sh, tw[c]) are tiles n_sh + off[c] ..
+// n_sh + off[c+1] - 1, read from its own row; a lane holding one of them
+// replaces its entries with the member's and keeps the tile's token range
+// (relative to t0, 16 bits each) and member.
+template <int D, int BS, int S, typename F>
+__device__ __forceinline__ void walk_run(const DecodeParams& p, __amdgpu_buffer_rsrc_t row, TableCache first,
+                                         int s, int kvh, int t0, int sh_end, int n_sh, int t_sh, const int* tw,
+                                         const int* off, int nv, int wave, int lane, F&& compute) {
+  constexpr int NC = D / 32;
+  const int n = nv > wave ? (nv - wave + kWaves - 1) / kWaves : 0;
+  const LaneOffsets<D, BS> lo = lane_offsets<D, BS>(lane);
+  constexpr int kChunk = 64 / S * S;
+  for (int k0 = 0; k0 < n; k0 += kChunk) {
+    TableCache tc = k0 == 0 ? first : fetch_table<BS>(row, t0 >> 4, wave, k0, lane);
+    int range = 0, member = -2;
+    {
+      const int v = wave + kWaves * (k0 + lane);
+      if (v >= n_sh && v < nv) {
+        const int w = v - n_sh;
+        int c = 0;
+        while (off[c + 1] <= w) ++c;
+        const int ts = t_sh + 16 * (w - off[c]);
+        const int te = tw[c];
+        // entries read lie before the member's context end: inside its table row
+        const int32_t* own = p.block_tables + size_t(s + c) * p.bt_s;
+        if constexpr (BS == 16) {
+          tc.e0 = own[ts >> 4];
+        } else if constexpr (BS == 32) {
+          tc.e0 = own[ts >> 5];
+        } else {
+          tc.e0 = own[ts >> 3];
+          tc.e1 = ts + 8 < te ? own[(ts >> 3) + 1] : tc.e0;
+        }
+        range = ((te - t0) << 16) | (ts - t0);
+        member = c;
+      }
+    }
+    const int m = min(kChunk, n - k0);
+    // tile j of the chunk (uniform): blocks, first token, mask end, member;
+    // selects rather than branches, so the tile loop stays one block
+    auto meta = [&](int j, int& b0, int& b1, int& ts, int& te, int& mem) {
+      const int v = wave + kWaves * (k0 + j);
+      const bool common = v < n_sh;
+      const int rg = __builtin_amdgcn_readlane(range, j);
+      ts = common ? t0 + 16 * v : t0 + (rg & 0xffff);
+      te = common ? sh_end : t0 + (rg >> 16);
+      mem = common ? -1 : __builtin_amdgcn_readlane(member, j);
+      b0 = __builtin_amdgcn_readlane(tc.e0, j);
+      b1 = 0;
+      if constexpr (BS == 8) {
+        const int e1 = __builtin_amdgcn_readlane(tc.e1, j);
+        b1 = common && ts + 8 >= te ? b0 : e1;
+      }
+    };
+    auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+      int b0, b1, ts, te, mem;
+      meta(min(j, m - 1), b0, b1, ts, te, mem);
+      load_tile<D, BS>(p, kvh, b0, b1, ts, te, j < m, lo, kt, vt);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto tile = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+      int b0, b1, ts, te, mem;
+      meta(min(j, m - 1), b0, b1, ts, te, mem);
+      compute(ts, te, j < m ? mem : -2, kt, vt);  // padding counts for no column
+    };
+    // whole rounds of S tiles; the padding tiles (past the run) load zeros
+    // without touching memory
+    const int rounds = (m + S - 1) / S;
+    u32x4 kk[S][NC], vv[S][NC];
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) load(i, kk[i], vv[i]);
+    for (int j = 0; j < rounds * S; j += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        load(j + i + S - 1, kk[(i + S - 1) % S], vv[(i + S - 1) % S]);
+        tile(j + i, kk[i], vv[i]);
+      }
+    }
+  }
+}
 
 template <int D, int BS, bool Fused>
 __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
-  __shared__ int differs[kMaxShare + 1];  // window members from s-1: 1 = not sharing s's partition
-  __shared__ float x_new[16];             // fused: the new token's scores (log2 units), by column
+  __shared__ int win_len[kMaxShare];      // window member i: clamped context length
+  __shared__ int win_fd[kMaxShare];       // member i >= 1: first partition entry differing from member i-1's
+  __shared__ int win_tw[kMaxShare];       // window member i: end of its pool tokens read in this partition
+  __shared__ int run_off[kMaxShare + 1];  // leader: first own tile of each member, after the common ones
+  __shared__ int run_plan[2];             // this workgroup's members (0: follower) and common end
+  __shared__ float x_new[16];             // fused: the new tokens' scores (log2 units), by column
   const DecodeParams& p = mp.d;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -1265,41 +1429,154 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   const int G = p.group;
   const int M = 16 / G;  // members one workgroup carries
   const int t0 = part * p.part_tokens;
+  const int t_end = t0 + p.part_tokens;
+  const int w0 = s - s % M;
+  const int si = s - w0;
+  const int hi = min(M, p.num_seqs - w0);  // window members present
+  const int E0 = t0 / BS;                  // first table entry of the partition (inside the rows)
+
+  // Every load that needs no length first, issued together: this wave's first
+  // table entries, and (lanes 0, 1, 2: s-1, s, s+1, or s where there is no
+  // such neighbour in the window) the lengths and the partition's first
+  // entries of s and its neighbours.  The entry index is kept inside the row;
+  // where the partition lies past the table no context reaches it.
   const auto row = table_row(p, s, BS);
   const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
+  const bool has_prev = M > 1 && si > 0, has_next = M > 1 && si + 1 < hi;
+  const int nb = lane == 0 && has_prev ? s - 1 : (lane == 2 && has_next ? s + 1 : s);
+  const int nb_len = p.context_lens[nb];
+  const int nb_ent = p.block_tables[size_t(nb) * p.bt_s + min(E0, p.max_len / BS - 1)];
+  const int len_prev = __builtin_amdgcn_readlane(nb_len, 0);
+  const int len_next = __builtin_amdgcn_readlane(nb_len, 2);
+  const int e_prev = __builtin_amdgcn_readlane(nb_ent, 0);
+  const int e_self = __builtin_amdgcn_readlane(nb_ent, 1);
+  const int e_next = __builtin_amdgcn_readlane(nb_ent, 2);
 
-  const int L = clamp_len(p, p.context_lens[s]);
+  const int L = clamp_len(p, __builtin_amdgcn_readlane(nb_len, 1));
   const int nparts = partitions(p, L);
   if (part >= (nparts > 0 ? nparts : 1)) return;
-  const int t1 = min(L, t0 + p.part_tokens);
-  const bool own_new = Fused && L > 0 && part == nparts - 1;  // workgroup-uniform
-  const int t_walk = own_new ? t1 - 1 : t1;                   // the pool's tokens read here
+  // the new token of a sequence whose last partition this is (fused step)
+  auto owns_new = [&](int len) { return Fused && len > t0 && len <= t_end; };
+  // end of the pool tokens this partition holds for a sequence of `len` tokens
+  auto pool_end = [&](int len) { return min(len, t_end) - (owns_new(len) ? 1 : 0); };
 
-  // Only a filled partition is shared; in a decode step also only one that
-  // holds none of its sequences' new tokens (a sequence's last token lies in
-  // its last partition): those are not in the pools yet when this kernel
-  // reads them.
-  const int share_len = t0 + p.part_tokens + (Fused ? 1 : 0);
-  int m = 1;  // members (sequences s .. s+m-1)
-  if (M > 1 && L >= share_len) {  // workgroup-uniform
-    const int w0 = s - s % M;
-    const int lo = max(s - 1, w0);
-    const int hi = min(w0 + M, p.num_seqs);
-    const int E = p.part_tokens / BS;  // table entries of the partition
-    for (int c = lo + int(threadIdx.x); c < hi; c += kThreads)
-      differs[c - lo] = clamp_len(p, p.context_lens[c]) < share_len;
-    __syncthreads();
-    const int32_t* mine = p.block_tables + size_t(s) * p.bt_s + t0 / BS;
-    for (int idx = threadIdx.x; idx < (hi - lo) * E; idx += kThreads) {
-      const int c = lo + idx / E;
-      const int e = idx - (c - lo) * E;
-      if (c != s && p.block_tables[size_t(c) * p.bt_s + t0 / BS + e] != mine[e]) differs[c - lo] = 1;
+  // The run this workgroup belongs to (workgroup-uniform).  A run needs a
+  // neighbour whose partition starts on the same block; without one (most
+  // partitions past a shared prefix) nothing more is read.
+  bool alone = M == 1 || L <= t0 || p.part_tokens > 32768 ||
+               !((has_prev && clamp_len(p, len_prev) > t0 && e_prev == e_self) ||
+                 (has_next && clamp_len(p, len_next) > t0 && e_next == e_self));
+  int m = 1, t_sh = 0;
+  if (!alone) {
+    // The window's lengths, and for each member the first entry of the
+    // partition where its table departs from its predecessor's: wave w takes
+    // members 1 + w, 5 + w, ..., one 64-entry chunk per lane step, and the
+    // lowest set bit of a ballot over the lanes' comparisons is the departure
+    // (entry indices kept inside the rows; past the used entries the values
+    // do not matter, as below).
+    const int E = p.part_tokens / BS;
+    const int last = p.max_len / BS - 1;
+    if (threadIdx.x < hi) win_len[threadIdx.x] = clamp_len(p, p.context_lens[w0 + threadIdx.x]);
+    constexpr int kRows = kMaxShare / kWaves;  // members a wave compares
+    int ea[kRows], eb[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {  // the first 64 entries of every row at once
+      const int i = min(1 + wave + kWaves * r, hi - 1);
+      const int idx = min(E0 + lane, last);
+      ea[r] = p.block_tables[size_t(w0 + i) * p.bt_s + idx];
+      eb[r] = p.block_tables[size_t(w0 + i - 1) * p.bt_s + idx];
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      const int i = 1 + wave + kWaves * r;
+      if (i >= hi) break;  // wave-uniform
+      uint64_t diff = __ballot(lane < E && ea[r] != eb[r]);
+      int fd = diff ? __builtin_ctzll(diff) : E;
+      for (int c0 = 64; c0 < E && !diff; c0 += 64) {  // longer partitions: further chunks
+        const int e = c0 + lane;
+        const int idx = min(E0 + e, last);
+        diff = __ballot(e < E && p.block_tables[size_t(w0 + i) * p.bt_s + idx] !=
+                                     p.block_tables[size_t(w0 + i - 1) * p.bt_s + idx]);
+        if (diff) fd = c0 + __builtin_ctzll(diff);
+      }
+      if (lane == 0) win_fd[i] = fd;
     }
     __syncthreads();
-    if (lo < s && differs[0] == 0) return;  // s-1 computes this partition for s
-    for (int c = s + 1; c < hi && differs[c - lo] == 0; ++c) ++m;
+    // pool tokens of each member, and its departure point over the entries
+    // both it and its predecessor use
+    auto used = [&](int len) { return len > t0 ? (min(len, t_end) - t0 + BS - 1) / BS : 0; };
+    const int my_len = lane < hi ? win_len[lane] : 0;
+    const int prev_len = lane > 0 && lane < hi ? win_len[lane - 1] : 0;
+    const int my_tw = pool_end(my_len);
+    const int my_fd = lane > 0 && lane < hi ? min(win_fd[lane], min(used(my_len), used(prev_len))) : 0;
+    if (threadIdx.x < hi) win_tw[threadIdx.x] = my_tw;
+    // Runs from the start of the window, each grown member by member while
+    // the members' own tiles stay within the common ones (own: the run's own
+    // tiles for the current common end, recounted only when that end moves).
+    // Wave 0 finds them (lane i holds member i) and every workgroup of the
+    // window finds the same; the others read this workgroup's part from LDS.
+    if (wave == 0) {
+      int lead = 0, mine_m = 0, mine_tsh = 0;
+      while (true) {
+        int k = E, mtw = __builtin_amdgcn_readlane(my_tw, lead), n = 1, tsh = t0, own = 0;
+        for (int j = lead + 1; j < hi; ++j) {
+          const int tw_j = __builtin_amdgcn_readlane(my_tw, j);
+          const int fd_j = __builtin_amdgcn_readlane(my_fd, j);
+          if (tw_j <= t0 || fd_j == 0) break;
+          const int k2 = min(k, fd_j);
+          const int mtw2 = min(mtw, tw_j);
+          const int tsh2 = t0 + (max(0, min(k2 * BS, mtw2 - t0)) & ~15);
+          const int common = (tsh2 - t0) >> 4;
+          if (common == 0) break;
+          int own2 = own + ((tw_j - tsh2 + 15) >> 4);
+          if (n == 1 || tsh2 != tsh) {  // the common end moved: recount the run
+            own2 = 0;
+            for (int c = lead; c <= j; ++c) own2 += (__builtin_amdgcn_readlane(my_tw, c) - tsh2 + 15) >> 4;
+          }
+          if (own2 > common) break;
+          k = k2;
+          mtw = mtw2;
+          tsh = tsh2;
+          own = own2;
+          n = j - lead + 1;
+        }
+        if (si < lead + n) {
+          mine_m = si == lead ? n : 0;  // 0: a follower
+          mine_tsh = tsh;
+          break;
+        }
+        lead += n;
+      }
+      if (lane == 0) {
+        run_plan[0] = mine_m;
+        run_plan[1] = mine_tsh;
+      }
+    }
+    __syncthreads();
+    m = __builtin_amdgcn_readfirstlane(run_plan[0]);
+    if (m == 0) return;  // the leader computes this partition for s
+    t_sh = __builtin_amdgcn_readfirstlane(run_plan[1]);
   }
   const int ncols = m * G;
+  // member c's context length (this workgroup's own without a window plan)
+  auto member_len = [&](int c) { return m == 1 ? L : win_len[si + c]; };
+
+  // the walk: tokens [t0, sh_end) for every member, then each member's own
+  const int sh_end = m > 1 ? t_sh : pool_end(L);
+  const int n_sh = sh_end > t0 ? (sh_end - t0 + 15) >> 4 : 0;
+  const int* tw = win_tw + si;
+  if (m > 1) {
+    if (threadIdx.x == 0) {
+      int total = 0;
+      for (int c = 0; c < m; ++c) {
+        run_off[c] = total;
+        total += (tw[c] - t_sh + 15) >> 4;
+      }
+      run_off[m] = total;
+    }
+    __syncthreads();
+  }
+  const int nv = __builtin_amdgcn_readfirstlane(n_sh + (m > 1 ? run_off[m] : 0));
 
   // column r: member r / G, head r % G
   const int ci = r / G;
@@ -1312,20 +1589,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   }
   MfmaAcc<D> acc;
   mfma_reset(acc);
-  walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t_walk, wave, lane,
-                                [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-    mfma_tile<D>(acc, q, p.scale_log2, ts, t_walk, lane, kt, vt);
+  walk_run<D, BS, kPipeSlots>(p, row, first, s, kvh, t0, sh_end, n_sh, t_sh, tw, run_off, nv, wave, lane,
+                              [&](int ts, int te, int mem, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    // the tile counts for every column (mem -1), one member's columns, or none
+    const int climit = (mem == -1 || mem == ci) ? te - 1 : -1;
+    const u32x4 pb = mfma_probs_limit<D>(acc, q, p.scale_log2, ts, climit, lane, kt);
+    if (ts + kTileTokens > te) mask_v<D>(vt, ts, te, lane);  // after QK^T: V arrives after K
+    mfma_pv<D>(acc, pb, vt);
   });
 
-  if (Fused && own_new) {
-    // the new token's score for s's columns (heads kvh * G + c, c < G):
-    // 16 threads per column, 8 dims each
+  if (Fused) {
+    // the new tokens' scores for the columns of members whose last partition
+    // this is: 16 threads per column, 8 dims each
     const int c = threadIdx.x >> 4;
     const int j = threadIdx.x & 15;
+    const int cm = c / G;
+    const bool own = c < ncols && owns_new(member_len(cm));
     float dot = 0.f;
-    if (c < G && 8 * j < D) {
-      const u32x4 qv = load16(p.q + size_t(s) * p.q_s + size_t(kvh * G + c) * p.q_h + 8 * j);
-      const u32x4 kv = load16(mp.k_new + size_t(s) * mp.kn_t + size_t(kvh) * mp.kn_h + 8 * j);
+    if (own && 8 * j < D) {
+      const u32x4 qv = load16(p.q + size_t(s + cm) * p.q_s + size_t(kvh * G + c - cm * G) * p.q_h + 8 * j);
+      const u32x4 kv = load16(mp.k_new + size_t(s + cm) * mp.kn_t + size_t(kvh) * mp.kn_h + 8 * j);
       const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1337,7 +1620,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
     dot += shfl_xor(dot, 2);
     dot += shfl_xor(dot, 4);
     dot += shfl_xor(dot, 8);
-    if (j == 0 && c < G) x_new[c] = dot * p.scale_log2;
+    if (j == 0) x_new[c] = own ? dot * p.scale_log2 : kNegInf;
   }
 
   // combine the waves; column c goes to sequence s + c / G, head kvh * G + c % G
@@ -1370,17 +1653,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
         lsum += sm.l[w][col] * e;
       }
     }
-    if (Fused && own_new && col < G) {  // fold in the new token: score x_new[col], value v_new[s, kvh, d]
+    const int sc = s + col / G;
+    if (Fused && x_new[col] != kNegInf) {  // fold in the new token: score x_new[col], value v_new[sc, kvh, d]
       const float x = x_new[col];
       const float M2 = fmaxf(M_, x);
       const float a = exp2f(M_ - M2);  // 0 where no pool token was read (M_ = -inf)
       const float b = exp2f(x - M2);
-      const float v = bf16_value(mp.v_new[size_t(s) * mp.vn_t + size_t(kvh) * mp.vn_h + d]);
+      const float v = bf16_value(mp.v_new[size_t(sc) * mp.vn_t + size_t(kvh) * mp.vn_h + d]);
       o = o * a + b * v;
       lsum = lsum * a + b;
       M_ = M2;
     }
-    const int sc = s + col / G;
     const int h = kvh * G + col % G;
     if (partitions(p, p.context_lens[sc]) <= 1) {
       store_out(p, sc, h, d, lsum > 0.f ? o / lsum : 0.f);
@@ -1613,65 +1896,6 @@ __device__ __forceinline__ void load_new_tile(const MultiParams& p, int r0, int 
     vt[c].w = (w[2] >> 16) | (w[3] & 0xffff0000u);
   }
 }
-
-// mfma_tile for new tokens: token 16u + 4*g4 + j is visible to this lane's
-// column when it is at most climit (the column's query index).  Masked
-// scores contribute exactly zero even before the column has seen a token.
-template <int D>
-__device__ __forceinline__ void mfma_tile_causal(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
-                                                 int tok0, int climit, int lane, const u32x4 (&kt)[D / 32],
-                                                 const u32x4 (&vt)[D / 32]) {
-  constexpr int NC = D / 32;
-  const int g4 = lane >> 4;
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int c = 0; c < NC; c += 2) {
-    s0 = mfma_16x16x32(kt[c], q[c], s0);
-    s1 = mfma_16x16x32(kt[c + 1], q[c + 1], s1);
-  }
-  const f32x4 sacc = s0 + s1;
-  float sc[4];
-  bool vis[4];
-  float mt = kNegInf;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    vis[j] = tok0 + 4 * g4 + j <= climit;
-    sc[j] = vis[j] ? sacc[j] * scale_log2 : kNegInf;
-    mt = fmaxf(mt, sc[j]);
-  }
-  if (__any(mt > a.m + kRescaleSlack)) {
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(a.m, mt);
-    const float alpha = a.m == kNegInf ? 0.f : exp2_ftz(a.m - m_new);
-    a.l *= alpha;
-#pragma unroll
-    for (int i = 0; i < 2 * NC; ++i) a.o[i] *= alpha;
-    a.m = m_new;
-  }
-  float pr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    pr[j] = vis[j] ? exp2_ftz(sc[j] - a.m) : 0.f;
-    a.l += pr[j];
-  }
-  uint32_t hb[4], lb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    hb[j] = bf16_bits(pr[j]);
-    lb[j] = bf16_bits(pr[j] - bf16_value(hb[j]));
-  }
-  const u32x4 pb = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), lb[0] | (lb[1] << 16),
-                    lb[2] | (lb[3] << 16)};
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};
-    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};
-    a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
-    a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
-  }
-}
-
 
 // A workgroup computes NS sets of 16 columns against each tile it loads, so
 // a (sequence, KV head) with up to 16 * NS columns reads its context once.
@@ -2080,6 +2304,14 @@ inline bool deep_pipeline(const DecodeParams& p, const LaunchCtx& c) {
   return int64_t(p.num_kv_heads) * p.head_groups * p.num_seqs * p.max_parts < c.cus;
 }
 
+// The shared-partition kernel takes a partitioned schedule of at most 16 q
+// heads per KV head whose grid fills the GPU: split on the MFMA path, or
+// unsplit where the automatic path would take the VALU kernel.
+inline bool shared_applies(const DecodeParams& p, Path path, const LaunchCtx& c) {
+  return p.group <= 16 && ((path == Path::Mfma && p.max_parts > 1) || (p.share_unsplit && p.max_parts == 1)) &&
+         int64_t(p.num_kv_heads) * p.num_seqs * p.max_parts >= c.cus;
+}
+
 template <int D, int BS>
 hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx& c) {
   static_assert(kDeepSlots > kPipeSlots, "");
@@ -2087,7 +2319,7 @@ hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx&
   if (path == Path::Mfma && deep_pipeline(p, c))
     e = launch_rows(kname("decode_mfma<%d,%d,%d>", D, BS, kDeepSlots), decode_mfma<D, BS, kDeepSlots>, p,
                     p.num_kv_heads * p.head_groups, c);
-  else if (path == Path::Mfma && p.max_parts > 1 && p.group <= 16)
+  else if (shared_applies(p, path, c))
     e = launch_main(kname("decode_shared<%d,%d,false>", D, BS), decode_shared<D, BS, false>,
                     dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c,
                     MultiParams{p});  // split: shared partitions read once (no ranking)
@@ -2181,12 +2413,10 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
   return hipErrorInvalidValue;
 }
 
-bool shared_step_applies(const DecodeParams& p, Path path, const LaunchCtx& c) {
-  return path == Path::Mfma && p.max_parts > 1 && p.group <= 16 && !deep_pipeline(p, c);
-}
+bool shared_step_applies(const DecodeParams& p, Path path, const LaunchCtx& c) { return shared_applies(p, path, c); }
 
 hipError_t launch_shared_step(const MultiParams& m, int head_dim, int block_size, const LaunchCtx& c) {
-  if (!shared_step_applies(m.d, Path::Mfma, c)) return hipErrorInvalidValue;
+  if (!shared_applies(m.d, m.d.share_unsplit ? Path::Valu : Path::Mfma, c)) return hipErrorInvalidValue;
   switch (head_dim * 100 + block_size) {
     case 6408: return launch_shared_step_d<64, 8>(m, c);
     case 6416: return launch_shared_step_d<64, 16>(m, c);

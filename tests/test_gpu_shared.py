@@ -25,7 +25,10 @@ pytestmark = pytest.mark.gpu
 
 def shared_workload(name, seed, groups, prompt, tail_max, *, hq, hkv, d, b, interleave=False):
     """Groups of forked sequences: each group shares one prompt of `prompt`
-    tokens, each member then holds U[0, tail_max] tokens of its own."""
+    tokens, each member then holds U[0, tail_max] tokens of its own (at least
+    one), the last of them this step's.  Copy-on-write from the earlier steps
+    is done (the private blocks hold their tokens); a member whose first own
+    token is this step's copies the shared block in this step."""
     rng = np.random.Generator(np.random.PCG64(seed))
     S = sum(groups)
     tails = rng.integers(0, tail_max, size=S, endpoint=True).tolist()
@@ -40,9 +43,12 @@ def shared_workload(name, seed, groups, prompt, tail_max, *, hq, hkv, d, b, inte
         children = [fork(pool, parent) for _ in range(size)]
         free(pool, parent)
         for child in children:
-            reserve_slots(pool, child, max(1, tails[k]))
+            reserve_slots(pool, child, max(1, tails[k]) - 1)  # earlier steps
             members.append(child)
             k += 1
+    pool.pending_copies.clear()  # copied when those steps wrote
+    for child in members:
+        reserve_slots(pool, child, 1)  # this step's token
     if interleave:  # round robin over the groups: no two neighbours share
         starts = np.cumsum([0] + list(groups))
         order = [starts[g] + i for i in range(max(groups)) for g in range(len(groups)) if i < groups[g]]
@@ -104,7 +110,8 @@ def run_step(w, part, fused):
         pa.cache_append(dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache)
         pa.decode_ex(out, dw.q, dw.k_cache, dw.v_cache, dw.block_tables, dw.context_lens, w.scale, w.block_size,
                      partition_tokens=part, workspace=ws)
-        want = [f"decode_shared<{d},{b},false>", f"combine_parts<{d}>"]
+        split = -(-(w.table_width * w.block_size) // part) > 1
+        want = [f"decode_shared<{d},{b},false>"] + ([f"combine_parts<{d}>"] if split else [])
     assert pa.last_launch() == want, f"route {pa.last_launch()}, expected {want}"
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), dw
@@ -120,7 +127,7 @@ def check_pools(w, dw, kst, vst):
 CASES = [
     ("mha_windows", 3001, [8, 3, 1, 20], 1024, 300, 4, 4, 128, 16, 512, False),
     ("mha_p1024", 3002, [8, 8, 5], 1024, 700, 2, 2, 128, 16, 1024, False),
-    ("gqa4_d64_b32_cow", 3003, [5, 2, 9], 700, 200, 16, 4, 64, 32, 256, False),
+    ("gqa4_d64_b32_cow", 3003, [5, 2, 9], 700, 2, 16, 4, 64, 32, 256, False),
     ("gqa8_b8", 3004, [3, 4, 2], 512, 100, 16, 2, 128, 8, 256, False),
     ("gqa2_short_members", 3005, [6, 6], 600, 500, 4, 2, 128, 16, 512, False),
     ("mha_interleaved", 3006, [4, 4, 4], 512, 100, 2, 2, 64, 16, 256, True),
@@ -188,3 +195,73 @@ def test_append_decode_refuses_reads_of_another_sequences_new_slot():
     assert e.value.code == pa.PA_ERR_CONTRACT and "new token of sequence 0" in str(e.value)
     torch.cuda.synchronize()
     assert np.array_equal(dev.bf16_bits(dw.k_cache), before), "a refused call wrote the pool"
+
+
+def planned_runs(w, part, fused):
+    """Host model of the shared-partition kernel's run rule (coverage check for
+    the tests below, not a parity reference): per partition, the runs of each
+    window of 16/G sequences, as (leader, members, common end)."""
+    B, S, G = w.block_size, w.num_seqs, w.num_q_heads // w.num_kv_heads
+    M, W = 16 // G, w.table_width
+    lens = np.minimum(np.maximum(w.context_lens, 0), W * B)
+    runs = []
+    for j in range(-(-(W * B) // part)):
+        t0, t_end, E0, E = j * part, (j + 1) * part, j * part // B, part // B
+
+        def pool_end(L):
+            return min(L, t_end) - (1 if fused and t0 < L <= t_end else 0)
+
+        def used(L):
+            return (min(L, t_end) - t0 + B - 1) // B if L > t0 else 0
+
+        for w0 in range(0, S, M):
+            hi = min(M, S - w0)
+            tw = [pool_end(int(lens[w0 + i])) for i in range(hi)]
+            fd = [0] * hi
+            for i in range(1, hi):
+                row = lambda r, e: w.block_tables[r, E0 + e] if E0 + e < W else 0  # noqa: E731
+                f = next((e for e in range(E) if row(w0 + i, e) != row(w0 + i - 1, e)), E)
+                fd[i] = min(f, used(int(lens[w0 + i])), used(int(lens[w0 + i - 1])))
+            lead = 0
+            while lead < hi:
+                k, mtw, n, tsh = E, tw[lead], 1, t0
+                for c in range(lead + 1, hi):
+                    if tw[c] <= t0 or fd[c] == 0:
+                        break
+                    k2, mtw2 = min(k, fd[c]), min(mtw, tw[c])
+                    tsh2 = t0 + (max(0, min(k2 * B, mtw2 - t0)) & ~15)
+                    common = (tsh2 - t0) >> 4
+                    if common == 0 or sum((tw[x] - tsh2 + 15) >> 4 for x in range(lead, c + 1)) > common:
+                        break
+                    k, mtw, tsh, n = k2, mtw2, tsh2, c - lead + 1
+                if lens[w0 + lead] > t0:
+                    runs.append((w0 + lead, n, tsh, [tw[x] for x in range(lead, lead + n)]))
+                lead += n
+    return runs
+
+
+# Partial sharing: prompts that end inside a partition (a copy-on-write tail
+# block) and short tails, so that runs read the common tiles once and then
+# each member's own tiles.  (name, seed, groups, prompt, tail_max, Hq, Hkv, D, B, partition)
+PARTIAL = [
+    ("fork_mha_p512", 3101, [8, 8, 8, 8], 1000, 20, 4, 4, 128, 16, 512),
+    ("fork_gqa2_p1024_b8", 3102, [4, 6, 5], 1990, 40, 8, 4, 128, 8, 1024),
+    ("fork_gqa4_d64_b32", 3103, [3, 4, 4], 490, 25, 16, 4, 64, 32, 512),
+    ("fork_unsplit_mha", 3104, [8, 8], 1000, 1, 4, 4, 128, 16, 1024),
+]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "append_decode"])
+@pytest.mark.parametrize("case", PARTIAL, ids=[c[0] for c in PARTIAL])
+def test_partial_sharing(case, fused):
+    name, seed, groups, prompt, tail_max, hq, hkv, d, b, part = case
+    w = grown_workload(name, seed, groups, prompt, tail_max, part, hq=hq, hkv=hkv, d=d, b=b)
+    runs = planned_runs(w, part, fused)
+    own = [r for r in runs if r[1] > 1 and any(t > r[2] for t in r[3])]
+    print(f"[{name} fused={fused}] S={w.num_seqs} runs {len(runs)}, with own tiles {len(own)}", flush=True)
+    assert own, "the batch has no run whose members read tiles of their own"
+    kst, vst, ref = reference(w)
+    got, dw = run_step(w, part, fused)
+    check_pools(w, dw, kst, vst)
+    a, r = assert_close(got, ref, name)
+    print(f"[{name}] max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
