@@ -174,56 +174,28 @@ def stats_us(ms):
             "p50": round(percentile(ms, 50) * 1e3, 2), "p90": round(percentile(ms, 90) * 1e3, 2)}
 
 
-def decode_kernels(w, part, cus):
-    """Kernels one automatic pa_decode call launches on this workload."""
-    g = w.num_q_heads // w.num_kv_heads
-    core = f"decode_{'mfma' if g >= 3 else 'valu'}"
-    tmpl = f"<{w.head_dim},{w.block_size}>" if g >= 3 else f"<{w.head_dim},{w.block_size},{g}>"
-    if part == -2:
-        return [core + "_sk" + tmpl, f"combine_sk<{w.head_dim}>"], "stream-K"
-    max_len = w.block_tables.shape[1] * w.block_size
-    parts = 1 if part == -1 else -(-max_len // part)
-    if g >= 3:  # pipeline slots: two once the grid has a workgroup per compute unit
-        wgs = w.num_seqs * w.num_kv_heads * -(-g // 16) * parts
-        tmpl = f"<{w.head_dim},{w.block_size},{2 if wgs >= cus else 4}>"
-    if parts == 1:
-        return [core + tmpl], "one workgroup per (sequence, head group), no split"
-    wgs = w.num_seqs * w.num_kv_heads * -(-g // 16) * parts
-    if g <= 16 and wgs >= cus:  # split schedules read shared partitions once
-        return ([f"decode_shared<{w.head_dim},{w.block_size},false>", f"combine_parts<{w.head_dim}>"],
-                f"partitions of {part} tokens, shared partitions read once")
-    return [core + tmpl, f"combine_parts<{w.head_dim}>"], f"partitions of {part} tokens"
-
-
-def fused_step(w, part, cus):
-    """How pa_append_decode (given the host copy of the lengths) runs this
-    workload: (append fused into the decode, its kernels, what the schedule
-    is, whether the main kernel writes the new tokens).  The unsplit MFMA
-    schedule is one launch; a stream-K batch on the MFMA path runs the
-    multi-token kernel over partitions sized on the lengths (so that about 512
-    workgroups share the tokens), then the row combine; a partitioned batch
-    whose grid fills the GPU runs the shared-partition kernel, which takes the
-    new token from k / v, and a combine that stores it; anything else appends
-    first and decodes as pa_decode_ex does."""
-    g = w.num_q_heads // w.num_kv_heads
-    sets = 2 if g > 16 else 1
-    span = w.block_tables.shape[1] * w.block_size
-    unsplit = part == -1 or part >= span
-    if g >= 3 and unsplit:
-        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},false>"], \
-            "one launch: the new token stored and attended", True
-    if g >= 3 and part == -2:
-        row_wgs = w.num_kv_heads * -(-g // (16 * sets))
-        tokens = int(sum(min(max(int(x), 0), span) for x in w.context_lens))
-        p = max(512, -(-(-(-tokens * row_wgs // 512)) // 256) * 256)
-        return True, [f"decode_multi<{w.head_dim},{w.block_size},{sets},true>", f"combine_rows<{w.head_dim}>"], \
-            f"partitions of {p} tokens sized on the host's lengths, only those holding tokens launched, " \
-            "the new token stored by the last one; then the row combine", True
-    if part > 0 and not unsplit and g <= 16 and w.num_seqs * w.num_kv_heads * -(-span // part) >= cus:
-        return True, [f"decode_shared<{w.head_dim},{w.block_size},true>", f"combine_append<{w.head_dim},{w.block_size}>"], \
-            f"partitions of {part} tokens, shared partitions read once, the new token taken from k / v by its " \
-            "last partition; then the combine, which stores the new tokens", False
-    return False, [], "append kernel, then the decode schedule", False
+def describe_launch(kernels, part):
+    """What a step's launches do, read from the kernel names the library
+    reports (pa_last_launch) and the automatic partition choice."""
+    main = next((k for k in kernels if not k.startswith(("copy_kernel", "append_kernel"))), "")
+    split = "stream-K" if part == -2 else (f"partitions of {part} tokens" if part > 0 else "no split")
+    if main.startswith("decode_multi") and main.endswith(",false>"):
+        text = "one launch: the new token stored and attended, one workgroup per (sequence, head group)"
+    elif main.startswith("decode_multi"):
+        text = ("partitions sized on the host's lengths, only those holding tokens launched, the new token "
+                "stored by the last one; then the row combine")
+    elif main.startswith("decode_shared") and main.endswith(",true>"):
+        text = (f"{split}; runs of consecutive sequences read their common blocks once, the new token taken "
+                "from k / v by its last partition; then the combine, which stores the new tokens")
+    elif main.startswith("decode_shared"):
+        text = f"{split}; runs of consecutive sequences read their common blocks once"
+    elif "_sk" in main:
+        text = "stream-K: equal token ranges per wave of a persistent grid, then the piece combine"
+    else:
+        text = split + ("" if len(kernels) < 2 or not kernels[-1].startswith("combine") else "; then the combine")
+    if kernels and kernels[0].startswith("append_kernel"):
+        text = "append kernel, then " + text
+    return text
 
 
 class Step:
@@ -231,7 +203,7 @@ class Step:
     it: the step's copy-on-write copies (if any), then pa_append_decode with the
     caller's workspace and a host copy of the lengths."""
 
-    def __init__(self, w, cus, stream, partition_tokens=0):
+    def __init__(self, w, stream, partition_tokens=0):
         import numpy as np
         import torch
 
@@ -244,11 +216,7 @@ class Step:
         self.out = torch.empty_like(self.dw.q)
         self.has_copies = int(w.copies.shape[0]) > 0
         max_len = int(w.block_tables.shape[1]) * w.block_size
-        self.part = pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
-        _, self.schedule = decode_kernels(w, self.part, cus)
-        fused, _, kind, _ = fused_step(w, self.part, cus)
-        if fused:
-            self.schedule = kind
+        self.part = partition_tokens or pa.schedule(w.num_seqs, w.num_q_heads, w.num_kv_heads, max_len)
         nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, partition_tokens)
         self.ws = pa.alloc_workspace(nb, "cuda:0") if nb else None
         self.host_lens = np.asarray(w.context_lens, dtype=np.int32)
@@ -261,6 +229,7 @@ class Step:
         if not self.kernels:
             raise RuntimeError(f"{w.name}: the step launched no decode kernel ({launched})")
         self.kernels_all = launched
+        self.schedule = describe_launch(launched, self.part)
         # bytes the main kernel must move: a physical block shared by several
         # sequences (a common prefix) counts once; the multi-token kernel also
         # writes the new tokens (a separate append kernel, or the combine after
@@ -581,7 +550,6 @@ def main():
         sys.exit(1)
     pa.load()
     torch.cuda.set_device(0)
-    cus = torch.cuda.get_device_properties(0).multi_processor_count
     flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.Stream()  # default priority
     torch.cuda.synchronize()
@@ -590,7 +558,7 @@ def main():
     tev = TimingEvents()
     E = tev.create
     with torch.cuda.stream(stream):
-        st = Step(w, cus, stream)
+        st = Step(w, stream)
         step_ms, kernel_ms = time_steps(st, args.steps, args.warmup, tev, flush)
         print(f"bench: {w.name} step {mean(step_ms) * 1e3:.1f} us, kernel {mean(kernel_ms) * 1e3:.1f} us",
               file=sys.stderr, flush=True)
@@ -660,7 +628,7 @@ def main():
                 configs[name] = head_row
                 continue
             cw = workloads.make(name)
-            cst = Step(cw, cus, stream)
+            cst = Step(cw, stream)
             sm, km = time_steps(cst, args.steps, args.warmup, tev, flush)
             configs[name] = config_row(cst, sm, km)
             print(f"bench: {name} step {mean(sm) * 1e3:.1f} us, kernel {mean(km) * 1e3:.1f} us",
