@@ -165,6 +165,26 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 mfma_16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c,
+                                                   0, 0, 0);
+}
+// o0 (dim 2r + 32c) and o1 (dim 2r + 32c + 1) += V P for one tile, as four
+// K = 16 MFMAs: this lane's V of tokens 4*g4 .. +3 straight from the loaded
+// registers (x, y: dim 2r + 32c; z, w: the next dim), P's hi then lo halves.
+// One K = 32 MFMA per dim would need V repeated in an operand quad; the
+// copies that builds keep the register allocator from holding the next
+// tile's loads in flight across the softmax (it waits for every load).
+__device__ __forceinline__ void pv16(f32x4& o0, f32x4& o1, u32x4 v, u32x4 pb) {
+  const u32x2 vx = {v.x, v.y}, vz = {v.z, v.w}, ph = {pb.x, pb.y}, pl = {pb.z, pb.w};
+  o0 = mfma_16x16x16(vx, ph, o0);
+  o1 = mfma_16x16x16(vz, ph, o1);
+  o0 = mfma_16x16x16(vx, pl, o0);
+  o1 = mfma_16x16x16(vz, pl, o1);
+}
+
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
 // 2^x with the hardware instruction: results below 2^-126 flush to zero,
@@ -328,9 +348,8 @@ __device__ __forceinline__ void mfma_reset(MfmaAcc<D>& a) {
 
 // Scores of one tile (QK^T), the online-softmax update of the column
 // references and sums, and P as the B operand of PV, split into hi + lo
-// bf16: with K = 32 one MFMA takes the high halves as its first four k
-// values and the low halves as the last four, against the same four V
-// values repeated.
+// bf16: x, y the high halves of this lane's four tokens, z, w the low ones
+// (pv16 takes each pair against the same V registers).
 template <int D>
 __device__ __forceinline__ u32x4 mfma_probs(MfmaAcc<D>& a, const u32x4 (&q)[D / 32], float scale_log2,
                                             bool partial, int ts, int t1, int lane,
@@ -392,10 +411,7 @@ __device__ __forceinline__ void mfma_tile(MfmaAcc<D>& a, const u32x4 (&q)[D / 32
   if (partial) mask_v<D>(vt, ts, t1, lane);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};  // dim 2r + 32c, tokens 4*g4 .. +3, twice
-    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};  // dim 2r + 32c + 1
-    a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
-    a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
+    pv16(a.o[2 * c], a.o[2 * c + 1], vt[c], pb);
   }
 }
 
@@ -413,13 +429,8 @@ __device__ __forceinline__ void mfma_tile_sets(MfmaAcc<D> (&a)[NS], const u32x4 
   if (partial) mask_v<D>(vt, ts, t1, lane);
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
-    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};
-    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};
 #pragma unroll
-    for (int cs = 0; cs < NS; ++cs) {
-      a[cs].o[2 * c] = mfma_16x16x32(a0, pb[cs], a[cs].o[2 * c]);
-      a[cs].o[2 * c + 1] = mfma_16x16x32(a1, pb[cs], a[cs].o[2 * c + 1]);
-    }
+    for (int cs = 0; cs < NS; ++cs) pv16(a[cs].o[2 * c], a[cs].o[2 * c + 1], vt[c], pb[cs]);
   }
 }
 
@@ -479,10 +490,7 @@ template <int D>
 __device__ __forceinline__ void mfma_pv(MfmaAcc<D>& a, u32x4 pb, const u32x4 (&vt)[D / 32]) {
 #pragma unroll
   for (int c = 0; c < D / 32; ++c) {
-    const u32x4 a0 = {vt[c].x, vt[c].y, vt[c].x, vt[c].y};
-    const u32x4 a1 = {vt[c].z, vt[c].w, vt[c].z, vt[c].w};
-    a.o[2 * c] = mfma_16x16x32(a0, pb, a.o[2 * c]);
-    a.o[2 * c + 1] = mfma_16x16x32(a1, pb, a.o[2 * c + 1]);
+    pv16(a.o[2 * c], a.o[2 * c + 1], vt[c], pb);
   }
 }
 
@@ -1114,7 +1122,45 @@ struct Smem {
   float m[kWaves][16];
   float l[kWaves][16];
   float o[kWaves][D][17];
+  float f[kWaves][16];  // column_weights: wave w's weight of column g
+  float M[16];          // column_weights: reference max and sum of column g
+  float L[16];
 };
+
+// After the waves' (m, l, o) are in sm and a barrier: per column g < ncols,
+// the reference max M over the waves, the sum L, and each wave's weight
+// 2^(m_w - M) / L (zero where the column saw no token), so that an output
+// element is a four-term dot product of sm.o and sm.f.  Ends with a barrier.
+template <int D>
+__device__ __forceinline__ void column_weights(Smem<D>& sm, int ncols) {
+  if (int(threadIdx.x) < ncols) {
+    const int g = threadIdx.x;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
+    float e[kWaves], l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      e[w] = M != kNegInf ? exp2f(sm.m[w][g] - M) : 0.f;
+      l += sm.l[w][g] * e[w];
+    }
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) sm.f[w][g] = e[w] * inv;
+    sm.M[g] = M;
+    sm.L[g] = l;
+  }
+  __syncthreads();
+}
+
+// Output element (d, column g): the waves' o weighted by column_weights.
+template <int D>
+__device__ __forceinline__ float weighted_o(const Smem<D>& sm, int d, int g) {
+  float o = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) o = fmaf(sm.o[w][d][g], sm.f[w][g], o);
+  return o;
+}
 
 // Combine the waves' (m, l, o) and write either the output (one partition)
 // or this partition's partial result for the combine kernel.
@@ -1122,30 +1168,20 @@ template <int D>
 __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>& sm, int s, int h0,
                                                  int ncols, int part, int nparts) {
   __syncthreads();
+  column_weights<D>(sm, ncols);
   for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
     const int g = idx / D;
     const int d = idx - g * D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][g]);
-    float o = 0.f, l = 0.f;
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float e = exp2f(sm.m[w][g] - M);
-        o += sm.o[w][d][g] * e;
-        l += sm.l[w][g] * e;
-      }
-    }
+    const float o = weighted_o<D>(sm, d, g);
     const int h = h0 + g;
     if (nparts <= 1) {
-      store_out(p, s, h, d, l > 0.f ? o / l : 0.f);
+      store_out(p, s, h, d, o);
     } else {
       const size_t row = (size_t(s) * p.num_q_heads + h) * p.max_parts + part;
-      p.ws_o[row * D + d] = o / l;
+      p.ws_o[row * D + d] = o;
       if (d == 0) {
-        p.ws_ml[row * 2 + 0] = M;
-        p.ws_ml[row * 2 + 1] = l;
+        p.ws_ml[row * 2 + 0] = sm.M[g];
+        p.ws_ml[row * 2 + 1] = sm.L[g];
       }
     }
   }
@@ -1897,6 +1933,32 @@ __device__ __forceinline__ void load_new_tile(const MultiParams& p, int r0, int 
   }
 }
 
+// The same tile (n <= 16 new tokens) from the pieces the append duty parks
+// in LDS: piece i * D/8 + j holds dims 8j .. 8j + 7 of new token i.
+template <int D>
+__device__ __forceinline__ void parked_new_tile(const u32x4* pk, const u32x4* pv, int n, int lane,
+                                                u32x4 (&kt)[D / 32], u32x4 (&vt)[D / 32]) {
+  constexpr int NC = D / 32;
+  constexpr int P = D / 8;
+  const int r = lane & 15;
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) kt[c] = r < n ? pk[r * P + g4 + 4 * c] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    uint32_t w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int j = 4 * g4 + t;  // dims 2r + 32c and +1: piece r / 4 + 4c, 32-bit word r % 4
+      w[t] = j < n ? reinterpret_cast<const uint32_t*>(&pv[j * P + (r >> 2) + 4 * c])[r & 3] : 0u;
+    }
+    vt[c].x = (w[0] & 0xffffu) | (w[1] << 16);
+    vt[c].y = (w[2] & 0xffffu) | (w[3] << 16);
+    vt[c].z = (w[0] >> 16) | (w[1] & 0xffff0000u);
+    vt[c].w = (w[2] >> 16) | (w[3] & 0xffff0000u);
+  }
+}
+
 // A workgroup computes NS sets of 16 columns against each tile it loads, so
 // a (sequence, KV head) with up to 16 * NS columns reads its context once.
 // Split: the cached context is cut into partitions (grid z), whose pieces the
@@ -2032,13 +2094,27 @@ void decode_multi(MultiParams mp) {
     park_v[threadIdx.x] = app_v;
     park_slot[threadIdx.x] = app_slot;
   }
+  // A single new tile whose pieces are all parked is taken from LDS, first,
+  // by the wave the round robin over the waves gives it (the one after the
+  // cached tiles' last): its loads then cost no trip to memory at the end of
+  // the walk.  The softmax does not depend on the order, up to rounding.
+  const int old_tiles = (t1 - t0 + 15) >> 4;
+  const bool new_parked = last && n > 0 && n <= kTileTokens && staged == n * (D / 8);  // workgroup-uniform
+  if (new_parked) {
+    __syncthreads();  // every piece parked
+    if (wave == old_tiles % kWaves) {
+      u32x4 kt[NC], vt[NC];
+      parked_new_tile<D>(park_k, park_v, n, lane, kt, vt);
+#pragma unroll
+      for (int cs = 0; cs < NS; ++cs) mfma_tile_causal<D>(acc[cs], q[cs], p.scale_log2, 0, qi[cs], lane, kt, vt);
+    }
+  }
   walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
                                            [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
   });
-  // the new tiles (last partition) continue the cached tiles' round robin over the waves
-  const int old_tiles = (t1 - t0 + 15) >> 4;
-  for (int u = (wave + kWaves - old_tiles % kWaves) % kWaves; last && 16 * u < n; u += kWaves) {
+  // otherwise the new tiles (last partition) continue the cached tiles' round robin over the waves
+  for (int u = (wave + kWaves - old_tiles % kWaves) % kWaves; last && !new_parked && 16 * u < n; u += kWaves) {
     u32x4 kt[NC], vt[NC];
     load_new_tile<D>(mp, r0, n, u, kvh, lane, kt, vt);
 #pragma unroll
@@ -2073,32 +2149,22 @@ void decode_multi(MultiParams mp) {
           sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc[cs].o[mm][j];
     }
     __syncthreads();
+    column_weights<D>(sm, ncols);
     for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
       const int col = idx / D;
       const int d = idx - col * D;
-      float M = kNegInf;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.m[w][col]);
-      float o = 0.f, lsum = 0.f;
-      if (M != kNegInf) {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float e = exp2f(sm.m[w][col] - M);
-          o += sm.o[w][d][col] * e;
-          lsum += sm.l[w][col] * e;
-        }
-      }
+      const float o = weighted_o<D>(sm, d, col);
       const int cc = cbase + col;
       const int i = cc / G;
       const int h = kvh * G + (cc - i * G);
       if (!Split || nparts <= 1) {
-        store_out(p, r0 + i, h, d, lsum > 0.f ? o / lsum : 0.f);
+        store_out(p, r0 + i, h, d, o);
       } else {  // this partition's piece of row r0 + i for the combine
         const size_t wrow = (size_t(r0 + i) * p.num_q_heads + h) * p.max_parts + part;
-        p.ws_o[wrow * D + d] = lsum > 0.f ? o / lsum : 0.f;
+        p.ws_o[wrow * D + d] = o;
         if (d == 0) {
-          p.ws_ml[wrow * 2 + 0] = M;
-          p.ws_ml[wrow * 2 + 1] = lsum;
+          p.ws_ml[wrow * 2 + 0] = sm.M[col];
+          p.ws_ml[wrow * 2 + 1] = sm.L[col];
         }
       }
     }
