@@ -1123,6 +1123,7 @@ struct Smem {
   float l[kWaves][16];
   float o[kWaves][D][17];
   float f[kWaves][16];  // column_weights: wave w's weight of column g
+  float fn[16];         // column_weights: weight of the folded-in new token of column g
   float M[16];          // column_weights: reference max and sum of column g
   float L[16];
 };
@@ -1130,9 +1131,11 @@ struct Smem {
 // After the waves' (m, l, o) are in sm and a barrier: per column g < ncols,
 // the reference max M over the waves, the sum L, and each wave's weight
 // 2^(m_w - M) / L (zero where the column saw no token), so that an output
-// element is a four-term dot product of sm.o and sm.f.  Ends with a barrier.
+// element is a four-term dot product of sm.o and sm.f.  With xn, column g
+// also takes one more token of score xn[g] (log2 units; -inf: none), whose
+// value then enters with weight sm.fn[g].  Ends with a barrier.
 template <int D>
-__device__ __forceinline__ void column_weights(Smem<D>& sm, int ncols) {
+__device__ __forceinline__ void column_weights(Smem<D>& sm, int ncols, const float* xn = nullptr) {
   if (int(threadIdx.x) < ncols) {
     const int g = threadIdx.x;
     float M = kNegInf;
@@ -1144,9 +1147,18 @@ __device__ __forceinline__ void column_weights(Smem<D>& sm, int ncols) {
       e[w] = M != kNegInf ? exp2f(sm.m[w][g] - M) : 0.f;
       l += sm.l[w][g] * e[w];
     }
+    float a = 1.f, b = 0.f;
+    if (xn && xn[g] != kNegInf) {
+      const float M2 = fmaxf(M, xn[g]);
+      a = exp2f(M - M2);  // 0 where the waves read no token (M = -inf)
+      b = exp2f(xn[g] - M2);
+      l = l * a + b;
+      M = M2;
+    }
     const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) sm.f[w][g] = e[w] * inv;
+    for (int w = 0; w < kWaves; ++w) sm.f[w][g] = e[w] * a * inv;
+    sm.fn[g] = b * inv;
     sm.M[g] = M;
     sm.L[g] = l;
   }
@@ -1674,41 +1686,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
       for (int j = 0; j < 4; ++j) sm.o[wave][2 * (4 * g4 + j) + 32 * (mm >> 1) + (mm & 1)][r] = acc.o[mm][j];
   }
   __syncthreads();
+  column_weights<D>(sm, ncols, Fused ? x_new : nullptr);
   for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
     const int col = idx / D;
     const int d = idx - col * D;
-    float M_ = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M_ = fmaxf(M_, sm.m[w][col]);
-    float o = 0.f, lsum = 0.f;
-    if (M_ != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float e = exp2f(sm.m[w][col] - M_);
-        o += sm.o[w][d][col] * e;
-        lsum += sm.l[w][col] * e;
-      }
-    }
+    float o = weighted_o<D>(sm, d, col);
     const int sc = s + col / G;
-    if (Fused && x_new[col] != kNegInf) {  // fold in the new token: score x_new[col], value v_new[sc, kvh, d]
-      const float x = x_new[col];
-      const float M2 = fmaxf(M_, x);
-      const float a = exp2f(M_ - M2);  // 0 where no pool token was read (M_ = -inf)
-      const float b = exp2f(x - M2);
-      const float v = bf16_value(mp.v_new[size_t(sc) * mp.vn_t + size_t(kvh) * mp.vn_h + d]);
-      o = o * a + b * v;
-      lsum = lsum * a + b;
-      M_ = M2;
-    }
+    if (Fused && sm.fn[col] != 0.f)  // the new token's value v_new[sc, kvh, d]
+      o = fmaf(sm.fn[col], bf16_value(mp.v_new[size_t(sc) * mp.vn_t + size_t(kvh) * mp.vn_h + d]), o);
     const int h = kvh * G + col % G;
     if (partitions(p, p.context_lens[sc]) <= 1) {
-      store_out(p, sc, h, d, lsum > 0.f ? o / lsum : 0.f);
+      store_out(p, sc, h, d, o);
     } else {
       const size_t wrow = (size_t(sc) * p.num_q_heads + h) * p.max_parts + part;
-      p.ws_o[wrow * D + d] = o / lsum;
+      p.ws_o[wrow * D + d] = o;
       if (d == 0) {
-        p.ws_ml[wrow * 2 + 0] = M_;
-        p.ws_ml[wrow * 2 + 1] = lsum;
+        p.ws_ml[wrow * 2 + 0] = sm.M[col];
+        p.ws_ml[wrow * 2 + 1] = sm.L[col];
       }
     }
   }
