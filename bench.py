@@ -19,7 +19,9 @@ it; they are created with hipEventDisableSystemFence, so recording them flushes
 no cache.  ``roofline`` is the step's main kernel alone, timed in as many
 further flushed steps by events that the GPU stamps at its start and end,
 against 8 TB/s.  ``two_call_step`` times the headline step as pa_cache_append +
-pa_decode.  ``paging_control`` times the same decode over an unpaged copy of the
+pa_decode.  ``fixed_cost`` times the headline's shapes with one token per
+sequence (what a launch costs with next to no bytes).  ``paging_control`` times
+the same decode over an unpaged copy of the
 cache; ``multi_query`` times pa_decode_multi (several new tokens per sequence:
 speculative verification) on the Llama-3-8B-shaped batch with 5 drafted tokens
 per sequence, and ``multi_query_long`` on 8 sequences of 32k tokens with 5
@@ -95,6 +97,8 @@ def parse():
                     help="seconds each CPU baseline worker spends on the oracle")
     ap.add_argument("--no-multi", action="store_true",
                     help="skip the multi-token (speculative verification) leg")
+    ap.add_argument("--no-fixed-cost", action="store_true",
+                    help="skip the one-token-per-sequence step (the launch's fixed cost)")
     ap.add_argument("--no-control", action="store_true",
                     help="skip the unpaged control (pa_decode_contiguous on a copy of the cache)")
     ap.add_argument("--unflushed", action="store_true",
@@ -538,7 +542,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the decode path shards by sequence or KV head with no exchange, see the design notes)",
+              "(the decode path shards by sequence or KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -630,6 +634,23 @@ def main():
             contig_ms = [tev.elapsed_ms(a, b) for a, b, _, _ in cev]
             unsplit_ms = [tev.elapsed_ms(c, d) for _, _, c, d in cev]
             del kc, vc, out_c
+        # the fixed cost of the step: the same shapes, grid and schedule family
+        # with one token per sequence (a few bytes each), timed the same way
+        fixed = None
+        if not args.no_fixed_cost:
+            fw = workloads.random_workload(w.seed, [1] * w.num_seqs, num_q_heads=w.num_q_heads,
+                                           num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                                           block_size=w.block_size, name=f"{w.name}_one_token")
+            fst = Step(fw, stream)
+            fsm, fkm = time_steps(fst, args.steps, args.warmup, tev, flush)
+            fixed = {"workload": f"{w.name}'s shapes ({w.num_seqs} sequences, {w.num_q_heads} q / "
+                                 f"{w.num_kv_heads} kv heads, D {w.head_dim}, B {w.block_size}) with one token "
+                                 "per sequence",
+                     "kernels": fst.kernels_all, "step_us": stats_us(fsm), "kernel_us": stats_us(fkm),
+                     "note": "what a launch of the step costs with next to no bytes: dispatch, the table fetch, "
+                             "one tile, the cross-wave combine, the output and the append; GPU-stamped events "
+                             "around the kernel as for the roofline"}
+            del fst, fw
         head_row = config_row(st, step_ms, kernel_ms)
         head_kernels, head_schedule, head_algo, head_desc = st.kernels_all, st.schedule, st.algo_bytes, st.step_desc()
         head_main = st.kernels[0]
@@ -736,6 +757,8 @@ def main():
                     "schedule (one workgroup per sequence and head group, MFMA), alternating, each "
                     "after a cache flush and timed by events around the call",
         }
+    if fixed is not None:
+        line["fixed_cost"] = fixed
     line["two_call_step"] = {
         "step_us": stats_us(two_ms),
         "value": round(eff_bytes / (mean(two_ms) / 1e3) / 1e9, 2),
