@@ -2212,23 +2212,28 @@ __global__ __launch_bounds__(256) void combine_append(MultiParams mp) {
   const int s = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int u = threadIdx.x * gridDim.x + blockIdx.x;
-  if (u < p.num_kv_heads * (D / 8)) {
-    const int64_t slot = mp.slots[s];
-    if (slot >= 0 && slot < mp.num_slots) {
-      const int h = u / (D / 8);
-      const int piece = u - h * (D / 8);
-      const u32x4 kv = load16(mp.k_new + size_t(s) * mp.kn_t + size_t(h) * mp.kn_h + piece * 8);
-      const u32x4 vv = load16(mp.v_new + size_t(s) * mp.vn_t + size_t(h) * mp.vn_h + piece * 8);
-      write_slot_piece<D, BS>(mp.k_store, mp.v_store, p.num_kv_heads, slot, h, piece, kv, vv);
-    }
+  // Every load first, the stores last: a store ahead of a load would hold it
+  // back until the store is acknowledged.
+  const int64_t slot = mp.slots[s];
+  const bool app = u < p.num_kv_heads * (D / 8) && slot >= 0 && slot < mp.num_slots;
+  const int ah = u / (D / 8);
+  const int piece = u - ah * (D / 8);
+  u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+  if (app) {
+    kv = load16(mp.k_new + size_t(s) * mp.kn_t + size_t(ah) * mp.kn_h + piece * 8);
+    vv = load16(mp.v_new + size_t(s) * mp.vn_t + size_t(ah) * mp.vn_h + piece * 8);
   }
-  if (idx >= p.num_q_heads * D) return;
-  const int nparts = partitions(p, p.context_lens[s]);
-  if (nparts <= 1) return;  // the decode kernel wrote this row directly
+  // rows whose context is split; the decode kernel wrote the others directly
+  const bool out = idx < p.num_q_heads * D && partitions(p, p.context_lens[s]) > 1;
   const int h = idx / D;
   const int d = idx - h * D;
-  const size_t row0 = (size_t(s) * p.num_q_heads + h) * p.max_parts;
-  store_out(p, s, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
+  float o = 0.f;
+  if (out) {
+    const size_t row0 = (size_t(s) * p.num_q_heads + h) * p.max_parts;
+    o = lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, partitions(p, p.context_lens[s]), d);
+  }
+  if (app) write_slot_piece<D, BS>(mp.k_store, mp.v_store, p.num_kv_heads, slot, ah, piece, kv, vv);
+  if (out) store_out(p, s, h, d, o);
 }
 
 // ---------------------------------------------------------------------------
