@@ -1466,6 +1466,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   __shared__ int run_off[kMaxShare + 1];  // leader: first own tile of each member, after the common ones
   __shared__ int run_plan[2];             // this workgroup's members (0: follower) and common end
   __shared__ float x_new[16];             // fused: the new tokens' scores (log2 units), by column
+  __shared__ u32x4 v_fold[kMaxShare][D / 8];  // fused: member i's new value, loaded ahead of any store
   const DecodeParams& p = mp.d;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -1657,6 +1658,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
     if (own && 8 * j < D) {
       const u32x4 qv = load16(p.q + size_t(s + cm) * p.q_s + size_t(kvh * G + c - cm * G) * p.q_h + 8 * j);
       const u32x4 kv = load16(mp.k_new + size_t(s + cm) * mp.kn_t + size_t(kvh) * mp.kn_h + 8 * j);
+      if (c == cm * G) v_fold[cm][j] = load16(mp.v_new + size_t(s + cm) * mp.vn_t + size_t(kvh) * mp.vn_h + 8 * j);
       const uint32_t qa[4] = {qv.x, qv.y, qv.z, qv.w}, ka[4] = {kv.x, kv.y, kv.z, kv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1687,15 +1689,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   }
   __syncthreads();
   column_weights<D>(sm, ncols, Fused ? x_new : nullptr);
+  // LDS and registers only from here to the stores: a global load after a
+  // store would wait for the store's acknowledgement
   for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
     const int col = idx / D;
     const int d = idx - col * D;
     float o = weighted_o<D>(sm, d, col);
-    const int sc = s + col / G;
-    if (Fused && sm.fn[col] != 0.f)  // the new token's value v_new[sc, kvh, d]
-      o = fmaf(sm.fn[col], bf16_value(mp.v_new[size_t(sc) * mp.vn_t + size_t(kvh) * mp.vn_h + d]), o);
+    const int cm = col / G;
+    const int sc = s + cm;
+    if (Fused && sm.fn[col] != 0.f) {  // the new token's value v_new[sc, kvh, d]
+      const u32x4 piece = v_fold[cm][d >> 3];
+      const uint32_t w = (d & 4) ? ((d & 2) ? piece.w : piece.z) : ((d & 2) ? piece.y : piece.x);
+      o = fmaf(sm.fn[col], (d & 1) ? bf_hi(w) : bf_lo(w), o);
+    }
     const int h = kvh * G + col % G;
-    if (partitions(p, p.context_lens[sc]) <= 1) {
+    if (partitions(p, member_len(cm)) <= 1) {
       store_out(p, sc, h, d, o);
     } else {
       const size_t wrow = (size_t(sc) * p.num_q_heads + h) * p.max_parts + part;
