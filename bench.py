@@ -44,8 +44,8 @@ DEFAULT_CONFIG = "llama3_8b_b64"
 # every seeded configuration, one row each in ``configs``
 CONFIG_ROWS = ("tiny_gqa4_d64", "llama3_8b_b64", "llama3_70b_b256", "opt13b_mha_prefix_b128",
                "long32k_b8", "long32k_b16", "long32k_b32", "opt13b_cow_fork_b128")
-# worker processes of the CPU baseline: this host's cores, at most the share
-# of one GPU's host on the GPU machines
+# worker processes of the CPU baseline: this host's cores, at most 16 (a
+# one-GPU share of a multi-GPU host's cores)
 CPU_WORKERS_MAX = 16
 
 # HBM bytes per launch of a step's main kernel, from two rocprofv3 --pmc runs
