@@ -60,26 +60,26 @@ KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h",
                   "paged_kv_cache_122_amd/csrc/pa_api.cpp")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "ed6361f6ba6e0b92d3c4f5aad840587cd16f9cd2142f8899cb0337aecb5a4f8b",
-    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 725868, "write_bytes": 10240, "mfma_busy_pct": 0.04,
+    "sources_sha256": "e5e269678fa93223a02ca340030c52456bb20e79877dfc7e532dc82c3785962d",
+    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 725794, "write_bytes": 10240, "mfma_busy_pct": 0.04,
         "source": "profiles/decode_multi_tiny_gqa4_d64_kernel_trace.md"},
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273997344, "write_bytes": 1310818, "mfma_busy_pct": 7.8,
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273996709, "write_bytes": 1310750, "mfma_busy_pct": 7.64,
         "source": "profiles/decode_multi_llama3_8b_b64_kernel_trace.md"},
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287991169, "write_bytes": 4457400, "mfma_busy_pct": 14.74,
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287990553, "write_bytes": 4459061, "mfma_busy_pct": 14.78,
         "source": "profiles/decode_multi_llama3_8b_verify5_b64_kernel_trace.md"},
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074910426, "write_bytes": 5558549, "mfma_busy_pct": 19.37,
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074908301, "write_bytes": 5559093, "mfma_busy_pct": 19.03,
         "source": "profiles/decode_multi_long32k_verify5_b16_kernel_trace.md"},
-    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907161129, "write_bytes": 7340032, "mfma_busy_pct": 9.26,
+    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907160542, "write_bytes": 7340032, "mfma_busy_pct": 9.15,
         "source": "profiles/decode_multi_llama3_70b_b256_kernel_trace.md"},
-    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745276709, "write_bytes": 5514050, "mfma_busy_pct": 9.31,
+    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745278242, "write_bytes": 5514279, "mfma_busy_pct": 9.22,
         "source": "profiles/decode_shared_opt13b_mha_prefix_b128_kernel_trace.md"},
-    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075057844, "write_bytes": 1163264, "mfma_busy_pct": 9.99,
+    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075058216, "write_bytes": 1163264, "mfma_busy_pct": 9.77,
         "source": "profiles/decode_multi_long32k_b8_kernel_trace.md"},
-    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074524284, "write_bytes": 1163436, "mfma_busy_pct": 9.8,
+    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074514881, "write_bytes": 1163525, "mfma_busy_pct": 9.7,
         "source": "profiles/decode_multi_long32k_b16_kernel_trace.md"},
-    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074262592, "write_bytes": 1163343, "mfma_busy_pct": 10.07,
+    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074262109, "write_bytes": 1163269, "mfma_busy_pct": 9.89,
         "source": "profiles/decode_multi_long32k_b32_kernel_trace.md"},
-    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350394005, "write_bytes": 1310720, "mfma_busy_pct": 5.82,
+    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350397035, "write_bytes": 1310720, "mfma_busy_pct": 5.83,
         "source": "profiles/decode_shared_opt13b_cow_fork_b128_kernel_trace.md"},
 }
 

@@ -1408,7 +1408,7 @@ __device__ __forceinline__ void walk_run(const DecodeParams& p, __amdgpu_buffer_
           tc.e0 = own[ts >> 3];
           tc.e1 = ts + 8 < te ? own[(ts >> 3) + 1] : tc.e0;
         }
-        range = ((te - t0) << 16) | (ts - t0);
+        range = int((uint32_t(te - t0) << 16) | uint32_t(ts - t0));  // both <= 32768: 16 bits each
         member = c;
       }
     }
@@ -1420,7 +1420,7 @@ __device__ __forceinline__ void walk_run(const DecodeParams& p, __amdgpu_buffer_
       const bool common = v < n_sh;
       const int rg = __builtin_amdgcn_readlane(range, j);
       ts = common ? t0 + 16 * v : t0 + (rg & 0xffff);
-      te = common ? sh_end : t0 + (rg >> 16);
+      te = common ? sh_end : t0 + int(uint32_t(rg) >> 16);
       mem = common ? -1 : __builtin_amdgcn_readlane(member, j);
       b0 = __builtin_amdgcn_readlane(tc.e0, j);
       b1 = 0;
@@ -1511,7 +1511,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
 
   // The run this workgroup belongs to (workgroup-uniform).  A run needs a
   // neighbour whose partition starts on the same block; without one (most
-  // partitions past a shared prefix) nothing more is read.
+  // partitions past a shared prefix) nothing more is read.  A run's tiles
+  // carry 16-bit token offsets inside the partition: at most 32768 tokens.
   bool alone = M == 1 || L <= t0 || p.part_tokens > 32768 ||
                !((has_prev && clamp_len(p, len_prev) > t0 && e_prev == e_self) ||
                  (has_next && clamp_len(p, len_next) > t0 && e_next == e_self));

@@ -248,6 +248,8 @@ PARTIAL = [
     ("fork_gqa2_p1024_b8", 3102, [4, 6, 5], 1990, 40, 8, 4, 128, 8, 1024),
     ("fork_gqa4_d64_b32", 3103, [3, 4, 4], 490, 25, 16, 4, 64, 32, 512),
     ("fork_unsplit_mha", 3104, [8, 8], 1000, 1, 4, 4, 128, 16, 1024),
+    # the largest partition that shares: members' own tiles reach its end, 32768 tokens in
+    ("fork_p32768_gqa2_b32", 3105, [2] * 8, 32000, 1000, 16, 8, 64, 32, 32768),
 ]
 
 
