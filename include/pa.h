@@ -183,9 +183,9 @@ typedef struct {
                                 -2: the stream-K schedule;
                                 else partitions of this many tokens, a positive
                                 multiple of 32 */
-  int32_t path;              /* 0: auto (MFMA when q heads per KV head >= 3, else VALU);
-                                1: force the VALU path (q heads per KV head <= 2);
-                                2: force the MFMA path */
+  int32_t path;              /* 0: auto (the MFMA path);
+                                1: the VALU path (q heads per KV head <= 2);
+                                2: the MFMA path */
   int64_t max_context_len;   /* partitioned schedule only.  0: table width *
                                 block_size; else an upper bound on every
                                 context_lens[s], used to size the launch */

@@ -196,7 +196,7 @@ int owned_workspace(size_t need, hipStream_t stream, void** out) {
 struct DecodePlan {
   int64_t S, Hq, Hkv, D, B, W, NB;
   int part_tokens, max_parts;
-  bool share_unsplit;   // automatic VALU path, unsplit: the shared-partition kernel where the grid fills the GPU
+  bool share_unsplit;   // automatic, unsplit, G <= 2: the shared-partition kernel where the grid fills the GPU
   bool stream;          // stream-K schedule (else partitioned)
   int workgroups_per_cu;
   pa::Path path;
@@ -307,8 +307,8 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
   const int64_t G = Hq / g.kv_heads;
   const int want = opts ? opts->path : 0;
   pa::Path path;
-  if (want == 0)
-    path = G >= 3 ? pa::Path::Mfma : pa::Path::Valu;
+  if (want == 0)  // MFMA costs nothing on padding columns: faster than VALU also at G = 1, 2
+    path = pa::Path::Mfma;
   else if (want == 1)
     path = pa::Path::Valu;
   else if (want == 2)
@@ -379,14 +379,14 @@ int plan_decode(const pa_tensor* out, const pa_tensor* q, const pa_tensor* k_cac
 
   pl->part_tokens = int(part);
   pl->max_parts = int(max_parts);
-  // A split schedule with the automatic path takes the MFMA kernel for any
-  // grouping up to 16: it reads a partition that consecutive sequences share
-  // (a common prefix) once for all of them, which the VALU kernel cannot.
-  if (want == 0 && max_parts > 1 && G <= 16) pl->path = pa::Path::Mfma;
+  // A split schedule with the automatic path takes the shared-partition
+  // kernel for any grouping up to 16 where the grid fills the GPU: it reads a
+  // partition that consecutive sequences share (a common prefix) once for all
+  // of them.
   // Unsplit with one or two q heads per KV head: where the grid fills the GPU
   // the shared-partition kernel takes it (one partition spanning the table),
   // so that prefix blocks neighbouring sequences share (parallel samples of
-  // a prompt) are read once; smaller grids keep the VALU kernel.
+  // a prompt) are read once; smaller grids take the MFMA decode.
   pl->share_unsplit = want == 0 && max_parts == 1 && G <= 2;
   pl->ws = pa::workspace_layout(S, Hq, D, max_parts);
   if (max_parts == 1) pl->ws.total = 0;
@@ -1231,15 +1231,22 @@ PA_EXPORT int pa_append_decode(pa_tensor* out, const pa_tensor* q, const pa_tens
   }
 
   // Route: the multi-token kernel in one launch where the schedule is unsplit
-  // on the MFMA path; with host lengths, also where the automatic schedule
-  // splits few pairs (partitions sized on those lengths, or unsplit where
-  // every context fits one); otherwise the append kernel, then the decode.
+  // on the MFMA path (unless the shared-partition kernel takes the unsplit
+  // grid, below); with host lengths, also where the automatic schedule splits
+  // few pairs (partitions sized on those lengths, or unsplit where every
+  // context fits one); otherwise the append kernel, then the decode.
   const int64_t pairs = pl.S * pl.Hkv * ((pl.Hq / pl.Hkv + 15) / 16);
   const bool mfma = pl.path == pa::Path::Mfma;
   const bool unsplit = !pl.stream && pl.max_parts == 1;
   const bool host_split = mfma && !unsplit && host_lens && opts->partition_tokens == 0 &&
                           (pl.stream || pairs < kFullGpuPairs);
-  if ((mfma && unsplit) || host_split) {
+  bool shared_unsplit = false;  // one or two q heads per KV head, a grid that fills the GPU
+  if (unsplit && pl.share_unsplit) {
+    int cus = 0;
+    if ((rc = device_cus(&cus)) != PA_OK) return rc;
+    shared_unsplit = pl.Hkv * pl.S >= cus;
+  }
+  if ((mfma && unsplit && !shared_unsplit) || host_split) {
     const CacheGeom g{pl.NB, pl.Hkv, pl.D, pl.B};
     pa::MultiParams m;
     if ((rc = multi_params(out, q, k, v, slot_mapping, nullptr, k_cache, v_cache, block_tables, context_lens,

@@ -2380,7 +2380,7 @@ inline bool deep_pipeline(const DecodeParams& p, const LaunchCtx& c) {
 
 // The shared-partition kernel takes a partitioned schedule of at most 16 q
 // heads per KV head whose grid fills the GPU: split on the MFMA path, or
-// unsplit where the automatic path would take the VALU kernel.
+// unsplit with one or two q heads per KV head on the automatic path.
 inline bool shared_applies(const DecodeParams& p, Path path, const LaunchCtx& c) {
   return p.group <= 16 && ((path == Path::Mfma && p.max_parts > 1) || (p.share_unsplit && p.max_parts == 1)) &&
          int64_t(p.num_kv_heads) * p.num_seqs * p.max_parts >= c.cus;
@@ -2490,7 +2490,7 @@ hipError_t launch_decode(const DecodeParams& p, const StreamParams* sk, int head
 bool shared_step_applies(const DecodeParams& p, Path path, const LaunchCtx& c) { return shared_applies(p, path, c); }
 
 hipError_t launch_shared_step(const MultiParams& m, int head_dim, int block_size, const LaunchCtx& c) {
-  if (!shared_applies(m.d, m.d.share_unsplit ? Path::Valu : Path::Mfma, c)) return hipErrorInvalidValue;
+  if (!shared_applies(m.d, Path::Mfma, c)) return hipErrorInvalidValue;
   switch (head_dim * 100 + block_size) {
     case 6408: return launch_shared_step_d<64, 8>(m, c);
     case 6416: return launch_shared_step_d<64, 16>(m, c);
