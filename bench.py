@@ -60,26 +60,26 @@ KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h",
                   "paged_kv_cache_122_amd/csrc/pa_api.cpp")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "e5e269678fa93223a02ca340030c52456bb20e79877dfc7e532dc82c3785962d",
-    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 725794, "write_bytes": 10240, "mfma_busy_pct": 0.04,
+    "sources_sha256": "3c840eca4b0fb7e9a3fe4196b43176fdb4d5300899eb67265aae9ac5478007e8",
+    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 725869, "write_bytes": 10240, "mfma_busy_pct": 0.04,
         "source": "profiles/decode_multi_tiny_gqa4_d64_kernel_trace.md"},
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273996709, "write_bytes": 1310750, "mfma_busy_pct": 7.64,
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273997057, "write_bytes": 1310750, "mfma_busy_pct": 7.86,
         "source": "profiles/decode_multi_llama3_8b_b64_kernel_trace.md"},
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287990553, "write_bytes": 4459061, "mfma_busy_pct": 14.78,
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287990983, "write_bytes": 4458552, "mfma_busy_pct": 14.74,
         "source": "profiles/decode_multi_llama3_8b_verify5_b64_kernel_trace.md"},
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074908301, "write_bytes": 5559093, "mfma_busy_pct": 19.03,
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074909508, "write_bytes": 5559043, "mfma_busy_pct": 19.15,
         "source": "profiles/decode_multi_long32k_verify5_b16_kernel_trace.md"},
-    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907160542, "write_bytes": 7340032, "mfma_busy_pct": 9.15,
+    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907160542, "write_bytes": 7340042, "mfma_busy_pct": 9.28,
         "source": "profiles/decode_multi_llama3_70b_b256_kernel_trace.md"},
-    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745278242, "write_bytes": 5514279, "mfma_busy_pct": 9.22,
+    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745277398, "write_bytes": 5524635, "mfma_busy_pct": 9.23,
         "source": "profiles/decode_shared_opt13b_mha_prefix_b128_kernel_trace.md"},
-    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075058216, "write_bytes": 1163264, "mfma_busy_pct": 9.77,
+    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075059274, "write_bytes": 1163264, "mfma_busy_pct": 9.87,
         "source": "profiles/decode_multi_long32k_b8_kernel_trace.md"},
-    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074514881, "write_bytes": 1163525, "mfma_busy_pct": 9.7,
+    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074523561, "write_bytes": 1163323, "mfma_busy_pct": 9.68,
         "source": "profiles/decode_multi_long32k_b16_kernel_trace.md"},
-    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074262109, "write_bytes": 1163269, "mfma_busy_pct": 9.89,
+    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074253523, "write_bytes": 1163350, "mfma_busy_pct": 9.98,
         "source": "profiles/decode_multi_long32k_b32_kernel_trace.md"},
-    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350397035, "write_bytes": 1310720, "mfma_busy_pct": 5.83,
+    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350397402, "write_bytes": 1310720, "mfma_busy_pct": 5.72,
         "source": "profiles/decode_shared_opt13b_cow_fork_b128_kernel_trace.md"},
 }
 
