@@ -317,7 +317,9 @@ int pa_decode_contiguous(pa_tensor* out, const pa_tensor* q, const pa_tensor* k,
  * The append and the attention are the two halves of a decode step ("vLLM -
  * PagedAttention" digest, "Fused CUDA Kernels": the write into the cache is
  * fused to cut launches; "PagedAttention from First Principles", section 5).
- * Where the decode schedule is unsplit on the MFMA path, one kernel does both:
+ * Where the decode schedule is unsplit on the MFMA path (but for the grids of
+ * one or two q heads per KV head that the shared-partition kernel takes,
+ * below), one kernel does both:
  * it stores the new token and takes its K/V from k / v for the attention.
  * Where the automatic schedule splits with fewer than 512 pairs (stream-K or
  * 512-token partitions) and opts carries host_context_lens, the multi-token
