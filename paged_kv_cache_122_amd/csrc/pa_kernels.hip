@@ -1370,6 +1370,48 @@ __device__ __forceinline__ void write_slot_piece(uint16_t* k_cache, uint16_t* v_
 // ---------------------------------------------------------------------------
 constexpr int kMaxShare = 16;  // members per workgroup at G = 1
 
+// Over each row of 16 lanes (DPP row shifts; a lane whose source would lie
+// before its row takes the identity): the value of the lane before, and the
+// inclusive prefix minimum and sum.
+__device__ __forceinline__ int row_shift1(int x) { return __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false); }
+
+__device__ __forceinline__ int row_scan_min(int x) {
+  x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = min(x, __builtin_amdgcn_update_dpp(INT_MAX, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  return x;
+}
+
+__device__ __forceinline__ int row_scan_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);
+  return x;
+}
+
+// Sequence of grid row y in decode_shared.  An unsplit grid padded to whole
+// windows (rows = windows * M, M members each) takes row y as member slot
+// j = y / windows of window y % windows, the slots in bit-reversed order when
+// M is a power of two: 0, M/2, M/4, 3M/4, ...  A window's runs start at its
+// first member and, for runs of 2, 4 or 8 parallel samples, at the multiples
+// of the run length, so the run leaders are dispatched ahead of the
+// followers, which only plan and leave, and the leaders of all windows start
+// together; the followers then take the slots the leaders leave free.  Rows
+// past the last sequence return -1.  Split grids keep the identity order:
+// there a partition's followers, queued behind its leaders, would hold back
+// the next partition's workgroups.
+__device__ __forceinline__ int shared_seq(int y, int M, int S) {
+  const int windows = (S + M - 1) / M;
+  if (gridDim.z != 1 || int(gridDim.y) != windows * M) return y;
+  const int j = y / windows;
+  int si = j;
+  if (M > 1 && (M & (M - 1)) == 0) si = int(__builtin_bitreverse32(uint32_t(j)) >> (32 - __builtin_ctz(M)));
+  const int s = (y - j * windows) * M + si;
+  return s < S ? s : -1;
+}
+
 // Walk a run's nv tiles, tiles wave, wave + 4, ... of it in this wave, with
 // the next S - 1 tiles' loads issued before the current one is computed (as
 // walk_tiles).  Tiles [0, n_sh) are the common tokens [t0, sh_end) of every
@@ -1461,10 +1503,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   constexpr int NC = D / 32;
   __shared__ Smem<D> sm;
   __shared__ int win_len[kMaxShare];      // window member i: clamped context length
-  __shared__ int win_fd[kMaxShare];       // member i >= 1: first partition entry differing from member i-1's
   __shared__ int win_tw[kMaxShare];       // window member i: end of its pool tokens read in this partition
   __shared__ int run_off[kMaxShare + 1];  // leader: first own tile of each member, after the common ones
-  __shared__ int run_plan[2];             // this workgroup's members (0: follower) and common end
   __shared__ float x_new[16];             // fused: the new tokens' scores (log2 units), by column
   __shared__ u32x4 v_fold[kMaxShare][D / 8];  // fused: member i's new value, loaded ahead of any store
   const DecodeParams& p = mp.d;
@@ -1473,10 +1513,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   const int r = lane & 15;
   const int g4 = lane >> 4;
   const int kvh = blockIdx.x;
-  const int s = blockIdx.y;
   const int part = blockIdx.z;
   const int G = p.group;
   const int M = 16 / G;  // members one workgroup carries
+  const int s = shared_seq(blockIdx.y, M, p.num_seqs);
+  if (s < 0) return;  // workgroup-uniform: padding of the last window
   const int t0 = part * p.part_tokens;
   const int t_end = t0 + p.part_tokens;
   const int w0 = s - s % M;
@@ -1492,9 +1533,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   const auto row = table_row(p, s, BS);
   const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
   const bool has_prev = M > 1 && si > 0, has_next = M > 1 && si + 1 < hi;
+  const int last = p.max_len / BS - 1;
   const int nb = lane == 0 && has_prev ? s - 1 : (lane == 2 && has_next ? s + 1 : s);
   const int nb_len = p.context_lens[nb];
-  const int nb_ent = p.block_tables[size_t(nb) * p.bt_s + min(E0, p.max_len / BS - 1)];
+  const int nb_ent = p.block_tables[size_t(nb) * p.bt_s + min(E0, last)];
+  // Behind those, wave 0 of a workgroup that may share loads what the window
+  // plan needs: every member's length (lane i: member i, members past the
+  // window repeat the last) and the partition's first 64 entries of every
+  // member's row (lane e: entry E0 + e, kept inside the row), so that the
+  // plan costs one trip to memory.  A workgroup found alone does not wait for
+  // them.  A run's tiles carry 16-bit token offsets inside the partition: at
+  // most 32768 tokens.
+  const bool may_share = M > 1 && p.part_tokens <= 32768;
+  int w_len = 0;
+  int w_ent[kMaxShare];
+  if (may_share && wave == 0) {
+    const int idx = min(E0 + lane, last);
+    w_len = p.context_lens[w0 + min(lane, hi - 1)];
+#pragma unroll
+    for (int i = 0; i < kMaxShare; ++i) w_ent[i] = p.block_tables[size_t(w0 + min(i, hi - 1)) * p.bt_s + idx];
+  }
   const int len_prev = __builtin_amdgcn_readlane(nb_len, 0);
   const int len_next = __builtin_amdgcn_readlane(nb_len, 2);
   const int e_prev = __builtin_amdgcn_readlane(nb_ent, 0);
@@ -1511,94 +1569,80 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
 
   // The run this workgroup belongs to (workgroup-uniform).  A run needs a
   // neighbour whose partition starts on the same block; without one (most
-  // partitions past a shared prefix) nothing more is read.  A run's tiles
-  // carry 16-bit token offsets inside the partition: at most 32768 tokens.
-  bool alone = M == 1 || L <= t0 || p.part_tokens > 32768 ||
-               !((has_prev && clamp_len(p, len_prev) > t0 && e_prev == e_self) ||
-                 (has_next && clamp_len(p, len_next) > t0 && e_next == e_self));
+  // partitions past a shared prefix) nothing more is read.
+  const bool alone = !may_share || L <= t0 ||
+                     !((has_prev && clamp_len(p, len_prev) > t0 && e_prev == e_self) ||
+                       (has_next && clamp_len(p, len_next) > t0 && e_next == e_self));
   int m = 1, t_sh = 0;
   if (!alone) {
-    // The window's lengths, and for each member the first entry of the
-    // partition where its table departs from its predecessor's: wave w takes
-    // members 1 + w, 5 + w, ..., one 64-entry chunk per lane step, and the
-    // lowest set bit of a ballot over the lanes' comparisons is the departure
-    // (entry indices kept inside the rows; past the used entries the values
-    // do not matter, as below).
-    const int E = p.part_tokens / BS;
-    const int last = p.max_len / BS - 1;
-    if (threadIdx.x < hi) win_len[threadIdx.x] = clamp_len(p, p.context_lens[w0 + threadIdx.x]);
-    constexpr int kRows = kMaxShare / kWaves;  // members a wave compares
-    int ea[kRows], eb[kRows];
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {  // the first 64 entries of every row at once
-      const int i = min(1 + wave + kWaves * r, hi - 1);
-      const int idx = min(E0 + lane, last);
-      ea[r] = p.block_tables[size_t(w0 + i) * p.bt_s + idx];
-      eb[r] = p.block_tables[size_t(w0 + i - 1) * p.bt_s + idx];
-    }
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-      const int i = 1 + wave + kWaves * r;
-      if (i >= hi) break;  // wave-uniform
-      uint64_t diff = __ballot(lane < E && ea[r] != eb[r]);
-      int fd = diff ? __builtin_ctzll(diff) : E;
-      for (int c0 = 64; c0 < E && !diff; c0 += 64) {  // longer partitions: further chunks
-        const int e = c0 + lane;
-        const int idx = min(E0 + e, last);
-        diff = __ballot(e < E && p.block_tables[size_t(w0 + i) * p.bt_s + idx] !=
-                                     p.block_tables[size_t(w0 + i - 1) * p.bt_s + idx]);
-        if (diff) fd = c0 + __builtin_ctzll(diff);
-      }
-      if (lane == 0) win_fd[i] = fd;
-    }
-    __syncthreads();
-    // pool tokens of each member, and its departure point over the entries
-    // both it and its predecessor use
-    auto used = [&](int len) { return len > t0 ? (min(len, t_end) - t0 + BS - 1) / BS : 0; };
-    const int my_len = lane < hi ? win_len[lane] : 0;
-    const int prev_len = lane > 0 && lane < hi ? win_len[lane - 1] : 0;
-    const int my_tw = pool_end(my_len);
-    const int my_fd = lane > 0 && lane < hi ? min(win_fd[lane], min(used(my_len), used(prev_len))) : 0;
-    if (threadIdx.x < hi) win_tw[threadIdx.x] = my_tw;
-    // Runs from the start of the window, each grown member by member while
-    // the members' own tiles stay within the common ones (own: the run's own
-    // tiles for the current common end, recounted only when that end moves).
-    // Wave 0 finds them (lane i holds member i) and every workgroup of the
-    // window finds the same; the others read this workgroup's part from LDS.
+    __shared__ int run_plan[2];  // this workgroup's members (0: a follower) and common end
     if (wave == 0) {
-      int lead = 0, mine_m = 0, mine_tsh = 0;
-      while (true) {
-        int k = E, mtw = __builtin_amdgcn_readlane(my_tw, lead), n = 1, tsh = t0, own = 0;
-        for (int j = lead + 1; j < hi; ++j) {
-          const int tw_j = __builtin_amdgcn_readlane(my_tw, j);
-          const int fd_j = __builtin_amdgcn_readlane(my_fd, j);
-          if (tw_j <= t0 || fd_j == 0) break;
-          const int k2 = min(k, fd_j);
-          const int mtw2 = min(mtw, tw_j);
-          const int tsh2 = t0 + (max(0, min(k2 * BS, mtw2 - t0)) & ~15);
-          const int common = (tsh2 - t0) >> 4;
-          if (common == 0) break;
-          int own2 = own + ((tw_j - tsh2 + 15) >> 4);
-          if (n == 1 || tsh2 != tsh) {  // the common end moved: recount the run
-            own2 = 0;
-            for (int c = lead; c <= j; ++c) own2 += (__builtin_amdgcn_readlane(my_tw, c) - tsh2 + 15) >> 4;
+      // member i >= 1 (lane i): the first entry of the partition where its row
+      // departs from member i-1's, the lowest set bit of a ballot over the
+      // lanes' comparisons, 64 entries a step
+      const int E = p.part_tokens / BS;
+      int fd_lane = E;
+      uint64_t same = 0;  // members whose first 64 entries all match their predecessor's
+#pragma unroll
+      for (int i = 1; i < kMaxShare; ++i) {
+        const uint64_t diff = __ballot(lane < E && w_ent[i] != w_ent[i - 1]);
+        if (lane == i && diff) fd_lane = int(__builtin_ctzll(diff));
+        if (!diff) same |= uint64_t(1) << i;
+      }
+      if (E > 64) {  // longer partitions: further chunks for those members
+        for (uint64_t u = same & ((uint64_t(1) << hi) - 2); u; u &= u - 1) {
+          const int i = int(__builtin_ctzll(u));
+          int fd = E;
+          for (int c0 = 64; c0 < E; c0 += 64) {
+            const int idx = min(E0 + c0 + lane, last);
+            const uint64_t diff = __ballot(c0 + lane < E && p.block_tables[size_t(w0 + i) * p.bt_s + idx] !=
+                                                                p.block_tables[size_t(w0 + i - 1) * p.bt_s + idx]);
+            if (diff) {
+              fd = c0 + int(__builtin_ctzll(diff));
+              break;
+            }
           }
-          if (own2 > common) break;
-          k = k2;
-          mtw = mtw2;
-          tsh = tsh2;
-          own = own2;
-          n = j - lead + 1;
+          if (lane == i) fd_lane = fd;
         }
+      }
+      // pool tokens of each member, and its departure point over the entries
+      // both it and its predecessor use (past them the values do not matter)
+      auto used = [&](int len) { return len > t0 ? (min(len, t_end) - t0 + BS - 1) / BS : 0; };
+      const int my_len = lane < hi ? clamp_len(p, w_len) : 0;
+      const int prev_len = row_shift1(my_len);
+      const int my_tw = pool_end(my_len);
+      const int my_fd = lane > 0 && lane < hi ? min(fd_lane, min(used(my_len), used(prev_len))) : 0;
+      if (lane < hi) {
+        win_len[lane] = my_len;
+        win_tw[lane] = my_tw;
+      }
+      // Runs from the start of the window, each grown member by member while
+      // the members' own tiles stay within the common ones; every workgroup of
+      // the window finds the same runs.  For the run from `lead`, lane j takes
+      // members lead .. j: their common tiles past t0 (up to the least
+      // departure point and pool end) and their own tiles past those (each
+      // member's tiles from t0 less the common ones), from prefix scans over
+      // the members; the first lane whose member cannot join ends the run.
+      const int tiles_from_t0 = (my_tw - t0 + 15) >> 4;
+      int lead = 0, mine = 0, mine_tsh = t0;
+      for (int it = 0; it < kMaxShare; ++it) {  // each run takes at least one member
+        const int mtw = row_scan_min(lane >= lead ? my_tw : INT_MAX);
+        const int k = min(E, row_scan_min(lane > lead ? my_fd : INT_MAX));
+        const int tiles = row_scan_sum(lane >= lead ? tiles_from_t0 : 0);
+        const int common = max(0, min(k * BS, mtw - t0)) >> 4;
+        const int own = tiles - (lane - lead + 1) * common;
+        const bool stop = lane > lead && lane < hi && (my_tw <= t0 || my_fd == 0 || common == 0 || own > common);
+        const uint64_t stops = __ballot(stop);
+        const int n = (stops ? int(__builtin_ctzll(stops)) : hi) - lead;
         if (si < lead + n) {
-          mine_m = si == lead ? n : 0;  // 0: a follower
-          mine_tsh = tsh;
+          mine = si == lead ? n : 0;
+          mine_tsh = t0 + 16 * (n > 1 ? __builtin_amdgcn_readlane(common, lead + n - 1) : 0);
           break;
         }
         lead += n;
       }
       if (lane == 0) {
-        run_plan[0] = mine_m;
+        run_plan[0] = mine;
         run_plan[1] = mine_tsh;
       }
     }
@@ -2386,6 +2430,15 @@ inline bool shared_applies(const DecodeParams& p, Path path, const LaunchCtx& c)
          int64_t(p.num_kv_heads) * p.num_seqs * p.max_parts >= c.cus;
 }
 
+// Grid rows of decode_shared: unsplit, the sequences padded to whole windows
+// of 16 / G members (shared_seq's order) where that stays within the 65535
+// rows a grid dimension takes; otherwise exactly the sequences.
+inline int shared_rows(const DecodeParams& p) {
+  const int M = 16 / p.group;
+  const int rows = (p.num_seqs + M - 1) / M * M;
+  return p.max_parts == 1 && rows <= 65535 ? rows : p.num_seqs;
+}
+
 template <int D, int BS>
 hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx& c) {
   static_assert(kDeepSlots > kPipeSlots, "");
@@ -2395,7 +2448,7 @@ hipError_t launch_partitioned(const DecodeParams& p, Path path, const LaunchCtx&
                     p.num_kv_heads * p.head_groups, c);
   else if (shared_applies(p, path, c))
     e = launch_main(kname("decode_shared<%d,%d,false>", D, BS), decode_shared<D, BS, false>,
-                    dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c,
+                    dim3(p.num_kv_heads, shared_rows(p), p.max_parts), dim3(kThreads), c,
                     MultiParams{p});  // split: shared partitions read once (no ranking)
   else if (path == Path::Mfma)
     e = launch_rows(kname("decode_mfma<%d,%d,%d>", D, BS, kPipeSlots), decode_mfma<D, BS, kPipeSlots>, p,
@@ -2417,7 +2470,7 @@ template <int D, int BS>
 hipError_t launch_shared_step_d(const MultiParams& m, const LaunchCtx& c) {
   const DecodeParams& p = m.d;
   hipError_t e = launch_main(kname("decode_shared<%d,%d,true>", D, BS), decode_shared<D, BS, true>,
-                             dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(kThreads), c, m);
+                             dim3(p.num_kv_heads, shared_rows(p), p.max_parts), dim3(kThreads), c, m);
   if (e != hipSuccess) return e;
   // num_kv_heads * D / 8 <= num_q_heads * D: the combine's rows cover the pieces
   const dim3 cgrid((p.num_q_heads * D + 255) / 256, p.num_seqs);
