@@ -60,26 +60,26 @@ KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h",
                   "paged_kv_cache_122_amd/csrc/pa_api.cpp")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "3c840eca4b0fb7e9a3fe4196b43176fdb4d5300899eb67265aae9ac5478007e8",
-    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 725869, "write_bytes": 10240, "mfma_busy_pct": 0.04,
+    "sources_sha256": "7d6614a43e987c851a7552ce1ce73acca89f04cec2f551472bd4e97f7dd70a95",
+    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 725795, "write_bytes": 10240, "mfma_busy_pct": 0.04,
         "source": "profiles/decode_multi_tiny_gqa4_d64_kernel_trace.md"},
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273997057, "write_bytes": 1310750, "mfma_busy_pct": 7.86,
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273996506, "write_bytes": 1310740, "mfma_busy_pct": 7.84,
         "source": "profiles/decode_multi_llama3_8b_b64_kernel_trace.md"},
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287990983, "write_bytes": 4458552, "mfma_busy_pct": 14.74,
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 287991500, "write_bytes": 4457765, "mfma_busy_pct": 14.63,
         "source": "profiles/decode_multi_llama3_8b_verify5_b64_kernel_trace.md"},
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074909508, "write_bytes": 5559043, "mfma_busy_pct": 19.15,
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074912017, "write_bytes": 5559115, "mfma_busy_pct": 19.07,
         "source": "profiles/decode_multi_long32k_verify5_b16_kernel_trace.md"},
-    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907160542, "write_bytes": 7340042, "mfma_busy_pct": 9.28,
+    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907160676, "write_bytes": 7340032, "mfma_busy_pct": 9.05,
         "source": "profiles/decode_multi_llama3_70b_b256_kernel_trace.md"},
-    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745277398, "write_bytes": 5524635, "mfma_busy_pct": 9.23,
+    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745309273, "write_bytes": 5521994, "mfma_busy_pct": 9.46,
         "source": "profiles/decode_shared_opt13b_mha_prefix_b128_kernel_trace.md"},
-    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075059274, "write_bytes": 1163264, "mfma_busy_pct": 9.87,
+    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075057943, "write_bytes": 1163264, "mfma_busy_pct": 9.8,
         "source": "profiles/decode_multi_long32k_b8_kernel_trace.md"},
-    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074523561, "write_bytes": 1163323, "mfma_busy_pct": 9.68,
+    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074525821, "write_bytes": 1163407, "mfma_busy_pct": 9.8,
         "source": "profiles/decode_multi_long32k_b16_kernel_trace.md"},
-    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074253523, "write_bytes": 1163350, "mfma_busy_pct": 9.98,
+    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074263744, "write_bytes": 1163397, "mfma_busy_pct": 10.01,
         "source": "profiles/decode_multi_long32k_b32_kernel_trace.md"},
-    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350397402, "write_bytes": 1310720, "mfma_busy_pct": 5.72,
+    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350424008, "write_bytes": 1310720, "mfma_busy_pct": 7.34,
         "source": "profiles/decode_shared_opt13b_cow_fork_b128_kernel_trace.md"},
 }
 
