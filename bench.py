@@ -175,6 +175,10 @@ class CacheFlush:
 
         torch.sum(self.buf, dim=0, out=self.out)
 
+    def written(self):
+        """The flush that writes the buffer instead (for comparison only)."""
+        self.buf.fill_(1.0)
+
 
 def sources_sha256():
     h = hashlib.sha256()
@@ -609,6 +613,10 @@ def main():
         step_ms, kernel_ms = time_steps(st, args.steps, args.warmup, tev, flush)
         print(f"bench: {w.name} step {mean(step_ms) * 1e3:.1f} us, kernel {mean(kernel_ms) * 1e3:.1f} us",
               file=sys.stderr, flush=True)
+        # the same main kernel after a flush that writes the buffer instead of
+        # reading it, for comparison: a written flush leaves dirty lines whose
+        # write-back lands in the timed kernel
+        _, written_kernel_ms = time_steps(st, args.steps, 0, tev, flush.written)
 
         # the step as two calls: pa_cache_append, then pa_decode's schedule
         tw = [(E(), E(), E()) for _ in range(args.steps)]
@@ -766,8 +774,15 @@ def main():
             "kernel": head_main,
             "timed": f"HIP events (created with hipEventDisableSystemFence) stamped by the GPU "
                      f"at the start and end of {head_main} (hipExtLaunchKernel), {args.steps} "
-                     "further steps, caches flushed",
+                     "further steps, caches flushed by reading a 1 GiB buffer",
         },
+    }
+    line["written_flush"] = {
+        "kernel_us": stats_us(written_kernel_ms),
+        "frac": round(head_algo / (mean(written_kernel_ms) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "note": f"{head_main} timed as for the roofline, but after writing the 1 GiB flush buffer instead of "
+                "reading it: the caches then hold dirty lines whose write-back runs inside the timed kernel; "
+                "for comparison only",
     }
     if contig_ms:
         line["paging_control"] = {
