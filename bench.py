@@ -568,7 +568,7 @@ def cpu_baseline(pool, n, affinity, w, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode path shards by sequence or KV head with no exchange)",
               file=sys.stderr)
         sys.exit(2)
