@@ -674,13 +674,27 @@ def main():
                                            block_size=w.block_size, name=f"{w.name}_one_token")
             fst = Step(fw, stream)
             fsm, fkm = time_steps(fst, args.steps, args.warmup, tev, flush)
+            # a launch of any kernel: a one-element fill between the same
+            # kind of events as the step
+            one = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+            fev = [(E(), E()) for _ in range(args.steps)]
+            for a, b in fev:
+                flush()
+                tev.record(a, stream)
+                one.fill_(1.0)
+                tev.record(b, stream)
+            stream.synchronize()
+            fill_ms = [tev.elapsed_ms(a, b) for a, b in fev]
             fixed = {"workload": f"{w.name}'s shapes ({w.num_seqs} sequences, {w.num_q_heads} q / "
                                  f"{w.num_kv_heads} kv heads, D {w.head_dim}, B {w.block_size}) with one token "
                                  "per sequence",
                      "kernels": fst.kernels_all, "step_us": stats_us(fsm), "kernel_us": stats_us(fkm),
+                     "one_element_fill_us": stats_us(fill_ms),
                      "note": "what a launch of the step costs with next to no bytes: dispatch, the table fetch, "
                              "one tile, the cross-wave combine, the output and the append; GPU-stamped events "
-                             "around the kernel as for the roofline"}
+                             "around the kernel as for the roofline. one_element_fill_us: a one-element torch "
+                             "fill between events around the call, as step_us is timed: the cost of launching "
+                             "any kernel"}
             del fst, fw
         head_row = config_row(st, step_ms, kernel_ms)
         head_kernels, head_schedule, head_algo, head_desc = st.kernels_all, st.schedule, st.algo_bytes, st.step_desc()
