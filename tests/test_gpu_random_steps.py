@@ -1,0 +1,103 @@
+"""Seeded random decode steps through pa_append_decode (after the step's
+copy-on-write copies through pa_copy_blocks), against the fp64 oracle: random
+groupings, head dims, block sizes, batch sizes from 1 to 400, length mixes up to
+20,000 tokens, and prefix-sharing forks whose prompts end inside a block (so
+copy-on-write fires), with and without a host copy of the lengths.  The batches
+reach every route of the step: the one-launch kernel, partitions sized on host
+lengths, the shared-partition kernel, stream-K and the partitioned kernels
+after the append.  Every row is checked (max|err| <= 1e-2, relative RMS <=
+2e-3) and the pools bit for bit."""
+
+import numpy as np
+import pytest
+
+from gpu_util import assert_close, need_gpu, oracle_step
+from paged_kv_cache_122_amd import workloads
+from paged_kv_cache_122_amd.blockpool import BlockPool, Sequence, fork, free, reserve_slots
+
+pytestmark = pytest.mark.gpu
+
+# context tokens x KV heads per case, so that the oracle takes a second or two
+BUDGET = 1.5e6
+
+
+def independent(rng, seed):
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    b = int(rng.choice([8, 16, 32]))
+    lmax = int(rng.choice([64, 1024, 4096, 20000]))
+    S = int(np.exp(rng.uniform(0, np.log(400))))
+    S = max(1, min(S, int(BUDGET / hkv / max(1, lmax / 2))))
+    lens = rng.integers(1, lmax, size=S, endpoint=True)
+    w = workloads.random_workload(seed, lens, num_q_heads=g * hkv, num_kv_heads=hkv, head_dim=d, block_size=b,
+                                  name=f"random_step{seed}")
+    return w, f"S={S} G={g} Hkv={hkv} D={d} B={b} Lmax={lmax}"
+
+
+def forks(rng, seed):
+    """Groups of samples forked from one prompt; each sample then appends its own
+    tokens (at least this step's), copying a shared, partly filled last block."""
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 8]))
+    d = int(rng.choice([64, 128]))
+    b = int(rng.choice([8, 16, 32]))
+    groups = int(rng.integers(1, 20))
+    per = int(rng.choice([2, 4, 8, 16]))
+    prompt = int(rng.integers(1, 3000))
+    tails = rng.integers(0, 400, size=groups * per).tolist()
+    while groups * per * (prompt + 200) * hkv > BUDGET and groups > 1:
+        groups -= 1
+    tails = tails[:groups * per]
+    need = groups * (workloads.blocks_for_tokens(prompt, b) + per) + sum(
+        workloads.blocks_for_tokens(t + 1, b) for t in tails)
+    nb = int(1.3 * need) + 8
+    pool = BlockPool(nb, b, free_order=rng.permutation(nb))
+    tables, lens = [], []
+    for gi in range(groups):
+        parent = Sequence()
+        reserve_slots(pool, parent, prompt)
+        children = [fork(pool, parent) for _ in range(per)]
+        free(pool, parent)
+        for j, child in enumerate(children):
+            reserve_slots(pool, child, tails[gi * per + j] + 1)
+            tables.append(child.table)
+            lens.append(child.length)
+    copies = list(pool.pending_copies) or None
+    w = workloads.build_workload(f"random_fork{seed}", seed, rng, num_q_heads=g * hkv, num_kv_heads=hkv,
+                                 head_dim=d, block_size=b, num_blocks=nb, tables=tables, context_lens=lens,
+                                 width=max(len(t) for t in tables), copies=copies)
+    return w, (f"forks {groups}x{per} prompt={prompt} G={g} Hkv={hkv} D={d} B={b} "
+               f"copies={0 if copies is None else len(copies)}")
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_step(case):
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    seed = 90000 + case
+    rng = np.random.Generator(np.random.PCG64(seed))
+    w, desc = (forks if case % 3 == 2 else independent)(rng, seed)
+    host = bool(rng.integers(0, 2))
+    print(f"[random step {case}] {desc} host_lens={host}", flush=True)
+    kst, vst, ref = oracle_step(w)
+    dw = dev.upload(w)
+    span = w.table_width * w.block_size
+    nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, span, 0)
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    if int(w.copies.shape[0]):
+        pa.copy_blocks(dw.k_cache, dw.v_cache, dw.copies)
+    pa.append_decode(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.k_cache, dw.v_cache, dw.block_tables,
+                     dw.context_lens, w.scale, w.block_size, workspace=ws,
+                     host_context_lens=np.asarray(w.context_lens, dtype=np.int32) if host else None)
+    torch.cuda.synchronize()
+    route = pa.last_launch()
+    assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), f"{desc}: K pool differs"
+    assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), f"{desc}: V pool differs"
+    a, r = assert_close(out.double().cpu().numpy(), ref, desc)
+    print(f"[random step {case}] {route} max|err| {a:.2e} rel RMS {r:.2e}", flush=True)
+    del dw
+    torch.cuda.empty_cache()
