@@ -187,6 +187,52 @@ def test_multi_random_batches(seed):
     assert_close(got, ref, f"random{seed}")
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_multi_random_large(case):
+    """Seeded random multi-token calls at larger sizes than above, through
+    pa_decode_multi_ex with the caller's workspace: 1-200 sequences, cached
+    lengths up to 12,000 (split and unsplit grids, one or two column sets),
+    1-24 new tokens each, host lengths on or off; pools bit-exact and every row
+    against the oracle."""
+    torch = need_gpu()
+    from paged_kv_cache_122_amd import _lib as pa
+    from paged_kv_cache_122_amd import device as dev
+
+    seed = 70000 + case
+    rng = np.random.Generator(np.random.PCG64(seed))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    d = int(rng.choice([64, 128]))
+    b = int(rng.choice([8, 16, 32]))
+    lmax = int(rng.choice([100, 2000, 12000]))
+    nmax = int(rng.choice([1, 2, 5, 8, 24]))
+    S = int(np.exp(rng.uniform(0, np.log(200))))
+    S = max(1, min(S, int(1.2e6 / hkv / max(1, lmax / 2))))  # the oracle's time
+    old = rng.integers(0, lmax, size=S, endpoint=True)
+    new = rng.integers(1, nmax, size=S, endpoint=True)
+    host = bool(rng.integers(0, 2))
+    w = workloads.multi_query_workload(seed, old.tolist(), new.tolist(), num_q_heads=g * hkv, num_kv_heads=hkv,
+                                       head_dim=d, block_size=b, name=f"multi_large{seed}")
+    desc = f"S={S} G={g} Hkv={hkv} D={d} B={b} Lmax={lmax} nmax={nmax} host={host}"
+    print(f"[multi large {case}] {desc}", flush=True)
+    kst, vst, ref = oracle_multi(w)
+    dw = dev.upload(w)
+    T = w.q.shape[0]
+    mql = int(np.diff(w.query_start).max())
+    span = w.table_width * w.block_size
+    nb = pa.multi_workspace_bytes(T, w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, mql, span, 0)
+    ws = pa.alloc_workspace(nb, "cuda") if nb else None
+    out = torch.empty(dw.q.shape, dtype=torch.float32, device="cuda")
+    pa.decode_multi_ex(out, dw.q, dw.k_new, dw.v_new, dw.slot_mapping, dw.query_start, dw.k_cache, dw.v_cache,
+                       dw.block_tables, dw.context_lens, w.scale, w.block_size, mql, workspace=ws,
+                       host_context_lens=np.asarray(w.context_lens, dtype=np.int32) if host else None)
+    torch.cuda.synchronize()
+    check_pools(w, dw, kst, vst)
+    assert_close(out.double().cpu().numpy(), ref, desc)
+    del dw
+    torch.cuda.empty_cache()
+
+
 def test_multi_split_long_contexts():
     """Few sequences with long contexts: the cached context is split into
     partitions whose pieces a combine kernel joins.  The 32k-token verification
