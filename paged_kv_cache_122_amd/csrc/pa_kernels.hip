@@ -213,6 +213,32 @@ __device__ __forceinline__ void store_out(const DecodeParams& p, int s, int h, i
     static_cast<uint16_t*>(p.out)[at] = uint16_t(bf16_bits(r));
 }
 
+// Dims d0 .. d0 + 7 of output row (s, h) in one 16-byte store (two for f32
+// outputs) where the row starts 16-byte aligned, element by element otherwise
+// (strided outputs).  d0 is a multiple of 8.
+__device__ __forceinline__ void store_out8(const DecodeParams& p, int s, int h, int d0, const float (&o)[8]) {
+  const size_t at = size_t(s) * p.out_s + size_t(h) * p.out_h + d0;
+  if (p.out_f32) {
+    float* dst = static_cast<float*>(p.out) + at;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      *reinterpret_cast<f32x4*>(dst) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(dst + 4) = f32x4{o[4], o[5], o[6], o[7]};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = o[j];
+    }
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(p.out) + at;
+    if ((reinterpret_cast<uintptr_t>(dst) & 15u) == 0) {
+      store16(dst, u32x4{bf16_bits(o[0]) | (bf16_bits(o[1]) << 16), bf16_bits(o[2]) | (bf16_bits(o[3]) << 16),
+                         bf16_bits(o[4]) | (bf16_bits(o[5]) << 16), bf16_bits(o[6]) | (bf16_bits(o[7]) << 16)});
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dst[j] = uint16_t(bf16_bits(o[j]));
+    }
+  }
+}
+
 // Context length as the kernels use it: negative lengths count as 0 and
 // lengths past the block table (a contract violation) are clamped to it.
 __device__ __forceinline__ int clamp_len(const DecodeParams& p, int L) {
@@ -1181,20 +1207,25 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
                                                  int ncols, int part, int nparts) {
   __syncthreads();
   column_weights<D>(sm, ncols);
-  for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
+  if (nparts <= 1) {  // the output, eight dims per thread
+    for (int idx = threadIdx.x; idx < ncols * (D / 8); idx += kThreads) {
+      const int g = idx / (D / 8);
+      const int d0 = 8 * (idx - g * (D / 8));
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = weighted_o<D>(sm, d0 + j, g);
+      store_out8(p, s, h0 + g, d0, o);
+    }
+    return;
+  }
+  for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {  // this partition's piece
     const int g = idx / D;
     const int d = idx - g * D;
-    const float o = weighted_o<D>(sm, d, g);
-    const int h = h0 + g;
-    if (nparts <= 1) {
-      store_out(p, s, h, d, o);
-    } else {
-      const size_t row = (size_t(s) * p.num_q_heads + h) * p.max_parts + part;
-      p.ws_o[row * D + d] = o;
-      if (d == 0) {
-        p.ws_ml[row * 2 + 0] = sm.M[g];
-        p.ws_ml[row * 2 + 1] = sm.L[g];
-      }
+    const size_t row = (size_t(s) * p.num_q_heads + h0 + g) * p.max_parts + part;
+    p.ws_o[row * D + d] = weighted_o<D>(sm, d, g);
+    if (d == 0) {
+      p.ws_ml[row * 2 + 0] = sm.M[g];
+      p.ws_ml[row * 2 + 1] = sm.L[g];
     }
   }
 }
@@ -1736,24 +1767,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_shared(MultiParams mp) {
   column_weights<D>(sm, ncols, Fused ? x_new : nullptr);
   // LDS and registers only from here to the stores: a global load after a
   // store would wait for the store's acknowledgement
-  for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
-    const int col = idx / D;
-    const int d = idx - col * D;
-    float o = weighted_o<D>(sm, d, col);
+  // eight dims per thread, one column's (so one member's) each
+  for (int idx = threadIdx.x; idx < ncols * (D / 8); idx += kThreads) {
+    const int col = idx / (D / 8);
+    const int d0 = 8 * (idx - col * (D / 8));
     const int cm = col / G;
     const int sc = s + cm;
-    if (Fused && sm.fn[col] != 0.f) {  // the new token's value v_new[sc, kvh, d]
-      const u32x4 piece = v_fold[cm][d >> 3];
-      const uint32_t w = (d & 4) ? ((d & 2) ? piece.w : piece.z) : ((d & 2) ? piece.y : piece.x);
-      o = fmaf(sm.fn[col], (d & 1) ? bf_hi(w) : bf_lo(w), o);
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = weighted_o<D>(sm, d0 + j, col);
+    if (Fused && sm.fn[col] != 0.f) {  // the new token's value v_new[sc, kvh, d0 .. d0 + 7]
+      const u32x4 piece = v_fold[cm][d0 >> 3];
+      const uint32_t w[4] = {piece.x, piece.y, piece.z, piece.w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o[j] = fmaf(sm.fn[col], (j & 1) ? bf_hi(w[j >> 1]) : bf_lo(w[j >> 1]), o[j]);
     }
     const int h = kvh * G + col % G;
     if (partitions(p, member_len(cm)) <= 1) {
-      store_out(p, sc, h, d, o);
+      store_out8(p, sc, h, d0, o);
     } else {
       const size_t wrow = (size_t(sc) * p.num_q_heads + h) * p.max_parts + part;
-      p.ws_o[wrow * D + d] = o;
-      if (d == 0) {
+      *reinterpret_cast<f32x4*>(p.ws_o + wrow * D + d0) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(p.ws_o + wrow * D + d0 + 4) = f32x4{o[4], o[5], o[6], o[7]};
+      if (d0 == 0) {
         p.ws_ml[wrow * 2 + 0] = sm.M[col];
         p.ws_ml[wrow * 2 + 1] = sm.L[col];
       }
@@ -2197,18 +2233,26 @@ void decode_multi(MultiParams mp) {
     }
     __syncthreads();
     column_weights<D>(sm, ncols);
-    for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
-      const int col = idx / D;
-      const int d = idx - col * D;
-      const float o = weighted_o<D>(sm, d, col);
-      const int cc = cbase + col;
-      const int i = cc / G;
-      const int h = kvh * G + (cc - i * G);
-      if (!Split || nparts <= 1) {
-        store_out(p, r0 + i, h, d, o);
-      } else {  // this partition's piece of row r0 + i for the combine
+    if (!Split || nparts <= 1) {  // the output, eight dims per thread
+      for (int idx = threadIdx.x; idx < ncols * (D / 8); idx += kThreads) {
+        const int col = idx / (D / 8);
+        const int d0 = 8 * (idx - col * (D / 8));
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = weighted_o<D>(sm, d0 + j, col);
+        const int cc = cbase + col;
+        const int i = cc / G;
+        store_out8(p, r0 + i, kvh * G + (cc - i * G), d0, o);
+      }
+    } else {  // this partition's piece of each row for the combine
+      for (int idx = threadIdx.x; idx < ncols * D; idx += kThreads) {
+        const int col = idx / D;
+        const int d = idx - col * D;
+        const int cc = cbase + col;
+        const int i = cc / G;
+        const int h = kvh * G + (cc - i * G);
         const size_t wrow = (size_t(r0 + i) * p.num_q_heads + h) * p.max_parts + part;
-        p.ws_o[wrow * D + d] = o;
+        p.ws_o[wrow * D + d] = weighted_o<D>(sm, d, col);
         if (d == 0) {
           p.ws_ml[wrow * 2 + 0] = sm.M[col];
           p.ws_ml[wrow * 2 + 1] = sm.L[col];
