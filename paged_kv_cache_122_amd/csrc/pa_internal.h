@@ -2,6 +2,7 @@
 // (pa_kernels.hip).  Not part of the public ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
@@ -115,6 +116,8 @@ struct MultiParams {
 
 static_assert(sizeof(MultiParams) + sizeof(StreamParams) <= 4096,
               "kernel arguments stay within 4 KiB");
+static_assert(offsetof(DecodeParams, order) % 4 == 0 && kMaxOrder % 2 == 0,
+              "the order array is read two entries per 32-bit word");
 
 struct CopyParams {
   const int64_t* pairs;  // [N, 2] (src, dst) physical block ids

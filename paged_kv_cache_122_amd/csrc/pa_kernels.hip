@@ -1250,7 +1250,11 @@ __device__ __forceinline__ void finish_partition(const DecodeParams& p, Smem<D>&
 // more, unless the host ranked them (has_order 1).
 __device__ __forceinline__ int ranked_seq(const DecodeParams& p, int y) {
   const int S = p.num_seqs;
-  if (p.has_order == 1) return p.order[y];  // ranked on the host: no round trip to the lengths
+  if (p.has_order == 1) {  // ranked on the host: no round trip to the lengths
+    // a 32-bit read at a workgroup-uniform index: a scalar load
+    const uint32_t w = reinterpret_cast<const uint32_t*>(p.order)[y >> 1];
+    return int((y & 1) ? w >> 16 : w & 0xffffu);
+  }
   if (p.max_parts > 1 || S > kMaxDeviceRanked || p.max_len >= (1 << 22)) return y;
   __shared__ uint32_t keys[kMaxDeviceRanked];
   __shared__ int pick;
@@ -2084,12 +2088,16 @@ void decode_multi(MultiParams mp) {
     s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
     part = 0;
   }
+  // the table entries of the wave's first tiles depend only on the sequence
+  // and the partition: their load goes out beside the length's
+  const auto row = table_row(p, s, BS);
+  const TableCache first = fetch_table<BS>(row, (Split ? part * p.part_tokens : 0) >> 4, wave, 0, lane);
+  const int L = clamp_len(p, p.context_lens[s]);
   const int G = p.group;
   // this sequence's rows, kept inside [0, T); at most max_query_len of them
   // (no query_start: row s, one new token per sequence)
   const int r0 = mp.query_start ? min(max(mp.query_start[s], 0), mp.num_rows) : min(s, mp.num_rows);
   const int r1 = mp.query_start ? min(max(mp.query_start[s + 1], r0), mp.num_rows) : min(s + 1, mp.num_rows);
-  const int L = clamp_len(p, p.context_lens[s]);
   const int n = min(min(r1 - r0, L), mp.max_query_len);
   const int L_old = L - n;
   // split schedule: partition `part` of the cached tokens; the new tokens
@@ -2150,8 +2158,6 @@ void decode_multi(MultiParams mp) {
     return;
   }
 
-  const auto row = table_row(p, s, BS);
-  const TableCache first = fetch_table<BS>(row, t0 >> 4, wave, 0, lane);
   // column set cs: columns col0 + 16 cs + r; columns past the last query
   // compute with a zero query (never stored) and see every new token
   u32x4 q[NS][NC];
