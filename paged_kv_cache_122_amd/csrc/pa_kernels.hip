@@ -1093,10 +1093,14 @@ constexpr int kDeepSlots = 4;
 // Walk this wave's tiles (tiles wave, wave + 4, ... of the partition [t0, t1))
 // with the next S - 1 tiles' loads issued before the current one is
 // computed.  `first` holds the table entries of the wave's first 64 tiles.
-template <int D, int BS, int S, typename F>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+template <int D, int BS, int S, typename F, typename H = NoHook>
 __device__ __forceinline__ void walk_tiles(const DecodeParams& p, __amdgpu_buffer_rsrc_t row,
                                            TableCache first, int kvh, int t0, int t1, int wave,
-                                           int lane, F&& compute) {
+                                           int lane, F&& compute, H&& after_first_loads = H{}) {
   constexpr int NC = D / 32;
   const int ntiles = (t1 - t0 + 15) >> 4;
   const int n = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
@@ -1105,23 +1109,38 @@ __device__ __forceinline__ void walk_tiles(const DecodeParams& p, __amdgpu_buffe
   // chunk has padding tiles, and those lie past the context
   constexpr int kChunk = 64 / S * S;
   TableCache tc = first;
-  for (int k0 = 0; k0 < n; k0 += kChunk) {
-    if (k0 > 0) tc = fetch_table<BS>(row, t0 >> 4, wave, k0, lane);
-    const int m = min(kChunk, n - k0);
-    auto start = [&](int j) { return t0 + 16 * (wave + kWaves * (k0 + j)); };
-    auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
-      const int jj = min(j, m - 1);
-      const int b0 = __builtin_amdgcn_readlane(tc.e0, jj);
-      int b1 = 0;
-      if constexpr (BS == 8) {
-        // the second block of a tile whose tokens all lie in the first is not
-        // in the table: read the first again (its tokens are masked)
-        b1 = __builtin_amdgcn_readlane(tc.e1, jj);
-        b1 = start(jj) + 8 < t1 ? b1 : b0;
-      }
-      load_tile<D, BS>(p, kvh, b0, b1, start(jj), t1, j < m, lo, kt, vt);
-      __builtin_amdgcn_sched_barrier(0);
-    };
+  int k0 = 0;
+  int m = min(kChunk, n);
+  auto start = [&](int j) { return t0 + 16 * (wave + kWaves * (k0 + j)); };
+  auto load = [&](int j, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
+    const int jj = min(j, m - 1);
+    const int b0 = __builtin_amdgcn_readlane(tc.e0, jj);
+    int b1 = 0;
+    if constexpr (BS == 8) {
+      // the second block of a tile whose tokens all lie in the first is not
+      // in the table: read the first again (its tokens are masked)
+      b1 = __builtin_amdgcn_readlane(tc.e1, jj);
+      b1 = start(jj) + 8 < t1 ? b1 : b0;
+    }
+    load_tile<D, BS>(p, kvh, b0, b1, start(jj), t1, j < m, lo, kt, vt);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  u32x4 kk[S][NC], vv[S][NC];
+  // The first chunk's first loads sit ahead of the chunk loop, in straight
+  // code, so that they wait for the table entries alone, not for loads the
+  // caller issued after the table's (in-order counter); then the hook.
+  if (n > 0) {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) load(i, kk[i], vv[i]);
+  }
+  after_first_loads();
+  for (; k0 < n; k0 += kChunk) {
+    if (k0 > 0) {
+      tc = fetch_table<BS>(row, t0 >> 4, wave, k0, lane);
+      m = min(kChunk, n - k0);
+#pragma unroll
+      for (int i = 0; i < S - 1; ++i) load(i, kk[i], vv[i]);
+    }
     // The trip count is rounded up to whole rounds of S tiles: the extra tiles
     // lie past t1 (only the last chunk is short), load as zeros without
     // touching memory and add nothing.  A
@@ -1129,9 +1148,6 @@ __device__ __forceinline__ void walk_tiles(const DecodeParams& p, __amdgpu_buffe
     // state from both edges, so the compiler waits only for the tile it uses
     // and keeps S - 1 tiles' loads in flight throughout.
     const int rounds = (m + S - 1) / S;
-    u32x4 kk[S][NC], vv[S][NC];
-#pragma unroll
-    for (int i = 0; i < S - 1; ++i) load(i, kk[i], vv[i]);
     for (int j = 0; j < rounds * S; j += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
@@ -2088,16 +2104,21 @@ void decode_multi(MultiParams mp) {
     s = ranked_seq(p, blockIdx.y);  // longest contexts first, as decode
     part = 0;
   }
-  // the table entries of the wave's first tiles depend only on the sequence
-  // and the partition: their load goes out beside the length's
+  // This sequence's rows [qa, qb) (no query_start: row s, one new token per
+  // sequence), its length and the table entries of the wave's first tiles
+  // (they depend only on the sequence and the partition) load together.
+  int qa = s, qb = s + 1;
+  if (mp.query_start) {
+    qa = mp.query_start[s];
+    qb = mp.query_start[s + 1];
+  }
   const auto row = table_row(p, s, BS);
   const TableCache first = fetch_table<BS>(row, (Split ? part * p.part_tokens : 0) >> 4, wave, 0, lane);
   const int L = clamp_len(p, p.context_lens[s]);
   const int G = p.group;
-  // this sequence's rows, kept inside [0, T); at most max_query_len of them
-  // (no query_start: row s, one new token per sequence)
-  const int r0 = mp.query_start ? min(max(mp.query_start[s], 0), mp.num_rows) : min(s, mp.num_rows);
-  const int r1 = mp.query_start ? min(max(mp.query_start[s + 1], r0), mp.num_rows) : min(s + 1, mp.num_rows);
+  // the rows, kept inside [0, T); at most max_query_len of them
+  const int r0 = min(max(qa, 0), mp.num_rows);
+  const int r1 = min(max(qb, r0), mp.num_rows);
   const int n = min(min(r1 - r0, L), mp.max_query_len);
   const int L_old = L - n;
   // split schedule: partition `part` of the cached tokens; the new tokens
@@ -2109,25 +2130,27 @@ void decode_multi(MultiParams mp) {
   const int t1 = Split ? min(L_old, t0 + p.part_tokens) : L_old;
 
   // The column-group-0 workgroup appends this head's new tokens: its loads
-  // are issued first and its pool stores come after the walk, since pool
-  // stores ahead of it would hold the walk's pool loads back (loads are not
-  // moved across stores that may alias them).  One 16-byte piece per thread
-  // here, parked in LDS during the walk (only the thread that loaded a piece
-  // reads it back, so no barrier); pieces past the first kThreads are copied
-  // at the end.
+  // go out right after the walk's first tile loads and its pool stores come
+  // after the walk, since pool stores ahead of it would hold the walk's pool
+  // loads back (loads are not moved across stores that may alias them).  One
+  // 16-byte piece per thread here, parked in LDS during the walk (only the
+  // thread that loaded a piece reads it back, so no barrier); pieces past the
+  // first kThreads are copied at the end.
   __shared__ u32x4 park_k[kThreads], park_v[kThreads];
   __shared__ int64_t park_slot[kThreads];
   const int units = cg == 0 && last && mp.append_rows == 0 ? n * (D / 8) : 0;
   const int staged = min(units, kThreads);
   u32x4 app_k = {0u, 0u, 0u, 0u}, app_v = {0u, 0u, 0u, 0u};
   int64_t app_slot = -1;
-  if (int(threadIdx.x) < staged) {
-    const int i = threadIdx.x / (D / 8);
-    const int piece = threadIdx.x - i * (D / 8);
-    app_slot = mp.slots[r0 + i];
-    app_k = load16(mp.k_new + size_t(r0 + i) * mp.kn_t + size_t(kvh) * mp.kn_h + piece * 8);
-    app_v = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
-  }
+  auto load_new = [&]() {
+    if (int(threadIdx.x) < staged) {
+      const int i = threadIdx.x / (D / 8);
+      const int piece = threadIdx.x - i * (D / 8);
+      app_slot = mp.slots[r0 + i];
+      app_k = load16(mp.k_new + size_t(r0 + i) * mp.kn_t + size_t(kvh) * mp.kn_h + piece * 8);
+      app_v = load16(mp.v_new + size_t(r0 + i) * mp.vn_t + size_t(kvh) * mp.vn_h + piece * 8);
+    }
+  };
   auto append = [&](u32x4 k0, u32x4 v0, int64_t slot0) {
     uint16_t* kc = mp.k_store;
     uint16_t* vc = mp.v_store;
@@ -2154,6 +2177,7 @@ void decode_multi(MultiParams mp) {
   const int cols = n * G;             // (query, head) columns of this KV head
   const int col0 = 16 * NS * cg;      // first column of this workgroup
   if (col0 >= cols) {                 // workgroup-uniform; column group 0 only when n == 0
+    load_new();
     append(app_k, app_v, app_slot);
     return;
   }
@@ -2162,45 +2186,52 @@ void decode_multi(MultiParams mp) {
   // compute with a zero query (never stored) and see every new token
   u32x4 q[NS][NC];
   int qi[NS];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int cs = 0; cs < NS; ++cs) {
-    const int c = col0 + 16 * cs + r;
-    const bool ok = c < cols;
-    qi[cs] = ok ? c / G : n - 1;
-    const int qh = kvh * G + (ok ? c - qi[cs] * G : 0);
+    for (int cs = 0; cs < NS; ++cs) {
+      const int c = col0 + 16 * cs + r;
+      const bool ok = c < cols;
+      qi[cs] = ok ? c / G : n - 1;
+      const int qh = kvh * G + (ok ? c - qi[cs] * G : 0);
 #pragma unroll
-    for (int k = 0; k < NC; ++k) {
-      q[cs][k] = u32x4{0u, 0u, 0u, 0u};
-      if (ok) q[cs][k] = load16(p.q + size_t(r0 + qi[cs]) * p.q_s + size_t(qh) * p.q_h + 8 * (g4 + 4 * k));
+      for (int k = 0; k < NC; ++k) {
+        q[cs][k] = u32x4{0u, 0u, 0u, 0u};
+        if (ok) q[cs][k] = load16(p.q + size_t(r0 + qi[cs]) * p.q_s + size_t(qh) * p.q_h + 8 * (g4 + 4 * k));
+      }
     }
-  }
+  };
   MfmaAcc<D> acc[NS];
 #pragma unroll
   for (int cs = 0; cs < NS; ++cs) mfma_reset(acc[cs]);
-  // after the table and query loads, so that its wait covers the append's loads only
-  if (int(threadIdx.x) < staged) {
-    park_k[threadIdx.x] = app_k;
-    park_v[threadIdx.x] = app_v;
-    park_slot[threadIdx.x] = app_slot;
-  }
   // A single new tile whose pieces are all parked is taken from LDS, first,
   // by the wave the round robin over the waves gives it (the one after the
   // cached tiles' last): its loads then cost no trip to memory at the end of
   // the walk.  The softmax does not depend on the order, up to rounding.
   const int old_tiles = (t1 - t0 + 15) >> 4;
   const bool new_parked = last && n > 0 && n <= kTileTokens && staged == n * (D / 8);  // workgroup-uniform
-  if (new_parked) {
-    __syncthreads();  // every piece parked
-    if (wave == old_tiles % kWaves) {
-      u32x4 kt[NC], vt[NC];
-      parked_new_tile<D>(park_k, park_v, n, lane, kt, vt);
-#pragma unroll
-      for (int cs = 0; cs < NS; ++cs) mfma_tile_causal<D>(acc[cs], q[cs], p.scale_log2, 0, qi[cs], lane, kt, vt);
-    }
-  }
+  // The queries and the new tokens load once each wave's first tile loads
+  // are out: ahead of them they would hold those back by a round trip.
   walk_tiles<D, BS, kPipeSlots>(p, row, first, kvh, t0, t1, wave, lane,
                                            [&](int ts, u32x4(&kt)[NC], u32x4(&vt)[NC]) {
     mfma_tile_sets<D, NS>(acc, q, p.scale_log2, ts, t1, lane, kt, vt);
+  }, [&]() {
+    load_q();
+    load_new();
+    if (int(threadIdx.x) < staged) {
+      park_k[threadIdx.x] = app_k;
+      park_v[threadIdx.x] = app_v;
+      park_slot[threadIdx.x] = app_slot;
+    }
+    if (new_parked) {
+      __syncthreads();  // every piece parked (every wave comes here once)
+      if (wave == old_tiles % kWaves) {
+        u32x4 kt[NC], vt[NC];
+        parked_new_tile<D>(park_k, park_v, n, lane, kt, vt);
+#pragma unroll
+        for (int cs = 0; cs < NS; ++cs)
+          mfma_tile_causal<D>(acc[cs], q[cs], p.scale_log2, 0, qi[cs], lane, kt, vt);
+      }
+    }
   });
   // otherwise the new tiles (last partition) continue the cached tiles' round robin over the waves
   for (int u = (wave + kWaves - old_tiles % kWaves) % kWaves; last && !new_parked && 16 * u < n; u += kWaves) {
