@@ -62,26 +62,26 @@ KERNEL_SOURCES = ("paged_kv_cache_122_amd/csrc/pa_kernels.hip",
                   "paged_kv_cache_122_amd/csrc/pa_internal.h",
                   "paged_kv_cache_122_amd/csrc/pa_api.cpp")
 MEASURED_TRAFFIC = {
-    "sources_sha256": "b65aed74987ea8b6577397228e3c2f35bb29eac0d4f76344247172d635ce68e2",
-    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 756516, "write_bytes": 10240, "mfma_busy_pct": 0.04,
+    "sources_sha256": "a78e63885cda54f565cf45f9d73c6983e762ed90af6ac6cffb525d6d959bbb33",
+    "tiny_gqa4_d64 decode_multi<64,16,1,false>": {"fetch_bytes": 755244, "write_bytes": 10240, "mfma_busy_pct": 0.04,
         "source": "profiles/decode_multi_tiny_gqa4_d64_kernel_trace.md"},
-    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 273993911, "write_bytes": 1310742, "mfma_busy_pct": 7.92,
+    "llama3_8b_b64 decode_multi<128,16,1,false>": {"fetch_bytes": 274013388, "write_bytes": 1310815, "mfma_busy_pct": 7.83,
         "source": "profiles/decode_multi_llama3_8b_b64_kernel_trace.md"},
-    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 288029229, "write_bytes": 4458781, "mfma_busy_pct": 15.38,
+    "llama3_8b_verify5_b64 decode_multi<128,16,2,false>": {"fetch_bytes": 288025763, "write_bytes": 4459013, "mfma_busy_pct": 15.19,
         "source": "profiles/decode_multi_llama3_8b_verify5_b64_kernel_trace.md"},
-    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074949164, "write_bytes": 5559288, "mfma_busy_pct": 19.32,
+    "long32k_verify5_b16 decode_multi<128,16,2,true>": {"fetch_bytes": 1074929293, "write_bytes": 5559120, "mfma_busy_pct": 19.29,
         "source": "profiles/decode_multi_long32k_verify5_b16_kernel_trace.md"},
-    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907124596, "write_bytes": 7340032, "mfma_busy_pct": 9.45,
+    "llama3_70b_b256 decode_multi<128,16,1,false>": {"fetch_bytes": 907148406, "write_bytes": 7340032, "mfma_busy_pct": 9.53,
         "source": "profiles/decode_multi_llama3_70b_b256_kernel_trace.md"},
-    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745313521, "write_bytes": 5525034, "mfma_busy_pct": 9.61,
+    "opt13b_mha_prefix_b128 decode_shared<128,16,true>": {"fetch_bytes": 1745314425, "write_bytes": 5525013, "mfma_busy_pct": 9.61,
         "source": "profiles/decode_shared_opt13b_mha_prefix_b128_kernel_trace.md"},
-    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075070530, "write_bytes": 1163264, "mfma_busy_pct": 9.89,
+    "long32k_b8 decode_multi<128,8,1,true>": {"fetch_bytes": 1075091130, "write_bytes": 1163264, "mfma_busy_pct": 9.87,
         "source": "profiles/decode_multi_long32k_b8_kernel_trace.md"},
-    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074536745, "write_bytes": 1163364, "mfma_busy_pct": 9.8,
+    "long32k_b16 decode_multi<128,16,1,true>": {"fetch_bytes": 1074542504, "write_bytes": 1163442, "mfma_busy_pct": 9.88,
         "source": "profiles/decode_multi_long32k_b16_kernel_trace.md"},
-    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074266700, "write_bytes": 1163411, "mfma_busy_pct": 9.92,
+    "long32k_b32 decode_multi<128,32,1,true>": {"fetch_bytes": 1074271589, "write_bytes": 1163423, "mfma_busy_pct": 10.05,
         "source": "profiles/decode_multi_long32k_b32_kernel_trace.md"},
-    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350438960, "write_bytes": 1310720, "mfma_busy_pct": 7.62,
+    "opt13b_cow_fork_b128 decode_shared<128,16,true>": {"fetch_bytes": 350435452, "write_bytes": 1310720, "mfma_busy_pct": 7.57,
         "source": "profiles/decode_shared_opt13b_cow_fork_b128_kernel_trace.md"},
 }
 
