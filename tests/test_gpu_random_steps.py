@@ -36,8 +36,12 @@ def independent(rng, seed):
 
 
 def forks(rng, seed):
-    """Groups of samples forked from one prompt; each sample then appends its own
-    tokens (at least this step's), copying a shared, partly filled last block."""
+    """Groups of samples forked from one prompt whose last block is partly
+    filled.  About half the samples append their first own token this step:
+    each of those copies the shared last block now (this step's copies, done
+    by pa_copy_blocks before the append).  The others appended earlier tokens
+    and made their copies when the first of them arrived, so their blocks
+    already hold their own tokens."""
     hkv = int(rng.choice([1, 2, 4, 8]))
     g = int(rng.choice([1, 2, 4, 8]))
     d = int(rng.choice([64, 128]))
@@ -49,21 +53,26 @@ def forks(rng, seed):
     while groups * per * (prompt + 200) * hkv > BUDGET and groups > 1:
         groups -= 1
     tails = tails[:groups * per]
+    tails = [0 if z else t for t, z in zip(tails, rng.random(len(tails)) < 0.5)]
     need = groups * (workloads.blocks_for_tokens(prompt, b) + per) + sum(
         workloads.blocks_for_tokens(t + 1, b) for t in tails)
     nb = int(1.3 * need) + 8
     pool = BlockPool(nb, b, free_order=rng.permutation(nb))
-    tables, lens = [], []
+    tables, lens, copies = [], [], []
     for gi in range(groups):
         parent = Sequence()
         reserve_slots(pool, parent, prompt)
         children = [fork(pool, parent) for _ in range(per)]
         free(pool, parent)
         for j, child in enumerate(children):
-            reserve_slots(pool, child, tails[gi * per + j] + 1)
+            before = len(pool.pending_copies)
+            tail = tails[gi * per + j]
+            reserve_slots(pool, child, tail + 1)
+            if tail == 0:  # its first token arrives this step: so does its copy
+                copies += pool.pending_copies[before:]
             tables.append(child.table)
             lens.append(child.length)
-    copies = list(pool.pending_copies) or None
+    copies = copies or None
     w = workloads.build_workload(f"random_fork{seed}", seed, rng, num_q_heads=g * hkv, num_kv_heads=hkv,
                                  head_dim=d, block_size=b, num_blocks=nb, tables=tables, context_lens=lens,
                                  width=max(len(t) for t in tables), copies=copies)
@@ -83,6 +92,7 @@ def test_random_step(case):
     host = bool(rng.integers(0, 2))
     print(f"[random step {case}] {desc} host_lens={host}", flush=True)
     kst, vst, ref = oracle_step(w)
+    assert np.all(np.isfinite(ref)), f"{desc}: the workload puts poisoned slots inside a context"
     dw = dev.upload(w)
     span = w.table_width * w.block_size
     nb = pa.workspace_bytes(w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, span, 0)
