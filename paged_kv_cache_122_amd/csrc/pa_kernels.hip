@@ -1012,6 +1012,73 @@ __device__ __forceinline__ float lse_combine(const float* ml, const float* o, si
   return num / den;
 }
 
+// The first batch of lse_combine's pieces loaded before the piece count is
+// known: rows k < cap (cap <= kCombineBatch, rows the workspace holds for
+// this output, written or not), so that the loads go out beside the length's
+// instead of after it.  lse_combine_from then uses the first n of them.
+struct FirstPieces {
+  float m[kCombineBatch], l[kCombineBatch], x[kCombineBatch];
+};
+
+template <int D>
+__device__ __forceinline__ FirstPieces lse_first_pieces(const float* ml, const float* o, size_t row0,
+                                                        size_t stride, int cap, int d) {
+  FirstPieces f;
+#pragma unroll
+  for (int k = 0; k < kCombineBatch; ++k) {
+    f.m[k] = kNegInf;
+    f.l[k] = 0.f;
+    f.x[k] = 0.f;
+    if (k < cap) {  // uniform: rows past cap are not loaded (cap 0: no workspace, nothing read)
+      const size_t row = row0 + size_t(k) * stride;
+      f.m[k] = ml[row * 2];
+      f.l[k] = ml[row * 2 + 1];
+      f.x[k] = o[row * D + d];
+    }
+  }
+  return f;
+}
+
+template <int D>
+__device__ __forceinline__ float lse_combine_from(const FirstPieces& f, const float* ml, const float* o,
+                                                  size_t row0, size_t stride, int n, int d) {
+  float M = kNegInf, num = 0.f, den = 0.f;
+#pragma unroll
+  for (int k = 0; k < kCombineBatch; ++k) {
+    if (k < n) {
+      const float Mn = fmaxf(M, f.m[k]);
+      const float a = exp2f(M - Mn);
+      const float b = f.l[k] * exp2f(f.m[k] - Mn);
+      num = num * a + b * f.x[k];
+      den = den * a + b;
+      M = Mn;
+    }
+  }
+  for (int i0 = kCombineBatch; i0 < n; i0 += kCombineBatch) {
+    float m[kCombineBatch], l[kCombineBatch], x[kCombineBatch];
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      const bool live = i0 + k < n;
+      const size_t row = row0 + size_t(live ? i0 + k : 0) * stride;
+      m[k] = live ? ml[row * 2] : kNegInf;
+      l[k] = live ? ml[row * 2 + 1] : 0.f;
+      x[k] = live ? o[row * D + d] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kCombineBatch; ++k) {
+      if (i0 + k < n) {
+        const float Mn = fmaxf(M, m[k]);
+        const float a = exp2f(M - Mn);
+        const float b = l[k] * exp2f(m[k] - Mn);
+        num = num * a + b * x[k];
+        den = den * a + b;
+        M = Mn;
+      }
+    }
+  }
+  return num / den;
+}
+
 // Combine the pieces of every pair cut between waves, and write zeros for
 // empty contexts.  One workgroup per (sequence, head group) pair.
 template <int D>
@@ -2308,15 +2375,27 @@ __global__ __launch_bounds__(256) void combine_rows(MultiParams mp) {
   const int s = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.num_q_heads * D) return;
-  const int r0 = mp.query_start ? min(max(mp.query_start[s], 0), mp.num_rows) : min(s, mp.num_rows);
-  const int r1 = mp.query_start ? min(max(mp.query_start[s + 1], r0), mp.num_rows) : min(s + 1, mp.num_rows);
+  int qa = s, qb = s + 1;
+  if (mp.query_start) {
+    qa = mp.query_start[s];
+    qb = mp.query_start[s + 1];
+  }
   const int L = clamp_len(p, p.context_lens[s]);
+  const int r0 = min(max(qa, 0), mp.num_rows);
+  const int r1 = min(max(qb, r0), mp.num_rows);
+  const int h = idx / D;
+  const int d = idx - h * D;
+  // this thread's first row (grid z strides over the rows): its pieces load
+  // beside the length's
+  const int i0 = blockIdx.z;
+  const bool has_first = i0 < min(r1 - r0, mp.max_query_len);
+  const size_t first_row0 = (size_t(has_first ? r0 + i0 : 0) * p.num_q_heads + h) * p.max_parts;
+  const FirstPieces f = lse_first_pieces<D>(p.ws_ml, p.ws_o, first_row0, 1, (p.ws_ml ? min(p.max_parts, kCombineBatch) : 0), d);
   const int n = min(min(r1 - r0, L), mp.max_query_len);
   const int nparts = multi_parts(p, L - n);
   if (nparts <= 1) return;  // the kernel wrote these rows directly
-  const int h = idx / D;
-  const int d = idx - h * D;
-  for (int i = blockIdx.z; i < n; i += gridDim.z) {
+  if (i0 < n) store_out(p, r0 + i0, h, d, lse_combine_from<D>(f, p.ws_ml, p.ws_o, first_row0, 1, nparts, d));
+  for (int i = i0 + gridDim.z; i < n; i += gridDim.z) {
     const size_t row0 = (size_t(r0 + i) * p.num_q_heads + h) * p.max_parts;
     store_out(p, r0 + i, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
   }
@@ -2328,12 +2407,13 @@ __global__ __launch_bounds__(256) void combine_parts(DecodeParams p) {
   const int s = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= p.num_q_heads * D) return;
-  const int nparts = partitions(p, p.context_lens[s]);
-  if (nparts <= 1) return;  // the decode kernel wrote this row directly
   const int h = idx / D;
   const int d = idx - h * D;
   const size_t row0 = (size_t(s) * p.num_q_heads + h) * p.max_parts;
-  store_out(p, s, h, d, lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, nparts, d));
+  const FirstPieces f = lse_first_pieces<D>(p.ws_ml, p.ws_o, row0, 1, (p.ws_ml ? min(p.max_parts, kCombineBatch) : 0), d);
+  const int nparts = partitions(p, p.context_lens[s]);
+  if (nparts <= 1) return;  // the decode kernel wrote this row directly
+  store_out(p, s, h, d, lse_combine_from<D>(f, p.ws_ml, p.ws_o, row0, 1, nparts, d));
 }
 
 // The same combine after decode_shared's fused step, which also stores the
@@ -2358,14 +2438,16 @@ __global__ __launch_bounds__(256) void combine_append(MultiParams mp) {
     vv = load16(mp.v_new + size_t(s) * mp.vn_t + size_t(ah) * mp.vn_h + piece * 8);
   }
   // rows whose context is split; the decode kernel wrote the others directly
-  const bool out = idx < p.num_q_heads * D && partitions(p, p.context_lens[s]) > 1;
   const int h = idx / D;
   const int d = idx - h * D;
+  const bool thread_out = idx < p.num_q_heads * D;
+  const size_t row0 = (size_t(s) * p.num_q_heads + (thread_out ? h : 0)) * p.max_parts;
+  const FirstPieces f = lse_first_pieces<D>(p.ws_ml, p.ws_o, row0, 1, (p.ws_ml ? min(p.max_parts, kCombineBatch) : 0),
+                                            thread_out ? d : 0);
+  const int nparts = partitions(p, p.context_lens[s]);
+  const bool out = thread_out && nparts > 1;
   float o = 0.f;
-  if (out) {
-    const size_t row0 = (size_t(s) * p.num_q_heads + h) * p.max_parts;
-    o = lse_combine<D>(p.ws_ml, p.ws_o, row0, 1, partitions(p, p.context_lens[s]), d);
-  }
+  if (out) o = lse_combine_from<D>(f, p.ws_ml, p.ws_o, row0, 1, nparts, d);
   if (app) write_slot_piece<D, BS>(mp.k_store, mp.v_store, p.num_kv_heads, slot, ah, piece, kv, vv);
   if (out) store_out(p, s, h, d, o);
 }
