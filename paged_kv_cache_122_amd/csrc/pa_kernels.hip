@@ -2029,6 +2029,13 @@ __device__ __forceinline__ void append_piece(const MultiParams& mp, int64_t u) {
   const int64_t i64 = u / per_row;
   if (i64 >= mp.num_rows) return;
   const int i = int(i64);
+  const int rem = int(u - i64 * per_row);
+  const int h = rem / (D / 8);
+  const int piece = rem - h * (D / 8);
+  // the piece and its slot depend only on the row: their loads go out first
+  const int64_t slot = mp.slots[i];
+  const u32x4 kv = load16(mp.k_new + size_t(i) * mp.kn_t + size_t(h) * mp.kn_h + piece * 8);
+  const u32x4 vv = load16(mp.v_new + size_t(i) * mp.vn_t + size_t(h) * mp.vn_h + piece * 8);
   int s = i, r0 = i, r1 = i + 1;  // no query_start: row s is sequence s's one new token
   if (mp.query_start) {
     // the last sequence whose rows start at or before row i (query_start is
@@ -2048,13 +2055,7 @@ __device__ __forceinline__ void append_piece(const MultiParams& mp, int64_t u) {
   }
   const int n = min(min(r1 - r0, clamp_len(p, p.context_lens[s])), mp.max_query_len);
   if (i - r0 >= n) return;
-  const int rem = int(u - i64 * per_row);
-  const int h = rem / (D / 8);
-  const int piece = rem - h * (D / 8);
-  const int64_t slot = mp.slots[i];
   if (slot < 0 || slot >= mp.num_slots) return;
-  const u32x4 kv = load16(mp.k_new + size_t(i) * mp.kn_t + size_t(h) * mp.kn_h + piece * 8);
-  const u32x4 vv = load16(mp.v_new + size_t(i) * mp.vn_t + size_t(h) * mp.vn_h + piece * 8);
   write_slot_piece<D, BS>(mp.k_store, mp.v_store, mp.d.num_kv_heads, slot, h, piece, kv, vv);
 }
 
@@ -2458,15 +2459,23 @@ __global__ __launch_bounds__(256) void combine_append(MultiParams mp) {
 template <int D, int BS>
 __global__ __launch_bounds__(256) void append_kernel(AppendParams p) {
   const int i = blockIdx.x;
-  const int64_t slot = p.slots[i];
-  if (slot < 0) return;
   const int units = p.num_kv_heads * (D / 8);
-  for (int u = blockIdx.y * blockDim.x + threadIdx.x; u < units; u += gridDim.y * blockDim.x) {
+  const int u0 = blockIdx.y * blockDim.x + threadIdx.x;
+  auto load = [&](int u, u32x4& kv, u32x4& vv) {
     const int h = u / (D / 8);
     const int piece = u - h * (D / 8);
-    const u32x4 kv = load16(p.k + size_t(i) * p.k_t + size_t(h) * p.k_h + piece * 8);
-    const u32x4 vv = load16(p.v + size_t(i) * p.v_t + size_t(h) * p.v_h + piece * 8);
-    write_slot_piece<D, BS>(p.k_cache, p.v_cache, p.num_kv_heads, slot, h, piece, kv, vv);
+    kv = load16(p.k + size_t(i) * p.k_t + size_t(h) * p.k_h + piece * 8);
+    vv = load16(p.v + size_t(i) * p.v_t + size_t(h) * p.v_h + piece * 8);
+  };
+  // the first piece loads beside the slot, not after it
+  const int64_t slot = p.slots[i];
+  u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+  if (u0 < units) load(u0, kv, vv);
+  if (slot < 0) return;
+  for (int u = u0; u < units; u += gridDim.y * blockDim.x) {
+    if (u != u0) load(u, kv, vv);
+    const int h = u / (D / 8);
+    write_slot_piece<D, BS>(p.k_cache, p.v_cache, p.num_kv_heads, slot, h, u - h * (D / 8), kv, vv);
   }
 }
 
