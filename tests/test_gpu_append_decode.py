@@ -170,14 +170,17 @@ def test_append_decode_block_sizes(b, d, hq, hkv):
     assert_close(out.double().cpu().numpy(), ref, f"ad_b{b}")
 
 
+@pytest.mark.parametrize("part", [256, 32])
 @pytest.mark.parametrize("g,d,b", [(1, 128, 16), (4, 64, 8), (16, 128, 32)], ids=["mha", "gqa4_d64_b8", "gqa16_b32"])
-def test_append_decode_shared_step_edges(g, d, b):
+def test_append_decode_shared_step_edges(g, d, b, part):
     """The partitioned step whose shared-partition kernel takes the append, at
-    partitions of 256 tokens: contexts of one token (nothing read from the
-    pool), lengths on and either side of partition boundaries (the new token
-    alone in the last partition, or ending it), empty sequences (slot -1) and
-    random ones; 40 sequences x 8 KV heads, so the schedule does not take the
-    deep pipeline.  Pools bit-exact, every row against the oracle."""
+    partitions of 256 tokens (and of 32, so that the combine joins up to 35
+    pieces of a row, more than one batch of its loads): contexts of one token
+    (nothing read from the pool), lengths on and either side of partition
+    boundaries (the new token alone in the last partition, or ending it),
+    empty sequences (slot -1) and random ones; 40 sequences x 8 KV heads, so
+    the schedule does not take the deep pipeline.  Pools bit-exact, every row
+    against the oracle, and the route is the shared step and its combine."""
     torch = need_gpu()
     from paged_kv_cache_122_amd import _lib as pa
     from paged_kv_cache_122_amd import device as dev
@@ -190,11 +193,13 @@ def test_append_decode_shared_step_edges(g, d, b):
     w = workloads.build_workload(f"shared_step_g{g}", 1300 + g, rng, num_q_heads=8 * g, num_kv_heads=8, head_dim=d,
                                  block_size=b, num_blocks=nb, tables=tables, context_lens=lens,
                                  width=max(len(t) for t in tables))
-    print(f"[shared_step G={g} D={d} B={b}] S={w.num_seqs}", flush=True)
+    print(f"[shared_step G={g} D={d} B={b} part={part}] S={w.num_seqs}", flush=True)
     dw = dev.upload(w)
     kst, vst, ref = oracle_step(w)
     out = torch.full(dw.q.shape, float("nan"), dtype=torch.float32, device="cuda")
-    _run(pa, dw, w, out, {"partition_tokens": 256})
+    _run(pa, dw, w, out, {"partition_tokens": part})
+    route = pa.last_launch()
+    assert route[0].startswith("decode_shared<") and route[-1].startswith("combine_append<"), route
     assert np.array_equal(dev.bf16_bits(dw.k_cache[dw.owned]), kst.blocks), "K pool differs"
     assert np.array_equal(dev.bf16_bits(dw.v_cache[dw.owned]), vst.blocks), "V pool differs"
     got = out.double().cpu().numpy()
